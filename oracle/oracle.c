@@ -1,0 +1,182 @@
+/*
+ * CPU oracle for the dense fp16 GEMM  C[M,N] = A[M,K] . B[K,N].
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's
+ * CPU-baseline leg may call this; the GPU library never does, and this file
+ * shares no code with it.
+ *
+ * What it computes is the definition, written out as the plain triple loop
+ * over output row i, output column j and reduction index k that the tiling
+ * tutorial ("Matrix multiplication and memory-access optimisation", section
+ * 02, the straightforward implementation) and the TileLang tutorial (ch. 14,
+ * rung 1, the defining triple loop) give:
+ *
+ *     C[i,j] = fp16_rne( sum_{k=0}^{K-1} A[i,k] * B[k,j] )
+ *
+ *   - Operands are read through element strides, as in the Triton article's
+ *     section "shape gives meaning, stride gives addresses":
+ *       A[i,k] = A[i*lda_m + k*lda_k],  B[k,j] = B[k*ldb_k + j*ldb_n],
+ *       C[i,j] = C[i*ldc + j]  (the output's own row stride).
+ *   - Every offset is formed in int64 before multiplying (same article,
+ *     section "addresses and bounds in one short kernel": 65536*65536 must be
+ *     2^32, not an int32 wrap to 0).
+ *   - The sum runs over exactly k = 0..K-1 (no padding, no modulo), from +0.0,
+ *     in ascending k, in binary64.  Products of two binary16 values have at
+ *     most 22 significant bits, so each product is exact in binary64; the
+ *     accumulated error is at most K * 2^-53 * sum|a*b|, far below half an
+ *     fp16 ulp of the result for the workloads here.
+ *   - One rounding to binary16 at the end, roundTiesToEven (the Triton
+ *     article's precision paragraph: fp16 inputs, wider accumulation, a final
+ *     conversion that may round or overflow; the rounding mode is IEEE 754's
+ *     default, ties to even, and overflow gives +-inf).
+ *
+ * Build: gcc -O2 -ffp-contract=off (no -ffast-math).
+ */
+#include <pthread.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- IEEE 754 binary16 codec, written from the format definition --------
+ * binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-24
+ *   exponent 1..30  : normal,    value = (1024 + fraction) * 2^(exponent-25)
+ *   exponent 31     : fraction 0 -> infinity, otherwise NaN             */
+
+double orc_f16_to_f64(uint16_t h) {
+  uint64_t sign = (uint64_t)(h >> 15) << 63;
+  uint32_t e = (h >> 10) & 0x1F;
+  uint32_t f = h & 0x3FF;
+  uint64_t bits;
+  double out;
+  if (e == 0) {
+    out = (double)f * 0x1p-24; /* exact: f < 2^10 */
+    return (h >> 15) ? -out : out;
+  }
+  if (e == 31) {
+    bits = sign | (0x7FFull << 52) | ((uint64_t)f << 42) | (f ? (1ull << 51) : 0);
+  } else {
+    /* normal: 1.f * 2^(e-15): binary64 exponent field e - 15 + 1023 */
+    bits = sign | ((uint64_t)(e - 15 + 1023) << 52) | ((uint64_t)f << 42);
+  }
+  memcpy(&out, &bits, sizeof out);
+  return out;
+}
+
+/* Nearest binary16 to a binary64 value, ties to even, by integer rounding of
+ * the binary64 significand at the binary16 quantum. */
+uint16_t orc_f64_to_f16(double x) {
+  uint64_t b;
+  memcpy(&b, &x, sizeof b);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  int ex = (int)((b >> 52) & 0x7FF);
+  uint64_t frac = b & ((1ull << 52) - 1);
+  if (ex == 0x7FF) return (uint16_t)(sign | (frac ? 0x7E00u : 0x7C00u));
+  if (ex == 0) return sign; /* binary64 zero or subnormal: far below 2^-25 */
+  int e = ex - 1023;                         /* x = sig * 2^(e-52) */
+  uint64_t sig = (1ull << 52) | frac;
+  int qe = (e < -14 ? -14 : e) - 10;         /* binary16 quantum exponent */
+  int shift = qe - (e - 52);                 /* >= 42 */
+  if (shift >= 64) return sign;              /* below a quarter quantum */
+  uint64_t q = sig >> shift;
+  uint64_t rem = sig & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1;
+  if (e < -14) {
+    /* subnormal quantum 2^-24; q == 1024 is the smallest normal, whose
+     * encoding 0x0400 is numerically the same as q. */
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  int E = e;
+  if (q == 2048) { q = 1024; E += 1; }       /* carry into the next binade */
+  if (E + 15 >= 31) return (uint16_t)(sign | 0x7C00u);
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024));
+}
+
+/* One output element: the defining sum, ascending k, binary64. */
+static double orc_dot(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                      int64_t ldb_k, int64_t ldb_n, int64_t i, int64_t j, int64_t K) {
+  double s = 0.0;
+  for (int64_t k = 0; k < K; ++k)
+    s += orc_f16_to_f64(A[i * lda_m + k * lda_k]) * orc_f16_to_f64(B[k * ldb_k + j * ldb_n]);
+  return s;
+}
+
+typedef struct {
+  const uint16_t* A; int64_t lda_m, lda_k;
+  const uint16_t* B; int64_t ldb_k, ldb_n;
+  uint16_t* C; int64_t ldc;
+  double* S;                 /* optional unrounded sums, [M][N] contiguous */
+  int64_t M, N, K;
+  const int64_t* pi;         /* point mode: output coordinates */
+  const int64_t* pj;
+  int64_t npts;
+  int nthreads, tid;
+} orc_job;
+
+static void* orc_rows(void* p) {
+  orc_job* j = (orc_job*)p;
+  for (int64_t i = j->tid; i < j->M; i += j->nthreads)
+    for (int64_t c = 0; c < j->N; ++c) {
+      double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, i, c, j->K);
+      j->C[i * j->ldc + c] = orc_f64_to_f16(s);
+      if (j->S) j->S[i * j->N + c] = s;
+    }
+  return NULL;
+}
+
+static void* orc_points(void* p) {
+  orc_job* j = (orc_job*)p;
+  for (int64_t t = j->tid; t < j->npts; t += j->nthreads) {
+    double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, j->pi[t], j->pj[t], j->K);
+    j->C[t] = orc_f64_to_f16(s);
+    if (j->S) j->S[t] = s;
+  }
+  return NULL;
+}
+
+static void orc_run(orc_job* proto, void* (*fn)(void*)) {
+  int n = proto->nthreads < 1 ? 1 : (proto->nthreads > 512 ? 512 : proto->nthreads);
+  pthread_t th[512];
+  orc_job jobs[512];
+  for (int t = 0; t < n; ++t) { jobs[t] = *proto; jobs[t].nthreads = n; jobs[t].tid = t; }
+  int started = 0;
+  for (int t = 1; t < n; ++t) {
+    if (pthread_create(&th[t], NULL, fn, &jobs[t]) != 0) break;
+    started = t;
+  }
+  fn(&jobs[0]);
+  for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+  for (int t = started + 1; t < n; ++t) fn(&jobs[t]);
+}
+
+/* Full product.  Threads take interleaved output rows; every element is the
+ * same sequential sum whichever thread computes it.  S may be NULL.
+ * Returns 0, or -1 for arguments outside the contract (sizes <= 0, NULL). */
+int orc_gemm_f16(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                 int64_t ldb_k, int64_t ldb_n, uint16_t* C, int64_t ldc, double* S,
+                 int64_t M, int64_t N, int64_t K, int nthreads) {
+  if (!A || !B || !C || M <= 0 || N <= 0 || K <= 0) return -1;
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, S, M, N, K, NULL, NULL, 0, nthreads, 0};
+  orc_run(&j, orc_rows);
+  return 0;
+}
+
+/* Selected outputs: out[t] = C[pi[t], pj[t]] (and S[t] its unrounded sum). */
+int orc_gemm_f16_points(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                        int64_t ldb_k, int64_t ldb_n, int64_t K, const int64_t* pi,
+                        const int64_t* pj, int64_t npts, uint16_t* out, double* S,
+                        int nthreads) {
+  if (!A || !B || !out || !pi || !pj || K <= 0 || npts < 0) return -1;
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, out, 0, S, 0, 0, K, pi, pj, npts, nthreads, 0};
+  orc_run(&j, orc_points);
+  return 0;
+}
+
+/* Array forms of the codec, for the tests that sweep all 65536 patterns. */
+void orc_f16_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t t = 0; t < n; ++t) out[t] = orc_f16_to_f64(in[t]);
+}
+
+void orc_f64_to_f16_array(const double* in, uint16_t* out, int64_t n) {
+  for (int64_t t = 0; t < n; ++t) out[t] = orc_f64_to_f16(in[t]);
+}

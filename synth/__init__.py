@@ -1,0 +1,130 @@
+"""Seeded synthetic fp16 inputs, shared by the GPU tests, the CPU oracle and
+the benchmark.
+
+This package holds no matrix-multiply arithmetic: it only maps
+(seed, tensor id, logical row, logical column) to a binary16 bit pattern with
+a counter-based hash (SplitMix64, Steele, Lea and Flood, OOPSLA 2014), so any
+element can be regenerated independently of how the matrix is stored.  A
+matrix generated in row-major storage and the same matrix generated as a
+transposed view hold identical logical values.
+
+Modes:
+  "uniform": U(-1, 1) drawn on the odd multiples of 2^-24, rounded to fp16
+             with ties to even (the pages' workloads draw fp16 operands
+             uniformly in [-1, 1]).
+  "int":     integers in [-4, 4], exact in fp16 (for bit-exact checks).
+
+`gen.c` is the fast path (threads over rows); `reference_rows` is a numpy
+restatement of the same definition used to pin it.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gen.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+MODES = {"uniform": 0, "int": 1}
+TENSOR_A, TENSOR_B = 0, 1
+
+_lib = None
+
+
+def build():
+    """Compile gen.c into libsynth.so next to it (gcc, no GPU involved)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.synth_fill.restype = ctypes.c_int
+        lib.synth_fill.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+            ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def host_threads():
+    return len(os.sched_getaffinity(0))
+
+
+def fill(dst, rows, cols, rs, cs, seed, tensor, mode="uniform", row0=0, row_index=None,
+         nthreads=None):
+    """Write logical element (row, c) of the (seed, tensor) matrix to
+    dst.flat[r*rs + c*cs] for r in [0, rows).  The logical row is
+    row_index[r] when row_index is given, else row0 + r.  `dst` is a
+    uint16 numpy array (any shape, C-contiguous storage is addressed flat)."""
+    assert dst.dtype == np.uint16 and dst.flags["C_CONTIGUOUS"]
+    if rows > 0 and cols > 0:
+        last = (rows - 1) * rs + (cols - 1) * cs
+        assert 0 <= last < dst.size, "fill would write outside dst"
+    idx = None
+    if row_index is not None:
+        idx = np.ascontiguousarray(row_index, dtype=np.int64)
+        assert idx.shape == (rows,)
+    rc = _load().synth_fill(
+        dst.ctypes.data, rows, cols, rs, cs, row0,
+        None if idx is None else idx.ctypes.data,
+        seed & 0xFFFFFFFFFFFFFFFF, tensor, MODES[mode], nthreads or host_threads())
+    if rc != 0:
+        raise ValueError("synth_fill rejected its arguments")
+    return dst
+
+
+def matrix(rows, cols, seed, tensor, mode="uniform", order="row", nthreads=None):
+    """The logical [rows, cols] matrix as uint16 fp16 bits.
+
+    order="row": returned array has shape (rows, cols) (row-major storage).
+    order="col": returned array has shape (cols, rows) and holds the
+    transpose, i.e. the storage of a transposed view with strides (1, rows)."""
+    if order == "row":
+        out = np.empty((rows, cols), dtype=np.uint16)
+        return fill(out, rows, cols, cols, 1, seed, tensor, mode, nthreads=nthreads)
+    if order == "col":
+        out = np.empty((cols, rows), dtype=np.uint16)
+        return fill(out, rows, cols, 1, rows, seed, tensor, mode, nthreads=nthreads)
+    raise ValueError(order)
+
+
+def rows_of(row_index, cols, seed, tensor, mode="uniform", nthreads=None):
+    """Selected logical rows (len(row_index), cols) of the (seed, tensor) matrix."""
+    idx = np.ascontiguousarray(row_index, dtype=np.int64)
+    out = np.empty((idx.size, cols), dtype=np.uint16)
+    return fill(out, idx.size, cols, cols, 1, seed, tensor, mode, row_index=idx,
+                nthreads=nthreads)
+
+
+# ---------------------------------------------------------------------------
+# numpy restatement of the same definition (used only to pin gen.c)
+
+_M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
+
+
+def _sm(x):
+    with np.errstate(over="ignore"):
+        z = (x + np.uint64(0x9E3779B97F4A7C15)) & _M64
+        z = ((z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)) & _M64
+        z = ((z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)) & _M64
+        return z ^ (z >> np.uint64(31))
+
+
+def reference_rows(row_index, cols, seed, tensor, mode="uniform"):
+    rows = np.asarray(row_index, dtype=np.uint64).reshape(-1, 1)
+    base_t = _sm(_sm(np.uint64(seed)) ^ np.uint64(tensor))
+    h = _sm(_sm(base_t ^ rows) ^ np.arange(cols, dtype=np.uint64).reshape(1, -1))
+    top = (h >> np.uint64(40)).astype(np.int64)
+    if mode == "int":
+        vals = (top % 9 - 4).astype(np.float32)
+    else:
+        vals = ((2 * top + 1 - (1 << 24)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+    return vals.astype(np.float16).view(np.uint16)
