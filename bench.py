@@ -1,0 +1,198 @@
+"""Benchmark of the fp16 GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the library's C-ABI (host validation and dispatch, then
+the kernel or kernels the plan picks) on the MoE-derived dense GEMM
+131072 x 2048 x 7168 (A [M,K] and B [K,N] row-major, U(-1,1) fp16 from the
+seeded generator, fp32 accumulation, fp16 C), with inputs resident in HBM.
+Prints one JSON line: throughput in TFLOPS of useful 2MNK work, the roofline
+of the dominant kernel (MFMA-bound: fraction of the dense fp16 peak), the
+CPU oracle timed on a bounded row sample, and the decode-shaped M = 1 case
+(N = 2048, K = 7168) in GB/s of algorithmic bytes against HBM bandwidth.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS & %MFMA peak, fp16 GEMM 131072x2048x7168; GB/s at M=1"
+PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PAGES_TFLOPS = 117.250897     # the pages' TileLang kernel on MetaX C500, same workload
+M, N, K = 131072, 2048, 7168
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skinny-reps", type=int, default=200)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_tiled_gemm_fp16_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kind)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def timed_launches(fn, stream, steps, warmup):
+    """Per-launch durations (ms) from HIP events recorded on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+
+
+def cpu_baseline(budget_s=15.0):
+    """The CPU oracle (as is) on whole output rows of the same product."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = oracle.threads()
+    B = synth.matrix(K, N, 4001, synth.TENSOR_B)
+
+    def rows_time(r):
+        A = synth.rows_of(np.arange(r), K, 4001, synth.TENSOR_A)
+        t = time.perf_counter()
+        oracle.gemm(A, (K, 1), B, (N, 1), r, N, K, nthreads=threads)
+        return time.perf_counter() - t
+
+    pilot = rows_time(threads)
+    rows = int(max(threads, min(4096, threads * round(budget_s / max(pilot, 1e-3)))))
+    dt = rows_time(rows)
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product ({rows}x{N} outputs, "
+                      f"full K), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this GEMM build "
+              "has no multi-GPU path; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dense_tiled_gemm_fp16_amd as g
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+
+    # ---- headline workload
+    a = to_dev(synth.matrix(M, K, 4001, synth.TENSOR_A))
+    b = to_dev(synth.matrix(K, N, 4001, synth.TENSOR_B))
+    c = torch.empty((M, N), dtype=torch.float16, device=dev)
+    plan = g.plan(a, b, c)
+    ws = None
+    if plan["workspace_bytes"]:
+        ws = torch.empty(plan["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        g.gemm(a, b, out=c, workspace=ws, stream=stream)
+
+    durs, wall = timed_launches(step, stream, args.steps, args.warmup)
+    flops = 2.0 * M * N * K
+    ms = sum(durs) / len(durs)
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic("main_131072x2048x7168")
+
+    # ---- decode-shaped M = 1
+    m1 = 1
+    copies = 40                                   # 40 x 28 MiB of B > 1 GiB
+    a1 = to_dev(synth.matrix(m1, K, 3001, synth.TENSOR_A))
+    b1 = to_dev(synth.matrix(K, N, 3001, synth.TENSOR_B))
+    bs = [b1.clone() for _ in range(copies)]
+    c1 = torch.empty((m1, N), dtype=torch.float16, device=dev)
+    p1 = g.plan(a1, b1, c1)
+    ws1 = None
+    if p1["workspace_bytes"]:
+        ws1 = torch.empty(p1["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+    it = [0]
+
+    def step1():
+        g.gemm(a1, bs[it[0] % copies], out=c1, workspace=ws1, stream=stream)
+        it[0] += 1
+
+    d1, _ = timed_launches(step1, stream, args.skinny_reps, 20)
+    d1.sort()
+    med1 = d1[len(d1) // 2]
+    bytes1 = 2.0 * (m1 * K + K * N + m1 * N)
+    skinny = {"workload": f"M={m1} N={N} K={K}, B rotated over {copies} copies",
+              "plan": {k: p1[k] for k in ("variant", "tile_m", "tile_n", "split_k", "grid",
+                                           "grid2")},
+              "median_us": med1 * 1e3, "GBps": bytes1 / (med1 * 1e-3) / 1e9,
+              "frac_hbm": bytes1 / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+              "timing": "HIP events around each call on its stream (all launches of the call)"}
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(tflops / PAGES_TFLOPS, 3), "dtype": "f16",
+        "data": "synthetic (seeded U(-1,1) fp16, counter-based generator)",
+        "config": {"workload": "MoE-derived dense GEMM 131072x2048x7168 fp16, fp32 accumulate",
+                   "M": M, "N": N, "K": K, "a_layout": "row-major", "b_layout": "row-major",
+                   "plan": {k: plan[k] for k in ("variant", "tile_m", "tile_n", "tile_k",
+                                                 "split_k", "panel", "a_path", "b_path",
+                                                 "grid")}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+                     "traffic": traffic},
+        "timing": {"method": "HIP events around each launch on its stream",
+                   "median_ms": sorted(durs)[len(durs) // 2], "min_ms": min(durs),
+                   "wall_s": wall},
+        "skinny_m1": skinny,
+        "vs_baseline_ref": "pages' TileLang kernel on MetaX C500, 117.25 TFLOPS (context only)",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,99 @@
+"""dense_tiled_gemm_fp16_amd: C = A.B for fp16 matrices on MI355X (gfx950).
+
+The computation runs in libgemmf16.so (hand-written HIP, C-ABI in
+include/gemm_f16.h).  This package only marshals arguments: torch supplies
+device memory and the current stream.
+
+    gemm(a, b, out=None, ...)      -> C (torch.float16, [M, N])
+    plan(a, b, out=None, ...)      -> dict describing the kernel that would run
+    workspace_bytes(M, N, K, ...)  -> bytes of split-K workspace needed
+"""
+import ctypes
+
+import torch
+
+from ._lib import (GEMM_OK, LIB_PATH, PATHS, STATUS, VARIANTS, Opts, PlanInfo, lib, make_opts,
+                   status_string)
+
+__all__ = ["gemm", "gemm_raw", "plan", "workspace_bytes", "GemmError", "LIB_PATH", "VARIANTS"]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, rc):
+        super().__init__(f"{STATUS.get(rc, rc)}: {status_string(rc)}")
+        self.status = rc
+
+
+def _check(a, b, out):
+    # Argument checks in the spirit of the Triton article's wrapper (section
+    # "addresses and bounds in one short kernel"); the library re-validates.
+    if a.ndim != 2 or b.ndim != 2:
+        raise ValueError("expected two matrices")
+    if not a.is_cuda or not b.is_cuda or a.device != b.device:
+        raise ValueError("inputs must share one GPU device")
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("only float16 inputs are supported")
+    m, k = a.shape
+    kb, n = b.shape
+    if k != kb or min(m, n, k) <= 0:
+        raise ValueError("incompatible or empty shape")
+    if min(a.stride() + b.stride()) <= 0:
+        raise ValueError("strides must be positive")
+    if out is None:
+        out = torch.empty((m, n), device=a.device, dtype=torch.float16)
+    else:
+        if out.dtype != torch.float16 or out.device != a.device or out.shape != (m, n):
+            raise ValueError("out must be a float16 [M, N] tensor on the inputs' device")
+        if out.stride(1) != 1 or out.stride(0) < n:
+            raise ValueError("out must be row-major with unit column stride")
+    return m, n, k, out
+
+
+def gemm_raw(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream=0, workspace=0,
+             workspace_bytes=0, opts=None):
+    """Direct call of gemm_f16_ex with integer device addresses; returns the status."""
+    o = opts if opts is not None else None
+    return lib.gemm_f16_ex(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream,
+                           workspace, workspace_bytes, ctypes.byref(o) if o is not None else None)
+
+
+def gemm(a, b, out=None, workspace=None, variant="auto", split_k=0, panel=0, tile=0,
+         stream=None):
+    """C = a @ b with fp32 accumulation and fp16 output, computed by libgemmf16."""
+    m, n, k, out = _check(a, b, out)
+    opts = make_opts(variant, split_k, panel, tile)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(a.device):
+        rc = lib.gemm_f16_ex(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
+                             b.stride(1), out.data_ptr(), out.stride(0), m, n, k,
+                             stream.cuda_stream, ws_ptr, ws_bytes, ctypes.byref(opts))
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return out
+
+
+def plan(a, b, out=None, variant="auto", split_k=0, panel=0, tile=0):
+    """The plan (kernel family, tile, split, raster panel, load paths, grid,
+    workspace) that gemm would execute for these tensors."""
+    m, n, k, out = _check(a, b, out)
+    opts = make_opts(variant, split_k, panel, tile)
+    info = PlanInfo()
+    with torch.cuda.device(a.device):
+        rc = lib.gemm_f16_plan(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
+                               b.stride(1), out.data_ptr(), out.stride(0), m, n, k,
+                               ctypes.byref(opts), ctypes.byref(info))
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    d = info.as_dict()
+    d["a_path"], d["b_path"] = PATHS[d["a_path"]], PATHS[d["b_path"]]
+    d["variant"] = {v: k for k, v in VARIANTS.items()}[d["variant"]]
+    return d
+
+
+def workspace_bytes(M, N, K, variant="auto", split_k=0, panel=0, tile=0):
+    opts = make_opts(variant, split_k, panel, tile)
+    return int(lib.gemm_f16_workspace_bytes(M, N, K, ctypes.byref(opts)))

@@ -1,0 +1,404 @@
+// Host side of libgemmf16: argument validation, planning (kernel family,
+// tile, K split, raster panel, operand load paths) and launches.  The C-ABI
+// is declared and documented in include/gemm_f16.h.
+//
+// Validation mirrors the Triton article's wrapper (section "addresses and
+// bounds in one short kernel"): shapes must be non-empty, strides positive,
+// and the output must not share storage with the inputs (its ownership
+// paragraph: one writer per output, no program may overwrite data another
+// program still has to read).  Everything is checked before the first HIP
+// call, so on any error nothing is enqueued and C is untouched.
+//
+// Kernel choice follows the TileLang tutorial's variant criteria (ch. 14,
+// section 4.1: split K when the output tiles cannot fill the compute units
+// and K is large) and the decode/prefill distinction of the tiling tutorial
+// (section 04: with very few rows of A the product is a weight-streaming,
+// bandwidth-bound problem).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/gemm_f16.h"
+#include "tile_kernel.hpp"
+
+using namespace gemmf16;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+// Tile configurations: <BM, BN, BK, waves along m, waves along n, MFMA edge>.
+typedef TileCfg<128, 128, 64, 2, 2, 32> CfgT128;  // main / split-K
+typedef TileCfg<64, 32, 32, 2, 2, 16> CfgT64x32;  // the pages' 64x32x32 geometry
+typedef TileCfg<16, 256, 64, 1, 4, 16> CfgS16;    // skinny, M <= 16
+typedef TileCfg<32, 256, 64, 1, 4, 32> CfgS32;    // skinny, M <= 32
+typedef TileCfg<64, 256, 64, 1, 4, 32> CfgS64;    // skinny, M <= 64
+
+enum TileId { TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5, TILE_MAX = 5 };
+
+typedef void (*kfn_t)(KArgs);
+
+struct TileInfo {
+  int id, bm, bn, bk, nt;
+  kfn_t final_fn[9];    // [a_path * 3 + b_path]
+  kfn_t partial_fn[9];
+};
+
+template <class CF, bool P>
+void fill_fns(kfn_t* f) {
+  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P>;
+  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P>;
+  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P>;
+  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P>;
+  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P>;
+  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P>;
+  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P>;
+  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P>;
+  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P>;
+}
+
+template <class CF>
+TileInfo make_info(int id) {
+  TileInfo t;
+  t.id = id;
+  t.bm = CF::BM;
+  t.bn = CF::BN;
+  t.bk = CF::BK;
+  t.nt = CF::NT;
+  fill_fns<CF, false>(t.final_fn);
+  fill_fns<CF, true>(t.partial_fn);
+  return t;
+}
+
+const TileInfo& tile_info(int id) {
+  static const TileInfo table[TILE_MAX + 1] = {
+      TileInfo{}, make_info<CfgT128>(TILE_T128), make_info<CfgT64x32>(TILE_T64X32),
+      make_info<CfgS16>(TILE_S16), make_info<CfgS32>(TILE_S32), make_info<CfgS64>(TILE_S64)};
+  return table[id];
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, cached per device.
+int device_cus(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return GEMM_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    return GEMM_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return GEMM_OK;
+}
+
+// Largest element offset of a rows x cols view, or false on int64 overflow.
+bool view_span(int64_t rows, int64_t cols, int64_t sr, int64_t sc, int64_t* out) {
+  int64_t a, b, s;
+  if (__builtin_mul_overflow(rows - 1, sr, &a) || __builtin_mul_overflow(cols - 1, sc, &b) ||
+      __builtin_add_overflow(a, b, &s) || s > INT64_MAX / 2 - 1)
+    return false;
+  *out = s;
+  return true;
+}
+
+bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
+int classify(const void* base, int64_t s_r, int64_t s_k) {
+  const bool aligned = ((uintptr_t)base & 15u) == 0;
+  if (aligned && s_k == 1 && s_r % 8 == 0) return PATH_KVEC;
+  if (aligned && s_r == 1 && s_k % 8 == 0) return PATH_RVEC;
+  return PATH_GATHER;
+}
+
+struct Plan {
+  int variant, tile_id, split, panel, a_path, b_path, c_vec;
+  int64_t GM, GN, grid, grid2, k_split;
+  size_t ws;
+};
+
+struct Call {
+  const void *A, *B, *C;
+  int64_t lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K;
+  int64_t spanA, spanB, spanC;
+};
+
+int validate(const Call& c) {
+  if (!c.A || !c.B || !c.C) return GEMM_ERR_NULL;
+  if (c.M <= 0 || c.N <= 0 || c.K <= 0) return GEMM_ERR_SHAPE;
+  if (c.lda_m <= 0 || c.lda_k <= 0 || c.ldb_k <= 0 || c.ldb_n <= 0) return GEMM_ERR_STRIDE;
+  if (c.ldc < c.N) return GEMM_ERR_LDC;
+  return GEMM_OK;
+}
+
+int spans(Call& c) {
+  if (!view_span(c.M, c.K, c.lda_m, c.lda_k, &c.spanA) ||
+      !view_span(c.K, c.N, c.ldb_k, c.ldb_n, &c.spanB) ||
+      !view_span(c.M, c.N, c.ldc, 1, &c.spanC))
+    return GEMM_ERR_SHAPE;
+  const uintptr_t a0 = (uintptr_t)c.A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
+  const uintptr_t b0 = (uintptr_t)c.B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+  const uintptr_t c0 = (uintptr_t)c.C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
+  if (a1 < a0 || b1 < b0 || c1 < c0) return GEMM_ERR_SHAPE;
+  if (ranges_overlap(c0, c1, a0, a1) || ranges_overlap(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
+  return GEMM_OK;
+}
+
+int check_opts(const gemm_f16_opts* o) {
+  if (!o) return GEMM_OK;
+  if (o->variant < GEMM_VARIANT_AUTO || o->variant > GEMM_VARIANT_TILE64X32) return GEMM_ERR_OPTS;
+  if (o->split_k < 0 || o->split_k > 256) return GEMM_ERR_OPTS;
+  if (!(o->panel == -1 || (o->panel >= 0 && o->panel <= 4096))) return GEMM_ERR_OPTS;
+  if (o->tile < 0 || o->tile > TILE_MAX) return GEMM_ERR_OPTS;
+  return GEMM_OK;
+}
+
+// Choose split and derive the per-split K extent (a multiple of BK).
+void set_split(Plan& p, int64_t K, int bk, int64_t split) {
+  if (split < 1) split = 1;
+  int64_t ks = cdiv(cdiv(K, split), bk) * bk;
+  p.k_split = ks;
+  p.split = (int)cdiv(K, ks);
+}
+
+int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
+  int rc = check_opts(o);
+  if (rc) return rc;
+  const int variant = o ? o->variant : GEMM_VARIANT_AUTO;
+  const int want_split = o ? o->split_k : 0;
+  const int want_panel = o ? o->panel : 0;
+  const int want_tile = o ? o->tile : 0;
+
+  int cus = 0;
+  auto need_cus = [&]() -> int {
+    if (cus > 0) return GEMM_OK;
+    return device_cus(&cus);
+  };
+
+  p.variant = variant;
+  if (p.variant == GEMM_VARIANT_AUTO) {
+    if ((rc = need_cus())) return rc;
+    if (c.M <= 64) {
+      p.variant = GEMM_VARIANT_SKINNY;
+    } else {
+      const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
+      const int64_t mn = c.M > c.N ? c.M : c.N;
+      p.variant = (2 * T <= cus && c.K >= 4 * mn) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
+    }
+  }
+
+  // Tile.
+  switch (p.variant) {
+    case GEMM_VARIANT_MAIN:
+    case GEMM_VARIANT_SPLITK:
+      p.tile_id = want_tile ? want_tile : TILE_T128;
+      break;
+    case GEMM_VARIANT_TILE64X32:
+      if (want_tile && want_tile != TILE_T64X32) return GEMM_ERR_OPTS;
+      p.tile_id = TILE_T64X32;
+      break;
+    case GEMM_VARIANT_SKINNY:
+      if (c.M > 64) return GEMM_ERR_OPTS;
+      p.tile_id = want_tile ? want_tile : (c.M <= 16 ? TILE_S16 : (c.M <= 32 ? TILE_S32 : TILE_S64));
+      break;
+    default:
+      return GEMM_ERR_OPTS;
+  }
+  const TileInfo& ti = tile_info(p.tile_id);
+  p.GM = cdiv(c.M, ti.bm);
+  p.GN = cdiv(c.N, ti.bn);
+  const int64_t T = p.GM * p.GN;
+
+  // K split.
+  if (p.variant == GEMM_VARIANT_SPLITK || p.variant == GEMM_VARIANT_SKINNY) {
+    int64_t s = want_split;
+    if (s == 0) {
+      if ((rc = need_cus())) return rc;
+      s = cdiv(2 * (int64_t)cus, T);
+      const int64_t max_by_k = cdiv(c.K, 2 * ti.bk);  // at least two K steps per split
+      if (s > max_by_k) s = max_by_k;
+      if (s > 64) s = 64;
+    }
+    set_split(p, c.K, ti.bk, s);
+  } else {
+    if (want_split > 1) return GEMM_ERR_OPTS;
+    set_split(p, c.K, ti.bk, 1);
+  }
+
+  // Raster.
+  if (want_panel != 0)
+    p.panel = want_panel;
+  else
+    p.panel = (p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_TILE64X32) ? 8 : -1;
+
+  p.a_path = classify(c.A, c.lda_m, c.lda_k);
+  p.b_path = classify(c.B, c.ldb_n, c.ldb_k);
+  p.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
+
+  int64_t grid;
+  if (__builtin_mul_overflow(T, (int64_t)p.split, &grid) || grid > (INT64_C(1) << 32) / ti.nt - 1)
+    return GEMM_ERR_SHAPE;
+  p.grid = grid;
+  p.ws = 0;
+  p.grid2 = 0;
+  if (p.split > 1) {
+    int64_t mn, bytes;
+    if (__builtin_mul_overflow(c.M, c.N, &mn) || __builtin_mul_overflow(mn, (int64_t)p.split, &bytes) ||
+        __builtin_mul_overflow(bytes, (int64_t)4, &bytes) || bytes > INT64_MAX - 256)
+      return GEMM_ERR_SHAPE;
+    p.ws = (size_t)((bytes + 255) / 256 * 256);
+    const int64_t quads = c.M * cdiv(c.N, 4);
+    int64_t g2 = cdiv(quads, 256);
+    if (g2 > 8192) g2 = 8192;
+    p.grid2 = g2;
+  }
+  return GEMM_OK;
+}
+
+void fill_info(const Plan& p, gemm_f16_plan_info* info) {
+  const TileInfo& ti = tile_info(p.tile_id);
+  info->variant = p.variant;
+  info->tile_m = ti.bm;
+  info->tile_n = ti.bn;
+  info->tile_k = ti.bk;
+  info->split_k = p.split;
+  info->panel = p.panel;
+  info->a_path = p.a_path;
+  info->b_path = p.b_path;
+  info->tile_id = p.tile_id;
+  info->grid = p.grid;
+  info->grid2 = p.grid2;
+  info->workspace_bytes = p.ws;
+}
+
+int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
+  const TileInfo& ti = tile_info(p.tile_id);
+  KArgs a;
+  a.A = (const uint16_t*)c.A;
+  a.lda_m = c.lda_m;
+  a.lda_k = c.lda_k;
+  a.B = (const uint16_t*)c.B;
+  a.ldb_k = c.ldb_k;
+  a.ldb_n = c.ldb_n;
+  a.C = (uint16_t*)c.C;
+  a.ldc = c.ldc;
+  a.W = (float*)ws;
+  a.M = c.M;
+  a.N = c.N;
+  a.K = c.K;
+  a.k_split = p.k_split;
+  a.GM = p.GM;
+  a.GN = p.GN;
+  a.panel = p.panel;
+  a.c_vec = p.c_vec;
+  const int sel = p.a_path * 3 + p.b_path;
+  kfn_t fn = (p.split > 1) ? ti.partial_fn[sel] : ti.final_fn[sel];
+  void* args[] = {&a};
+  if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  if (p.split > 1) {
+    const float* W = (const float*)ws;
+    int S = p.split;
+    int64_t M = c.M, N = c.N, ldc = c.ldc;
+    uint16_t* C = (uint16_t*)c.C;
+    int cv = p.c_vec;
+    void* rargs[] = {&W, &S, &M, &N, &C, &ldc, &cv};
+    if (hipLaunchKernel((const void*)splitk_reduce, dim3((unsigned)p.grid2), dim3(256), rargs, 0,
+                        stream) != hipSuccess)
+      return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                  int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                  const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
+  Call c{A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
+  int rc = validate(c);
+  if (rc) return rc;
+  if ((rc = spans(c))) return rc;
+  Plan p;
+  if ((rc = make_plan(c, opts, p))) return rc;
+  if (info) fill_info(p, info);
+  return GEMM_OK;
+}
+
+int gemm_f16_ex(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream,
+                void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts) {
+  Call c{A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
+  int rc = validate(c);
+  if (rc) return rc;
+  if ((rc = spans(c))) return rc;
+  Plan p;
+  if ((rc = make_plan(c, opts, p))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.ws == 0) return launch(c, p, nullptr, s);
+  if (workspace) {
+    if (workspace_bytes < p.ws || ((uintptr_t)workspace & 255u)) return GEMM_ERR_WORKSPACE;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + p.ws;
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+    const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
+    if (ranges_overlap(w0, w1, a0, a1) || ranges_overlap(w0, w1, b0, b1) ||
+        ranges_overlap(w0, w1, c0, c1))
+      return GEMM_ERR_ALIAS;
+    return launch(c, p, workspace, s);
+  }
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, p.ws, s) != hipSuccess) return GEMM_ERR_HIP;
+  rc = launch(c, p, ws, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK) rc = GEMM_ERR_HIP;
+  return rc;
+}
+
+int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+             int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_f16_ex(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, nullptr, 0, nullptr);
+}
+
+size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
+  // Shape-only plan on non-overlapping, aligned stand-in addresses.
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  Call c{(const void*)0x100000000000ull, (const void*)0x200000000000ull,
+         (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
+  if (spans(c)) return 0;
+  Plan p;
+  if (make_plan(c, opts, p)) return 0;
+  return p.ws;
+}
+
+const char* gemm_f16_status_string(int status) {
+  switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_NULL: return "A, B or C is NULL";
+    case GEMM_ERR_SHAPE: return "M, N or K <= 0, an address span overflows int64, or the grid is too large";
+    case GEMM_ERR_STRIDE: return "a stride of A or B is <= 0";
+    case GEMM_ERR_LDC: return "ldc < N";
+    case GEMM_ERR_ALIAS: return "C (or the workspace) overlaps an input";
+    case GEMM_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case GEMM_ERR_OPTS: return "invalid options (variant, split, panel or tile)";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gemm_f16_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+// The tiled MFMA kernel and the split-K reduction (gfx950 / CDNA4).
+//
+// One workgroup owns one BM x BN output tile and one K range (the whole of K
+// unless the launch is split).  It clears an fp32 accumulator, walks its K
+// range in BK steps through a two-stage LDS ring, and stores once; every
+// valid output has exactly one writer and after q steps the accumulator
+// holds exactly the contributions of the valid k of those steps (the Triton
+// article's sections "parallelise over outputs, keep K in the accumulator"
+// and the ownership/loop-invariant paragraph; the tiling tutorial's section
+// 03 and the double-buffering of section 06).
+//
+// Inner product: v_mfma_f32_32x32x16_f16 (MI = 32) or
+// v_mfma_f32_16x16x32_f16 (MI = 16).  The MFMA is issued with the B tile as
+// its first operand and the A tile as its second, i.e. it computes the
+// transposed block C^T[n][m]; in that orientation each lane ends up holding
+// 4 consecutive n of one output row m, which become one 8-byte store.
+//
+// Split K (TileLang tutorial ch. 14, section 4.1; Triton article, section
+// "neighbouring programs share cache", last paragraph): with PARTIAL the
+// workgroup writes its fp32 partial tile to W[split][M][N] instead of C, and
+// splitk_reduce sums the partials in ascending split order, so the result is
+// bit-identical from run to run (no atomics).  fp32 partials, never fp16
+// (TileLang tutorial ch. 14, pitfall 4).
+#pragma once
+
+#include "tile_common.hpp"
+
+namespace gemmf16 {
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int MI = MI_;                     // MFMA output block edge
+  static constexpr int KI = (MI == 32) ? 16 : 32;    // k per MFMA
+  static constexpr int WTM = BM / WAVES_M;           // wave tile, rows (m)
+  static constexpr int WTN = BN / WAVES_N;           // wave tile, cols (n)
+  static constexpr int FM = WTM / MI, FN = WTN / MI; // MFMA blocks per wave
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static_assert(MI == 32 || MI == 16, "MFMA shape");
+  static_assert(WTM % MI == 0 && WTN % MI == 0 && BK % KI == 0, "tile shape");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+struct KArgs {
+  const uint16_t* A;
+  int64_t lda_m, lda_k;
+  const uint16_t* B;
+  int64_t ldb_k, ldb_n;
+  uint16_t* C;
+  int64_t ldc;
+  float* W;          // split partials [S][M][N] (PARTIAL launches only)
+  int64_t M, N, K;
+  int64_t k_split;   // K elements per split, a multiple of BK
+  int64_t GM, GN;    // tile grid
+  int32_t panel;     // raster group height, <= 0 = plain order
+  int32_t c_vec;     // C rows take 8-byte stores (ldc % 4 == 0, C 8-byte aligned)
+};
+
+template <int MI>
+struct Acc;
+template <>
+struct Acc<32> { typedef f32x16 type; static constexpr int N = 16; };
+template <>
+struct Acc<16> { typedef f32x4 type; static constexpr int N = 4; };
+
+template <int MI>
+__device__ __forceinline__ typename Acc<MI>::type mfma(f16x8 a, f16x8 b, typename Acc<MI>::type c) {
+  if constexpr (MI == 32)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 4 consecutive outputs C[m][n..n+3] (fp16, round to nearest even).
+__device__ __forceinline__ void store4_f16(const KArgs& a, int64_t m, int64_t n, float v0, float v1,
+                                           float v2, float v3) {
+  if (m >= a.M || n >= a.N) return;
+  uint16_t* p = a.C + m * a.ldc + n;
+  const _Float16 h[4] = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+  if (a.c_vec && n + 4 <= a.N) {
+    *reinterpret_cast<f16x4*>(p) = f16x4{h[0], h[1], h[2], h[3]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < a.N) reinterpret_cast<_Float16*>(p)[e] = h[e];
+  }
+}
+
+// 4 consecutive fp32 partials W[split][m][n..n+3].
+__device__ __forceinline__ void store4_f32(const KArgs& a, int64_t split, int64_t m, int64_t n,
+                                           float v0, float v1, float v2, float v3) {
+  if (m >= a.M || n >= a.N) return;
+  float* p = a.W + (split * a.M + m) * a.N + n;
+  if ((a.N & 3) == 0) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v0, v1, v2, v3};
+  } else {
+    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < a.N) p[e] = v[e];
+  }
+}
+
+template <class CF, int APATH, int BPATH, bool PARTIAL>
+__global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
+  constexpr int BK = CF::BK, MI = CF::MI, KI = CF::KI;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+
+  const int64_t T = a.GM * a.GN;
+  int64_t w = blockIdx.x;
+  int64_t split = 0;
+  if constexpr (PARTIAL) {
+    split = w / T;
+    w -= split * T;
+  }
+  int64_t pm, pn;
+  raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
+  const int64_t kb = split * a.k_split;
+  const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
+
+  OperandStage<CF::BM, BK, CF::NT, APATH> sa;
+  OperandStage<CF::BN, BK, CF::NT, BPATH> sb;
+  sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, tid);
+  sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, tid);
+
+  typedef typename Acc<MI>::type acc_t;
+  acc_t acc[CF::FN][CF::FM];
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j)
+#pragma unroll
+      for (int e = 0; e < Acc<MI>::N; ++e) acc[i][j][e] = 0.0f;
+
+  const int64_t nk = (ke - kb + BK - 1) / BK;
+  sa.load(kb, ke);
+  sb.load(kb, ke);
+  sa.store(smem);
+  sb.store(smem + CF::A_BYTES);
+  __syncthreads();
+
+  // Lane's position inside an MFMA operand block: row lane % MI, octet lane / MI.
+  const int lr = lane % MI, lc = lane / MI;
+  for (int64_t it = 0; it < nk; ++it) {
+    const int cur = (int)(it & 1);
+    if (it + 1 < nk) {
+      sa.load(kb + (it + 1) * BK, ke);
+      sb.load(kb + (it + 1) * BK, ke);
+    }
+    const char* ta = smem + cur * CF::STAGE;
+    const char* tb = ta + CF::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / KI; ++ks) {
+      const int c = ks * (KI / 8) + lc;
+      f16x8 fa[CF::FN], fb[CF::FM];
+#pragma unroll
+      for (int i = 0; i < CF::FN; ++i)
+        fa[i] = *reinterpret_cast<const f16x8*>(tb + cell_off<CF::BN>(wn * CF::WTN + i * MI + lr, c));
+#pragma unroll
+      for (int j = 0; j < CF::FM; ++j)
+        fb[j] = *reinterpret_cast<const f16x8*>(ta + cell_off<CF::BM>(wm * CF::WTM + j * MI + lr, c));
+#pragma unroll
+      for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<MI>(fa[i], fb[j], acc[i][j]);
+    }
+    if (it + 1 < nk) {
+      sa.store(smem + (cur ^ 1) * CF::STAGE);
+      sb.store(smem + (cur ^ 1) * CF::STAGE + CF::A_BYTES);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  MFMA output layout (C^T block, MI x MI): lane holds column
+  // j = lane % MI (our m) and, for register group g, 4 consecutive rows
+  // (our n) starting at 8g + 4*(lane/32) for MI = 32, 4*(lane/16) for MI = 16.
+  constexpr int G = Acc<MI>::N / 4;
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j) {
+      const int64_t m = m0 + wm * CF::WTM + j * MI + lr;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int nl = (MI == 32) ? (8 * g + 4 * (lane >> 5)) : (4 * (lane >> 4));
+        const int64_t n = n0 + wn * CF::WTN + i * MI + nl;
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if constexpr (PARTIAL)
+          store4_f32(a, split, m, n, v0, v1, v2, v3);
+        else
+          store4_f16(a, m, n, v0, v1, v2, v3);
+      }
+    }
+}
+
+// C[m][n] = fp16_rne( sum_{s=0}^{S-1} W[s][m][n] ), ascending s.  Each thread
+// owns 4 consecutive n of one row; grid-stride over the M x ceil(N/4) quads.
+__global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int64_t M, int64_t N,
+                                                     uint16_t* C, int64_t ldc, int c_vec) {
+  const int64_t NQ = (N + 3) / 4;
+  const int64_t total = M * NQ;
+  const int64_t MN = M * N;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = q / NQ, n = (q - m * NQ) * 4;
+    const float* p = W + m * N + n;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    if ((N & 3) == 0) {
+      for (int s = 0; s < S; ++s) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p + s * MN);
+        s0 += v[0]; s1 += v[1]; s2 += v[2]; s3 += v[3];
+      }
+    } else {
+      for (int s = 0; s < S; ++s) {
+        const float* ps = p + s * MN;
+        s0 += ps[0];
+        if (n + 1 < N) s1 += ps[1];
+        if (n + 2 < N) s2 += ps[2];
+        if (n + 3 < N) s3 += ps[3];
+      }
+    }
+    uint16_t* c = C + m * ldc + n;
+    const _Float16 h[4] = {(_Float16)s0, (_Float16)s1, (_Float16)s2, (_Float16)s3};
+    if (c_vec && n + 4 <= N) {
+      *reinterpret_cast<f16x4*>(c) = f16x4{h[0], h[1], h[2], h[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) reinterpret_cast<_Float16*>(c)[e] = h[e];
+    }
+  }
+}
+
+}  // namespace gemmf16

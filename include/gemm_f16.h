@@ -1,0 +1,146 @@
+/*
+ * gemm_f16.h -- dense fp16 matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ *     C[M,N] = A[M,K] . B[K,N]
+ *
+ * fp16 (IEEE binary16) inputs, fp32 accumulation, fp16 output rounded to
+ * nearest-even.  The operation is the one the pages define: every output is
+ * the K-term dot product of a row of A and a column of B (TileLang tutorial
+ * ch. 14, section 1.1; "Matrix multiplication and memory-access
+ * optimisation", section 01; "Triton GEMM: from one output tile to addresses,
+ * bounds and data reuse", introduction: no bias, activation, batch or
+ * quantisation; fp16 in, fp32 accumulator, fp16 out).
+ *
+ * Addressing (Triton article, section "shape gives meaning, stride gives
+ * addresses"): all strides are in ELEMENTS, not bytes, and all arithmetic on
+ * them is 64-bit (same article, section "addresses and bounds in one short
+ * kernel"):
+ *     A[i,k] at A + i*lda_m + k*lda_k
+ *     B[k,j] at B + k*ldb_k + j*ldb_n
+ *     C[i,j] at C + i*ldc + j          (C is row-major with unit column stride)
+ * Transposed views and positive-stride slices of larger buffers are legal.
+ * Elements outside the M x K and K x N views are never read, and outputs
+ * outside M x N (including the ldc - N padding of each C row) are never
+ * written (same article, section "three dimensions that do not divide").
+ *
+ * Ownership: the caller owns A, B, C and any workspace; the library keeps no
+ * pointer after a call returns.  Pointers are DEVICE pointers on the current
+ * HIP device.  Every entry point that launches work is asynchronous on the
+ * given hipStream_t (passed as void*, NULL = the default stream) and never
+ * synchronises; a fault inside a kernel surfaces at the caller's next
+ * synchronisation.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued;
+ * on any error nothing is launched and C is untouched.  Results are
+ * deterministic: the same inputs and options give bit-identical C (no
+ * atomics in any reduction).
+ */
+#ifndef GEMM_F16_H
+#define GEMM_F16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  The argument contract follows the Triton article's wrapper
+ * (section "addresses and bounds in one short kernel"): empty shapes, zero or
+ * negative strides and outputs that share storage with inputs are outside
+ * it. */
+enum gemm_status {
+  GEMM_OK = 0,
+  GEMM_ERR_NULL = -1,      /* A, B or C is NULL                                  */
+  GEMM_ERR_SHAPE = -2,     /* M, N or K <= 0, an address span overflows int64,   */
+                           /* or the grid exceeds the launch limit               */
+  GEMM_ERR_STRIDE = -3,    /* lda_m, lda_k, ldb_k or ldb_n <= 0                   */
+  GEMM_ERR_LDC = -4,       /* ldc < N: two outputs would share an address        */
+  GEMM_ERR_ALIAS = -5,     /* C's byte range overlaps A's or B's                 */
+  GEMM_ERR_WORKSPACE = -6, /* the workspace given is smaller than required       */
+  GEMM_ERR_OPTS = -7,      /* invalid forced variant, split, panel or tile       */
+  GEMM_ERR_HIP = -8        /* a HIP runtime call failed (no device, launch, ...) */
+};
+
+/* Kernel families (gemm_f16_opts.variant / gemm_f16_plan_info.variant). */
+enum gemm_variant {
+  GEMM_VARIANT_AUTO = 0,    /* choose from the shape (the default)                */
+  GEMM_VARIANT_MAIN = 1,    /* one workgroup per output tile, whole K            */
+  GEMM_VARIANT_SKINNY = 2,  /* M <= 64: B streamed once, K split, fixed-order sum */
+  GEMM_VARIANT_SPLITK = 3,  /* tiles x K ranges into fp32 partials, then a       */
+                            /* second pass sums the ranges in fixed order        */
+  GEMM_VARIANT_TILE64X32 = 4 /* main structure with the pages' 64x32x32 tile    */
+};
+
+typedef struct gemm_f16_opts {
+  int32_t variant; /* enum gemm_variant                                          */
+  int32_t split_k; /* K ranges for SPLITK/SKINNY; 0 = choose; 1..256              */
+  int32_t panel;   /* raster group height in tiles; 0 = choose; -1 = plain       */
+                   /* row-major tile order without XCD remapping; 1..4096        */
+  int32_t tile;    /* main-kernel tile id (0 = choose; see gemm_f16_plan_info)   */
+} gemm_f16_opts;
+
+typedef struct gemm_f16_plan_info {
+  int32_t variant;          /* the family that runs (never AUTO)                 */
+  int32_t tile_m, tile_n, tile_k; /* workgroup tile                              */
+  int32_t split_k;          /* K ranges (1 = none)                               */
+  int32_t panel;            /* raster group height in tiles (-1 = plain order)   */
+  int32_t a_path, b_path;   /* operand load path: 0 gather, 1 vector along K,    */
+                            /* 2 vector along M (A) or N (B) with a transpose    */
+  int32_t tile_id;          /* the tile configuration chosen                     */
+  int64_t grid;             /* workgroups in the first launch                    */
+  int64_t grid2;            /* workgroups in the reduction launch (0 = none)     */
+  uint64_t workspace_bytes; /* device workspace the call needs (0 = none)        */
+} gemm_f16_plan_info;
+
+/*
+ * C := A.B  with automatic kernel choice.  Equivalent to gemm_f16_ex with no
+ * workspace and default options.  If the chosen kernel needs a workspace
+ * (split-K partials), it is allocated stream-ordered on `stream`
+ * (hipMallocAsync) and released stream-ordered after the last launch.
+ */
+int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
+             const void* B, int64_t ldb_k, int64_t ldb_n,
+             void* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * As gemm_f16, with an optional caller-owned device workspace and options.
+ * workspace may be NULL (the library allocates stream-ordered when needed);
+ * otherwise it must hold at least gemm_f16_workspace_bytes(...) bytes, be
+ * 256-byte aligned, and not overlap A, B or C.  The workspace needs no
+ * initialisation and its contents are garbage afterwards.  opts may be NULL.
+ */
+int gemm_f16_ex(const void* A, int64_t lda_m, int64_t lda_k,
+                const void* B, int64_t ldb_k, int64_t ldb_n,
+                void* C, int64_t ldc,
+                int64_t M, int64_t N, int64_t K, void* stream,
+                void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts);
+
+/*
+ * The plan gemm_f16_ex would execute for these arguments, without launching
+ * anything.  Performs the same validation (return codes as above) and fills
+ * *info.  Needs the current HIP device only when opts ask for automatic
+ * choices (the compute-unit count feeds them); GEMM_ERR_HIP otherwise.
+ */
+int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k,
+                  const void* B, int64_t ldb_k, int64_t ldb_n,
+                  const void* C, int64_t ldc,
+                  int64_t M, int64_t N, int64_t K,
+                  const gemm_f16_opts* opts, gemm_f16_plan_info* info);
+
+/* Workspace bytes gemm_f16_ex needs for this shape and these options
+ * (0 when the plan has no K split).  Returns 0 for invalid arguments too. */
+size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
+
+/* Static, NUL-terminated description of a return code. */
+const char* gemm_f16_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gemm_f16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_H */

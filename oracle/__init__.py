@@ -63,7 +63,8 @@ def _load():
 
 
 def threads():
-    return len(os.sched_getaffinity(0))
+    """Worker threads: the cores this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def f16_to_f64(bits):

@@ -55,7 +55,8 @@ def _load():
 
 
 def host_threads():
-    return len(os.sched_getaffinity(0))
+    """Worker threads: the cores this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def fill(dst, rows, cols, rs, cs, seed, tensor, mode="uniform", row0=0, row_index=None,

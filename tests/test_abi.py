@@ -1,0 +1,129 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects every argument outside the contract before touching a
+device (so no GPU is needed).  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_tiled_gemm_fp16_amd as g
+from dense_tiled_gemm_fp16_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16.h")
+
+# Aligned, non-overlapping stand-in device addresses: validation never
+# dereferences them.
+PA, PB, PC, PW = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_f16\w*)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_list():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(g.lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_version():
+    for rc, name in _lib.STATUS.items():
+        s = g.lib.gemm_f16_status_string(rc).decode()
+        assert s and s != "unknown status", name
+    assert g.lib.gemm_f16_status_string(12345).decode() == "unknown status"
+    assert g.lib.gemm_f16_version() >= 100
+
+
+def call(A=PA, lda_m=64, lda_k=1, B=PB, ldb_k=32, ldb_n=1, C=PC, ldc=32, M=16, N=32, K=64,
+         ws=0, ws_bytes=0, opts=None):
+    return g.gemm_raw(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, 0, ws, ws_bytes, opts)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=0), -1), (dict(B=0), -1), (dict(C=0), -1),
+    (dict(M=0), -2), (dict(N=0), -2), (dict(K=0), -2), (dict(M=-3), -2),
+    (dict(lda_m=0), -3), (dict(lda_k=-1), -3), (dict(ldb_k=0), -3), (dict(ldb_n=-2), -3),
+    (dict(ldc=31), -4),
+    (dict(C=PA + 64), -5),                      # C starts inside A
+    (dict(C=PB - 64), -5),                      # C runs into B
+    (dict(lda_m=2 ** 62, M=4), -2),             # span overflows int64
+    (dict(ldb_k=2 ** 61, K=9), -2),
+])
+def test_rejected_before_any_device_work(kw, code):
+    assert call(**kw) == code
+
+
+def test_option_errors():
+    bad = [_lib.Opts(9, 0, 0, 0), _lib.Opts(-1, 0, 0, 0), _lib.Opts(3, -1, 0, 0),
+           _lib.Opts(3, 257, 0, 0), _lib.Opts(1, 0, -2, 0), _lib.Opts(1, 0, 5000, 0),
+           _lib.Opts(1, 0, 0, 99)]
+    for o in bad:
+        assert call(opts=o) == -7
+    # skinny is only for M <= 64; main takes no K split
+    assert call(M=65, opts=_lib.Opts(2, 4, -1, 0)) == -7
+    assert call(opts=_lib.Opts(1, 4, 8, 0)) == -7
+
+
+def test_workspace_errors():
+    o = _lib.Opts(3, 4, -1, 1)                  # forced split-K: no device query needed
+    need = g.workspace_bytes(16, 32, 1024, variant="splitk", split_k=4, panel=-1, tile=1)
+    assert need == 4 * 16 * 32 * 4
+    kw = dict(K=1024, lda_m=1024, opts=o)
+    assert call(ws=PW, ws_bytes=need - 1, **kw) == -6
+    assert call(ws=PW + 16, ws_bytes=need, **kw) == -6        # not 256-byte aligned
+    assert call(ws=PA, ws_bytes=need, **kw) == -5             # overlaps A
+
+
+def forced_plan(M, N, K, lda, ldb, ldc, variant, split, panel, tile, A=PA, B=PB, C=PC):
+    info = _lib.PlanInfo()
+    o = _lib.Opts(variant, split, panel, tile)
+    rc = g.lib.gemm_f16_plan(A, lda[0], lda[1], B, ldb[0], ldb[1], C, ldc, M, N, K,
+                             ctypes.byref(o), ctypes.byref(info))
+    assert rc == 0, rc
+    return info
+
+
+def test_plan_of_the_pages_edge_geometry():
+    # 130x70x65 with the 64x32x32 tile: a 3x3 grid (Triton article, section
+    # "three dimensions that do not divide"); rows of 65 and 70 halves are not
+    # 16-byte multiples, so both operands take the element-wise path.
+    p = forced_plan(130, 70, 65, (65, 1), (70, 1), 70, 4, 0, -1, 0)
+    assert (p.tile_m, p.tile_n, p.tile_k) == (64, 32, 32)
+    assert p.grid == 9 and p.split_k == 1 and p.workspace_bytes == 0
+    assert (p.a_path, p.b_path) == (0, 0)
+
+
+def test_plan_paths_follow_strides_and_alignment():
+    # A K-contiguous and B N-contiguous (the row-major case)
+    p = forced_plan(4096, 4096, 4096, (4096, 1), (4096, 1), 4096, 1, 0, 8, 1)
+    assert (p.a_path, p.b_path) == (1, 2) and p.grid == 32 * 32
+    # B as a transposed view (stride (1, K)): K-contiguous too
+    p = forced_plan(4096, 1061, 8192, (8192, 1), (1, 8192), 1061, 1, 0, 8, 1)
+    assert (p.a_path, p.b_path) == (1, 1)
+    # A as a transposed view: M-contiguous
+    p = forced_plan(256, 256, 256, (1, 256), (256, 1), 256, 1, 0, 8, 1)
+    assert (p.a_path, p.b_path) == (2, 2)
+    # misaligned base falls back to the element-wise path
+    p = forced_plan(256, 256, 256, (256, 1), (256, 1), 256, 1, 0, 8, 1, A=PA + 2)
+    assert p.a_path == 0
+
+
+def test_plan_split_k_extents():
+    p = forced_plan(512, 512, 65536, (65536, 1), (512, 1), 512, 3, 16, -1, 1)
+    assert p.split_k == 16 and p.grid == 16 * 16 and p.grid2 > 0
+    assert p.workspace_bytes == 16 * 512 * 512 * 4
+    # the split count never leaves an empty K range
+    p = forced_plan(512, 512, 100, (100, 1), (512, 1), 512, 3, 7, -1, 1)
+    assert p.split_k == 2          # K = 100 in 64-wide steps: two ranges at most

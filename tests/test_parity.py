@@ -1,0 +1,407 @@
+"""GPU parity: libgemmf16 (through its C-ABI) against the CPU oracle on the
+same seeded inputs.
+
+Acceptance (from the oracle's contract): bit-exact on integer inputs in
+[-4, 4] with K <= 128 (every partial sum is an integer of magnitude <= 2048,
+exact in fp32 and fp16); elementwise |C_gpu - C_oracle| <= 1e-2 + 2e-3|C_oracle|
+on U(-1, 1) inputs.  Every kernel family is forced on every shape it accepts;
+inputs are passed as views into NaN-filled buffers where the layout allows,
+so any read outside a view turns an output into NaN; outputs are pre-filled
+with NaN and surrounded by canaries, so a missing or stray write is seen.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_gemm_fp16_amd as g
+import oracle
+import synth
+from gpu_util import (DEV, ORACLE_THREADS, assert_bits_equal, assert_close, say, to_dev,
+                      to_host, val)
+
+pytestmark = pytest.mark.gpu
+
+NAN16 = 0x7E00
+CANARY = 0x5A5A
+
+
+def dev_nan(n):
+    return torch.full((n,), float("nan"), dtype=torch.float16, device=DEV)
+
+
+def place(logical, layout, pad=(0, 0)):
+    """Put a logical [R, C] fp16-bit matrix on the GPU and return a torch view
+    of shape [R, C] with the requested storage:
+      "row"  row-major, strides (C + pad[1], 1) inside a NaN buffer with
+             pad[0] leading NaN rows (pad = (0, 0): a plain contiguous tensor)
+      "col"  a transposed view: stored [C, R], strides (1, R + pad[1])."""
+    R, Cc = logical.shape
+    if layout == "row":
+        if pad == (0, 0):
+            return to_dev(logical)
+        ld = Cc + pad[1]
+        buf = dev_nan((R + pad[0] + 1) * ld)
+        v = buf[pad[0] * ld: pad[0] * ld + R * ld].view(R, ld)[:, :Cc]
+        v.copy_(to_dev(logical))
+        return v
+    if layout == "col":
+        if pad == (0, 0):
+            return to_dev(np.ascontiguousarray(logical.T)).t()
+        ld = R + pad[1]
+        buf = dev_nan((Cc + pad[0] + 1) * ld)
+        v = buf[pad[0] * ld: pad[0] * ld + Cc * ld].view(Cc, ld)[:, :R]
+        v.copy_(to_dev(np.ascontiguousarray(logical.T)))
+        return v.t()
+    raise ValueError(layout)
+
+
+class Out:
+    """An [M, N] output view with row stride ldc inside a buffer pre-filled
+    with NaN (the view) and a canary pattern (everything else)."""
+
+    def __init__(self, M, N, ldc=None, guard=64):
+        ldc = ldc or N
+        self.M, self.N, self.ldc, self.guard = M, N, ldc, guard
+        host = np.full(guard + M * ldc + guard, CANARY, dtype=np.uint16)
+        host[guard:guard + M * ldc].reshape(M, ldc)[:, :N] = NAN16
+        self.buf = to_dev(host)
+        self.view = self.buf[guard:guard + M * ldc].view(M, ldc)[:, :N]
+
+    def result(self):
+        host = to_host(self.buf)
+        inner = host[self.guard:self.guard + self.M * self.ldc].reshape(self.M, self.ldc)
+        assert np.all(host[:self.guard] == CANARY) and np.all(host[-self.guard:] == CANARY), \
+            "write outside the output buffer"
+        assert np.all(inner[:, self.N:] == CANARY), "write into the ldc padding"
+        return np.ascontiguousarray(inner[:, :self.N])
+
+
+def run(a, b, out=None, **kw):
+    say(f"gemm M={a.shape[0]} N={b.shape[1]} K={a.shape[1]} a.stride={a.stride()} "
+        f"b.stride={b.stride()} opts={kw}")
+    o = out.view if out is not None else None
+    c = g.gemm(a, b, out=o, **kw)
+    torch.cuda.synchronize()
+    return out.result() if out is not None else to_host(c)
+
+
+def reference(A, B, rows=None):
+    """Oracle on the logical row-major host matrices (all rows or some)."""
+    K, N = B.shape
+    if rows is not None:
+        A = np.ascontiguousarray(A[rows])
+    return oracle.gemm(A, (K, 1), B, (N, 1), A.shape[0], N, K, nthreads=ORACLE_THREADS)
+
+
+def check(gpu, ref, mode, what):
+    if mode == "int":
+        assert_bits_equal(gpu, ref, what)
+    else:
+        assert_close(gpu, ref, what)
+
+
+VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"),
+            dict(variant="splitk", split_k=2), dict(variant="splitk", split_k=3),
+            dict(variant="splitk", split_k=7), dict(variant="main", panel=-1),
+            dict(variant="main", panel=1), dict(variant="main", tile=3)]
+
+
+# ------------------------------------------------------------------ the edge case
+
+@pytest.mark.parametrize("mode", ["uniform", "int"])
+@pytest.mark.parametrize("b_layout", ["row", "col"])
+def test_edge_130x70x65(mode, b_layout):
+    M, N, K = 130, 70, 65
+    seed = 1001 if mode == "uniform" else 1002
+    A = synth.matrix(M, K, seed, synth.TENSOR_A, mode)
+    B = synth.matrix(K, N, seed, synth.TENSOR_B, mode)
+    ref = reference(A, B)
+    a, b = place(A, "row"), place(B, b_layout)
+    for kw in VARIANTS:
+        out = Out(M, N, ldc=N + 5)
+        check(run(a, b, out, **kw), ref, mode, f"130x70x65 {mode} B={b_layout} {kw}")
+    p = g.plan(a, b, variant="tile64x32")
+    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["grid"]) == (64, 32, 32, 9)
+    with pytest.raises(g.GemmError):
+        g.gemm(a, b, variant="skinny")          # skinny is for M <= 64
+
+
+# ------------------------------------------------------------------ layouts and ragged tails
+
+LAYOUT_SHAPES = [(300, 200, 128), (257, 136, 120), (96, 1000, 64), (1000, 24, 128),
+                 (129, 129, 127), (64, 72, 131)]
+
+
+@pytest.mark.parametrize("shape", LAYOUT_SHAPES)
+@pytest.mark.parametrize("a_layout,b_layout", [("row", "row"), ("row", "col"), ("col", "row"),
+                                               ("col", "col")])
+def test_layouts_integer_exact(shape, a_layout, b_layout):
+    M, N, K = shape
+    A = synth.matrix(M, K, 7, synth.TENSOR_A, "int")
+    B = synth.matrix(K, N, 7, synth.TENSOR_B, "int")
+    ref = reference(A, B)
+    for pad in [(0, 0), (3, 8)]:
+        a, b = place(A, a_layout, pad), place(B, b_layout, pad)
+        for kw in VARIANTS:
+            check(run(a, b, Out(M, N, ldc=N + 3), **kw), ref, "int",
+                  f"{shape} A={a_layout} B={b_layout} pad={pad} {kw}")
+
+
+def test_layout_paths_are_exercised():
+    A = synth.matrix(300, 128, 7, 0, "int")
+    B = synth.matrix(128, 200, 7, 1, "int")
+    seen = set()
+    for al in ("row", "col"):
+        for bl in ("row", "col"):
+            for pad in [(0, 0), (3, 8), (0, 3)]:
+                p = g.plan(place(A, al, pad), place(B, bl, pad))
+                seen.add((p["a_path"], p["b_path"]))
+    assert {"kvec", "rvec", "gather"} <= {x for pair in seen for x in pair}
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 1000), (257, 136, 777), (513, 260, 2051)])
+@pytest.mark.parametrize("a_layout,b_layout", [("row", "row"), ("row", "col"), ("col", "row")])
+def test_layouts_uniform(shape, a_layout, b_layout):
+    M, N, K = shape
+    A = synth.matrix(M, K, 11, synth.TENSOR_A)
+    B = synth.matrix(K, N, 11, synth.TENSOR_B)
+    ref = reference(A, B)
+    a, b = place(A, a_layout, (2, 8)), place(B, b_layout, (1, 8))
+    for kw in VARIANTS:
+        check(run(a, b, Out(M, N), **kw), ref, "uniform", f"{shape} {a_layout}/{b_layout} {kw}")
+
+
+def test_tiny_shapes_brute_force():
+    sizes = [1, 2, 3, 5, 8, 13]
+    for M in sizes:
+        for N in sizes:
+            for K in sizes:
+                A = synth.matrix(M, K, 100 + M, 0, "int")
+                B = synth.matrix(K, N, 200 + N, 1, "int")
+                ref = reference(A, B)
+                a, b = place(A, "row", (1, 2)), place(B, "col", (1, 2))
+                for kw in (dict(variant="auto"), dict(variant="main"),
+                           dict(variant="tile64x32"), dict(variant="splitk", split_k=2)):
+                    check(run(a, b, Out(M, N), **kw), ref, "int", f"{M}x{N}x{K} {kw}")
+                if M <= 64:
+                    check(run(a, b, Out(M, N), variant="skinny"), ref, "int", f"{M}x{N}x{K} skinny")
+
+
+# ------------------------------------------------------------------ square sweep
+
+@pytest.mark.parametrize("n", [256, 1024])
+def test_square_full(n):
+    A = synth.matrix(n, n, 2000 + n, 0)
+    B = synth.matrix(n, n, 2000 + n, 1)
+    ref = reference(A, B)
+    a, b = to_dev(A), to_dev(B)
+    for kw in (dict(variant="auto"), dict(variant="main"), dict(variant="splitk", split_k=4)):
+        check(run(a, b, Out(n, n), **kw), ref, "uniform", f"square {n} {kw}")
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_square_sampled(n):
+    A = synth.matrix(n, n, 2000 + n, 0)
+    B = synth.matrix(n, n, 2000 + n, 1)
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, n - 1], rng.integers(0, n, 20)]))
+    ref = reference(A, B, rows)
+    gpu = run(to_dev(A), to_dev(B))
+    check(gpu[rows], ref, "uniform", f"square {n}")
+
+
+# ------------------------------------------------------------------ skinny / decode
+
+@pytest.mark.parametrize("M", [1, 7, 16, 33, 64])
+def test_skinny_full(M):
+    N, K = 2048, 7168
+    A = synth.matrix(M, K, 3000 + M, 0)
+    B = synth.matrix(K, N, 3000 + M, 1)
+    ref = reference(A, B)
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    assert p["variant"] == "skinny"
+    for kw in (dict(variant="auto"), dict(variant="skinny", split_k=1),
+               dict(variant="skinny", split_k=8), dict(variant="main"),
+               dict(variant="splitk", split_k=5)):
+        check(run(a, b, Out(M, N), **kw), ref, "uniform", f"skinny M={M} {kw}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_skinny_integer_exact(M):
+    N, K = 2048, 128
+    A = synth.matrix(M, K, 3100 + M, 0, "int")
+    B = synth.matrix(K, N, 3100 + M, 1, "int")
+    ref = reference(A, B)
+    a, b = to_dev(A), to_dev(B)
+    for kw in (dict(variant="auto"), dict(variant="skinny", split_k=2)):
+        check(run(a, b, Out(M, N), **kw), ref, "int", f"skinny int M={M} {kw}")
+
+
+def test_split_k_512x512x65536():
+    M = N = 512
+    K = 65536
+    A = synth.matrix(M, K, 3004, 0)
+    B = synth.matrix(K, N, 3004, 1)
+    rows = np.array([0, 1, 127, 128, 300, 511])
+    ref = reference(A, B, rows)
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    assert p["variant"] == "splitk" and p["split_k"] > 1
+    first = run(a, b)
+    check(first[rows], ref, "uniform", "split-K auto")
+    again = run(a, b)
+    assert_bits_equal(again, first, "split-K rerun")
+    for kw in (dict(variant="splitk", split_k=16), dict(variant="splitk", split_k=7),
+               dict(variant="main")):
+        check(run(a, b, **kw)[rows], ref, "uniform", f"split-K {kw}")
+
+
+# ------------------------------------------------------------------ full-size configurations
+
+def test_moe_131072x2048x7168_sampled():
+    M, N, K = 131072, 2048, 7168
+    A = synth.matrix(M, K, 4001, 0)
+    B = synth.matrix(K, N, 4001, 1)
+    rng = np.random.default_rng(4001)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, M - 129, M - 128, M - 1],
+                                     rng.integers(0, M, 24)]))
+    ref = reference(A, B, rows)
+    a, b = to_dev(A), to_dev(B)
+    del A
+    p = g.plan(a, b)
+    assert p["variant"] == "main"
+    gpu = run(a, b)
+    check(gpu[rows], ref, "uniform", "MoE 131072x2048x7168")
+
+
+def test_int64_stride_262181x1061x8192_sampled():
+    M, N, K = 262181, 1061, 8192
+    A = synth.matrix(M, K, 5001, 0)
+    Bt = synth.matrix(K, N, 5001, 1, order="col")     # stored [N][K]
+    rng = np.random.default_rng(5001)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 131071, 131072, 262143, 262144, 262145,
+                                      M - 38, M - 37, M - 1], rng.integers(0, M, 16)]))
+    B = np.ascontiguousarray(Bt.T)
+    ref = reference(A, B, rows)
+    a = to_dev(A)
+    del A
+    b = to_dev(Bt).t()                                  # [K, N] view, strides (1, K)
+    assert b.stride() == (1, K)
+    gpu = run(a, b)
+    check(gpu[rows], ref, "uniform", "262181x1061x8192")
+
+
+def test_int64_stride_integer_slice_exact():
+    """K = 128 slice of the stress buffers: element offsets past 2^31 are
+    checked bit-exactly (the buffers are NaN outside the slice)."""
+    M, N, Kfull, K = 262181, 1061, 8192, 128
+    A = synth.matrix(M, K, 5002, 0, "int")
+    Bt = synth.matrix(K, N, 5002, 1, "int", order="col")   # [N][K]
+    abuf = torch.full((M, Kfull), float("nan"), dtype=torch.float16, device=DEV)
+    abuf[:, :K].copy_(to_dev(A))
+    bbuf = torch.full((N, Kfull), float("nan"), dtype=torch.float16, device=DEV)
+    bbuf[:, :K].copy_(to_dev(Bt))
+    a = abuf[:, :K]
+    b = bbuf[:, :K].t()
+    assert a.stride() == (Kfull, 1) and b.stride() == (1, Kfull)
+    rows = np.array([0, 1, 131071, 131072, 262143, 262144, 262145, M - 1])
+    ref = reference(A, np.ascontiguousarray(Bt.T), rows)
+    for kw in (dict(variant="auto"), dict(variant="splitk", split_k=2)):
+        gpu = run(a, b, **kw)
+        check(gpu[rows], ref, "int", f"int64 slice {kw}")
+
+
+def test_offsets_of_2_pow_32_elements():
+    """Row, k and output strides of exactly 2^32 elements: a 32-bit offset
+    would wrap to 0 and read or write the wrong element (Triton article,
+    section "addresses and bounds in one short kernel")."""
+    big = 2 ** 32
+    N = 64
+    # lda_m = 2^32
+    buf = dev_nan(big + 8)
+    buf[0] = 1.0
+    buf[big] = 2.0
+    a = torch.as_strided(buf, (2, 1), (big, 1))
+    B = synth.matrix(1, N, 5003, 1, "int")
+    ref = reference(np.array([[0x3C00], [0x4000]], np.uint16), B)
+    check(run(a, to_dev(B)), ref, "int", "lda_m = 2^32")
+    del buf, a
+    # ldb_k = 2^32
+    bbuf = dev_nan(big + N + 8)
+    B2 = synth.matrix(2, N, 5004, 1, "int")
+    bbuf[:N].copy_(to_dev(B2[0]))
+    bbuf[big:big + N].copy_(to_dev(B2[1]))
+    b = torch.as_strided(bbuf, (2, N), (big, 1))
+    A2 = synth.matrix(4, 2, 5004, 0, "int")
+    check(run(to_dev(A2), b), reference(A2, B2), "int", "ldb_k = 2^32")
+    del bbuf, b
+    # ldc = 2^32
+    cbuf = torch.full((big + N + 8,), 7.0, dtype=torch.float16, device=DEV)
+    c = torch.as_strided(cbuf, (2, N), (big, 1))
+    A3 = synth.matrix(2, 3, 5005, 0, "int")
+    B3 = synth.matrix(3, N, 5005, 1, "int")
+    say("gemm ldc = 2^32")
+    g.gemm(to_dev(A3), to_dev(B3), out=c)
+    torch.cuda.synchronize()
+    ref = reference(A3, B3)
+    got = np.stack([to_host(cbuf[:N]), to_host(cbuf[big:big + N])])
+    assert_bits_equal(got, ref, "ldc = 2^32")
+    assert torch.all(cbuf[N:N + 8] == 7.0) and torch.all(cbuf[big - 8:big] == 7.0)
+
+
+# ------------------------------------------------------------------ properties
+
+def test_repeat_runs_are_bit_identical():
+    M, N, K = 700, 600, 3000
+    A = synth.matrix(M, K, 6001, 0)
+    B = synth.matrix(K, N, 6001, 1)
+    a, b = to_dev(A), to_dev(B)
+    for kw in VARIANTS:
+        first = run(a, b, **kw)
+        assert_bits_equal(run(a, b, **kw), first, f"rerun {kw}")
+
+
+def test_split_counts_agree_on_integers():
+    M, N, K = 200, 300, 128
+    A = synth.matrix(M, K, 6002, 0, "int")
+    B = synth.matrix(K, N, 6002, 1, "int")
+    a, b = to_dev(A), to_dev(B)
+    base = run(a, b, variant="main")
+    assert_bits_equal(base, reference(A, B), "main")
+    for s in (1, 2, 3, 7, 16):
+        assert_bits_equal(run(a, b, variant="splitk", split_k=s), base, f"split {s}")
+
+
+def test_caller_workspace_is_used_and_needs_no_reset():
+    M, N, K = 512, 512, 8192
+    A = synth.matrix(M, K, 6003, 0)
+    B = synth.matrix(K, N, 6003, 1)
+    a, b = to_dev(A), to_dev(B)
+    need = g.workspace_bytes(M, N, K, variant="splitk", split_k=8)
+    ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    first = run(a, b, workspace=ws, variant="splitk", split_k=8)
+    ws.fill_(12345.0)
+    assert_bits_equal(run(a, b, workspace=ws, variant="splitk", split_k=8), first, "workspace")
+    rows = np.array([0, 255, 511])
+    check(first[rows], reference(A, B, rows), "uniform", "workspace")
+    with pytest.raises(g.GemmError) as e:
+        g.gemm(a, b, workspace=ws[:16], variant="splitk", split_k=8)
+    assert e.value.status == -6
+
+
+def test_wrapper_rejects_bad_arguments():
+    a = torch.zeros((4, 8), dtype=torch.float16, device=DEV)
+    b = torch.zeros((8, 3), dtype=torch.float16, device=DEV)
+    with pytest.raises(TypeError):
+        g.gemm(a.float(), b)
+    with pytest.raises(ValueError):
+        g.gemm(a, b.t())
+    with pytest.raises(ValueError):
+        g.gemm(a[:0], b)
+    with pytest.raises(ValueError):
+        g.gemm(a.cpu(), b)
+    big = torch.zeros(64, dtype=torch.float16, device=DEV)
+    with pytest.raises(g.GemmError) as e:                  # output overlapping an input
+        g.gemm(big[:32].view(4, 8), b, out=big[16:28].view(4, 3))
+    assert e.value.status == -5
