@@ -22,7 +22,8 @@
 #include <cstring>
 
 #include "../../include/gemm_f16.h"
-#include "tile_kernel.hpp"
+#include "reduce_kernel.hpp"
+#include "tiles.hpp"
 
 using namespace gemmf16;
 
@@ -30,53 +31,11 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
-// Tile configurations: <BM, BN, BK, waves along m, waves along n, MFMA edge>.
-typedef TileCfg<128, 128, 64, 2, 2, 32> CfgT128;  // main / split-K
-typedef TileCfg<64, 32, 32, 2, 2, 16> CfgT64x32;  // the pages' 64x32x32 geometry
-typedef TileCfg<16, 256, 64, 1, 4, 16> CfgS16;    // skinny, M <= 16
-typedef TileCfg<32, 256, 64, 1, 4, 32> CfgS32;    // skinny, M <= 32
-typedef TileCfg<64, 256, 64, 1, 4, 32> CfgS64;    // skinny, M <= 64
-
-enum TileId { TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5, TILE_MAX = 5 };
-
-typedef void (*kfn_t)(KArgs);
-
-struct TileInfo {
-  int id, bm, bn, bk, nt;
-  kfn_t final_fn[9];    // [a_path * 3 + b_path]
-  kfn_t partial_fn[9];
-};
-
-template <class CF, bool P>
-void fill_fns(kfn_t* f) {
-  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P>;
-  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P>;
-  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P>;
-  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P>;
-  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P>;
-  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P>;
-  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P>;
-  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P>;
-  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P>;
-}
-
-template <class CF>
-TileInfo make_info(int id) {
-  TileInfo t;
-  t.id = id;
-  t.bm = CF::BM;
-  t.bn = CF::BN;
-  t.bk = CF::BK;
-  t.nt = CF::NT;
-  fill_fns<CF, false>(t.final_fn);
-  fill_fns<CF, true>(t.partial_fn);
-  return t;
-}
-
 const TileInfo& tile_info(int id) {
   static const TileInfo table[TILE_MAX + 1] = {
-      TileInfo{}, make_info<CfgT128>(TILE_T128), make_info<CfgT64x32>(TILE_T64X32),
-      make_info<CfgS16>(TILE_S16), make_info<CfgS32>(TILE_S32), make_info<CfgS64>(TILE_S64)};
+      TileInfo{},           tile_info_t128(),     tile_info_t64x32(), tile_info_s16(),
+      tile_info_s32(),      tile_info_s64(),      tile_info_t256(),   tile_info_t256x128(),
+      tile_info_t128x256(),   tile_info_t256w8a(), tile_info_t256w8b(), tile_info_dma256()};
   return table[id];
 }
 
@@ -199,9 +158,21 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     }
   }
 
+  p.a_path = classify(c.A, c.lda_m, c.lda_k);
+  p.b_path = classify(c.B, c.ldb_n, c.ldb_k);
+
   // Tile.
   switch (p.variant) {
     case GEMM_VARIANT_MAIN:
+      if (want_tile) {
+        p.tile_id = want_tile;
+      } else {
+        // 256x256 tiles once they give at least half a wave of workgroups.
+        if ((rc = need_cus())) return rc;
+        const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
+        p.tile_id = (2 * t256 >= cus) ? TILE_DMA256 : TILE_T128;
+      }
+      break;
     case GEMM_VARIANT_SPLITK:
       p.tile_id = want_tile ? want_tile : TILE_T128;
       break;
@@ -215,6 +186,16 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
       break;
     default:
       return GEMM_ERR_OPTS;
+  }
+  // A tile whose kernels do not cover this operand layout hands over to its
+  // fallback (the LDS-DMA tile needs K-contiguous A and, for N-contiguous B,
+  // N a multiple of 8).
+  for (;;) {
+    const TileInfo& t = tile_info(p.tile_id);
+    const bool ok = t.final_fn[p.a_path * 3 + p.b_path] != nullptr &&
+                    !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult));
+    if (ok) break;
+    p.tile_id = t.fallback;
   }
   const TileInfo& ti = tile_info(p.tile_id);
   p.GM = cdiv(c.M, ti.bm);
@@ -241,10 +222,10 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   if (want_panel != 0)
     p.panel = want_panel;
   else
-    p.panel = (p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_TILE64X32) ? 8 : -1;
+    p.panel = (p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_TILE64X32)
+                  ? (ti.bm >= 256 ? 4 : 8)
+                  : -1;
 
-  p.a_path = classify(c.A, c.lda_m, c.lda_k);
-  p.b_path = classify(c.B, c.ldb_n, c.ldb_k);
   p.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
 
   int64_t grid;

@@ -108,6 +108,12 @@ struct OperandStage {
   }
 
   // Load the tile's k range [k0, k0 + BK), clipped at k_end (exclusive).
+  //   ROWMASK: some rows of the tile may lie outside [0, R_tot).  Such rows
+  //            are read from the last valid row (an in-bounds address) and
+  //            replaced by zeros, or skipped entirely on the RVEC path.
+  //   KMASK:   the k range may end inside the tile (the last K step).
+  // With neither flag the loads are straight-line code with no branches.
+  template <bool ROWMASK, bool KMASK>
   __device__ __forceinline__ void load(int64_t k0, int64_t k_end) {
     if constexpr (PATH == PATH_RVEC) {
 #pragma unroll
@@ -117,19 +123,25 @@ struct OperandStage {
         const int g = unit % (R / 8), c = unit / (R / 8);
         const int64_t rr = r0 + 8 * g;            // first row of the 8-row group
         const int64_t kk = k0 + 8 * c;            // first k of the octet
-        int nr = (int)((R_tot - rr) < 8 ? (R_tot - rr) : 8);
-        int nk = (int)((k_end - kk) < 8 ? (k_end - kk) : 8);
-        if (nr < 0) nr = 0;
-        if (nk < 0) nk = 0;
+        int nk = 8;
+        if constexpr (KMASK) {
+          const int64_t d = k_end - kk;
+          nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
+        }
+        int nr = 8;
+        if constexpr (ROWMASK) {
+          const int64_t d = R_tot - rr;
+          nr = d < 0 ? 0 : (d < 8 ? (int)d : 8);
+        }
         const uint16_t* p = base + (nr > 0 ? rr : 0) + (nk > 0 ? kk : 0) * s_k;
+        if (!ROWMASK || nr == 8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (e < nk && nr == 8)
-            v[u * 8 + e] = *reinterpret_cast<const u32x4*>(p + e * s_k);
-          else if (e < nk && nr > 0)
-            v[u * 8 + e] = load_partial8(p + e * s_k, 1, nr);
-          else
-            v[u * 8 + e] = zero4();
+          for (int e = 0; e < 8; ++e)
+            v[u * 8 + e] = (!KMASK || e < nk) ? *reinterpret_cast<const u32x4*>(p + e * s_k) : zero4();
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            v[u * 8 + e] = (e < nk && nr > 0) ? load_partial8(p + e * s_k, 1, nr) : zero4();
         }
       }
     } else {
@@ -138,21 +150,30 @@ struct OperandStage {
       for (int i = 0; i < CPT; ++i) {
         const int cell = tid + NT * i;
         if (CELLS % NT != 0 && cell >= CELLS) break;
-        const int r = cell / OCT;
-        const int64_t rr = r0 + r;
+        int64_t rr = r0 + cell / OCT;
+        bool rv = true;
+        if constexpr (ROWMASK) {
+          rv = rr < R_tot;
+          rr = rv ? rr : R_tot - 1;
+        }
         const int64_t kk = k0 + 8 * c;
-        int nk = (int)((k_end - kk) < 8 ? (k_end - kk) : 8);
-        if (nk < 0 || rr >= R_tot) nk = 0;
-        if (nk == 0) {
-          v[i] = zero4();
-          continue;
+        int nk = 8;
+        if constexpr (KMASK) {
+          const int64_t d = k_end - kk;
+          nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
         }
-        const uint16_t* p = base + rr * s_r + kk * s_k;
+        const uint16_t* p = base + rr * s_r + (nk > 0 ? kk : 0) * s_k;
+        u32x4 x;
         if constexpr (PATH == PATH_KVEC) {
-          v[i] = (nk == 8) ? *reinterpret_cast<const u32x4*>(p) : load_partial8(p, 1, nk);
+          if (!KMASK || nk == 8)
+            x = *reinterpret_cast<const u32x4*>(p);
+          else
+            x = load_partial8(p, 1, nk);
         } else {
-          v[i] = load_partial8(p, s_k, nk);
+          x = load_partial8(p, s_k, nk);
         }
+        if constexpr (ROWMASK) x = rv ? x : zero4();
+        v[i] = x;
       }
     }
   }

@@ -19,8 +19,9 @@
 // "neighbouring programs share cache", last paragraph): with PARTIAL the
 // workgroup writes its fp32 partial tile to W[split][M][N] instead of C, and
 // splitk_reduce sums the partials in ascending split order, so the result is
-// bit-identical from run to run (no atomics).  fp32 partials, never fp16
-// (TileLang tutorial ch. 14, pitfall 4).
+// bit-identical from run to run (no atomics; the reduction kernel is in
+// reduce_kernel.hpp).  fp32 partials, never fp16 (TileLang tutorial ch. 14,
+// pitfall 4).
 #pragma once
 
 #include "tile_common.hpp"
@@ -105,10 +106,85 @@ __device__ __forceinline__ void store4_f32(const KArgs& a, int64_t split, int64_
   }
 }
 
+// MFMAs of one BK step from one LDS stage.  Operand fragments are double
+// buffered in registers: the reads for k-step ks+1 are issued before the
+// MFMAs of k-step ks so LDS latency hides behind matrix work.
+template <class CF>
+__device__ __forceinline__ void compute_stage(const char* ta, const char* tb,
+                                              typename Acc<CF::MI>::type (&acc)[CF::FN][CF::FM],
+                                              int wm, int wn, int lane) {
+  constexpr int MI = CF::MI, KI = CF::KI, KS = CF::BK / KI;
+  const int lr = lane % MI, lc = lane / MI;
+  f16x8 fa[2][CF::FN], fb[2][CF::FM];
+  auto read = [&](int ks, int slot) {
+    const int c = ks * (KI / 8) + lc;
+#pragma unroll
+    for (int i = 0; i < CF::FN; ++i)
+      fa[slot][i] = *reinterpret_cast<const f16x8*>(tb + cell_off<CF::BN>(wn * CF::WTN + i * MI + lr, c));
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j)
+      fb[slot][j] = *reinterpret_cast<const f16x8*>(ta + cell_off<CF::BM>(wm * CF::WTM + j * MI + lr, c));
+  };
+  read(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) read(ks + 1, (ks + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<MI>(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+  }
+}
+
+// The K loop over [kb, ke): full BK steps run branch-free; a ragged last step
+// (K or the split end not a multiple of BK) is loaded with K masks.  Two LDS
+// stages: while stage t is consumed, step t+1 is fetched into registers and
+// then written to the other stage; one barrier per step.
+template <class CF, bool ROWMASK, class SA, class SB>
+__device__ __forceinline__ void main_loop(SA& sa, SB& sb, char* smem,
+                                          typename Acc<CF::MI>::type (&acc)[CF::FN][CF::FM],
+                                          int64_t kb, int64_t ke, int wm, int wn, int lane) {
+  constexpr int BK = CF::BK;
+  const int64_t nfull = (ke - kb) / BK;
+  const bool tail = (ke - kb) % BK != 0;
+  if (nfull > 0) {
+    sa.template load<ROWMASK, false>(kb, ke);
+    sb.template load<ROWMASK, false>(kb, ke);
+  } else {
+    sa.template load<ROWMASK, true>(kb, ke);
+    sb.template load<ROWMASK, true>(kb, ke);
+  }
+  sa.store(smem);
+  sb.store(smem + CF::A_BYTES);
+  __syncthreads();
+  int64_t t = 0;
+  for (; t + 1 < nfull; ++t) {
+    const int cur = (int)(t & 1);
+    sa.template load<ROWMASK, false>(kb + (t + 1) * BK, ke);
+    sb.template load<ROWMASK, false>(kb + (t + 1) * BK, ke);
+    compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
+    sa.store(smem + (cur ^ 1) * CF::STAGE);
+    sb.store(smem + (cur ^ 1) * CF::STAGE + CF::A_BYTES);
+    __syncthreads();
+  }
+  if (tail && nfull > 0) {
+    const int cur = (int)(t & 1);
+    sa.template load<ROWMASK, true>(kb + nfull * BK, ke);
+    sb.template load<ROWMASK, true>(kb + nfull * BK, ke);
+    compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
+    sa.store(smem + (cur ^ 1) * CF::STAGE);
+    sb.store(smem + (cur ^ 1) * CF::STAGE + CF::A_BYTES);
+    __syncthreads();
+    ++t;
+  }
+  const int cur = (int)(t & 1);
+  compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
+}
+
 template <class CF, int APATH, int BPATH, bool PARTIAL>
 __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
-  constexpr int BK = CF::BK, MI = CF::MI, KI = CF::KI;
+  constexpr int BK = CF::BK, MI = CF::MI;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
@@ -140,49 +216,17 @@ __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
       for (int e = 0; e < Acc<MI>::N; ++e) acc[i][j][e] = 0.0f;
 
-  const int64_t nk = (ke - kb + BK - 1) / BK;
-  sa.load(kb, ke);
-  sb.load(kb, ke);
-  sa.store(smem);
-  sb.store(smem + CF::A_BYTES);
-  __syncthreads();
-
-  // Lane's position inside an MFMA operand block: row lane % MI, octet lane / MI.
-  const int lr = lane % MI, lc = lane / MI;
-  for (int64_t it = 0; it < nk; ++it) {
-    const int cur = (int)(it & 1);
-    if (it + 1 < nk) {
-      sa.load(kb + (it + 1) * BK, ke);
-      sb.load(kb + (it + 1) * BK, ke);
-    }
-    const char* ta = smem + cur * CF::STAGE;
-    const char* tb = ta + CF::A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < BK / KI; ++ks) {
-      const int c = ks * (KI / 8) + lc;
-      f16x8 fa[CF::FN], fb[CF::FM];
-#pragma unroll
-      for (int i = 0; i < CF::FN; ++i)
-        fa[i] = *reinterpret_cast<const f16x8*>(tb + cell_off<CF::BN>(wn * CF::WTN + i * MI + lr, c));
-#pragma unroll
-      for (int j = 0; j < CF::FM; ++j)
-        fb[j] = *reinterpret_cast<const f16x8*>(ta + cell_off<CF::BM>(wm * CF::WTM + j * MI + lr, c));
-#pragma unroll
-      for (int i = 0; i < CF::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<MI>(fa[i], fb[j], acc[i][j]);
-    }
-    if (it + 1 < nk) {
-      sa.store(smem + (cur ^ 1) * CF::STAGE);
-      sb.store(smem + (cur ^ 1) * CF::STAGE + CF::A_BYTES);
-    }
-    __syncthreads();
-  }
+  const bool interior = (m0 + CF::BM <= a.M) && (n0 + CF::BN <= a.N);
+  if (interior)
+    main_loop<CF, false>(sa, sb, smem, acc, kb, ke, wm, wn, lane);
+  else
+    main_loop<CF, true>(sa, sb, smem, acc, kb, ke, wm, wn, lane);
 
   // Epilogue.  MFMA output layout (C^T block, MI x MI): lane holds column
   // j = lane % MI (our m) and, for register group g, 4 consecutive rows
   // (our n) starting at 8g + 4*(lane/32) for MI = 32, 4*(lane/16) for MI = 16.
   constexpr int G = Acc<MI>::N / 4;
+  const int lr = lane % MI;
 #pragma unroll
   for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
@@ -200,44 +244,6 @@ __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
           store4_f16(a, m, n, v0, v1, v2, v3);
       }
     }
-}
-
-// C[m][n] = fp16_rne( sum_{s=0}^{S-1} W[s][m][n] ), ascending s.  Each thread
-// owns 4 consecutive n of one row; grid-stride over the M x ceil(N/4) quads.
-__global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int64_t M, int64_t N,
-                                                     uint16_t* C, int64_t ldc, int c_vec) {
-  const int64_t NQ = (N + 3) / 4;
-  const int64_t total = M * NQ;
-  const int64_t MN = M * N;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = q / NQ, n = (q - m * NQ) * 4;
-    const float* p = W + m * N + n;
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    if ((N & 3) == 0) {
-      for (int s = 0; s < S; ++s) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(p + s * MN);
-        s0 += v[0]; s1 += v[1]; s2 += v[2]; s3 += v[3];
-      }
-    } else {
-      for (int s = 0; s < S; ++s) {
-        const float* ps = p + s * MN;
-        s0 += ps[0];
-        if (n + 1 < N) s1 += ps[1];
-        if (n + 2 < N) s2 += ps[2];
-        if (n + 3 < N) s3 += ps[3];
-      }
-    }
-    uint16_t* c = C + m * ldc + n;
-    const _Float16 h[4] = {(_Float16)s0, (_Float16)s1, (_Float16)s2, (_Float16)s3};
-    if (c_vec && n + 4 <= N) {
-      *reinterpret_cast<f16x4*>(c) = f16x4{h[0], h[1], h[2], h[3]};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < N) reinterpret_cast<_Float16*>(c)[e] = h[e];
-    }
-  }
 }
 
 }  // namespace gemmf16

@@ -1,0 +1,6 @@
+// Kernel instantiations for one tile configuration (see tiles.hpp).
+#include "tiles.hpp"
+
+namespace gemmf16 {
+TileInfo tile_info_t128() { return make_info<CfgT128>(TILE_T128); }
+}  // namespace gemmf16

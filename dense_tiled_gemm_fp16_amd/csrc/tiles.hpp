@@ -1,0 +1,100 @@
+// Tile configurations and the per-configuration kernel tables.  Each
+// configuration is instantiated in its own translation unit (tile_<id>.hip)
+// so the library builds in parallel; the host side only sees TileInfo.
+#pragma once
+
+#include "dma_kernel.hpp"
+#include "tile_kernel.hpp"
+
+namespace gemmf16 {
+
+// <BM, BN, BK, waves along m, waves along n, MFMA edge>
+typedef TileCfg<128, 128, 64, 2, 2, 32> CfgT128;    // main / split-K, mid-size problems
+typedef TileCfg<64, 32, 32, 2, 2, 16> CfgT64x32;    // the pages' 64x32x32 geometry
+typedef TileCfg<16, 256, 64, 1, 4, 16> CfgS16;      // skinny, M <= 16
+typedef TileCfg<32, 256, 64, 1, 4, 32> CfgS32;      // skinny, M <= 32
+typedef TileCfg<64, 256, 64, 1, 4, 32> CfgS64;      // skinny, M <= 64
+typedef TileCfg<256, 256, 64, 2, 2, 32> CfgT256;    // large problems, 128x128 per wave
+typedef TileCfg<256, 128, 64, 2, 2, 32> CfgT256x128;
+typedef TileCfg<128, 256, 64, 2, 2, 32> CfgT128x256;
+typedef TileCfg<256, 256, 64, 2, 4, 32> CfgT256W8A;  // 8 waves, 128x64 per wave
+typedef TileCfg<256, 256, 64, 4, 2, 32> CfgT256W8B;  // 8 waves, 64x128 per wave
+typedef DmaCfg<4> CfgDma256;                        // 256x256x32, 4-stage LDS-DMA ring
+
+enum TileId {
+  TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5,
+  TILE_T256 = 6, TILE_T256X128 = 7, TILE_T128X256 = 8, TILE_T256W8A = 9,
+  TILE_T256W8B = 10, TILE_DMA256 = 11, TILE_MAX = 11
+};
+
+typedef void (*kfn_t)(KArgs);
+
+struct TileInfo {
+  int id, bm, bn, bk, nt;
+  kfn_t final_fn[9];    // [a_path * 3 + b_path]; nullptr = layout not supported
+  kfn_t partial_fn[9];
+  int fallback;         // tile used for layouts this one does not support
+  int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
+};
+
+template <class CF, bool P>
+void fill_fns(kfn_t* f) {
+  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P>;
+  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P>;
+  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P>;
+  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P>;
+  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P>;
+  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P>;
+  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P>;
+  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P>;
+  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P>;
+}
+
+template <class CF>
+TileInfo make_info(int id) {
+  TileInfo t;
+  t.id = id;
+  t.bm = CF::BM;
+  t.bn = CF::BN;
+  t.bk = CF::BK;
+  t.nt = CF::NT;
+  fill_fns<CF, false>(t.final_fn);
+  fill_fns<CF, true>(t.partial_fn);
+  t.fallback = 0;
+  t.n_mult = 0;
+  return t;
+}
+
+// The LDS-DMA kernel takes K-contiguous A with K- or N-contiguous B only.
+template <class CF>
+TileInfo make_dma_info(int id, int fallback) {
+  TileInfo t;
+  t.id = id;
+  t.bm = CF::BM;
+  t.bn = CF::BN;
+  t.bk = CF::BK;
+  t.nt = CF::NT;
+  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = nullptr;
+  t.final_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, false>;
+  t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false>;
+  t.partial_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true>;
+  t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, true>;
+  t.fallback = fallback;
+  t.n_mult = 8;
+  return t;
+}
+
+// Defined in tile_<id>.hip.
+TileInfo tile_info_t128();
+TileInfo tile_info_t64x32();
+TileInfo tile_info_s16();
+TileInfo tile_info_s32();
+TileInfo tile_info_s64();
+TileInfo tile_info_t256();
+TileInfo tile_info_t256x128();
+TileInfo tile_info_t128x256();
+TileInfo tile_info_t256w8a();
+TileInfo tile_info_t256w8b();
+TileInfo tile_info_dma256();
+
+}  // namespace gemmf16

@@ -103,7 +103,8 @@ def check(gpu, ref, mode, what):
 VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"),
             dict(variant="splitk", split_k=2), dict(variant="splitk", split_k=3),
             dict(variant="splitk", split_k=7), dict(variant="main", panel=-1),
-            dict(variant="main", panel=1), dict(variant="main", tile=3)]
+            dict(variant="main", panel=1), dict(variant="main", tile=3),
+            dict(variant="main", tile=11), dict(variant="splitk", tile=11, split_k=3)]
 
 
 # ------------------------------------------------------------------ the edge case
