@@ -45,19 +45,23 @@
 
 namespace gemmf16 {
 
-template <int STAGES_>
+template <int STAGES_, int WAVES_M_ = 2, int WAVES_N_ = 2>
 struct DmaCfg {
   static constexpr int BM = 256, BN = 256, BK = 32, STAGES = STAGES_;
-  static constexpr int WAVES_M = 2, WAVES_N = 2, NT = 256;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * NW;
   static constexpr int MI = 32, KI = 16, KS = BK / KI;   // 2 MFMA k-steps per stage
-  static constexpr int WTM = 128, WTN = 128, FM = 4, FN = 4;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;   // 16 KiB each
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS = STAGES * STAGE;
-  static constexpr int DMA_A = A_BYTES / 1024 / 4;   // DMA instructions per wave per stage
-  static constexpr int DMA_B = B_BYTES / 1024 / 4;
+  static constexpr int DMA_A = A_BYTES / 1024 / NW;   // DMA instructions per wave per stage
+  static constexpr int DMA_B = B_BYTES / 1024 / NW;
   static constexpr int DMA_PER_STAGE = DMA_A + DMA_B;
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(DMA_A * NW * 1024 == A_BYTES && DMA_B * NW * 1024 == B_BYTES, "DMA split");
+  static_assert(FN * FM >= 4, "DMA placement");
 };
 
 // octet slot permutation of the 64-byte rows: distinct banks for 8 and for 16
@@ -94,6 +98,38 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
                : "memory", "m0");
 }
 
+// NI consecutive 1 KiB DMA slots with a single m0: the instruction offset is
+// added to both the global and the LDS address, so the source pointer of
+// slot i is biased by -1024*i bytes (-512 elements) and the offset restores
+// it.  One m0 write per batch instead of one per instruction keeps the wave
+// from stalling on m0 rewrites between MFMAs.
+template <int NI>
+__device__ __forceinline__ void dma16_batch(const uint16_t* const* p, int64_t off, uint32_t lds) {
+  static_assert(NI == 1 || NI == 2 || NI == 4, "batch size");
+  if constexpr (NI == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, off offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, off offset:3072"
+        :
+        : "s"(lds), "v"(p[0] + off), "v"(p[1] + off - 512), "v"(p[2] + off - 1024),
+          "v"(p[3] + off - 1536)
+        : "memory", "m0");
+  } else if constexpr (NI == 2) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %2, off offset:1024"
+        :
+        : "s"(lds), "v"(p[0] + off), "v"(p[1] + off - 512)
+        : "memory", "m0");
+  } else {
+    dma16(p[0] + off, lds);
+  }
+}
+
 __device__ __forceinline__ f16x8 read_tr_pair(const char* p0, const char* p1) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
@@ -119,13 +155,13 @@ struct DmaSource {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if constexpr (KMAJOR) {
-        const int r = (4 * wave + i) * 16 + lane / 4;
+        const int r = (NI * wave + i) * 16 + lane / 4;
         const int c = (lane % 4) ^ fa(r);
         int64_t rr = r0 + r;
         if (rr > R_tot - 1) rr = R_tot - 1;
         p[i] = base + rr * s_r + (kb + 8 * c) * s_k;
       } else {
-        const int k = (4 * wave + i) * 2 + lane / 32;
+        const int k = (NI * wave + i) * 2 + lane / 32;
         const int slot = lane % 32;
         const int b = (slot / 2) ^ hb(k);
         int64_t n = r0 + b * 16 + (slot % 2) * 8;
@@ -136,11 +172,15 @@ struct DmaSource {
     step = (int64_t)32 * s_k;
   }
 
-  // Issue the DMA of the step `t` BK-steps past kb into the stage at lds.
+  // All of this wave's DMA instructions of the step `t` BK-steps past kb,
+  // into the operand area whose first slot for this wave is at lds_wave.
+  __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
+    dma16_batch<NI>(p, t * step, lds_wave);
+  }
+
+  // Same, from a pointer to the operand area of a stage.
   __device__ __forceinline__ void issue(const char* lds_op, int wave, int64_t t) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_op) + 4 * wave * 1024);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(p[i] + t * step, base + i * 1024);
+    issue_batch(__builtin_amdgcn_readfirstlane(lds_addr(lds_op) + NI * wave * 1024), t);
   }
 
   // Masked register fill of a ragged step (k < k_end kept, zero fill), into
@@ -152,18 +192,18 @@ struct DmaSource {
       const uint16_t* q = p[i] + t * step;
       u32x4 v;
       if constexpr (KMAJOR) {
-        const int r = (4 * wave + i) * 16 + lane / 4;
+        const int r = (NI * wave + i) * 16 + lane / 4;
         const int c = (lane % 4) ^ fa(r);
         const int64_t kk = kb + t * 32 + 8 * c;
         const int64_t d = k_end - kk;
         const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
         v = load_partial8(q, s_k, nk);
       } else {
-        const int k = (4 * wave + i) * 2 + lane / 32;
+        const int k = (NI * wave + i) * 2 + lane / 32;
         const bool ok = kb + t * 32 + k < k_end;
         v = ok ? *reinterpret_cast<const u32x4*>(q) : zero4();
       }
-      *reinterpret_cast<u32x4*>(lds_op + (4 * wave + i) * 1024 + lane * 16) = v;
+      *reinterpret_cast<u32x4*>(lds_op + (NI * wave + i) * 1024 + lane * 16) = v;
     }
   }
 };
@@ -205,6 +245,25 @@ __device__ __forceinline__ void read_frags(DmaFrags<CF>& f, const char* ta, cons
   }
 }
 
+// The MFMAs of one k-step with this wave's DMA batches of the step
+// STAGES-1 ahead placed a quarter and three quarters of the way through, so
+// their address and m0 setup issue in the shadow of matrix work.
+template <class CF, class SA, class SB>
+__device__ __forceinline__ void mma_frags_dma(const DmaFrags<CF>& f, f32x16 (&acc)[CF::FN][CF::FM],
+                                              SA& sa, SB& sb, uint32_t la, uint32_t lb,
+                                              int64_t t) {
+  constexpr int NQ = CF::FN * CF::FM;
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.fa_[i], f.fb_[j], acc[i][j], 0, 0, 0);
+      const int q = i * CF::FM + j;
+      if (q == NQ / 4 - 1) sa.issue_batch(la, t);
+      if (q == 3 * NQ / 4 - 1) sb.issue_batch(lb, t);
+    }
+}
+
 template <class CF>
 __device__ __forceinline__ void mma_frags(const DmaFrags<CF>& f, f32x16 (&acc)[CF::FN][CF::FM]) {
 #pragma unroll
@@ -215,7 +274,7 @@ __device__ __forceinline__ void mma_frags(const DmaFrags<CF>& f, f32x16 (&acc)[C
 }
 
 template <class CF, bool BKMAJOR, bool PARTIAL>
-__global__ __launch_bounds__(256) void gemm_dma_kernel(KArgs a) {
+__global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -256,37 +315,42 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(KArgs a) {
   DmaFrags<CF> f0, f1;
 
   if (nfull > 0) {
-    // Prologue: steps 0 .. STAGES-2 in flight; steps 0 and 1 complete.
-    const int64_t pro = nfull < CF::STAGES - 1 ? nfull : CF::STAGES - 1;
-    for (int64_t t = 0; t < pro; ++t) {
-      sa.issue(stage_a(t), wave, t);
-      sb.issue(stage_b(t), wave, t);
+    // Prologue: steps 0 .. STAGES-2 in flight (clamped to the last full step
+    // when there are fewer), steps 0 and 1 complete.
+    for (int64_t t = 0; t < CF::STAGES - 1; ++t) {
+      const int64_t tt = t < nfull ? t : nfull - 1;
+      sa.issue(stage_a(t), wave, tt);
+      sb.issue(stage_b(t), wave, tt);
     }
-    if (pro >= 3)
-      wait_vmcnt<CF::DMA_PER_STAGE * (CF::STAGES - 3)>();
-    else
-      wait_vmcnt<0>();
+    wait_vmcnt<CF::DMA_PER_STAGE * (CF::STAGES - 3)>();
     wg_barrier();
     read_frags<CF, BKMAJOR>(f0, stage_a(0), stage_b(0), 0, wm, wn, lane);
 
+    // Steady state, branch-free.  Phases are fenced with sched_barrier so
+    // each batch of LDS reads is issued a whole k-step (16 MFMAs) before its
+    // use.  In the last STAGES-1 steps the DMA re-loads the last full step
+    // into the stage of step t-1, which no wave reads any more.
     for (int64_t t = 0; t < nfull; ++t) {
-      const bool issue = t + CF::STAGES - 1 < nfull;
-      if (issue) {
-        sa.issue(stage_a(t + CF::STAGES - 1), wave, t + CF::STAGES - 1);
-        sb.issue(stage_b(t + CF::STAGES - 1), wave, t + CF::STAGES - 1);
-      }
+      const int64_t ahead = t + CF::STAGES - 1;
+      const int64_t tt = ahead < nfull ? ahead : nfull - 1;
+      const uint32_t la =
+          __builtin_amdgcn_readfirstlane(lds_addr(stage_a(ahead)) + CF::DMA_A * wave * 1024);
+      const uint32_t lb =
+          __builtin_amdgcn_readfirstlane(lds_addr(stage_b(ahead)) + CF::DMA_B * wave * 1024);
       read_frags<CF, BKMAJOR>(f1, stage_a(t), stage_b(t), 1, wm, wn, lane);
-      mma_frags<CF>(f0, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_frags_dma<CF>(f0, acc, sa, sb, la, lb, tt);
+      __builtin_amdgcn_sched_barrier(0);
       // First fragments of step t+1 (complete since the last barrier).  On
       // the last step this reads a stale stage and the values go unused.
       read_frags<CF, BKMAJOR>(f0, stage_a(t + 1), stage_b(t + 1), 0, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
       mma_frags<CF>(f1, acc);
-      if (issue)
-        wait_vmcnt<CF::DMA_PER_STAGE * (CF::STAGES - 3)>();   // step t+2 landed
-      else
-        wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<CF::DMA_PER_STAGE * (CF::STAGES - 3)>();   // step t+2 landed
       wg_barrier();
     }
+    wait_vmcnt<0>();   // no LDS transfer may still be in flight past this point
   }
   if (tail) {
     // Ragged last step: masked fill of stage nfull % STAGES (free: every read

@@ -20,11 +20,14 @@ typedef TileCfg<128, 256, 64, 2, 2, 32> CfgT128x256;
 typedef TileCfg<256, 256, 64, 2, 4, 32> CfgT256W8A;  // 8 waves, 128x64 per wave
 typedef TileCfg<256, 256, 64, 4, 2, 32> CfgT256W8B;  // 8 waves, 64x128 per wave
 typedef DmaCfg<4> CfgDma256;                        // 256x256x32, 4-stage LDS-DMA ring
+typedef DmaCfg<4, 2, 4> CfgDma256W8A;               // same tile, 8 waves of 128x64
+typedef DmaCfg<4, 4, 2> CfgDma256W8B;               // same tile, 8 waves of 64x128
 
 enum TileId {
   TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5,
   TILE_T256 = 6, TILE_T256X128 = 7, TILE_T128X256 = 8, TILE_T256W8A = 9,
-  TILE_T256W8B = 10, TILE_DMA256 = 11, TILE_MAX = 11
+  TILE_T256W8B = 10, TILE_DMA256 = 11, TILE_DMA256W8A = 12,
+  TILE_DMA256W8B = 13, TILE_MAX = 13
 };
 
 typedef void (*kfn_t)(KArgs);
@@ -96,5 +99,7 @@ TileInfo tile_info_t128x256();
 TileInfo tile_info_t256w8a();
 TileInfo tile_info_t256w8b();
 TileInfo tile_info_dma256();
+TileInfo tile_info_dma256w8a();
+TileInfo tile_info_dma256w8b();
 
 }  // namespace gemmf16

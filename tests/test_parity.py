@@ -104,7 +104,8 @@ VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"
             dict(variant="splitk", split_k=2), dict(variant="splitk", split_k=3),
             dict(variant="splitk", split_k=7), dict(variant="main", panel=-1),
             dict(variant="main", panel=1), dict(variant="main", tile=3),
-            dict(variant="main", tile=11), dict(variant="splitk", tile=11, split_k=3)]
+            dict(variant="main", tile=11), dict(variant="splitk", tile=11, split_k=3),
+            dict(variant="main", tile=13), dict(variant="splitk", tile=13, split_k=2)]
 
 
 # ------------------------------------------------------------------ the edge case
