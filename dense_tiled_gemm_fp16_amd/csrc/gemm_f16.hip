@@ -22,6 +22,7 @@
 #include <cstring>
 
 #include "../../include/gemm_f16.h"
+#include "gemv_kernel.hpp"
 #include "reduce_kernel.hpp"
 #include "tiles.hpp"
 
@@ -30,6 +31,13 @@ using namespace gemmf16;
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
+
+// The decode-shaped VALU kernel: rows of B per thread per pass.
+constexpr int kGemvRpt = 8;
+constexpr int64_t kGemvRowsPerPass = 8 * kGemvRpt;
+
+typedef void (*kfn_gemv)(GemvArgs);
+typedef void (*kfn_reduce)(const float*, int, int64_t, int64_t, uint16_t*, int64_t, int);
 
 const TileInfo& tile_info(int id) {
   static const TileInfo table[TILE_MAX + 1] = {
@@ -85,6 +93,8 @@ int classify(const void* base, int64_t s_r, int64_t s_k) {
 
 struct Plan {
   int variant, tile_id, split, panel, a_path, b_path, c_vec;
+  int gemv_mt;  // > 0: the decode-shaped VALU kernel with this many A rows
+  int red_lanes;  // lanes per output quad in the split reduction
   int64_t GM, GN, grid, grid2, k_split;
   size_t ws;
 };
@@ -133,6 +143,28 @@ void set_split(Plan& p, int64_t K, int bk, int64_t split) {
   p.split = (int)cdiv(K, ks);
 }
 
+// Workspace and reduction launch of a plan with p.split K ranges.  The
+// reduction's lane-group width depends on the output size only, so a forced
+// plan needs no device query: small outputs (decode shapes) spread each
+// output's sum over more lanes to hide the latency of the partials' loads.
+int plan_partials(const Call& c, Plan& p) {
+  p.ws = 0;
+  p.grid2 = 0;
+  p.red_lanes = 1;
+  if (p.split <= 1) return GEMM_OK;
+  int64_t mn, bytes;
+  if (__builtin_mul_overflow(c.M, c.N, &mn) || __builtin_mul_overflow(mn, (int64_t)p.split, &bytes) ||
+      __builtin_mul_overflow(bytes, (int64_t)4, &bytes) || bytes > INT64_MAX - 256)
+    return GEMM_ERR_SHAPE;
+  p.ws = (size_t)((bytes + 255) / 256 * 256);
+  const int64_t quads = c.M * cdiv(c.N, 4);
+  p.red_lanes = (quads <= 16384 && p.split >= 16) ? 16 : ((quads <= 65536 && p.split >= 4) ? 4 : 1);
+  int64_t g2 = cdiv(quads * p.red_lanes, 256);
+  if (g2 > 8192) g2 = 8192;
+  p.grid2 = g2;
+  return GEMM_OK;
+}
+
 int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   int rc = check_opts(o);
   if (rc) return rc;
@@ -158,6 +190,12 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
       p.variant = (2 * T <= cus && c.K >= 4 * mn) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
     }
   }
+
+  // Option combinations that no plan accepts are rejected before any device
+  // query.
+  if ((p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_TILE64X32) && want_split > 1)
+    return GEMM_ERR_OPTS;
+  if (p.variant == GEMM_VARIANT_SKINNY && c.M > 64) return GEMM_ERR_OPTS;
 
   p.a_path = classify(c.A, c.lda_m, c.lda_k);
   p.b_path = classify(c.B, c.ldb_n, c.ldb_k);
@@ -188,6 +226,31 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     default:
       return GEMM_ERR_OPTS;
   }
+  // M <= 4 with N-contiguous B: the decode-shaped VALU kernel (from M = 5 on
+  // the 16-row MFMA skinny tile streams B as fast and spends less VALU time).
+  p.gemv_mt = 0;
+  p.red_lanes = 1;
+  if (p.variant == GEMM_VARIANT_SKINNY && !want_tile && c.M <= 4 && p.b_path == PATH_RVEC) {
+    p.gemv_mt = c.M <= 1 ? 1 : (c.M <= 2 ? 2 : 4);
+    p.GM = 1;
+    p.GN = cdiv(c.N, 256);
+    int64_t s = want_split;
+    if (s == 0) {
+      if ((rc = need_cus())) return rc;
+      s = cdiv(2 * (int64_t)cus, p.GN);  // about two workgroups per compute unit
+    }
+    p.k_split = cdiv(cdiv(c.K, s), kGemvRowsPerPass) * kGemvRowsPerPass;
+    p.split = (int)cdiv(c.K, p.k_split);
+    p.panel = -1;
+    p.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
+    int64_t grid;
+    if (__builtin_mul_overflow(p.GN, (int64_t)p.split, &grid) || grid > INT32_MAX)
+      return GEMM_ERR_SHAPE;
+    p.grid = grid;
+    p.tile_id = TILE_S16;   // reported tile id of the skinny family
+    return plan_partials(c, p);
+  }
+
   // A tile whose kernels do not cover this operand layout hands over to its
   // fallback (the LDS-DMA tile needs K-contiguous A and, for N-contiguous B,
   // N a multiple of 8).
@@ -233,28 +296,15 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   if (__builtin_mul_overflow(T, (int64_t)p.split, &grid) || grid > (INT64_C(1) << 32) / ti.nt - 1)
     return GEMM_ERR_SHAPE;
   p.grid = grid;
-  p.ws = 0;
-  p.grid2 = 0;
-  if (p.split > 1) {
-    int64_t mn, bytes;
-    if (__builtin_mul_overflow(c.M, c.N, &mn) || __builtin_mul_overflow(mn, (int64_t)p.split, &bytes) ||
-        __builtin_mul_overflow(bytes, (int64_t)4, &bytes) || bytes > INT64_MAX - 256)
-      return GEMM_ERR_SHAPE;
-    p.ws = (size_t)((bytes + 255) / 256 * 256);
-    const int64_t quads = c.M * cdiv(c.N, 4);
-    int64_t g2 = cdiv(quads, 256);
-    if (g2 > 8192) g2 = 8192;
-    p.grid2 = g2;
-  }
-  return GEMM_OK;
+  return plan_partials(c, p);
 }
 
 void fill_info(const Plan& p, gemm_f16_plan_info* info) {
   const TileInfo& ti = tile_info(p.tile_id);
   info->variant = p.variant;
-  info->tile_m = ti.bm;
-  info->tile_n = ti.bn;
-  info->tile_k = ti.bk;
+  info->tile_m = p.gemv_mt ? p.gemv_mt : ti.bm;
+  info->tile_n = p.gemv_mt ? 256 : ti.bn;
+  info->tile_k = p.gemv_mt ? (int32_t)kGemvRowsPerPass : ti.bk;
   info->split_k = p.split;
   info->panel = p.panel;
   info->a_path = p.a_path;
@@ -265,7 +315,49 @@ void fill_info(const Plan& p, gemm_f16_plan_info* info) {
   info->workspace_bytes = p.ws;
 }
 
+// Second launch of a split plan: sum the partials in ws into C.
+int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
+  if (p.split <= 1) return GEMM_OK;
+  const float* W = (const float*)ws;
+  int S = p.split;
+  int64_t M = c.M, N = c.N, ldc = c.ldc;
+  uint16_t* C = (uint16_t*)c.C;
+  int cv = p.c_vec;
+  kfn_reduce fn = p.red_lanes == 16 ? splitk_reduce<16> : (p.red_lanes == 4 ? splitk_reduce<4> : splitk_reduce<1>);
+  void* rargs[] = {&W, &S, &M, &N, &C, &ldc, &cv};
+  if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid2), dim3(256), rargs, 0, stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+template <int MT>
+kfn_gemv pick_gemv() { return gemv_kernel<MT, kGemvRpt>; }
+
+int launch_gemv(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
+  GemvArgs g;
+  g.A = (const uint16_t*)c.A;
+  g.lda_m = c.lda_m;
+  g.lda_k = c.lda_k;
+  g.B = (const uint16_t*)c.B;
+  g.ldb_k = c.ldb_k;
+  g.C = (uint16_t*)c.C;
+  g.ldc = c.ldc;
+  g.P = (float*)ws;
+  g.M = c.M;
+  g.N = c.N;
+  g.K = c.K;
+  g.kr = p.k_split;
+  g.GN = (int32_t)p.GN;
+  g.S = p.split;
+  kfn_gemv fn = p.gemv_mt == 1 ? pick_gemv<1>() : p.gemv_mt == 2 ? pick_gemv<2>() : pick_gemv<4>();
+  void* args[] = {&g};
+  if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(256), args, 0, stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return launch_reduce(c, p, ws, stream);
+}
+
 int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
+  if (p.gemv_mt) return launch_gemv(c, p, ws, stream);
   const TileInfo& ti = tile_info(p.tile_id);
   KArgs a;
   a.A = (const uint16_t*)c.A;
@@ -290,18 +382,7 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
-  if (p.split > 1) {
-    const float* W = (const float*)ws;
-    int S = p.split;
-    int64_t M = c.M, N = c.N, ldc = c.ldc;
-    uint16_t* C = (uint16_t*)c.C;
-    int cv = p.c_vec;
-    void* rargs[] = {&W, &S, &M, &N, &C, &ldc, &cv};
-    if (hipLaunchKernel((const void*)splitk_reduce, dim3((unsigned)p.grid2), dim3(256), rargs, 0,
-                        stream) != hipSuccess)
-      return GEMM_ERR_HIP;
-  }
-  return GEMM_OK;
+  return launch_reduce(c, p, ws, stream);
 }
 
 }  // namespace

@@ -1,45 +1,81 @@
 // Second pass of split K: the fixed-order reduction of fp32 partials.
-// Included by the host translation unit only (a non-template kernel).
+// Included by the host translation unit only (non-inline kernels).
 #pragma once
 
 #include "tile_common.hpp"
 
 namespace gemmf16 {
 
-// C[m][n] = fp16_rne( sum_{s=0}^{S-1} W[s][m][n] ), ascending s.  Each thread
-// owns 4 consecutive n of one row; grid-stride over the M x ceil(N/4) quads.
+// C[m][n] = fp16_rne( sum over s of W[s][m][n] ) in a fixed order.
+//
+// A group of L consecutive lanes owns 4 consecutive n of one row (a "quad");
+// lane j of the group sums the contiguous block of K ranges
+// [j * ceil(S/L), (j+1) * ceil(S/L)) in ascending s, and the group then adds
+// the L block sums in ascending j.  For a given (S, L) the order is fixed, so
+// results are bit-reproducible; the host picks L from the output size only.
+// Loads are issued eight at a time before they are added, so that a lane
+// waits for one memory round trip per eight partials rather than per partial
+// (the partials of a small output were written by other XCDs and come from
+// memory, not from this XCD's L2).
+template <int L>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int64_t M, int64_t N,
                                                      uint16_t* C, int64_t ldc, int c_vec) {
+  static_assert(L >= 1 && 64 % L == 0, "a lane group lies inside one wave");
   const int64_t NQ = (N + 3) / 4;
   const int64_t total = M * NQ;
   const int64_t MN = M * N;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * blockDim.x) {
+  const int lane = (int)(threadIdx.x % L);
+  const int per = (S + L - 1) / L;
+  const int sb = lane * per < S ? lane * per : S;
+  const int se = sb + per < S ? sb + per : S;
+  const int64_t step = (int64_t)gridDim.x * (blockDim.x / L);
+  for (int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / L; q < total; q += step) {
     const int64_t m = q / NQ, n = (q - m * NQ) * 4;
+    const int nv = (N - n < 4) ? (int)(N - n) : 4;
     const float* p = W + m * N + n;
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    if ((N & 3) == 0) {
-      for (int s = 0; s < S; ++s) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(p + s * MN);
-        s0 += v[0]; s1 += v[1]; s2 += v[2]; s3 += v[3];
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = sb; s0 < se; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float* ps = p + (int64_t)(s0 + j) * MN;
+        if (s0 + j >= se) {
+          v[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        } else if ((N & 3) == 0) {
+          v[j] = *reinterpret_cast<const f32x4*>(ps);
+        } else {
+          v[j] = f32x4{ps[0], nv > 1 ? ps[1] : 0.0f, nv > 2 ? ps[2] : 0.0f, nv > 3 ? ps[3] : 0.0f};
+        }
       }
-    } else {
-      for (int s = 0; s < S; ++s) {
-        const float* ps = p + s * MN;
-        s0 += ps[0];
-        if (n + 1 < N) s1 += ps[1];
-        if (n + 2 < N) s2 += ps[2];
-        if (n + 3 < N) s3 += ps[3];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < se) {
+          acc[0] += v[j][0];
+          acc[1] += v[j][1];
+          acc[2] += v[j][2];
+          acc[3] += v[j][3];
+        }
+    }
+    float tot[4] = {acc[0], acc[1], acc[2], acc[3]};
+    if constexpr (L > 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) t += __shfl(acc[e], j, L);
+        tot[e] = t;
       }
     }
-    uint16_t* c = C + m * ldc + n;
-    const _Float16 h[4] = {(_Float16)s0, (_Float16)s1, (_Float16)s2, (_Float16)s3};
-    if (c_vec && n + 4 <= N) {
-      *reinterpret_cast<f16x4*>(c) = f16x4{h[0], h[1], h[2], h[3]};
-    } else {
+    if (lane == 0) {
+      uint16_t* c = C + m * ldc + n;
+      const _Float16 h[4] = {(_Float16)tot[0], (_Float16)tot[1], (_Float16)tot[2], (_Float16)tot[3]};
+      if (c_vec && nv == 4) {
+        *reinterpret_cast<f16x4*>(c) = f16x4{h[0], h[1], h[2], h[3]};
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < N) reinterpret_cast<_Float16*>(c)[e] = h[e];
+        for (int e = 0; e < 4; ++e)
+          if (e < nv) reinterpret_cast<_Float16*>(c)[e] = h[e];
+      }
     }
   }
 }
