@@ -35,6 +35,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skinny-reps", type=int, default=400, help="decode calls timed")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 1 GiB device copy (a known-size reference for HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -60,6 +65,62 @@ def measured_traffic(kind):
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
     return e.get("bytes_per_launch")
+
+
+COPY_KIB = float(1 << 20)      # the calibration copy reads and writes 1 GiB
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """Per-launch HBM bytes of this build's kernels from FETCH_SIZE / WRITE_SIZE.
+
+    Each counter is scaled by bytes-moved / counter-reading of the 1 GiB
+    device copy (the largest dispatches of the runtime's copy kernel in the
+    same run), so the factor absorbs whatever fraction of the memory
+    channels the counter samples."""
+    import csv
+    import statistics
+
+    def load(path, counter):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        copy = sorted(per.get("__amd_rocclr_copyBuffer", []))[-3:]
+        if not copy:
+            raise SystemExit(f"{path}: no calibration copy found (run with --copy-calibration)")
+        return per, COPY_KIB / statistics.median(copy)
+
+    fetch, f_scale = load(fetch_csv, "FETCH_SIZE")
+    write, w_scale = load(write_csv, "WRITE_SIZE")
+
+    def kernel(substr):
+        names = [k for k in fetch if substr in k]
+        if not names:
+            return None
+        name = max(names, key=lambda k: statistics.mean(fetch[k]))
+        fb = statistics.mean(fetch[name]) * f_scale * 1024.0
+        wb = statistics.mean(write.get(name, [0.0])) * w_scale * 1024.0
+        return name, fb, wb
+
+    out = {"calibration": {"copy_bytes": COPY_KIB * 1024, "fetch_scale": f_scale,
+                           "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer"},
+           "source_hash": kernel_source_hash()}
+    alg = {"main_131072x2048x7168": ("gemm_dma_kernel", 2.0 * (M * K + K * N), 2.0 * M * N),
+           "skinny_m1_partials": ("gemv_kernel", 2.0 * (K + K * N), None),
+           "skinny_m1_reduce": ("splitk_reduce", None, 2.0 * N)}
+    for key, (sub, alg_read, alg_write) in alg.items():
+        k = kernel(sub)
+        if k is None:
+            continue
+        name, fb, wb = k
+        out[key] = {"kernel": name, "fetch_bytes": fb, "write_bytes": wb,
+                    "bytes_per_launch": fb + wb, "algorithmic_read_bytes": alg_read,
+                    "algorithmic_write_bytes": alg_write, "source_hash": out["source_hash"]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def timed_launches(fn, stream, steps, warmup):
@@ -105,6 +166,9 @@ def cpu_baseline(budget_s=15.0):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this GEMM build "
               "has no multi-GPU path; see DESIGN.md for how it would shard.", file=sys.stderr)
@@ -121,6 +185,14 @@ def main():
 
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- headline workload
     a = to_dev(synth.matrix(M, K, 4001, synth.TENSOR_A))
