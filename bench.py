@@ -106,7 +106,7 @@ def summarize_pmc(fetch_csv, write_csv):
     out = {"calibration": {"copy_bytes": COPY_KIB * 1024, "fetch_scale": f_scale,
                            "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer"},
            "source_hash": kernel_source_hash()}
-    alg = {"main_131072x2048x7168": ("gemm_dma_kernel", 2.0 * (M * K + K * N), 2.0 * M * N),
+    alg = {"main_131072x2048x7168": ("gemm_dma", 2.0 * (M * K + K * N), 2.0 * M * N),
            "skinny_m1_partials": ("gemv_kernel", 2.0 * (K + K * N), None),
            "skinny_m1_reduce": ("splitk_reduce", None, 2.0 * N)}
     for key, (sub, alg_read, alg_write) in alg.items():

@@ -1,0 +1,281 @@
+// LDS-DMA main kernel with full-line A rows (gfx950).
+//
+// The same method and k-step schedule as dma_kernel.hpp (one workgroup per
+// 256 x 256 tile, 32-k steps, MFMA 32x32x16, counted waits and a raw
+// barrier), with one change in how A reaches LDS.  There, a 32-k step of a
+// K-contiguous A row is 64 bytes, so each global_load_lds_dwordx4 touches
+// sixteen half-used 128-byte lines, and the load path's cost follows the
+// number of lines touched rather than the bytes moved.  Here A is staged 64 k
+// at a time in 128-byte LDS rows ("super-steps"): one DMA instruction covers
+// eight whole lines, half as many per byte.
+//
+// LDS: three A super-slots of 256 x 64 (32 KiB each) and four B stages of
+// 32 x 256 (16 KiB each), 160 KiB in all.  In k-step t = 2u + h a wave issues
+// half h of A super-step u + 2 and all of its B k-step t + 3, so every step
+// issues the same four instructions and "all but this step's" is one fixed
+// vmcnt.  Super-step u + 2 overwrites the slot of super-step u - 1, whose
+// last reads were before the barrier that ended step 2u - 1.
+//
+// A slot layout: row r at r * 128 bytes; its octet c (k 8c .. 8c+7 of the
+// super-step) in 16-byte slot c ^ f8(r), with f8(r) = (r ^ (r >> 3)) & 7, so
+// that 8 consecutive rows, and 16 consecutive rows of one parity, reading
+// the same octet hit distinct 16-byte bank groups.
+//
+// A ragged remainder of fewer than 64 k (an odd number of full 32-k steps
+// and/or a K tail) is filled by masked register loads with zero fill after
+// the pipelined loop.
+#pragma once
+
+#include "dma_kernel.hpp"
+
+namespace gemmf16 {
+
+template <int WAVES_M_ = 4, int WAVES_N_ = 2>
+struct DmaA128Cfg {
+  static constexpr int BM = 256, BN = 256, BK = 32;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * NW;
+  static constexpr int MI = 32, KI = 16, KS = BK / KI;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_SLOT = BM * 64 * 2, A_SLOTS = 3;     // 32 KiB per 64-k super-step
+  static constexpr int B_STAGE = BN * BK * 2, B_STAGES = 4;   // 16 KiB per 32-k step
+  static constexpr int B_BASE = A_SLOTS * A_SLOT;
+  static constexpr int LDS = B_BASE + B_STAGES * B_STAGE;
+  static constexpr int DMA_A = A_SLOT / 1024 / NW;            // per wave per super-step
+  static constexpr int DMA_B = B_STAGE / 1024 / NW;           // per wave per step
+  static constexpr int DMA_PER_STEP = DMA_A / 2 + DMA_B;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert((DMA_A == 4 || DMA_A == 8) && DMA_A * NW * 1024 == A_SLOT, "DMA split (A)");
+  static_assert(DMA_B * NW * 1024 == B_STAGE, "DMA split (B)");
+  static_assert(FN * FM >= 4, "DMA placement");
+};
+
+__device__ __forceinline__ int f8(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Per-lane sources of this wave's NI A instructions of a super-step:
+// instruction i covers rows (NI w + i) * 8 .. +8; lane l -> row +l/8, 16-byte
+// slot l%8 -> octet (l%8) ^ f8(row).  Rows past M read the last valid row.
+template <int NI>
+struct ASource128 {
+  const uint16_t* p[NI];
+  int64_t step;  // elements per 64-k super-step
+
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t s_r, int64_t s_k,
+                                       int64_t R_tot, int64_t r0, int64_t kb, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (NI * wave + i) * 8 + lane / 8;
+      const int c = (lane % 8) ^ f8(r);
+      int64_t rr = r0 + r;
+      if (rr > R_tot - 1) rr = R_tot - 1;
+      p[i] = base + rr * s_r + (kb + 8 * c) * s_k;
+    }
+    step = (int64_t)64 * s_k;
+  }
+
+  // Instructions H*NI/2 .. of super-step u into LDS at lds (the slot's byte
+  // address of the first of them for this wave).
+  template <int H>
+  __device__ __forceinline__ void issue_half(uint32_t lds, int64_t u) {
+    dma16_batch<NI / 2>(&p[H * (NI / 2)], u * step, lds);
+  }
+
+  // Masked register fill of the 64 k from k0 (k < k_end kept, zero fill)
+  // into the same LDS bytes the DMA would write.
+  __device__ __forceinline__ void fill_masked(char* slot, int wave, int lane, int64_t u, int64_t kb,
+                                              int64_t k_end, int64_t s_k) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (NI * wave + i) * 8 + lane / 8;
+      const int c = (lane % 8) ^ f8(r);
+      const int64_t kk = kb + u * 64 + 8 * c;
+      const int64_t d = k_end - kk;
+      const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
+      const u32x4 v = load_partial8(p[i] + (nk > 0 ? u * step : 0), s_k, nk);
+      *reinterpret_cast<u32x4*>(slot + (NI * wave + i) * 1024 + lane * 16) = v;
+    }
+  }
+};
+
+// Fragments of k-substep ks of the 32-k step in half H of a super-step.
+template <class CF, int H>
+__device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta, const char* tb,
+                                                int ks, int wm, int wn, int lane) {
+  const int lr = lane % 32, lo = lane / 32;
+  const int c = 4 * H + 2 * ks + lo;
+#pragma unroll
+  for (int j = 0; j < CF::FM; ++j) {
+    const int r = wm * CF::WTM + j * 32 + lr;
+    f.fb_[j] = *reinterpret_cast<const f16x8*>(ta + r * 128 + ((c ^ f8(r)) * 16));
+  }
+  const int g = lane / 16, s = lane % 16;
+  const int kr = ks * 16 + 8 * (g / 2) + s / 4;
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i) {
+    const int n = wn * CF::WTN + i * 32 + 16 * (g % 2);
+    const char* p0 = tb + kr * 512 + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
+    f.fa_[i] = read_tr_pair(p0, p0 + 4 * 512);
+  }
+}
+
+template <class CF, int H, class SA, class SB>
+__device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
+                                                   f32x16 (&acc)[CF::FN][CF::FM], SA& sa,
+                                                   SB& sb, uint32_t la, uint32_t lb, int64_t ua,
+                                                   int64_t tb) {
+  constexpr int NQ = CF::FN * CF::FM;
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.fa_[i], f.fb_[j], acc[i][j], 0, 0, 0);
+      const int q = i * CF::FM + j;
+      if (q == NQ / 4 - 1) sa.template issue_half<H>(la, ua);
+      if (q == 3 * NQ / 4 - 1) sb.issue_batch(lb, tb);
+    }
+}
+
+// K-contiguous A, N-contiguous B only.
+template <class CF, bool PARTIAL>
+__global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+
+  const int64_t T = a.GM * a.GN;
+  int64_t w = blockIdx.x;
+  int64_t split = 0;
+  if constexpr (PARTIAL) {
+    split = w / T;
+    w -= split * T;
+  }
+  int64_t pm, pn;
+  raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
+  const int64_t kb = split * a.k_split;
+  const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
+
+  ASource128<CF::DMA_A> sa;
+  DmaSource<CF::DMA_B, false> sb;
+  sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, kb, wave, lane);
+  sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, kb, wave, lane);
+
+  f32x16 acc[CF::FN][CF::FM];
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto slot_a = [&](int64_t u) { return smem + (int)(u % CF::A_SLOTS) * CF::A_SLOT; };
+  auto stage_b = [&](int64_t t) { return smem + CF::B_BASE + (int)(t % CF::B_STAGES) * CF::B_STAGE; };
+  auto lds_a = [&](int64_t u, int h) {
+    return __builtin_amdgcn_readfirstlane(lds_addr(slot_a(u)) + (CF::DMA_A * wave + (CF::DMA_A / 2) * h) * 1024);
+  };
+  auto lds_b = [&](int64_t t) {
+    return __builtin_amdgcn_readfirstlane(lds_addr(stage_b(t)) + CF::DMA_B * wave * 1024);
+  };
+
+  const int64_t nsup = (ke - kb) / 64;     // whole 64-k super-steps
+  const int64_t nfull2 = 2 * nsup;         // 32-k steps they hold
+  const int64_t rem = (ke - kb) - 64 * nsup;
+  DmaFrags<CF> f0, f1;
+
+  if (nsup > 0) {
+    // Prologue: A super-steps 0 and 1, B steps 0, 1, 2 (clamped); then A(0),
+    // B(0) and B(1) complete (only A(1) and B(2) may still be in flight).
+    const int64_t u1 = nsup > 1 ? 1 : 0;
+    sa.template issue_half<0>(lds_a(0, 0), 0);
+    sa.template issue_half<1>(lds_a(0, 1), 0);
+    sb.issue_batch(lds_b(0), 0);
+    sb.issue_batch(lds_b(1), 1);
+    sa.template issue_half<0>(lds_a(1, 0), u1);
+    sa.template issue_half<1>(lds_a(1, 1), u1);
+    sb.issue_batch(lds_b(2), nfull2 > 2 ? 2 : nfull2 - 1);
+    wait_vmcnt<CF::DMA_A + CF::DMA_B>();
+    wg_barrier();
+    read_frags_a128<CF, 0>(f0, slot_a(0), stage_b(0), 0, wm, wn, lane);
+
+    for (int64_t u = 0; u < nsup; ++u) {
+      const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
+      // ---- step t = 2u (first half of super-step u)
+      {
+        const int64_t t = 2 * u;
+        const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
+        const uint32_t la = lds_a(u + 2, 0), lb = lds_b(t + 3);
+        read_frags_a128<CF, 0>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags_dma_a128<CF, 0>(f0, acc, sa, sb, la, lb, ua, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags_a128<CF, 1>(f0, slot_a(u), stage_b(t + 1), 0, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags<CF>(f1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<CF::DMA_PER_STEP>();
+        wg_barrier();
+      }
+      // ---- step t = 2u + 1 (second half)
+      {
+        const int64_t t = 2 * u + 1;
+        const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
+        const uint32_t la = lds_a(u + 2, 1), lb = lds_b(t + 3);
+        read_frags_a128<CF, 1>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags_dma_a128<CF, 1>(f0, acc, sa, sb, la, lb, ua, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        // First fragments of step t+1 (super-step u+1; stale and unused on
+        // the last step).
+        read_frags_a128<CF, 0>(f0, slot_a(u + 1), stage_b(t + 1), 0, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags<CF>(f1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<CF::DMA_PER_STEP>();
+        wg_barrier();
+      }
+    }
+    wait_vmcnt<0>();   // no LDS transfer may still be in flight past this point
+  }
+  if (rem > 0) {
+    // Remainder (< 64 k): masked fill of A super-slot nsup and B stages of
+    // steps nfull2 and nfull2 + 1, all free after the last barrier.
+    sa.fill_masked(slot_a(nsup), wave, lane, nsup, kb, ke, a.lda_k);
+    sb.fill_masked(stage_b(nfull2), wave, lane, nfull2, kb, ke, a.ldb_k);
+    if (rem > 32) sb.fill_masked(stage_b(nfull2 + 1), wave, lane, nfull2 + 1, kb, ke, a.ldb_k);
+    __syncthreads();
+    read_frags_a128<CF, 0>(f0, slot_a(nsup), stage_b(nfull2), 0, wm, wn, lane);
+    read_frags_a128<CF, 0>(f1, slot_a(nsup), stage_b(nfull2), 1, wm, wn, lane);
+    mma_frags<CF>(f0, acc);
+    mma_frags<CF>(f1, acc);
+    if (rem > 32) {
+      read_frags_a128<CF, 1>(f0, slot_a(nsup), stage_b(nfull2 + 1), 0, wm, wn, lane);
+      read_frags_a128<CF, 1>(f1, slot_a(nsup), stage_b(nfull2 + 1), 1, wm, wn, lane);
+      mma_frags<CF>(f0, acc);
+      mma_frags<CF>(f1, acc);
+    }
+  }
+
+  // Epilogue: the same C^T-block layout as the other kernels.
+  const int lr = lane % 32;
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j) {
+      const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if constexpr (PARTIAL)
+          store4_f32(a, split, m, n, v0, v1, v2, v3);
+        else
+          store4_f16(a, m, n, v0, v1, v2, v3);
+      }
+    }
+}
+
+}  // namespace gemmf16

@@ -44,7 +44,7 @@ const TileInfo& tile_info(int id) {
       TileInfo{},           tile_info_t128(),     tile_info_t64x32(), tile_info_s16(),
       tile_info_s32(),      tile_info_s64(),      tile_info_t256(),   tile_info_t256x128(),
       tile_info_t128x256(),   tile_info_t256w8a(), tile_info_t256w8b(), tile_info_dma256(),
-      tile_info_dma256w8a(), tile_info_dma256w8b()};
+      tile_info_dma256w8a(), tile_info_dma256w8b(), tile_info_dma256a128()};
   return table[id];
 }
 
@@ -209,7 +209,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
         // 256x256 tiles once they give at least half a wave of workgroups.
         if ((rc = need_cus())) return rc;
         const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
-        p.tile_id = (2 * t256 >= cus) ? TILE_DMA256W8B : TILE_T128;
+        p.tile_id = (2 * t256 >= cus) ? TILE_DMA256A128 : TILE_T128;
       }
       break;
     case GEMM_VARIANT_SPLITK:

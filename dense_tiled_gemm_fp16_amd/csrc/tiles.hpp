@@ -3,6 +3,7 @@
 // so the library builds in parallel; the host side only sees TileInfo.
 #pragma once
 
+#include "dma_a128_kernel.hpp"
 #include "dma_kernel.hpp"
 #include "tile_kernel.hpp"
 
@@ -22,12 +23,13 @@ typedef TileCfg<256, 256, 64, 4, 2, 32> CfgT256W8B;  // 8 waves, 64x128 per wave
 typedef DmaCfg<4> CfgDma256;                        // 256x256x32, 4-stage LDS-DMA ring
 typedef DmaCfg<4, 2, 4> CfgDma256W8A;               // same tile, 8 waves of 128x64
 typedef DmaCfg<4, 4, 2> CfgDma256W8B;               // same tile, 8 waves of 64x128
+typedef DmaA128Cfg<4, 2> CfgDmaA128;                // same tile, A staged in 128-byte rows
 
 enum TileId {
   TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5,
   TILE_T256 = 6, TILE_T256X128 = 7, TILE_T128X256 = 8, TILE_T256W8A = 9,
   TILE_T256W8B = 10, TILE_DMA256 = 11, TILE_DMA256W8A = 12,
-  TILE_DMA256W8B = 13, TILE_MAX = 13
+  TILE_DMA256W8B = 13, TILE_DMA256A128 = 14, TILE_MAX = 14
 };
 
 typedef void (*kfn_t)(KArgs);
@@ -87,6 +89,23 @@ TileInfo make_dma_info(int id, int fallback) {
   return t;
 }
 
+// The full-line-A LDS-DMA kernel takes K-contiguous A with N-contiguous B.
+template <class CF>
+TileInfo make_dma_a128_info(int id, int fallback) {
+  TileInfo t;
+  t.id = id;
+  t.bm = CF::BM;
+  t.bn = CF::BN;
+  t.bk = CF::BK;
+  t.nt = CF::NT;
+  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = nullptr;
+  t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false>;
+  t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, true>;
+  t.fallback = fallback;
+  t.n_mult = 8;
+  return t;
+}
+
 // Defined in tile_<id>.hip.
 TileInfo tile_info_t128();
 TileInfo tile_info_t64x32();
@@ -101,5 +120,6 @@ TileInfo tile_info_t256w8b();
 TileInfo tile_info_dma256();
 TileInfo tile_info_dma256w8a();
 TileInfo tile_info_dma256w8b();
+TileInfo tile_info_dma256a128();
 
 }  // namespace gemmf16

@@ -105,7 +105,8 @@ VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"
             dict(variant="splitk", split_k=7), dict(variant="main", panel=-1),
             dict(variant="main", panel=1), dict(variant="main", tile=3),
             dict(variant="main", tile=11), dict(variant="splitk", tile=11, split_k=3),
-            dict(variant="main", tile=13), dict(variant="splitk", tile=13, split_k=2)]
+            dict(variant="main", tile=13), dict(variant="splitk", tile=13, split_k=2),
+            dict(variant="main", tile=14), dict(variant="splitk", tile=14, split_k=3)]
 
 
 # ------------------------------------------------------------------ the edge case
@@ -210,6 +211,26 @@ def test_square_sampled(n):
     ref = reference(A, B, rows)
     gpu = run(to_dev(A), to_dev(B))
     check(gpu[rows], ref, "uniform", f"square {n}")
+
+
+# ------------------------------------------------------------------ LDS-DMA tiles, K remainders
+
+@pytest.mark.parametrize("tile", [13, 14])
+@pytest.mark.parametrize("K", [32, 64, 96, 100, 160, 241])
+def test_dma_tiles_k_remainders(tile, K):
+    # Whole 64-k super-steps, an odd 32-k step and ragged K tails, on a tile
+    # grid with ragged M and N edges; integer sums stay exact in fp32.
+    M, N = 300, 264
+    for mode in ("int", "uniform"):
+        A = synth.matrix(M, K, 8000 + K, 0, mode)
+        B = synth.matrix(K, N, 8000 + K, 1, mode)
+        ref = reference(A, B)
+        # A's rows padded with NaN to a multiple of 8 elements: the K tail of
+        # every row is followed by poison that must never be read.
+        a, b = place(A, "row", (1, (-K) % 8 + 8)), to_dev(B)
+        assert g.plan(a, b, variant="main", tile=tile)["tile_id"] == tile
+        for kw in (dict(variant="main", tile=tile), dict(variant="splitk", tile=tile, split_k=3)):
+            check(run(a, b, Out(M, N), **kw), ref, mode, f"dma tile K={K} {mode} {kw}")
 
 
 # ------------------------------------------------------------------ skinny / decode
