@@ -98,8 +98,10 @@ struct ASource128 {
   }
 };
 
-// Fragments of k-substep ks of the 32-k step in half H of a super-step.
-template <class CF, int H>
+// Fragments of k-substep ks of the 32-k step in half H of a super-step.  B
+// stages are laid out as in dma_kernel.hpp: N-major 512-byte k-rows, or,
+// for a K-contiguous B (BKMAJOR), 64-byte n-rows like its A tiles.
+template <class CF, int H, bool BKMAJOR>
 __device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta, const char* tb,
                                                 int ks, int wm, int wn, int lane) {
   const int lr = lane % 32, lo = lane / 32;
@@ -109,13 +111,22 @@ __device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta,
     const int r = wm * CF::WTM + j * 32 + lr;
     f.fb_[j] = *reinterpret_cast<const f16x8*>(ta + r * 128 + ((c ^ f8(r)) * 16));
   }
-  const int g = lane / 16, s = lane % 16;
-  const int kr = ks * 16 + 8 * (g / 2) + s / 4;
+  if constexpr (BKMAJOR) {
+    const int cb = ks * 2 + lo;
 #pragma unroll
-  for (int i = 0; i < CF::FN; ++i) {
-    const int n = wn * CF::WTN + i * 32 + 16 * (g % 2);
-    const char* p0 = tb + kr * 512 + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
-    f.fa_[i] = read_tr_pair(p0, p0 + 4 * 512);
+    for (int i = 0; i < CF::FN; ++i) {
+      const int r = wn * CF::WTN + i * 32 + lr;
+      f.fa_[i] = *reinterpret_cast<const f16x8*>(tb + r * 64 + ((cb ^ fa(r)) * 16));
+    }
+  } else {
+    const int g = lane / 16, s = lane % 16;
+    const int kr = ks * 16 + 8 * (g / 2) + s / 4;
+#pragma unroll
+    for (int i = 0; i < CF::FN; ++i) {
+      const int n = wn * CF::WTN + i * 32 + 16 * (g % 2);
+      const char* p0 = tb + kr * 512 + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
+      f.fa_[i] = read_tr_pair(p0, p0 + 4 * 512);
+    }
   }
 }
 
@@ -136,8 +147,8 @@ __device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
     }
 }
 
-// K-contiguous A, N-contiguous B only.
-template <class CF, bool PARTIAL>
+// K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
+template <class CF, bool BKMAJOR, bool PARTIAL>
 __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
@@ -159,7 +170,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
 
   ASource128<CF::DMA_A> sa;
-  DmaSource<CF::DMA_B, false> sb;
+  DmaSource<CF::DMA_B, BKMAJOR> sb;
   sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, kb, wave, lane);
   sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, kb, wave, lane);
 
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     sb.issue_batch(lds_b(2), nfull2 > 2 ? 2 : nfull2 - 1);
     wait_vmcnt<CF::DMA_A + CF::DMA_B>();
     wg_barrier();
-    read_frags_a128<CF, 0>(f0, slot_a(0), stage_b(0), 0, wm, wn, lane);
+    read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(0), stage_b(0), 0, wm, wn, lane);
 
     for (int64_t u = 0; u < nsup; ++u) {
       const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
@@ -207,11 +218,11 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
         const int64_t t = 2 * u;
         const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
         const uint32_t la = lds_a(u + 2, 0), lb = lds_b(t + 3);
-        read_frags_a128<CF, 0>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
+        read_frags_a128<CF, 0, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
         mma_frags_dma_a128<CF, 0>(f0, acc, sa, sb, la, lb, ua, tb);
         __builtin_amdgcn_sched_barrier(0);
-        read_frags_a128<CF, 1>(f0, slot_a(u), stage_b(t + 1), 0, wm, wn, lane);
+        read_frags_a128<CF, 1, BKMAJOR>(f0, slot_a(u), stage_b(t + 1), 0, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
         mma_frags<CF>(f1, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -223,13 +234,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
         const int64_t t = 2 * u + 1;
         const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
         const uint32_t la = lds_a(u + 2, 1), lb = lds_b(t + 3);
-        read_frags_a128<CF, 1>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
+        read_frags_a128<CF, 1, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
         mma_frags_dma_a128<CF, 1>(f0, acc, sa, sb, la, lb, ua, tb);
         __builtin_amdgcn_sched_barrier(0);
         // First fragments of step t+1 (super-step u+1; stale and unused on
         // the last step).
-        read_frags_a128<CF, 0>(f0, slot_a(u + 1), stage_b(t + 1), 0, wm, wn, lane);
+        read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(u + 1), stage_b(t + 1), 0, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
         mma_frags<CF>(f1, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -246,13 +257,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     sb.fill_masked(stage_b(nfull2), wave, lane, nfull2, kb, ke, a.ldb_k);
     if (rem > 32) sb.fill_masked(stage_b(nfull2 + 1), wave, lane, nfull2 + 1, kb, ke, a.ldb_k);
     __syncthreads();
-    read_frags_a128<CF, 0>(f0, slot_a(nsup), stage_b(nfull2), 0, wm, wn, lane);
-    read_frags_a128<CF, 0>(f1, slot_a(nsup), stage_b(nfull2), 1, wm, wn, lane);
+    read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(nsup), stage_b(nfull2), 0, wm, wn, lane);
+    read_frags_a128<CF, 0, BKMAJOR>(f1, slot_a(nsup), stage_b(nfull2), 1, wm, wn, lane);
     mma_frags<CF>(f0, acc);
     mma_frags<CF>(f1, acc);
     if (rem > 32) {
-      read_frags_a128<CF, 1>(f0, slot_a(nsup), stage_b(nfull2 + 1), 0, wm, wn, lane);
-      read_frags_a128<CF, 1>(f1, slot_a(nsup), stage_b(nfull2 + 1), 1, wm, wn, lane);
+      read_frags_a128<CF, 1, BKMAJOR>(f0, slot_a(nsup), stage_b(nfull2 + 1), 0, wm, wn, lane);
+      read_frags_a128<CF, 1, BKMAJOR>(f1, slot_a(nsup), stage_b(nfull2 + 1), 1, wm, wn, lane);
       mma_frags<CF>(f0, acc);
       mma_frags<CF>(f1, acc);
     }

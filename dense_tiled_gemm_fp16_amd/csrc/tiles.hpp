@@ -89,7 +89,7 @@ TileInfo make_dma_info(int id, int fallback) {
   return t;
 }
 
-// The full-line-A LDS-DMA kernel takes K-contiguous A with N-contiguous B.
+// The full-line-A LDS-DMA kernel takes K-contiguous A with K- or N-contiguous B.
 template <class CF>
 TileInfo make_dma_a128_info(int id, int fallback) {
   TileInfo t;
@@ -99,8 +99,10 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   t.bk = CF::BK;
   t.nt = CF::NT;
   for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = nullptr;
-  t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false>;
-  t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, true>;
+  t.final_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false>;
+  t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false>;
+  t.partial_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, true>;
+  t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, true>;
   t.fallback = fallback;
   t.n_mult = 8;
   return t;

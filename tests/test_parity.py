@@ -217,7 +217,8 @@ def test_square_sampled(n):
 
 @pytest.mark.parametrize("tile", [13, 14])
 @pytest.mark.parametrize("K", [32, 64, 96, 100, 160, 241])
-def test_dma_tiles_k_remainders(tile, K):
+@pytest.mark.parametrize("b_layout", ["row", "col"])
+def test_dma_tiles_k_remainders(tile, K, b_layout):
     # Whole 64-k super-steps, an odd 32-k step and ragged K tails, on a tile
     # grid with ragged M and N edges; integer sums stay exact in fp32.
     M, N = 300, 264
@@ -225,9 +226,11 @@ def test_dma_tiles_k_remainders(tile, K):
         A = synth.matrix(M, K, 8000 + K, 0, mode)
         B = synth.matrix(K, N, 8000 + K, 1, mode)
         ref = reference(A, B)
-        # A's rows padded with NaN to a multiple of 8 elements: the K tail of
-        # every row is followed by poison that must never be read.
-        a, b = place(A, "row", (1, (-K) % 8 + 8)), to_dev(B)
+        # Rows of A (and of a K-contiguous B) padded with NaN to a multiple of
+        # 8 elements: every K tail is followed by poison that must never be read.
+        pad = (-K) % 8 + 8
+        a = place(A, "row", (1, pad))
+        b = to_dev(B) if b_layout == "row" else place(B, "col", (1, pad))
         assert g.plan(a, b, variant="main", tile=tile)["tile_id"] == tile
         for kw in (dict(variant="main", tile=tile), dict(variant="splitk", tile=tile, split_k=3)):
             check(run(a, b, Out(M, N), **kw), ref, mode, f"dma tile K={K} {mode} {kw}")
