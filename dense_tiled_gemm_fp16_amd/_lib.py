@@ -19,6 +19,7 @@ VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4}
 PATHS = {0: "gather", 1: "kvec", 2: "rvec"}
 
 EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes",
+           "gemm_f16_grouped", "gemm_f16_grouped_workspace_bytes",
            "gemm_f16_status_string", "gemm_f16_version"]
 
 
@@ -50,6 +51,11 @@ def _load():
     lib.gemm_f16_plan.restype = ctypes.c_int
     lib.gemm_f16_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(Opts)]
     lib.gemm_f16_workspace_bytes.restype = sz
+    lib.gemm_f16_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, i64, vp, i32,
+                                     i64, i64, i64, vp, vp, sz]
+    lib.gemm_f16_grouped.restype = ctypes.c_int
+    lib.gemm_f16_grouped_workspace_bytes.argtypes = [i32]
+    lib.gemm_f16_grouped_workspace_bytes.restype = sz
     lib.gemm_f16_status_string.argtypes = [ctypes.c_int]
     lib.gemm_f16_status_string.restype = ctypes.c_char_p
     lib.gemm_f16_version.argtypes = []

@@ -148,8 +148,9 @@ __device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
 }
 
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
-template <class CF, bool BKMAJOR, bool PARTIAL>
+template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false>
 __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
+  static_assert(!(PARTIAL && GROUPED), "grouped launches are never split");
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,7 +165,11 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     w -= split * T;
   }
   int64_t pm, pn;
-  raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  if constexpr (GROUPED) {
+    if (!group_tile(a, w, pm, pn)) return;   // uniform per workgroup, before any barrier
+  } else {
+    raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  }
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
   const int64_t kb = split * a.k_split;
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;

@@ -23,6 +23,7 @@
 
 #include "../../include/gemm_f16.h"
 #include "gemv_kernel.hpp"
+#include "group_kernel.hpp"
 #include "reduce_kernel.hpp"
 #include "tiles.hpp"
 
@@ -377,6 +378,10 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   a.GN = p.GN;
   a.panel = p.panel;
   a.c_vec = p.c_vec;
+  a.g_off = nullptr;
+  a.g_tiles = nullptr;
+  a.ldb_g = 0;
+  a.G = 0;
   const int sel = p.a_path * 3 + p.b_path;
   kfn_t fn = (p.split > 1) ? ti.partial_fn[sel] : ti.final_fn[sel];
   void* args[] = {&a};
@@ -385,9 +390,146 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   return launch_reduce(c, p, ws, stream);
 }
 
+// ---- grouped launches
+
+constexpr int32_t kMaxGroups = 1 << 20;
+
+size_t grouped_ws_bytes(int32_t G) { return (size_t)((16 * ((int64_t)G + 1) + 255) / 256 * 256); }
+
+struct GroupCall {
+  const void *A, *B, *C;
+  const int64_t* off;
+  int64_t lda_m, lda_k, ldb_g, ldb_k, ldb_n, ldc, M, N, K;
+  int32_t G;
+  int64_t spanA, spanB, spanC;
+};
+
+int validate_grouped(GroupCall& c) {
+  if (!c.A || !c.B || !c.C || !c.off) return GEMM_ERR_NULL;
+  if (c.G < 1 || c.G > kMaxGroups || c.M <= 0 || c.N <= 0 || c.K <= 0) return GEMM_ERR_SHAPE;
+  if (c.lda_m <= 0 || c.lda_k <= 0 || c.ldb_k <= 0 || c.ldb_n <= 0 || c.ldb_g < 0)
+    return GEMM_ERR_STRIDE;
+  if (c.ldc < c.N) return GEMM_ERR_LDC;
+  int64_t sb, g_off;
+  if (!view_span(c.M, c.K, c.lda_m, c.lda_k, &c.spanA) || !view_span(c.K, c.N, c.ldb_k, c.ldb_n, &sb) ||
+      !view_span(c.M, c.N, c.ldc, 1, &c.spanC) ||
+      __builtin_mul_overflow((int64_t)(c.G - 1), c.ldb_g, &g_off) ||
+      __builtin_add_overflow(sb, g_off, &c.spanB) || c.spanB > INT64_MAX / 2 - 1)
+    return GEMM_ERR_SHAPE;
+  const uintptr_t a0 = (uintptr_t)c.A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
+  const uintptr_t b0 = (uintptr_t)c.B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+  const uintptr_t c0 = (uintptr_t)c.C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
+  if (a1 < a0 || b1 < b0 || c1 < c0) return GEMM_ERR_SHAPE;
+  if (ranges_overlap(c0, c1, a0, a1) || ranges_overlap(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
+  return GEMM_OK;
+}
+
+// The tile and kernel of a grouped launch: the full-line-A LDS-DMA tile when
+// the groups average at least one of its 256-row tiles and the layouts suit
+// it, the 128 x 128 register-path tile otherwise.
+int grouped_plan(const GroupCall& c, int* tile_id, kfn_t* fn, int64_t* grid) {
+  // Groups start at arbitrary rows, so an M-contiguous A (vectors along m)
+  // would lose its alignment: it takes the element-wise path.
+  int a_path = classify(c.A, c.lda_m, c.lda_k);
+  if (a_path == PATH_RVEC) a_path = PATH_GATHER;
+  const int b_path = classify(c.B, c.ldb_n, c.ldb_k);
+  const bool ldb_g_ok = c.ldb_g % 8 == 0;   // every group's B keeps the 16-byte alignment
+  int id = TILE_T128;
+  const TileInfo& d = tile_info(TILE_DMA256A128);
+  if (ldb_g_ok && c.M >= (int64_t)256 * c.G && d.grouped_fn[a_path * 3 + b_path] &&
+      !(b_path == PATH_RVEC && (c.N % d.n_mult != 0 || c.N < d.n_mult)))
+    id = TILE_DMA256A128;
+  const TileInfo& ti = tile_info(id);
+  // Layout classes were taken on group 0's B; other groups share them only if
+  // ldb_g keeps the alignment, else take the element-wise path for B.
+  const int bp = ldb_g_ok ? b_path : PATH_GATHER;
+  *fn = ti.grouped_fn[a_path * 3 + bp];
+  if (!*fn) return GEMM_ERR_OPTS;
+  const int64_t GN = cdiv(c.N, ti.bn), rows = cdiv(c.M, ti.bm) + c.G;
+  if (__builtin_mul_overflow(rows, GN, grid) || *grid > (INT64_C(1) << 31) - 1) return GEMM_ERR_SHAPE;
+  *tile_id = id;
+  return GEMM_OK;
+}
+
+int launch_grouped(const GroupCall& c, int tile_id, kfn_t fn, int64_t grid, void* ws, hipStream_t s) {
+  const TileInfo& ti = tile_info(tile_id);
+  int64_t* off = (int64_t*)ws;
+  int64_t* tiles = off + (c.G + 1);
+  {
+    const int64_t* oin = c.off;
+    int32_t G = c.G, BM = ti.bm;
+    int64_t M = c.M;
+    void* args[] = {&oin, &G, &M, &BM, &off, &tiles};
+    if (hipLaunchKernel((const void*)group_setup, dim3(1), dim3(1024), args, 0, s) != hipSuccess)
+      return GEMM_ERR_HIP;
+  }
+  KArgs a;
+  a.A = (const uint16_t*)c.A;
+  a.lda_m = c.lda_m;
+  a.lda_k = c.lda_k;
+  a.B = (const uint16_t*)c.B;
+  a.ldb_k = c.ldb_k;
+  a.ldb_n = c.ldb_n;
+  a.C = (uint16_t*)c.C;
+  a.ldc = c.ldc;
+  a.W = nullptr;
+  a.M = c.M;
+  a.N = c.N;
+  a.K = c.K;
+  a.k_split = c.K;
+  a.GM = cdiv(c.M, ti.bm) + c.G;
+  a.GN = cdiv(c.N, ti.bn);
+  a.panel = -1;
+  a.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
+  a.g_off = off;
+  a.g_tiles = tiles;
+  a.ldb_g = c.ldb_g;
+  a.G = c.G;
+  void* args[] = {&a};
+  if (hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(ti.nt), args, 0, s) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_f16_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_g,
+                     int64_t ldb_k, int64_t ldb_n, void* C, int64_t ldc, const int64_t* offsets,
+                     int32_t G, int64_t M_total, int64_t N, int64_t K, void* stream,
+                     void* workspace, size_t workspace_bytes) {
+  GroupCall c{A, B, C, offsets, lda_m, lda_k, ldb_g, ldb_k, ldb_n, ldc, M_total, N, K, G, 0, 0, 0};
+  int rc = validate_grouped(c);
+  if (rc) return rc;
+  int tile_id = 0;
+  kfn_t fn = nullptr;
+  int64_t grid = 0;
+  if ((rc = grouped_plan(c, &tile_id, &fn, &grid))) return rc;
+  const size_t need = grouped_ws_bytes(G);
+  hipStream_t s = (hipStream_t)stream;
+  if (workspace) {
+    if (workspace_bytes < need || ((uintptr_t)workspace & 255u)) return GEMM_ERR_WORKSPACE;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+    const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
+    if (ranges_overlap(w0, w1, a0, a1) || ranges_overlap(w0, w1, b0, b1) ||
+        ranges_overlap(w0, w1, c0, c1))
+      return GEMM_ERR_ALIAS;
+    return launch_grouped(c, tile_id, fn, grid, workspace, s);
+  }
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, need, s) != hipSuccess) return GEMM_ERR_HIP;
+  rc = launch_grouped(c, tile_id, fn, grid, ws, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK) rc = GEMM_ERR_HIP;
+  return rc;
+}
+
+size_t gemm_f16_grouped_workspace_bytes(int32_t G) {
+  return (G < 1 || G > kMaxGroups) ? 0 : grouped_ws_bytes(G);
+}
+
 
 int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
                   int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,

@@ -59,7 +59,45 @@ struct KArgs {
   int64_t GM, GN;    // tile grid
   int32_t panel;     // raster group height, <= 0 = plain order
   int32_t c_vec;     // C rows take 8-byte stores (ldc % 4 == 0, C 8-byte aligned)
+  // Grouped launches only (see group_tile): per-group row offsets (G + 1,
+  // clamped to [0, M]), prefix sums of per-group row tiles (G + 1), the
+  // element distance between consecutive groups' B, and the group count.
+  const int64_t* g_off;
+  const int64_t* g_tiles;
+  int64_t ldb_g;
+  int32_t G;
 };
+
+// Grouped product (TileLang tutorial ch. 14, section 4.3: one launch over
+// several GEMMs that share N and K, with per-group row counts; here group g
+// owns rows [off[g], off[g+1]) of A and C and its own B).  The grid is an
+// upper bound computed without the row counts: workgroups at or past the
+// live count L = tiles[G] * GN return false.  Live ids are first given the
+// XCD remap of raster_tile (each XCD a contiguous run, so the GN workgroups
+// of one row tile share its A rows in one L2); id w then takes row tile
+// t = w / GN of the concatenated per-group tile lists and column tile
+// w % GN.  The group is the last g with tiles[g] <= t (binary search), and A,
+// C, B and M are rebased on it.
+__device__ __forceinline__ bool group_tile(KArgs& a, int64_t w, int64_t& pm, int64_t& pn) {
+  const int64_t L = a.g_tiles[a.G] * a.GN;
+  if (w >= L) return false;
+  const int64_t per = L / 8;
+  if (w < per * 8) w = (w % 8) * per + w / 8;
+  const int64_t t = w / a.GN;
+  pn = w - t * a.GN;
+  int lo = 0, hi = a.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.g_tiles[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int64_t r0 = a.g_off[lo], r1 = a.g_off[lo + 1];
+  pm = t - a.g_tiles[lo];
+  a.A += r0 * a.lda_m;
+  a.C += r0 * a.ldc;
+  a.B += (int64_t)lo * a.ldb_g;
+  a.M = r1 - r0;
+  return true;
+}
 
 template <int MI>
 struct Acc;
@@ -181,8 +219,9 @@ __device__ __forceinline__ void main_loop(SA& sa, SB& sb, char* smem,
   compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
 }
 
-template <class CF, int APATH, int BPATH, bool PARTIAL>
+template <class CF, int APATH, int BPATH, bool PARTIAL, bool GROUPED = false>
 __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
+  static_assert(!(PARTIAL && GROUPED), "grouped launches are never split");
   __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
   constexpr int BK = CF::BK, MI = CF::MI;
   const int tid = threadIdx.x;
@@ -197,7 +236,11 @@ __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
     w -= split * T;
   }
   int64_t pm, pn;
-  raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  if constexpr (GROUPED) {
+    if (!group_tile(a, w, pm, pn)) return;   // uniform per workgroup, before any barrier
+  } else {
+    raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  }
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
   const int64_t kb = split * a.k_split;
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;

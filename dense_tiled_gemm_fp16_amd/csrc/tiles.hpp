@@ -38,24 +38,25 @@ struct TileInfo {
   int id, bm, bn, bk, nt;
   kfn_t final_fn[9];    // [a_path * 3 + b_path]; nullptr = layout not supported
   kfn_t partial_fn[9];
+  kfn_t grouped_fn[9];  // grouped launches (nullptr: not instantiated for this tile)
   int fallback;         // tile used for layouts this one does not support
   int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
 };
 
-template <class CF, bool P>
+template <class CF, bool P, bool G = false>
 void fill_fns(kfn_t* f) {
-  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P>;
-  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P>;
-  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P>;
-  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P>;
-  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P>;
-  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P>;
-  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P>;
-  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P>;
-  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P>;
+  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P, G>;
+  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P, G>;
+  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P, G>;
+  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P, G>;
+  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P, G>;
+  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P, G>;
+  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P, G>;
+  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P, G>;
+  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P, G>;
 }
 
-template <class CF>
+template <class CF, bool WITH_GROUPED = false>
 TileInfo make_info(int id) {
   TileInfo t;
   t.id = id;
@@ -65,6 +66,8 @@ TileInfo make_info(int id) {
   t.nt = CF::NT;
   fill_fns<CF, false>(t.final_fn);
   fill_fns<CF, true>(t.partial_fn);
+  for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
+  if constexpr (WITH_GROUPED) fill_fns<CF, false, true>(t.grouped_fn);
   t.fallback = 0;
   t.n_mult = 0;
   return t;
@@ -79,7 +82,7 @@ TileInfo make_dma_info(int id, int fallback) {
   t.bn = CF::BN;
   t.bk = CF::BK;
   t.nt = CF::NT;
-  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = nullptr;
+  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = t.grouped_fn[i] = nullptr;
   t.final_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, false>;
   t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false>;
   t.partial_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true>;
@@ -98,8 +101,10 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   t.bn = CF::BN;
   t.bk = CF::BK;
   t.nt = CF::NT;
-  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = nullptr;
+  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = t.grouped_fn[i] = nullptr;
   t.final_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false>;
+  t.grouped_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false, true>;
+  t.grouped_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, true>;
   t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false>;
   t.partial_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, true>;
   t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, true>;

@@ -133,6 +133,41 @@ int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k,
  * (0 when the plan has no K split).  Returns 0 for invalid arguments too. */
 size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
 
+/*
+ * Grouped product, one launch over G products that share N and K (the
+ * TileLang tutorial, ch. 14, section 4.3: grouped GEMM with per-group row
+ * counts, as for the experts of a mixture-of-experts layer):
+ *
+ *     for g in [0, G):  C[r, :] = A[r, :] . B_g   for r in [offsets[g], offsets[g+1])
+ *
+ *   A        [M_total, K], element strides (lda_m, lda_k): the rows of all
+ *            groups, group by group (e.g. tokens sorted by expert).
+ *   B        G matrices [K, N]; B_g[k,j] at B + g*ldb_g + k*ldb_k + j*ldb_n.
+ *            ldb_g >= 0 (0: every group uses the same B).
+ *   C        [M_total, N], row stride ldc >= N, column stride 1.
+ *   offsets  DEVICE pointer to G + 1 int64 row offsets, non-decreasing,
+ *            within [0, M_total].  They are read on the device (the host
+ *            never needs the row counts).  Values outside [0, M_total] are
+ *            clamped into it, so no access ever leaves the views above; with
+ *            decreasing offsets, rows claimed by two groups get unspecified
+ *            values.  Rows of C outside every group are not written.
+ *   workspace  NULL (allocated stream-ordered) or at least
+ *            gemm_f16_grouped_workspace_bytes(G) bytes, 256-byte aligned,
+ *            not overlapping A, B or C; no initialisation needed.
+ *
+ * Same numerics, validation and return codes as gemm_f16; G must be in
+ * [1, 2^20].  Asynchronous on `stream`; deterministic.
+ */
+int gemm_f16_grouped(const void* A, int64_t lda_m, int64_t lda_k,
+                     const void* B, int64_t ldb_g, int64_t ldb_k, int64_t ldb_n,
+                     void* C, int64_t ldc,
+                     const int64_t* offsets, int32_t G,
+                     int64_t M_total, int64_t N, int64_t K, void* stream,
+                     void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes gemm_f16_grouped needs for G groups (0 if G is invalid). */
+size_t gemm_f16_grouped_workspace_bytes(int32_t G);
+
 /* Static, NUL-terminated description of a return code. */
 const char* gemm_f16_status_string(int status);
 

@@ -124,6 +124,28 @@ def gemm(A, lda, B, ldb, M, N, K, a_off=0, b_off=0, C=None, ldc=None, c_off=0,
     return (C, S) if exact else C
 
 
+def gemm_grouped(A, Bs, offsets, N, K, C=None, nthreads=None):
+    """Grouped product (TileLang tutorial ch. 14, section 4.3): for each group
+    g, rows offsets[g] .. offsets[g+1]-1 of C are those rows of A times B_g,
+    each by the plain definition of gemm() above.  A is [M, K] and Bs is
+    [G, K, N] (row-major fp16 bits); rows of C outside every group keep their
+    value (C is a fresh zero array when None)."""
+    M = A.shape[0]
+    G = Bs.shape[0]
+    if len(offsets) != G + 1:
+        raise ValueError("need G + 1 offsets")
+    if C is None:
+        C = np.zeros((M, N), dtype=np.uint16)
+    for g in range(G):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if not 0 <= r0 <= r1 <= M:
+            raise ValueError("offsets must be non-decreasing inside [0, M]")
+        if r1 > r0:
+            C[r0:r1] = gemm(np.ascontiguousarray(A[r0:r1]), (K, 1), np.ascontiguousarray(Bs[g]),
+                            (N, 1), r1 - r0, N, K, nthreads=nthreads)
+    return C
+
+
 def gemm_points(A, lda, B, ldb, K, rows, cols, a_off=0, b_off=0, exact=False, nthreads=None):
     """Selected outputs C[rows[t], cols[t]] of the same product, each computed
     on its own.  Returns fp16 bits (and the unrounded sums when exact=True)."""

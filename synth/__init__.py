@@ -105,6 +105,21 @@ def rows_of(row_index, cols, seed, tensor, mode="uniform", nthreads=None):
                 nthreads=nthreads)
 
 
+def group_sizes(G, total, seed, skew=0.8):
+    """Seeded row counts of G groups summing to `total` (e.g. tokens routed
+    to each expert of a mixture-of-experts layer): weights (rank + 1)^-skew in
+    a seeded random order, rounded down, the remainder given one row at a
+    time to the heaviest groups.  Synthetic stand-in for routing data."""
+    rng = np.random.default_rng(seed)
+    w = (np.arange(G, dtype=np.float64) + 1.0) ** -skew
+    w = w[rng.permutation(G)]
+    sizes = np.floor(w / w.sum() * total).astype(np.int64)
+    order = np.argsort(-w, kind="stable")
+    for i in range(int(total - sizes.sum())):
+        sizes[order[i % G]] += 1
+    return sizes
+
+
 # ---------------------------------------------------------------------------
 # numpy restatement of the same definition (used only to pin gen.c)
 

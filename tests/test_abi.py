@@ -127,3 +127,37 @@ def test_plan_split_k_extents():
     # the split count never leaves an empty K range
     p = forced_plan(512, 512, 100, (100, 1), (512, 1), 512, 3, 7, -1, 1)
     assert p.split_k == 2          # K = 100 in 64-wide steps: two ranges at most
+
+
+# ---------------------------------------------------------------- grouped entry point
+
+PO = 0x7E0000000000            # stand-in device address of the offsets
+
+
+def gcall(A=PA, lda_m=64, lda_k=1, B=PB, ldb_g=64 * 32, ldb_k=32, ldb_n=1, C=PC, ldc=32,
+          off=PO, G=4, M=16, N=32, K=64, ws=0, ws_bytes=0):
+    return g.lib.gemm_f16_grouped(A, lda_m, lda_k, B, ldb_g, ldb_k, ldb_n, C, ldc, off, G, M, N,
+                                  K, 0, ws, ws_bytes)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(off=0), -1), (dict(A=0), -1), (dict(B=0), -1), (dict(C=0), -1),
+    (dict(G=0), -2), (dict(G=(1 << 20) + 1), -2), (dict(M=0), -2), (dict(K=-1), -2),
+    (dict(ldb_g=-1), -3), (dict(lda_k=0), -3), (dict(ldb_n=0), -3),
+    (dict(ldc=31), -4),
+    (dict(C=PB + 3 * 64 * 32 * 2 + 64), -5),   # C inside the last group's B
+    (dict(C=PA + 2), -5),
+    (dict(ldb_g=2 ** 61, G=9), -2),             # B's span overflows int64
+])
+def test_grouped_rejected_before_any_device_work(kw, code):
+    assert gcall(**kw) == code
+
+
+def test_grouped_workspace():
+    need = g.lib.gemm_f16_grouped_workspace_bytes(4)
+    assert need == 256                          # 16 * (G + 1) bytes, rounded up to 256
+    assert g.lib.gemm_f16_grouped_workspace_bytes(0) == 0
+    assert g.lib.gemm_f16_grouped_workspace_bytes(1000) == (16 * 1001 + 255) // 256 * 256
+    assert gcall(ws=PW, ws_bytes=need - 1) == -6
+    assert gcall(ws=PW + 16, ws_bytes=need) == -6
+    assert gcall(ws=PC, ws_bytes=need) == -5    # workspace overlapping C

@@ -305,3 +305,46 @@ def test_rejects_views_past_their_buffer():
         oracle.gemm(A, (5, 1), A, (1, 1), 3, 1, 5)
     with pytest.raises(ValueError):
         oracle.gemm(A, (5, 1), A, (1, 1), 0, 1, 5)
+
+
+# ---------------------------------------------------------------- grouped product
+
+def test_grouped_single_group_is_the_plain_product():
+    A = synth.matrix(37, 19, 51, 0)
+    B = synth.matrix(19, 23, 51, 1)
+    got = oracle.gemm_grouped(A, B[None], [0, 37], 23, 19)
+    assert np.array_equal(got, oracle.gemm(A, (19, 1), B, (23, 1), 37, 23, 19))
+
+
+def test_grouped_brute_force_exact_integers():
+    # Per group, every output equals the exact integer dot product with that
+    # group's own B; rows outside the groups keep their prior value.
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        G = int(rng.integers(1, 6))
+        sizes = rng.integers(0, 5, G)
+        lead, tail = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        M = lead + int(sizes.sum()) + tail
+        if M == 0:
+            continue
+        N, K = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        offsets = np.concatenate([[lead], lead + np.cumsum(sizes)])
+        Ai = rng.integers(-4, 5, (M, K))
+        Bi = rng.integers(-4, 5, (G, K, N))
+        C0 = np.full((M, N), 0x7E00, dtype=np.uint16)      # a NaN canary
+        got = oracle.gemm_grouped(f16(Ai), f16(Bi), offsets, N, K, C=C0.copy())
+        for r in range(M):
+            g = [h for h in range(G) if offsets[h] <= r < offsets[h + 1]]
+            if not g:
+                assert np.array_equal(got[r], C0[r])
+                continue
+            want = [sum(int(Ai[r, k]) * int(Bi[g[0], k, j]) for k in range(K)) for j in range(N)]
+            assert val(got[r]).tolist() == want
+
+
+def test_grouped_rejects_bad_offsets():
+    A = synth.matrix(4, 3, 1, 0)
+    B = synth.matrix(3, 2, 1, 1)[None]
+    for bad in ([0, 5], [-1, 3], [3, 2]):
+        with pytest.raises(ValueError):
+            oracle.gemm_grouped(A, B, bad, 2, 3)

@@ -16,65 +16,10 @@ import torch
 import dense_tiled_gemm_fp16_amd as g
 import oracle
 import synth
-from gpu_util import (DEV, ORACLE_THREADS, assert_bits_equal, assert_close, say, to_dev,
-                      to_host, val)
+from gpu_util import (CANARY, DEV, NAN16, ORACLE_THREADS, Out, assert_bits_equal, assert_close,
+                      dev_nan, place, say, to_dev, to_host, val)
 
 pytestmark = pytest.mark.gpu
-
-NAN16 = 0x7E00
-CANARY = 0x5A5A
-
-
-def dev_nan(n):
-    return torch.full((n,), float("nan"), dtype=torch.float16, device=DEV)
-
-
-def place(logical, layout, pad=(0, 0)):
-    """Put a logical [R, C] fp16-bit matrix on the GPU and return a torch view
-    of shape [R, C] with the requested storage:
-      "row"  row-major, strides (C + pad[1], 1) inside a NaN buffer with
-             pad[0] leading NaN rows (pad = (0, 0): a plain contiguous tensor)
-      "col"  a transposed view: stored [C, R], strides (1, R + pad[1])."""
-    R, Cc = logical.shape
-    if layout == "row":
-        if pad == (0, 0):
-            return to_dev(logical)
-        ld = Cc + pad[1]
-        buf = dev_nan((R + pad[0] + 1) * ld)
-        v = buf[pad[0] * ld: pad[0] * ld + R * ld].view(R, ld)[:, :Cc]
-        v.copy_(to_dev(logical))
-        return v
-    if layout == "col":
-        if pad == (0, 0):
-            return to_dev(np.ascontiguousarray(logical.T)).t()
-        ld = R + pad[1]
-        buf = dev_nan((Cc + pad[0] + 1) * ld)
-        v = buf[pad[0] * ld: pad[0] * ld + Cc * ld].view(Cc, ld)[:, :R]
-        v.copy_(to_dev(np.ascontiguousarray(logical.T)))
-        return v.t()
-    raise ValueError(layout)
-
-
-class Out:
-    """An [M, N] output view with row stride ldc inside a buffer pre-filled
-    with NaN (the view) and a canary pattern (everything else)."""
-
-    def __init__(self, M, N, ldc=None, guard=64):
-        ldc = ldc or N
-        self.M, self.N, self.ldc, self.guard = M, N, ldc, guard
-        host = np.full(guard + M * ldc + guard, CANARY, dtype=np.uint16)
-        host[guard:guard + M * ldc].reshape(M, ldc)[:, :N] = NAN16
-        self.buf = to_dev(host)
-        self.view = self.buf[guard:guard + M * ldc].view(M, ldc)[:, :N]
-
-    def result(self):
-        host = to_host(self.buf)
-        inner = host[self.guard:self.guard + self.M * self.ldc].reshape(self.M, self.ldc)
-        assert np.all(host[:self.guard] == CANARY) and np.all(host[-self.guard:] == CANARY), \
-            "write outside the output buffer"
-        assert np.all(inner[:, self.N:] == CANARY), "write into the ldc padding"
-        return np.ascontiguousarray(inner[:, :self.N])
-
 
 def run(a, b, out=None, **kw):
     say(f"gemm M={a.shape[0]} N={b.shape[1]} K={a.shape[1]} a.stride={a.stride()} "

@@ -35,3 +35,10 @@ def test_seed_and_tensor_change_the_stream():
     assert not np.array_equal(a, synth.matrix(16, 16, seed=2, tensor=0))
     assert not np.array_equal(a, synth.matrix(16, 16, seed=1, tensor=1))
     assert np.array_equal(a, synth.matrix(16, 16, seed=1, tensor=0, nthreads=3))
+
+
+def test_group_sizes_partition():
+    for G, total, seed in ((1, 5, 0), (8, 1000, 3), (32, 131072, 11), (7, 3, 2)):
+        s = synth.group_sizes(G, total, seed)
+        assert s.shape == (G,) and s.min() >= 0 and int(s.sum()) == total
+        assert np.array_equal(s, synth.group_sizes(G, total, seed))   # seeded
