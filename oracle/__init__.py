@@ -1,4 +1,4 @@
-"""CPU oracle for C = A.B with fp16 inputs and fp16 output.
+"""CPU oracle for C = A.B with fp16 (or bfloat16) inputs and output.
 
 TEST INFRASTRUCTURE ONLY.  Only `tests/`, the smoke check in
 `__graft_entry__.py` and the CPU-baseline leg of `bench.py` may import this
@@ -8,8 +8,9 @@ the seeded input generator in `synth/`, which holds no GEMM arithmetic.
 
 Contents
   oracle.c  the defining triple loop in binary64 with a single
-            round-to-nearest-even to binary16, and its own binary16 codec
-            (see that file's header for the passages it follows);
+            round-to-nearest-even to binary16 (or bfloat16), and its own
+            codecs for both formats (see that file's header for the passages
+            it follows);
   model.py  a small pure-Python model of the tiled method (programs that own
             output tiles, K rounds, three-axis masks, read counting) used to
             reproduce the pages' worked examples;
@@ -58,6 +59,15 @@ def _load():
         lib.orc_f16_to_f64_array.argtypes = [vp, vp, i64]
         lib.orc_f64_to_f16_array.restype = None
         lib.orc_f64_to_f16_array.argtypes = [vp, vp, i64]
+        for name in ("orc_gemm_bf16",):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = lib.orc_gemm_f16.argtypes
+        lib.orc_gemm_bf16_points.restype = ctypes.c_int
+        lib.orc_gemm_bf16_points.argtypes = lib.orc_gemm_f16_points.argtypes
+        lib.orc_bf16_to_f64_array.restype = None
+        lib.orc_bf16_to_f64_array.argtypes = [vp, vp, i64]
+        lib.orc_f64_to_bf16_array.restype = None
+        lib.orc_f64_to_bf16_array.argtypes = [vp, vp, i64]
         _lib = lib
     return _lib
 
@@ -81,6 +91,20 @@ def f64_to_f16(x):
     return out
 
 
+def bf16_to_f64(bits):
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().orc_bf16_to_f64_array(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def f64_to_bf16(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_f64_to_bf16_array(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
 def _span(off, rows, cols, rs, cs):
     """Largest element offset touched by a rows x cols view (strides >= 0)."""
     return off + (rows - 1) * rs + (cols - 1) * cs
@@ -92,11 +116,12 @@ def _check_buf(buf, name):
 
 
 def gemm(A, lda, B, ldb, M, N, K, a_off=0, b_off=0, C=None, ldc=None, c_off=0,
-         exact=False, nthreads=None):
-    """C[i,j] = fp16_rne(sum_k A[i,k] B[k,j]) for the strided views
+         exact=False, nthreads=None, dtype="f16"):
+    """C[i,j] = rne(sum_k A[i,k] B[k,j]) for the strided views
         A[i,k] = A.flat[a_off + i*lda[0] + k*lda[1]]
         B[k,j] = B.flat[b_off + k*ldb[0] + j*ldb[1]]
     written to C.flat[c_off + i*ldc + j] (a fresh (M, N) array when C is None).
+    dtype "f16" (binary16) or "bf16" (bfloat16) for inputs and output.
     Returns C, or (C, S) with S the unrounded binary64 sums when exact=True."""
     _check_buf(A, "A")
     _check_buf(B, "B")
@@ -115,7 +140,8 @@ def gemm(A, lda, B, ldb, M, N, K, a_off=0, b_off=0, C=None, ldc=None, c_off=0,
     if _span(c_off, M, N, ldc, 1) >= C.size:
         raise ValueError("output view reaches past its buffer")
     S = np.empty((M, N), dtype=np.float64) if exact else None
-    rc = _load().orc_gemm_f16(
+    fn = {"f16": _load().orc_gemm_f16, "bf16": _load().orc_gemm_bf16}[dtype]
+    rc = fn(
         A.ctypes.data + 2 * a_off, lda[0], lda[1], B.ctypes.data + 2 * b_off, ldb[0], ldb[1],
         C.ctypes.data + 2 * c_off, ldc, None if S is None else S.ctypes.data, M, N, K,
         nthreads or threads())
@@ -124,7 +150,7 @@ def gemm(A, lda, B, ldb, M, N, K, a_off=0, b_off=0, C=None, ldc=None, c_off=0,
     return (C, S) if exact else C
 
 
-def gemm_grouped(A, Bs, offsets, N, K, C=None, nthreads=None):
+def gemm_grouped(A, Bs, offsets, N, K, C=None, nthreads=None, dtype="f16"):
     """Grouped product (TileLang tutorial ch. 14, section 4.3): for each group
     g, rows offsets[g] .. offsets[g+1]-1 of C are those rows of A times B_g,
     each by the plain definition of gemm() above.  A is [M, K] and Bs is
@@ -142,13 +168,14 @@ def gemm_grouped(A, Bs, offsets, N, K, C=None, nthreads=None):
             raise ValueError("offsets must be non-decreasing inside [0, M]")
         if r1 > r0:
             C[r0:r1] = gemm(np.ascontiguousarray(A[r0:r1]), (K, 1), np.ascontiguousarray(Bs[g]),
-                            (N, 1), r1 - r0, N, K, nthreads=nthreads)
+                            (N, 1), r1 - r0, N, K, nthreads=nthreads, dtype=dtype)
     return C
 
 
-def gemm_points(A, lda, B, ldb, K, rows, cols, a_off=0, b_off=0, exact=False, nthreads=None):
+def gemm_points(A, lda, B, ldb, K, rows, cols, a_off=0, b_off=0, exact=False, nthreads=None,
+                dtype="f16"):
     """Selected outputs C[rows[t], cols[t]] of the same product, each computed
-    on its own.  Returns fp16 bits (and the unrounded sums when exact=True)."""
+    on its own.  Returns output bits (and the unrounded sums when exact=True)."""
     _check_buf(A, "A")
     _check_buf(B, "B")
     rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -165,7 +192,8 @@ def gemm_points(A, lda, B, ldb, K, rows, cols, a_off=0, b_off=0, exact=False, nt
             raise ValueError("point reaches past its buffer")
     out = np.empty(rows.size, dtype=np.uint16)
     S = np.empty(rows.size, dtype=np.float64) if exact else None
-    rc = _load().orc_gemm_f16_points(
+    fn = {"f16": _load().orc_gemm_f16_points, "bf16": _load().orc_gemm_bf16_points}[dtype]
+    rc = fn(
         A.ctypes.data + 2 * a_off, lda[0], lda[1], B.ctypes.data + 2 * b_off, ldb[0], ldb[1], K,
         rows.ctypes.data, cols.ctypes.data, rows.size, out.ctypes.data,
         None if S is None else S.ctypes.data, nthreads or threads())

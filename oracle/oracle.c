@@ -92,12 +92,69 @@ uint16_t orc_f64_to_f16(double x) {
   return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024));
 }
 
+/* ---- bfloat16 codec, written from the format definition -----------------
+ * bfloat16: the upper 16 bits of an IEEE 754 binary32 -- 1 sign bit,
+ * 8 exponent bits (bias 127), 7 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-133
+ *   exponent 1..254 : normal,    value = (128 + fraction) * 2^(exponent-134)
+ *   exponent 255    : fraction 0 -> infinity, otherwise NaN             */
+
+double orc_bf16_to_f64(uint16_t h) {
+  uint64_t sign = (uint64_t)(h >> 15) << 63;
+  uint32_t e = (h >> 7) & 0xFF;
+  uint32_t f = h & 0x7F;
+  uint64_t bits;
+  double out;
+  if (e == 0) {
+    out = (double)f * 0x1p-133; /* exact */
+    return (h >> 15) ? -out : out;
+  }
+  if (e == 255) {
+    bits = sign | (0x7FFull << 52) | ((uint64_t)f << 45) | (f ? (1ull << 51) : 0);
+  } else {
+    bits = sign | ((uint64_t)(e - 127 + 1023) << 52) | ((uint64_t)f << 45);
+  }
+  memcpy(&out, &bits, sizeof out);
+  return out;
+}
+
+/* Nearest bfloat16 to a binary64 value, ties to even (one rounding, straight
+ * from binary64), by integer rounding of the significand at the bfloat16
+ * quantum. */
+uint16_t orc_f64_to_bf16(double x) {
+  uint64_t b;
+  memcpy(&b, &x, sizeof b);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  int ex = (int)((b >> 52) & 0x7FF);
+  uint64_t frac = b & ((1ull << 52) - 1);
+  if (ex == 0x7FF) return (uint16_t)(sign | (frac ? 0x7FC0u : 0x7F80u));
+  if (ex == 0) return sign; /* binary64 zero or subnormal: far below 2^-134 */
+  int e = ex - 1023;                         /* x = sig * 2^(e-52) */
+  uint64_t sig = (1ull << 52) | frac;
+  int qe = (e < -126 ? -126 : e) - 7;        /* bfloat16 quantum exponent */
+  int shift = qe - (e - 52);                 /* >= 45 */
+  if (shift >= 64) return sign;              /* below a quarter quantum */
+  uint64_t q = sig >> shift;
+  uint64_t rem = sig & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1;
+  if (e < -126) return (uint16_t)(sign | (uint16_t)q);   /* q == 128: smallest normal */
+  int E = e;
+  if (q == 256) { q = 128; E += 1; }
+  if (E + 127 >= 255) return (uint16_t)(sign | 0x7F80u);
+  return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)(q - 128));
+}
+
+typedef double (*orc_dec_fn)(uint16_t);
+typedef uint16_t (*orc_enc_fn)(double);
+
 /* One output element: the defining sum, ascending k, binary64. */
 static double orc_dot(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
-                      int64_t ldb_k, int64_t ldb_n, int64_t i, int64_t j, int64_t K) {
+                      int64_t ldb_k, int64_t ldb_n, int64_t i, int64_t j, int64_t K,
+                      orc_dec_fn dec) {
   double s = 0.0;
   for (int64_t k = 0; k < K; ++k)
-    s += orc_f16_to_f64(A[i * lda_m + k * lda_k]) * orc_f16_to_f64(B[k * ldb_k + j * ldb_n]);
+    s += dec(A[i * lda_m + k * lda_k]) * dec(B[k * ldb_k + j * ldb_n]);
   return s;
 }
 
@@ -110,6 +167,8 @@ typedef struct {
   const int64_t* pi;         /* point mode: output coordinates */
   const int64_t* pj;
   int64_t npts;
+  orc_dec_fn dec;            /* element format: binary16 or bfloat16 */
+  orc_enc_fn enc;
   int nthreads, tid;
 } orc_job;
 
@@ -117,8 +176,8 @@ static void* orc_rows(void* p) {
   orc_job* j = (orc_job*)p;
   for (int64_t i = j->tid; i < j->M; i += j->nthreads)
     for (int64_t c = 0; c < j->N; ++c) {
-      double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, i, c, j->K);
-      j->C[i * j->ldc + c] = orc_f64_to_f16(s);
+      double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, i, c, j->K, j->dec);
+      j->C[i * j->ldc + c] = j->enc(s);
       if (j->S) j->S[i * j->N + c] = s;
     }
   return NULL;
@@ -127,8 +186,9 @@ static void* orc_rows(void* p) {
 static void* orc_points(void* p) {
   orc_job* j = (orc_job*)p;
   for (int64_t t = j->tid; t < j->npts; t += j->nthreads) {
-    double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, j->pi[t], j->pj[t], j->K);
-    j->C[t] = orc_f64_to_f16(s);
+    double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, j->pi[t], j->pj[t], j->K,
+                       j->dec);
+    j->C[t] = j->enc(s);
     if (j->S) j->S[t] = s;
   }
   return NULL;
@@ -156,7 +216,20 @@ int orc_gemm_f16(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t
                  int64_t ldb_k, int64_t ldb_n, uint16_t* C, int64_t ldc, double* S,
                  int64_t M, int64_t N, int64_t K, int nthreads) {
   if (!A || !B || !C || M <= 0 || N <= 0 || K <= 0) return -1;
-  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, S, M, N, K, NULL, NULL, 0, nthreads, 0};
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, S, M, N, K, NULL, NULL, 0,
+               orc_f16_to_f64, orc_f64_to_f16, nthreads, 0};
+  orc_run(&j, orc_rows);
+  return 0;
+}
+
+/* The same product for bfloat16 inputs and output (fp32 accumulation on the
+ * GPU side; here the same binary64 sum and one rounding to bfloat16). */
+int orc_gemm_bf16(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                  int64_t ldb_k, int64_t ldb_n, uint16_t* C, int64_t ldc, double* S,
+                  int64_t M, int64_t N, int64_t K, int nthreads) {
+  if (!A || !B || !C || M <= 0 || N <= 0 || K <= 0) return -1;
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, S, M, N, K, NULL, NULL, 0,
+               orc_bf16_to_f64, orc_f64_to_bf16, nthreads, 0};
   orc_run(&j, orc_rows);
   return 0;
 }
@@ -167,7 +240,19 @@ int orc_gemm_f16_points(const uint16_t* A, int64_t lda_m, int64_t lda_k, const u
                         const int64_t* pj, int64_t npts, uint16_t* out, double* S,
                         int nthreads) {
   if (!A || !B || !out || !pi || !pj || K <= 0 || npts < 0) return -1;
-  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, out, 0, S, 0, 0, K, pi, pj, npts, nthreads, 0};
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, out, 0, S, 0, 0, K, pi, pj, npts,
+               orc_f16_to_f64, orc_f64_to_f16, nthreads, 0};
+  orc_run(&j, orc_points);
+  return 0;
+}
+
+int orc_gemm_bf16_points(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                         int64_t ldb_k, int64_t ldb_n, int64_t K, const int64_t* pi,
+                         const int64_t* pj, int64_t npts, uint16_t* out, double* S,
+                         int nthreads) {
+  if (!A || !B || !out || !pi || !pj || K <= 0 || npts < 0) return -1;
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, out, 0, S, 0, 0, K, pi, pj, npts,
+               orc_bf16_to_f64, orc_f64_to_bf16, nthreads, 0};
   orc_run(&j, orc_points);
   return 0;
 }
@@ -179,4 +264,12 @@ void orc_f16_to_f64_array(const uint16_t* in, double* out, int64_t n) {
 
 void orc_f64_to_f16_array(const double* in, uint16_t* out, int64_t n) {
   for (int64_t t = 0; t < n; ++t) out[t] = orc_f64_to_f16(in[t]);
+}
+
+void orc_bf16_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t t = 0; t < n; ++t) out[t] = orc_bf16_to_f64(in[t]);
+}
+
+void orc_f64_to_bf16_array(const double* in, uint16_t* out, int64_t n) {
+  for (int64_t t = 0; t < n; ++t) out[t] = orc_f64_to_bf16(in[t]);
 }

@@ -27,6 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gen.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 MODES = {"uniform": 0, "int": 1}
+FORMATS = {"f16": 0, "bf16": 2}
 TENSOR_A, TENSOR_B = 0, 1
 
 _lib = None
@@ -60,11 +61,12 @@ def host_threads():
 
 
 def fill(dst, rows, cols, rs, cs, seed, tensor, mode="uniform", row0=0, row_index=None,
-         nthreads=None):
+         nthreads=None, fmt="f16"):
     """Write logical element (row, c) of the (seed, tensor) matrix to
     dst.flat[r*rs + c*cs] for r in [0, rows).  The logical row is
     row_index[r] when row_index is given, else row0 + r.  `dst` is a
-    uint16 numpy array (any shape, C-contiguous storage is addressed flat)."""
+    uint16 numpy array (any shape, C-contiguous storage is addressed flat).
+    fmt "f16" writes binary16 bits, "bf16" bfloat16 bits of the same value."""
     assert dst.dtype == np.uint16 and dst.flags["C_CONTIGUOUS"]
     if rows > 0 and cols > 0:
         last = (rows - 1) * rs + (cols - 1) * cs
@@ -76,13 +78,13 @@ def fill(dst, rows, cols, rs, cs, seed, tensor, mode="uniform", row0=0, row_inde
     rc = _load().synth_fill(
         dst.ctypes.data, rows, cols, rs, cs, row0,
         None if idx is None else idx.ctypes.data,
-        seed & 0xFFFFFFFFFFFFFFFF, tensor, MODES[mode], nthreads or host_threads())
+        seed & 0xFFFFFFFFFFFFFFFF, tensor, MODES[mode] | FORMATS[fmt], nthreads or host_threads())
     if rc != 0:
         raise ValueError("synth_fill rejected its arguments")
     return dst
 
 
-def matrix(rows, cols, seed, tensor, mode="uniform", order="row", nthreads=None):
+def matrix(rows, cols, seed, tensor, mode="uniform", order="row", nthreads=None, fmt="f16"):
     """The logical [rows, cols] matrix as uint16 fp16 bits.
 
     order="row": returned array has shape (rows, cols) (row-major storage).
@@ -90,19 +92,19 @@ def matrix(rows, cols, seed, tensor, mode="uniform", order="row", nthreads=None)
     transpose, i.e. the storage of a transposed view with strides (1, rows)."""
     if order == "row":
         out = np.empty((rows, cols), dtype=np.uint16)
-        return fill(out, rows, cols, cols, 1, seed, tensor, mode, nthreads=nthreads)
+        return fill(out, rows, cols, cols, 1, seed, tensor, mode, nthreads=nthreads, fmt=fmt)
     if order == "col":
         out = np.empty((cols, rows), dtype=np.uint16)
-        return fill(out, rows, cols, 1, rows, seed, tensor, mode, nthreads=nthreads)
+        return fill(out, rows, cols, 1, rows, seed, tensor, mode, nthreads=nthreads, fmt=fmt)
     raise ValueError(order)
 
 
-def rows_of(row_index, cols, seed, tensor, mode="uniform", nthreads=None):
+def rows_of(row_index, cols, seed, tensor, mode="uniform", nthreads=None, fmt="f16"):
     """Selected logical rows (len(row_index), cols) of the (seed, tensor) matrix."""
     idx = np.ascontiguousarray(row_index, dtype=np.int64)
     out = np.empty((idx.size, cols), dtype=np.uint16)
     return fill(out, idx.size, cols, cols, 1, seed, tensor, mode, row_index=idx,
-                nthreads=nthreads)
+                nthreads=nthreads, fmt=fmt)
 
 
 def group_sizes(G, total, seed, skew=0.8):
@@ -134,7 +136,7 @@ def _sm(x):
         return z ^ (z >> np.uint64(31))
 
 
-def reference_rows(row_index, cols, seed, tensor, mode="uniform"):
+def reference_rows(row_index, cols, seed, tensor, mode="uniform", fmt="f16"):
     rows = np.asarray(row_index, dtype=np.uint64).reshape(-1, 1)
     base_t = _sm(_sm(np.uint64(seed)) ^ np.uint64(tensor))
     h = _sm(_sm(base_t ^ rows) ^ np.arange(cols, dtype=np.uint64).reshape(1, -1))
@@ -143,4 +145,7 @@ def reference_rows(row_index, cols, seed, tensor, mode="uniform"):
         vals = (top % 9 - 4).astype(np.float32)
     else:
         vals = ((2 * top + 1 - (1 << 24)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+    if fmt == "bf16":   # float32 -> bfloat16, ties to even, by torch (values exact in float32)
+        import torch
+        return torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     return vals.astype(np.float16).view(np.uint16)

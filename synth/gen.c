@@ -17,6 +17,8 @@
  *                  multiple of 2^-24 inside (-1, 1), exact in binary32; the
  *                  element is x rounded to binary16 (ties to even).
  *   SYNTH_INT:     (h >> 40) % 9 - 4, an integer in [-4, 4] (exact in fp16).
+ * With SYNTH_BF16 added to the mode the same value is rounded to bfloat16
+ * (ties to even) instead of binary16.
  */
 #include <math.h>
 #include <pthread.h>
@@ -25,6 +27,7 @@
 
 #define SYNTH_UNIFORM 0
 #define SYNTH_INT 1
+#define SYNTH_BF16 2
 
 static inline uint64_t sm_step(uint64_t x) {
   uint64_t z = x + 0x9E3779B97F4A7C15ull;
@@ -56,14 +59,39 @@ static uint16_t synth_to_half(double x) {
   return (uint16_t)(sign | (uint16_t)((ev + 15) << 10) | mant);
 }
 
+/* Round a finite double to bfloat16 (8 exponent bits, 7 fraction bits),
+ * ties to even, the same way: scale to the quantum, nearbyint, re-encode. */
+static uint16_t synth_to_bf16(double x) {
+  uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  const double big = ldexp(1.0, 128) * (1.0 - ldexp(1.0, -9));  /* rounds to 2^128 */
+  if (a >= big) return (uint16_t)(sign | 0x7F80u);
+  int e2;
+  frexp(a, &e2);
+  int ex = e2 - 1;
+  if (ex < -126) ex = -126;
+  double q = ldexp(1.0, ex - 7);
+  double m = nearbyint(a / q);
+  double v = m * q;
+  if (v < ldexp(1.0, -126)) return (uint16_t)(sign | (uint16_t)(v / ldexp(1.0, -133)));
+  frexp(v, &e2);
+  int ev = e2 - 1;
+  if (ev + 127 >= 255) return (uint16_t)(sign | 0x7F80u);
+  uint16_t mant = (uint16_t)(v / ldexp(1.0, ev - 7) - 128.0);
+  return (uint16_t)(sign | (uint16_t)((ev + 127) << 7) | mant);
+}
+
 static inline uint16_t synth_value(uint64_t h, int mode) {
-  if (mode == SYNTH_INT) {
-    int v = (int)((h >> 40) % 9u) - 4;
-    return synth_to_half((double)v);
+  const int bf = mode & SYNTH_BF16;
+  double x;
+  if ((mode & 1) == SYNTH_INT) {
+    x = (double)((int)((h >> 40) % 9u) - 4);
+  } else {
+    int64_t u = (int64_t)(h >> 40);
+    x = (double)(2 * u + 1 - (1ll << 24)) * 0x1p-24;
   }
-  int64_t u = (int64_t)(h >> 40);
-  double x = (double)(2 * u + 1 - (1ll << 24)) * 0x1p-24;
-  return synth_to_half(x);
+  return bf ? synth_to_bf16(x) : synth_to_half(x);
 }
 
 typedef struct {
@@ -96,7 +124,7 @@ static void* synth_worker(void* p) {
 int synth_fill(uint16_t* dst, int64_t rows, int64_t cols, int64_t rs, int64_t cs,
                int64_t row0, const int64_t* row_index, uint64_t seed, uint64_t tensor,
                int mode, int nthreads) {
-  if (!dst || rows < 0 || cols < 0 || (mode != SYNTH_UNIFORM && mode != SYNTH_INT)) return -1;
+  if (!dst || rows < 0 || cols < 0 || mode < 0 || mode > (SYNTH_INT | SYNTH_BF16)) return -1;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if (rows < nthreads) nthreads = rows > 0 ? (int)rows : 1;

@@ -348,3 +348,68 @@ def test_grouped_rejects_bad_offsets():
     for bad in ([0, 5], [-1, 3], [3, 2]):
         with pytest.raises(ValueError):
             oracle.gemm_grouped(A, B, bad, 2, 3)
+
+
+# ---------------------------------------------------------------- bfloat16
+
+def _torch_bf16_from_f32(x):
+    """float32 values -> bfloat16 bits by torch (ties to even; a single
+    rounding, since the inputs are exact in float32)."""
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_to_f64(bits)
+    with np.errstate(invalid="ignore"):       # signalling NaN patterns
+        ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    back = oracle.f64_to_bf16(got)
+    assert np.array_equal(back[~nan], bits[~nan])
+
+
+def test_bf16_encode_matches_torch_on_float32_values():
+    rng = np.random.default_rng(99)
+    x = (rng.standard_normal(500_000) * 10.0 ** rng.uniform(-40, 38, 500_000)).astype(np.float32)
+    x = np.concatenate([x, np.float32([0.0, -0.0, 1.0, 3.0e38, -3.0e38, 1e-40, 1.1e-38])])
+    assert np.array_equal(oracle.f64_to_bf16(x.astype(np.float64)), _torch_bf16_from_f32(x))
+
+
+def test_bf16_every_midpoint_ties_to_even():
+    lo = np.arange(0, 0x7F7F, dtype=np.uint16)
+    mid = (oracle.bf16_to_f64(lo) + oracle.bf16_to_f64(lo + 1)) / 2.0
+    got = oracle.f64_to_bf16(mid)
+    assert np.all(got & 1 == 0)
+    assert np.array_equal(got, _torch_bf16_from_f32(mid.astype(np.float32)))
+
+
+def test_bf16_closed_forms():
+    cases = {
+        1 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,   # above the midpoint: up (via float32 it would tie to 1.0)
+        1 + 2.0 ** -8: 0x3F80,                # the midpoint itself: to even
+        1 + 3 * 2.0 ** -8: 0x3F82,            # midpoint between 0x3F81 and 0x3F82: to even
+        2.0 ** 128 * (1 - 2.0 ** -9): 0x7F80,  # halfway to 2^128: overflows to infinity
+        2.0 ** 128 * (1 - 2.0 ** -8): 0x7F7F,  # the largest finite value
+        2.0 ** -133: 0x0001, 2.0 ** -134: 0x0000, 3 * 2.0 ** -134: 0x0002,
+        -(2.0 ** -126): 0x8080,
+    }
+    got = oracle.f64_to_bf16(np.array(list(cases)))
+    assert got.tolist() == list(cases.values())
+
+
+def test_bf16_brute_force_small_products():
+    # Integer inputs: each output is the exact integer sum rounded once to
+    # bfloat16 (torch's float32 -> bfloat16 on the exact sum).
+    rng = np.random.default_rng(3)
+    for M, N, K in itertools.product((1, 3, 8), (1, 5), (1, 4, 9, 40)):
+        Ai = rng.integers(-4, 5, (M, K))
+        Bi = rng.integers(-4, 5, (K, N))
+        A = _torch_bf16_from_f32(Ai)
+        B = _torch_bf16_from_f32(Bi)
+        got = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, dtype="bf16")
+        assert np.array_equal(got, _torch_bf16_from_f32(Ai @ Bi))

@@ -42,3 +42,14 @@ def test_group_sizes_partition():
         s = synth.group_sizes(G, total, seed)
         assert s.shape == (G,) and s.min() >= 0 and int(s.sum()) == total
         assert np.array_equal(s, synth.group_sizes(G, total, seed))   # seeded
+
+
+@pytest.mark.parametrize("mode", ["uniform", "int"])
+def test_bf16_format_matches_the_numpy_torch_restatement(mode):
+    rows = np.array([0, 1, 7, 1000, 123456])
+    got = synth.rows_of(rows, 300, 77, 3, mode, fmt="bf16")
+    assert np.array_equal(got, synth.reference_rows(rows, 300, 77, 3, mode, fmt="bf16"))
+    # the same logical values as the binary16 matrix, rounded to bfloat16
+    f16 = synth.rows_of(rows, 300, 77, 3, mode).view(np.float16).astype(np.float64)
+    bf = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(bf - f16) <= np.abs(f16) * 2.0 ** -8 + 2.0 ** -24)
