@@ -284,6 +284,24 @@ def main():
                "timing": "HIP events around each call (set-up and product launches)"}
     del bg
 
+    # ---- bfloat16: the same product in the other 16-bit format
+    del a
+    ab = to_dev(synth.matrix(M, K, 4001, synth.TENSOR_A, fmt="bf16")).view(torch.bfloat16)
+    bb = to_dev(synth.matrix(K, N, 4001, synth.TENSOR_B, fmt="bf16")).view(torch.bfloat16)
+    cb = c.view(torch.bfloat16)
+
+    def step_b():
+        g.gemm(ab, bb, out=cb, stream=stream)
+
+    db, _ = timed_launches(step_b, stream, max(5, args.steps // 5), 2)
+    msb = sum(db) / len(db)
+    bf16 = {"workload": f"{M}x{N}x{K}, bfloat16 inputs and output, fp32 accumulation",
+            "plan": {k: g.plan(ab, bb, cb)[k] for k in ("variant", "tile_id", "split_k")},
+            "ms": msb, "TFLOPS": flops / (msb * 1e-3) / 1e12,
+            "frac": flops / (msb * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+            "timing": "HIP events around each call"}
+    del ab, bb
+
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -303,6 +321,7 @@ def main():
                    "wall_s": wall},
         "skinny_m1": skinny,
         "grouped_moe": grouped,
+        "bf16": bf16,
         "vs_baseline_ref": "pages' TileLang kernel on MetaX C500, 117.25 TFLOPS (context only)",
     }
     if not args.no_cpu_baseline:

@@ -4,7 +4,7 @@ The computation runs in libgemmf16.so (hand-written HIP, C-ABI in
 include/gemm_f16.h).  This package only marshals arguments: torch supplies
 device memory and the current stream.
 
-    gemm(a, b, out=None, ...)      -> C (torch.float16, [M, N])
+    gemm(a, b, out=None, ...)      -> C ([M, N], float16 or bfloat16 like a and b)
     gemm_grouped(a, b, offsets)    -> C, group g: C[off[g]:off[g+1]] = A[...] @ b[g]
     plan(a, b, out=None, ...)      -> dict describing the kernel that would run
     workspace_bytes(M, N, K, ...)  -> bytes of split-K workspace needed
@@ -33,8 +33,8 @@ def _check(a, b, out):
         raise ValueError("expected two matrices")
     if not a.is_cuda or not b.is_cuda or a.device != b.device:
         raise ValueError("inputs must share one GPU device")
-    if a.dtype != torch.float16 or b.dtype != torch.float16:
-        raise TypeError("only float16 inputs are supported")
+    if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
+        raise TypeError("inputs must both be float16 or both bfloat16")
     m, k = a.shape
     kb, n = b.shape
     if k != kb or min(m, n, k) <= 0:
@@ -42,10 +42,10 @@ def _check(a, b, out):
     if min(a.stride() + b.stride()) <= 0:
         raise ValueError("strides must be positive")
     if out is None:
-        out = torch.empty((m, n), device=a.device, dtype=torch.float16)
+        out = torch.empty((m, n), device=a.device, dtype=a.dtype)
     else:
-        if out.dtype != torch.float16 or out.device != a.device or out.shape != (m, n):
-            raise ValueError("out must be a float16 [M, N] tensor on the inputs' device")
+        if out.dtype != a.dtype or out.device != a.device or out.shape != (m, n):
+            raise ValueError("out must be an [M, N] tensor of the inputs' dtype and device")
         if out.stride(1) != 1 or out.stride(0) < n:
             raise ValueError("out must be row-major with unit column stride")
     return m, n, k, out
@@ -59,9 +59,14 @@ def gemm_raw(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream=0, worksp
                            workspace, workspace_bytes, ctypes.byref(o) if o is not None else None)
 
 
+def _fn(a, name):
+    return getattr(lib, name if a.dtype == torch.float16 else name.replace("gemm_f16", "gemm_bf16"))
+
+
 def gemm(a, b, out=None, workspace=None, variant="auto", split_k=0, panel=0, tile=0,
          stream=None):
-    """C = a @ b with fp32 accumulation and fp16 output, computed by libgemmf16."""
+    """C = a @ b with fp32 accumulation, output in the inputs' format (float16
+    or bfloat16), computed by libgemmf16."""
     m, n, k, out = _check(a, b, out)
     opts = make_opts(variant, split_k, panel, tile)
     if stream is None:
@@ -70,9 +75,9 @@ def gemm(a, b, out=None, workspace=None, variant="auto", split_k=0, panel=0, til
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(a.device):
-        rc = lib.gemm_f16_ex(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
-                             b.stride(1), out.data_ptr(), out.stride(0), m, n, k,
-                             stream.cuda_stream, ws_ptr, ws_bytes, ctypes.byref(opts))
+        rc = _fn(a, "gemm_f16_ex")(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
+                                   b.stride(0), b.stride(1), out.data_ptr(), out.stride(0), m, n,
+                                   k, stream.cuda_stream, ws_ptr, ws_bytes, ctypes.byref(opts))
     if rc != GEMM_OK:
         raise GemmError(rc)
     return out
@@ -120,9 +125,9 @@ def plan(a, b, out=None, variant="auto", split_k=0, panel=0, tile=0):
     opts = make_opts(variant, split_k, panel, tile)
     info = PlanInfo()
     with torch.cuda.device(a.device):
-        rc = lib.gemm_f16_plan(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
-                               b.stride(1), out.data_ptr(), out.stride(0), m, n, k,
-                               ctypes.byref(opts), ctypes.byref(info))
+        rc = _fn(a, "gemm_f16_plan")(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
+                                     b.stride(0), b.stride(1), out.data_ptr(), out.stride(0), m, n,
+                                     k, ctypes.byref(opts), ctypes.byref(info))
     if rc != GEMM_OK:
         raise GemmError(rc)
     d = info.as_dict()

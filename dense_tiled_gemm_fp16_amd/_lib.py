@@ -19,6 +19,7 @@ VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4}
 PATHS = {0: "gather", 1: "kvec", 2: "rvec"}
 
 EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes",
+           "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_plan", "gemm_bf16_workspace_bytes",
            "gemm_f16_grouped", "gemm_f16_grouped_workspace_bytes",
            "gemm_f16_status_string", "gemm_f16_version"]
 
@@ -51,6 +52,15 @@ def _load():
     lib.gemm_f16_plan.restype = ctypes.c_int
     lib.gemm_f16_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(Opts)]
     lib.gemm_f16_workspace_bytes.restype = sz
+    for pre in ("gemm_bf16",):
+        getattr(lib, pre).argtypes = args12
+        getattr(lib, pre).restype = ctypes.c_int
+        getattr(lib, pre + "_ex").argtypes = lib.gemm_f16_ex.argtypes
+        getattr(lib, pre + "_ex").restype = ctypes.c_int
+        getattr(lib, pre + "_plan").argtypes = lib.gemm_f16_plan.argtypes
+        getattr(lib, pre + "_plan").restype = ctypes.c_int
+        getattr(lib, pre + "_workspace_bytes").argtypes = lib.gemm_f16_workspace_bytes.argtypes
+        getattr(lib, pre + "_workspace_bytes").restype = sz
     lib.gemm_f16_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, i64, vp, i32,
                                      i64, i64, i64, vp, vp, sz]
     lib.gemm_f16_grouped.restype = ctypes.c_int

@@ -130,7 +130,7 @@ __device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta,
   }
 }
 
-template <class CF, int H, class SA, class SB>
+template <class CF, int H, int DT, class SA, class SB>
 __device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
                                                    f32x16 (&acc)[CF::FN][CF::FM], SA& sa,
                                                    SB& sb, uint32_t la, uint32_t lb, int64_t ua,
@@ -140,7 +140,7 @@ __device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
   for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
     for (int j = 0; j < CF::FM; ++j) {
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.fa_[i], f.fb_[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
       const int q = i * CF::FM + j;
       if (q == NQ / 4 - 1) sa.template issue_half<H>(la, ua);
       if (q == 3 * NQ / 4 - 1) sb.issue_batch(lb, tb);
@@ -148,7 +148,7 @@ __device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
 }
 
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
-template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false>
+template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false, int DT = DT_F16>
 __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   static_assert(!(PARTIAL && GROUPED), "grouped launches are never split");
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
@@ -225,11 +225,11 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
         const uint32_t la = lds_a(u + 2, 0), lb = lds_b(t + 3);
         read_frags_a128<CF, 0, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
-        mma_frags_dma_a128<CF, 0>(f0, acc, sa, sb, la, lb, ua, tb);
+        mma_frags_dma_a128<CF, 0, DT>(f0, acc, sa, sb, la, lb, ua, tb);
         __builtin_amdgcn_sched_barrier(0);
         read_frags_a128<CF, 1, BKMAJOR>(f0, slot_a(u), stage_b(t + 1), 0, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
-        mma_frags<CF>(f1, acc);
+        mma_frags<CF, DT>(f1, acc);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<CF::DMA_PER_STEP>();
         wg_barrier();
@@ -241,13 +241,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
         const uint32_t la = lds_a(u + 2, 1), lb = lds_b(t + 3);
         read_frags_a128<CF, 1, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
-        mma_frags_dma_a128<CF, 1>(f0, acc, sa, sb, la, lb, ua, tb);
+        mma_frags_dma_a128<CF, 1, DT>(f0, acc, sa, sb, la, lb, ua, tb);
         __builtin_amdgcn_sched_barrier(0);
         // First fragments of step t+1 (super-step u+1; stale and unused on
         // the last step).
         read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(u + 1), stage_b(t + 1), 0, wm, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
-        mma_frags<CF>(f1, acc);
+        mma_frags<CF, DT>(f1, acc);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<CF::DMA_PER_STEP>();
         wg_barrier();
@@ -264,13 +264,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     __syncthreads();
     read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(nsup), stage_b(nfull2), 0, wm, wn, lane);
     read_frags_a128<CF, 0, BKMAJOR>(f1, slot_a(nsup), stage_b(nfull2), 1, wm, wn, lane);
-    mma_frags<CF>(f0, acc);
-    mma_frags<CF>(f1, acc);
+    mma_frags<CF, DT>(f0, acc);
+    mma_frags<CF, DT>(f1, acc);
     if (rem > 32) {
       read_frags_a128<CF, 1, BKMAJOR>(f0, slot_a(nsup), stage_b(nfull2 + 1), 0, wm, wn, lane);
       read_frags_a128<CF, 1, BKMAJOR>(f1, slot_a(nsup), stage_b(nfull2 + 1), 1, wm, wn, lane);
-      mma_frags<CF>(f0, acc);
-      mma_frags<CF>(f1, acc);
+      mma_frags<CF, DT>(f0, acc);
+      mma_frags<CF, DT>(f1, acc);
     }
   }
 
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
         if constexpr (PARTIAL)
           store4_f32(a, split, m, n, v0, v1, v2, v3);
         else
-          store4_f16(a, m, n, v0, v1, v2, v3);
+          store4_out<DT>(a, m, n, v0, v1, v2, v3);
       }
     }
 }

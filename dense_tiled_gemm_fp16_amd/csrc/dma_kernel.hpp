@@ -264,13 +264,12 @@ __device__ __forceinline__ void mma_frags_dma(const DmaFrags<CF>& f, f32x16 (&ac
     }
 }
 
-template <class CF>
+template <class CF, int DT = DT_F16>
 __device__ __forceinline__ void mma_frags(const DmaFrags<CF>& f, f32x16 (&acc)[CF::FN][CF::FM]) {
 #pragma unroll
   for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::FM; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.fa_[i], f.fb_[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
 }
 
 template <class CF, bool BKMAJOR, bool PARTIAL>
@@ -379,7 +378,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
         if constexpr (PARTIAL)
           store4_f32(a, split, m, n, v0, v1, v2, v3);
         else
-          store4_f16(a, m, n, v0, v1, v2, v3);
+          store4_out<DT_F16>(a, m, n, v0, v1, v2, v3);
       }
     }
 }

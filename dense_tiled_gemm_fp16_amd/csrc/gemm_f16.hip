@@ -101,6 +101,7 @@ struct Plan {
 };
 
 struct Call {
+  int dt;  // element format of A, B and C (DT_F16 or DT_BF16)
   const void *A, *B, *C;
   int64_t lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K;
   int64_t spanA, spanB, spanC;
@@ -166,6 +167,12 @@ int plan_partials(const Call& c, Plan& p) {
   return GEMM_OK;
 }
 
+bool has_format(const TileInfo& t, int dt) {
+  for (int i = 0; i < 9; ++i)
+    if (t.final_fn[dt][i]) return true;
+  return false;
+}
+
 int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   int rc = check_opts(o);
   if (rc) return rc;
@@ -193,8 +200,11 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   }
 
   // Option combinations that no plan accepts are rejected before any device
-  // query.
+  // query.  bfloat16 is built for the 128x128, skinny and full-line-A tiles.
   if ((p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_TILE64X32) && want_split > 1)
+    return GEMM_ERR_OPTS;
+  if (c.dt != DT_F16 && (p.variant == GEMM_VARIANT_TILE64X32 ||
+                         (want_tile && !has_format(tile_info(want_tile), c.dt))))
     return GEMM_ERR_OPTS;
   if (p.variant == GEMM_VARIANT_SKINNY && c.M > 64) return GEMM_ERR_OPTS;
 
@@ -257,10 +267,12 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   // N a multiple of 8).
   for (;;) {
     const TileInfo& t = tile_info(p.tile_id);
-    const bool ok = t.final_fn[p.a_path * 3 + p.b_path] != nullptr &&
+    const bool ok = t.final_fn[c.dt][p.a_path * 3 + p.b_path] != nullptr &&
                     !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult));
     if (ok) break;
-    p.tile_id = t.fallback;
+    // fp16 tiles hand over along their fallback chain; bfloat16 goes straight
+    // to the 128x128 tile, which covers every layout in both formats.
+    p.tile_id = c.dt == DT_F16 ? t.fallback : TILE_T128;
   }
   const TileInfo& ti = tile_info(p.tile_id);
   p.GM = cdiv(c.M, ti.bm);
@@ -324,7 +336,9 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   int64_t M = c.M, N = c.N, ldc = c.ldc;
   uint16_t* C = (uint16_t*)c.C;
   int cv = p.c_vec;
-  kfn_reduce fn = p.red_lanes == 16 ? splitk_reduce<16> : (p.red_lanes == 4 ? splitk_reduce<4> : splitk_reduce<1>);
+  kfn_reduce fn = c.dt == DT_F16
+      ? (p.red_lanes == 16 ? splitk_reduce<16, DT_F16> : (p.red_lanes == 4 ? splitk_reduce<4, DT_F16> : splitk_reduce<1, DT_F16>))
+      : (p.red_lanes == 16 ? splitk_reduce<16, DT_BF16> : (p.red_lanes == 4 ? splitk_reduce<4, DT_BF16> : splitk_reduce<1, DT_BF16>));
   void* rargs[] = {&W, &S, &M, &N, &C, &ldc, &cv};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid2), dim3(256), rargs, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
@@ -332,7 +346,7 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
 }
 
 template <int MT>
-kfn_gemv pick_gemv() { return gemv_kernel<MT, kGemvRpt>; }
+kfn_gemv pick_gemv(int dt) { return dt == DT_F16 ? gemv_kernel<MT, kGemvRpt, DT_F16> : gemv_kernel<MT, kGemvRpt, DT_BF16>; }
 
 int launch_gemv(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   GemvArgs g;
@@ -350,7 +364,7 @@ int launch_gemv(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   g.kr = p.k_split;
   g.GN = (int32_t)p.GN;
   g.S = p.split;
-  kfn_gemv fn = p.gemv_mt == 1 ? pick_gemv<1>() : p.gemv_mt == 2 ? pick_gemv<2>() : pick_gemv<4>();
+  kfn_gemv fn = p.gemv_mt == 1 ? pick_gemv<1>(c.dt) : p.gemv_mt == 2 ? pick_gemv<2>(c.dt) : pick_gemv<4>(c.dt);
   void* args[] = {&g};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(256), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
@@ -383,11 +397,64 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   a.ldb_g = 0;
   a.G = 0;
   const int sel = p.a_path * 3 + p.b_path;
-  kfn_t fn = (p.split > 1) ? ti.partial_fn[sel] : ti.final_fn[sel];
+  kfn_t fn = (p.split > 1) ? ti.partial_fn[c.dt][sel] : ti.final_fn[c.dt][sel];
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
   return launch_reduce(c, p, ws, stream);
+}
+
+int plan_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+              int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+              const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
+  Call c{dt, A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
+  int rc = validate(c);
+  if (rc) return rc;
+  if ((rc = spans(c))) return rc;
+  Plan p;
+  if ((rc = make_plan(c, opts, p))) return rc;
+  if (info) fill_info(p, info);
+  return GEMM_OK;
+}
+
+int ex_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+            int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream,
+            void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts) {
+  Call c{dt, A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
+  int rc = validate(c);
+  if (rc) return rc;
+  if ((rc = spans(c))) return rc;
+  Plan p;
+  if ((rc = make_plan(c, opts, p))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.ws == 0) return launch(c, p, nullptr, s);
+  if (workspace) {
+    if (workspace_bytes < p.ws || ((uintptr_t)workspace & 255u)) return GEMM_ERR_WORKSPACE;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + p.ws;
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+    const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
+    if (ranges_overlap(w0, w1, a0, a1) || ranges_overlap(w0, w1, b0, b1) ||
+        ranges_overlap(w0, w1, c0, c1))
+      return GEMM_ERR_ALIAS;
+    return launch(c, p, workspace, s);
+  }
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, p.ws, s) != hipSuccess) return GEMM_ERR_HIP;
+  rc = launch(c, p, ws, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK) rc = GEMM_ERR_HIP;
+  return rc;
+}
+
+size_t ws_impl(int dt, int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
+  // Shape-only plan on non-overlapping, aligned stand-in addresses.
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  Call c{dt, (const void*)0x100000000000ull, (const void*)0x200000000000ull,
+         (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
+  if (spans(c)) return 0;
+  Plan p;
+  if (make_plan(c, opts, p)) return 0;
+  return p.ws;
 }
 
 // ---- grouped launches
@@ -534,59 +601,47 @@ size_t gemm_f16_grouped_workspace_bytes(int32_t G) {
 int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
                   int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                   const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
-  Call c{A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
-  int rc = validate(c);
-  if (rc) return rc;
-  if ((rc = spans(c))) return rc;
-  Plan p;
-  if ((rc = make_plan(c, opts, p))) return rc;
-  if (info) fill_info(p, info);
-  return GEMM_OK;
+  return plan_impl(DT_F16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info);
 }
 
 int gemm_f16_ex(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
                 int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream,
                 void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts) {
-  Call c{A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
-  int rc = validate(c);
-  if (rc) return rc;
-  if ((rc = spans(c))) return rc;
-  Plan p;
-  if ((rc = make_plan(c, opts, p))) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  if (p.ws == 0) return launch(c, p, nullptr, s);
-  if (workspace) {
-    if (workspace_bytes < p.ws || ((uintptr_t)workspace & 255u)) return GEMM_ERR_WORKSPACE;
-    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + p.ws;
-    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
-    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
-    const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
-    if (ranges_overlap(w0, w1, a0, a1) || ranges_overlap(w0, w1, b0, b1) ||
-        ranges_overlap(w0, w1, c0, c1))
-      return GEMM_ERR_ALIAS;
-    return launch(c, p, workspace, s);
-  }
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, p.ws, s) != hipSuccess) return GEMM_ERR_HIP;
-  rc = launch(c, p, ws, s);
-  if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK) rc = GEMM_ERR_HIP;
-  return rc;
+  return ex_impl(DT_F16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, workspace,
+                 workspace_bytes, opts);
 }
 
 int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
              int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
-  return gemm_f16_ex(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, nullptr, 0, nullptr);
+  return ex_impl(DT_F16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, nullptr, 0,
+                 nullptr);
 }
 
 size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
-  // Shape-only plan on non-overlapping, aligned stand-in addresses.
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
-  Call c{(const void*)0x100000000000ull, (const void*)0x200000000000ull,
-         (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
-  if (spans(c)) return 0;
-  Plan p;
-  if (make_plan(c, opts, p)) return 0;
-  return p.ws;
+  return ws_impl(DT_F16, M, N, K, opts);
+}
+
+int gemm_bf16_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                   int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                   const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
+  return plan_impl(DT_BF16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info);
+}
+
+int gemm_bf16_ex(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                 int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream,
+                 void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts) {
+  return ex_impl(DT_BF16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, workspace,
+                 workspace_bytes, opts);
+}
+
+int gemm_bf16(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+              int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  return ex_impl(DT_BF16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, nullptr, 0,
+                 nullptr);
+}
+
+size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
+  return ws_impl(DT_BF16, M, N, K, opts);
 }
 
 const char* gemm_f16_status_string(int status) {

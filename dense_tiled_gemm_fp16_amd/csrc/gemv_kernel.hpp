@@ -44,23 +44,24 @@ struct GemvArgs {
 // k extent of one A staging chunk (a multiple of 8 * RPT for every RPT used).
 constexpr int kGemvChunk = 1024;
 
+template <int DT>
 __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t w = v[d];
-    f[2 * d] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-    f[2 * d + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    f[2 * d] = cvt_in<DT>((uint16_t)(w & 0xFFFFu));
+    f[2 * d + 1] = cvt_in<DT>((uint16_t)(w >> 16));
   }
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // acc[m][j] += sum over the RPT rows of A[m][k] * B[k][n + j], fp32.
-//   MT >= 2: v_dot2_f32_f16 on pairs of consecutive rows (the fp16 products
-//   are exact in fp32; each instruction adds two of them), the pairs of B
-//   assembled with one byte permute per two rows and column.
-//   MT == 1: one fused multiply-add per product (no permutes needed).
-template <int MT, int RPT>
+//   fp16, MT >= 2: v_dot2_f32_f16 on pairs of consecutive rows (the fp16
+//   products are exact in fp32; each instruction adds two of them), the
+//   pairs of B assembled with one byte permute per two rows and column.
+//   Otherwise (MT == 1, or bfloat16): one fused multiply-add per product.
+template <int MT, int RPT, int DT>
 __device__ __forceinline__ void fma_rows(float (&acc)[MT][8], const u32x4* v,
                                          const uint16_t (*As)[kGemvChunk], int j0) {
   u32x4 aw[MT][RPT / 8];
@@ -68,7 +69,7 @@ __device__ __forceinline__ void fma_rows(float (&acc)[MT][8], const u32x4* v,
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int q = 0; q < RPT / 8; ++q) aw[m][q] = *reinterpret_cast<const u32x4*>(&As[m][j0 + 8 * q]);
-  if constexpr (MT >= 2) {
+  if constexpr (MT >= 2 && DT == DT_F16) {
 #pragma unroll
     for (int i = 0; i < RPT; i += 2) {
 #pragma unroll
@@ -89,11 +90,11 @@ __device__ __forceinline__ void fma_rows(float (&acc)[MT][8], const u32x4* v,
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int q = 0; q < RPT / 8; ++q) unpack8(aw[m][q], &av[m][8 * q]);
+      for (int q = 0; q < RPT / 8; ++q) unpack8<DT>(aw[m][q], &av[m][8 * q]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       float b[8];
-      unpack8(v[i], b);
+      unpack8<DT>(v[i], b);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -115,8 +116,9 @@ __device__ __forceinline__ void load_rows(u32x4* v, const uint16_t* p0, int64_t 
   }
 }
 
-// MT: rows of A handled (>= M); RPT: rows of B per thread per pass.
-template <int MT, int RPT>
+// MT: rows of A handled (>= M); RPT: rows of B per thread per pass; DT: the
+// element format.
+template <int MT, int RPT, int DT>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   static_assert(RPT % 8 == 0 && kGemvChunk % (8 * RPT) == 0, "pass shape");
   __shared__ __attribute__((aligned(16))) uint16_t As[MT][kGemvChunk];
@@ -155,10 +157,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       load_rows<RPT>(v0, p0, a.ldb_k, j0, cl);
       for (; j0 < cl; j0 += 16 * RPT) {
         load_rows<RPT>(v1, p0, a.ldb_k, j0 + 8 * RPT, cl);
-        fma_rows<MT, RPT>(acc, v0, As, j0);
+        fma_rows<MT, RPT, DT>(acc, v0, As, j0);
         if (j0 + 8 * RPT >= cl) break;
         load_rows<RPT>(v0, p0, a.ldb_k, j0 + 16 * RPT, cl);
-        fma_rows<MT, RPT>(acc, v1, As, j0 + 8 * RPT);
+        fma_rows<MT, RPT, DT>(acc, v1, As, j0 + 8 * RPT);
       }
     } else if (nvalid > 0) {
       // The ragged last vector of a row: element loads, one pass at a time.
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
           v[i] = (j0 + i < cl) ? load_partial8(p0 + (j0 + i) * a.ldb_k, 1, nvalid) : zero4();
-        fma_rows<MT, RPT>(acc, v, As, j0);
+        fma_rows<MT, RPT, DT>(acc, v, As, j0);
       }
     }
   }
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     for (int r = 0; r < 8; ++r) t += red[r][tid];
     if (col < a.N) {
       if (a.S == 1)
-        reinterpret_cast<_Float16*>(a.C)[m * a.ldc + col] = (_Float16)t;
+        a.C[m * a.ldc + col] = cvt_out<DT>(t);
       else
         a.P[(s * a.M + m) * a.N + col] = t;
     }

@@ -6,7 +6,8 @@
 
 namespace gemmf16 {
 
-// C[m][n] = fp16_rne( sum over s of W[s][m][n] ) in a fixed order.
+// C[m][n] = rne( sum over s of W[s][m][n] ) in a fixed order (fp16 or
+// bfloat16 output, by DT).
 //
 // A group of L consecutive lanes owns 4 consecutive n of one row (a "quad");
 // lane j of the group sums the contiguous block of K ranges
@@ -17,7 +18,7 @@ namespace gemmf16 {
 // waits for one memory round trip per eight partials rather than per partial
 // (the partials of a small output were written by other XCDs and come from
 // memory, not from this XCD's L2).
-template <int L>
+template <int L, int DT>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int64_t M, int64_t N,
                                                      uint16_t* C, int64_t ldc, int c_vec) {
   static_assert(L >= 1 && 64 % L == 0, "a lane group lies inside one wave");
@@ -68,13 +69,14 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int6
     }
     if (lane == 0) {
       uint16_t* c = C + m * ldc + n;
-      const _Float16 h[4] = {(_Float16)tot[0], (_Float16)tot[1], (_Float16)tot[2], (_Float16)tot[3]};
+      const uint16_t h[4] = {cvt_out<DT>(tot[0]), cvt_out<DT>(tot[1]), cvt_out<DT>(tot[2]),
+                             cvt_out<DT>(tot[3])};
       if (c_vec && nv == 4) {
-        *reinterpret_cast<f16x4*>(c) = f16x4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<u32x2*>(c) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (e < nv) reinterpret_cast<_Float16*>(c)[e] = h[e];
+          if (e < nv) c[e] = h[e];
       }
     }
   }

@@ -44,6 +44,31 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum LoadPath { PATH_GATHER = 0, PATH_KVEC = 1, PATH_RVEC = 2 };
 
+// Element formats of A, B and C (accumulation is fp32 for both).  Loads and
+// LDS staging move 16-bit elements whatever the format; only the MFMA, the
+// VALU decode of inputs and the final conversion differ.
+enum DType { DT_F16 = 0, DT_BF16 = 1 };
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// fp32 -> output element, round to nearest even (v_cvt_f16_f32 /
+// v_cvt_pk_bf16_f32 in the default rounding mode).
+template <int DT>
+__device__ __forceinline__ uint16_t cvt_out(float v) {
+  if constexpr (DT == DT_F16)
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+  else
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Input element -> fp32 (exact for both formats).
+template <int DT>
+__device__ __forceinline__ float cvt_in(uint16_t h) {
+  if constexpr (DT == DT_F16)
+    return (float)__builtin_bit_cast(_Float16, h);
+  else
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ (r >> 3)) & 7; }
 
 // Byte offset of cell (r, c) in an operand tile with R rows.

@@ -106,26 +106,35 @@ struct Acc<32> { typedef f32x16 type; static constexpr int N = 16; };
 template <>
 struct Acc<16> { typedef f32x4 type; static constexpr int N = 4; };
 
-template <int MI>
+template <int MI, int DT>
 __device__ __forceinline__ typename Acc<MI>::type mfma(f16x8 a, f16x8 b, typename Acc<MI>::type c) {
-  if constexpr (MI == 32)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  if constexpr (DT == DT_F16) {
+    if constexpr (MI == 32)
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  } else {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+    if constexpr (MI == 32)
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+  }
 }
 
-// 4 consecutive outputs C[m][n..n+3] (fp16, round to nearest even).
-__device__ __forceinline__ void store4_f16(const KArgs& a, int64_t m, int64_t n, float v0, float v1,
+// 4 consecutive outputs C[m][n..n+3] (round to nearest even).
+template <int DT>
+__device__ __forceinline__ void store4_out(const KArgs& a, int64_t m, int64_t n, float v0, float v1,
                                            float v2, float v3) {
   if (m >= a.M || n >= a.N) return;
   uint16_t* p = a.C + m * a.ldc + n;
-  const _Float16 h[4] = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+  const uint16_t h[4] = {cvt_out<DT>(v0), cvt_out<DT>(v1), cvt_out<DT>(v2), cvt_out<DT>(v3)};
   if (a.c_vec && n + 4 <= a.N) {
-    *reinterpret_cast<f16x4*>(p) = f16x4{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x2*>(p) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (n + e < a.N) reinterpret_cast<_Float16*>(p)[e] = h[e];
+      if (n + e < a.N) p[e] = h[e];
   }
 }
 
@@ -147,7 +156,7 @@ __device__ __forceinline__ void store4_f32(const KArgs& a, int64_t split, int64_
 // MFMAs of one BK step from one LDS stage.  Operand fragments are double
 // buffered in registers: the reads for k-step ks+1 are issued before the
 // MFMAs of k-step ks so LDS latency hides behind matrix work.
-template <class CF>
+template <class CF, int DT>
 __device__ __forceinline__ void compute_stage(const char* ta, const char* tb,
                                               typename Acc<CF::MI>::type (&acc)[CF::FN][CF::FM],
                                               int wm, int wn, int lane) {
@@ -170,7 +179,7 @@ __device__ __forceinline__ void compute_stage(const char* ta, const char* tb,
 #pragma unroll
     for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
-      for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<MI>(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+      for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<MI, DT>(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
   }
 }
 
@@ -178,7 +187,7 @@ __device__ __forceinline__ void compute_stage(const char* ta, const char* tb,
 // (K or the split end not a multiple of BK) is loaded with K masks.  Two LDS
 // stages: while stage t is consumed, step t+1 is fetched into registers and
 // then written to the other stage; one barrier per step.
-template <class CF, bool ROWMASK, class SA, class SB>
+template <class CF, int DT, bool ROWMASK, class SA, class SB>
 __device__ __forceinline__ void main_loop(SA& sa, SB& sb, char* smem,
                                           typename Acc<CF::MI>::type (&acc)[CF::FN][CF::FM],
                                           int64_t kb, int64_t ke, int wm, int wn, int lane) {
@@ -200,7 +209,7 @@ __device__ __forceinline__ void main_loop(SA& sa, SB& sb, char* smem,
     const int cur = (int)(t & 1);
     sa.template load<ROWMASK, false>(kb + (t + 1) * BK, ke);
     sb.template load<ROWMASK, false>(kb + (t + 1) * BK, ke);
-    compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
+    compute_stage<CF, DT>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
     sa.store(smem + (cur ^ 1) * CF::STAGE);
     sb.store(smem + (cur ^ 1) * CF::STAGE + CF::A_BYTES);
     __syncthreads();
@@ -209,17 +218,17 @@ __device__ __forceinline__ void main_loop(SA& sa, SB& sb, char* smem,
     const int cur = (int)(t & 1);
     sa.template load<ROWMASK, true>(kb + nfull * BK, ke);
     sb.template load<ROWMASK, true>(kb + nfull * BK, ke);
-    compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
+    compute_stage<CF, DT>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
     sa.store(smem + (cur ^ 1) * CF::STAGE);
     sb.store(smem + (cur ^ 1) * CF::STAGE + CF::A_BYTES);
     __syncthreads();
     ++t;
   }
   const int cur = (int)(t & 1);
-  compute_stage<CF>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
+  compute_stage<CF, DT>(smem + cur * CF::STAGE, smem + cur * CF::STAGE + CF::A_BYTES, acc, wm, wn, lane);
 }
 
-template <class CF, int APATH, int BPATH, bool PARTIAL, bool GROUPED = false>
+template <class CF, int APATH, int BPATH, bool PARTIAL, bool GROUPED = false, int DT = DT_F16>
 __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
   static_assert(!(PARTIAL && GROUPED), "grouped launches are never split");
   __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
@@ -261,9 +270,9 @@ __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
 
   const bool interior = (m0 + CF::BM <= a.M) && (n0 + CF::BN <= a.N);
   if (interior)
-    main_loop<CF, false>(sa, sb, smem, acc, kb, ke, wm, wn, lane);
+    main_loop<CF, DT, false>(sa, sb, smem, acc, kb, ke, wm, wn, lane);
   else
-    main_loop<CF, true>(sa, sb, smem, acc, kb, ke, wm, wn, lane);
+    main_loop<CF, DT, true>(sa, sb, smem, acc, kb, ke, wm, wn, lane);
 
   // Epilogue.  MFMA output layout (C^T block, MI x MI): lane holds column
   // j = lane % MI (our m) and, for register group g, 4 consecutive rows
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
         if constexpr (PARTIAL)
           store4_f32(a, split, m, n, v0, v1, v2, v3);
         else
-          store4_f16(a, m, n, v0, v1, v2, v3);
+          store4_out<DT>(a, m, n, v0, v1, v2, v3);
       }
     }
 }

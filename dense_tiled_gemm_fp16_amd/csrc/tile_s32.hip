@@ -2,5 +2,5 @@
 #include "tiles.hpp"
 
 namespace gemmf16 {
-TileInfo tile_info_s32() { return make_info<CfgS32>(TILE_S32); }
+TileInfo tile_info_s32() { return make_info<CfgS32, false, true>(TILE_S32); }
 }  // namespace gemmf16

@@ -2,5 +2,5 @@
 #include "tiles.hpp"
 
 namespace gemmf16 {
-TileInfo tile_info_s64() { return make_info<CfgS64>(TILE_S64); }
+TileInfo tile_info_s64() { return make_info<CfgS64, false, true>(TILE_S64); }
 }  // namespace gemmf16

@@ -2,5 +2,5 @@
 #include "tiles.hpp"
 
 namespace gemmf16 {
-TileInfo tile_info_t128() { return make_info<CfgT128, true>(TILE_T128); }
+TileInfo tile_info_t128() { return make_info<CfgT128, true, true>(TILE_T128); }
 }  // namespace gemmf16

@@ -36,27 +36,34 @@ typedef void (*kfn_t)(KArgs);
 
 struct TileInfo {
   int id, bm, bn, bk, nt;
-  kfn_t final_fn[9];    // [a_path * 3 + b_path]; nullptr = layout not supported
-  kfn_t partial_fn[9];
-  kfn_t grouped_fn[9];  // grouped launches (nullptr: not instantiated for this tile)
+  kfn_t final_fn[2][9];    // [format][a_path * 3 + b_path]; nullptr = not supported
+  kfn_t partial_fn[2][9];
+  kfn_t grouped_fn[9];     // grouped launches, fp16 (nullptr: not instantiated)
   int fallback;         // tile used for layouts this one does not support
   int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
 };
 
-template <class CF, bool P, bool G = false>
+template <class CF, bool P, bool G = false, int DT = DT_F16>
 void fill_fns(kfn_t* f) {
-  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P, G>;
-  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P, G>;
-  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P, G>;
-  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P, G>;
-  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P, G>;
-  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P, G>;
-  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P, G>;
-  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P, G>;
-  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P, G>;
+  f[0] = gemm_tile_kernel<CF, PATH_GATHER, PATH_GATHER, P, G, DT>;
+  f[1] = gemm_tile_kernel<CF, PATH_GATHER, PATH_KVEC, P, G, DT>;
+  f[2] = gemm_tile_kernel<CF, PATH_GATHER, PATH_RVEC, P, G, DT>;
+  f[3] = gemm_tile_kernel<CF, PATH_KVEC, PATH_GATHER, P, G, DT>;
+  f[4] = gemm_tile_kernel<CF, PATH_KVEC, PATH_KVEC, P, G, DT>;
+  f[5] = gemm_tile_kernel<CF, PATH_KVEC, PATH_RVEC, P, G, DT>;
+  f[6] = gemm_tile_kernel<CF, PATH_RVEC, PATH_GATHER, P, G, DT>;
+  f[7] = gemm_tile_kernel<CF, PATH_RVEC, PATH_KVEC, P, G, DT>;
+  f[8] = gemm_tile_kernel<CF, PATH_RVEC, PATH_RVEC, P, G, DT>;
 }
 
-template <class CF, bool WITH_GROUPED = false>
+inline void clear_fns(TileInfo& t) {
+  for (int d = 0; d < 2; ++d)
+    for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
+  for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
+}
+
+// Register-path tiles: fp16 always; bfloat16 and grouped launches where asked.
+template <class CF, bool WITH_GROUPED = false, bool WITH_BF16 = false>
 TileInfo make_info(int id) {
   TileInfo t;
   t.id = id;
@@ -64,9 +71,13 @@ TileInfo make_info(int id) {
   t.bn = CF::BN;
   t.bk = CF::BK;
   t.nt = CF::NT;
-  fill_fns<CF, false>(t.final_fn);
-  fill_fns<CF, true>(t.partial_fn);
-  for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
+  clear_fns(t);
+  fill_fns<CF, false>(t.final_fn[DT_F16]);
+  fill_fns<CF, true>(t.partial_fn[DT_F16]);
+  if constexpr (WITH_BF16) {
+    fill_fns<CF, false, false, DT_BF16>(t.final_fn[DT_BF16]);
+    fill_fns<CF, true, false, DT_BF16>(t.partial_fn[DT_BF16]);
+  }
   if constexpr (WITH_GROUPED) fill_fns<CF, false, true>(t.grouped_fn);
   t.fallback = 0;
   t.n_mult = 0;
@@ -82,11 +93,11 @@ TileInfo make_dma_info(int id, int fallback) {
   t.bn = CF::BN;
   t.bk = CF::BK;
   t.nt = CF::NT;
-  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = t.grouped_fn[i] = nullptr;
-  t.final_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, false>;
-  t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false>;
-  t.partial_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true>;
-  t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, true>;
+  clear_fns(t);
+  t.final_fn[DT_F16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, false>;
+  t.final_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false>;
+  t.partial_fn[DT_F16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true>;
+  t.partial_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, true>;
   t.fallback = fallback;
   t.n_mult = 8;
   return t;
@@ -101,13 +112,17 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   t.bn = CF::BN;
   t.bk = CF::BK;
   t.nt = CF::NT;
-  for (int i = 0; i < 9; ++i) t.final_fn[i] = t.partial_fn[i] = t.grouped_fn[i] = nullptr;
-  t.final_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false>;
+  clear_fns(t);
+  t.final_fn[DT_F16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false>;
+  t.final_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false>;
+  t.partial_fn[DT_F16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, true>;
+  t.partial_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, true>;
+  t.final_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false, false, DT_BF16>;
+  t.final_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, false, DT_BF16>;
+  t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, true, false, DT_BF16>;
+  t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, true, false, DT_BF16>;
   t.grouped_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false, true>;
   t.grouped_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, true>;
-  t.final_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false>;
-  t.partial_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, true>;
-  t.partial_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, true>;
   t.fallback = fallback;
   t.n_mult = 8;
   return t;

@@ -134,6 +134,34 @@ int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k,
 size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
 
 /*
+ * The same product with bfloat16 inputs and output: A, B and C hold
+ * bfloat16 (the upper 16 bits of an IEEE binary32) instead of binary16;
+ * accumulation is fp32 and C is rounded to nearest-even bfloat16.  The same
+ * arguments, validation, options (variant AUTO, MAIN, SKINNY or SPLITK; the
+ * 64x32x32 variant and tiles other than the 128x128, skinny and full-line-A
+ * ones are fp16-only and return GEMM_ERR_OPTS), workspace contract and
+ * return codes as the fp16 functions above.  The pages fix fp16; bfloat16 is
+ * the same computation in the other 16-bit format the matrix cores take
+ * (TileLang tutorial, ch. 14, section 5: lower-precision variants keep the
+ * GEMM skeleton and change the matrix instruction).
+ */
+int gemm_bf16(const void* A, int64_t lda_m, int64_t lda_k,
+              const void* B, int64_t ldb_k, int64_t ldb_n,
+              void* C, int64_t ldc,
+              int64_t M, int64_t N, int64_t K, void* stream);
+int gemm_bf16_ex(const void* A, int64_t lda_m, int64_t lda_k,
+                 const void* B, int64_t ldb_k, int64_t ldb_n,
+                 void* C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, void* stream,
+                 void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts);
+int gemm_bf16_plan(const void* A, int64_t lda_m, int64_t lda_k,
+                   const void* B, int64_t ldb_k, int64_t ldb_n,
+                   const void* C, int64_t ldc,
+                   int64_t M, int64_t N, int64_t K,
+                   const gemm_f16_opts* opts, gemm_f16_plan_info* info);
+size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
+
+/*
  * Grouped product, one launch over G products that share N and K (the
  * TileLang tutorial, ch. 14, section 4.3: grouped GEMM with per-group row
  * counts, as for the experts of a mixture-of-experts layer):

@@ -52,6 +52,24 @@ def assert_close(gpu_bits, ref_bits, what=""):
                     f"gpu {val(gpu_bits)[idx]} oracle {val(ref_bits)[idx]})")
 
 
+def bf16_val(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+
+
+def assert_close_bf16(gpu_bits, ref_bits, what=""):
+    """bfloat16 outputs: |C_gpu - C_oracle| <= 1e-2 + 8e-3 |C_oracle| (one
+    bfloat16 unit in the last place is at most 2^-7 |C|; the fp32 sums of the
+    two sides may fall on either side of a rounding boundary)."""
+    g, r = bf16_val(gpu_bits), bf16_val(ref_bits)
+    err = np.abs(g - r)
+    bad = ~(err <= 1e-2 + 8e-3 * np.abs(r))
+    if bad.any():
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} bfloat16 outputs outside 1e-2 + 8e-3|C| "
+                             f"(first at {idx}: gpu {g[idx]} oracle {r[idx]})")
+
+
 def assert_bits_equal(gpu_bits, ref_bits, what=""):
     if not np.array_equal(gpu_bits, ref_bits):
         diff = np.argwhere(gpu_bits != ref_bits)

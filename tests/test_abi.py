@@ -22,7 +22,7 @@ PA, PB, PC, PW = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_f16\w*)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_b?f16\w*)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_binding_list():
@@ -161,3 +161,17 @@ def test_grouped_workspace():
     assert gcall(ws=PW, ws_bytes=need - 1) == -6
     assert gcall(ws=PW + 16, ws_bytes=need) == -6
     assert gcall(ws=PC, ws_bytes=need) == -5    # workspace overlapping C
+
+
+def test_bf16_options_and_plans():
+    def bcall(o):
+        return g.lib.gemm_bf16_ex(PA, 64, 1, PB, 32, 1, PC, 32, 16, 32, 64, 0, 0, 0, o)
+    assert bcall(_lib.Opts(4, 0, 0, 0)) == -7      # the 64x32x32 variant is fp16-only
+    assert bcall(_lib.Opts(1, 0, 4, 11)) == -7     # a tile without bfloat16 kernels
+    assert bcall(_lib.Opts(1, 0, 4, 99)) == -7
+    info = _lib.PlanInfo()
+    o = _lib.Opts(3, 4, -1, 1)                     # forced split-K on the 128x128 tile
+    rc = g.lib.gemm_bf16_plan(PA, 1024, 1, PB, 32, 1, PC, 32, 16, 32, 1024, ctypes.byref(o),
+                              ctypes.byref(info))
+    assert rc == 0 and info.split_k == 4 and info.workspace_bytes == 4 * 16 * 32 * 4
+    assert g.lib.gemm_bf16_workspace_bytes(16, 32, 1024, ctypes.byref(o)) == 4 * 16 * 32 * 4
