@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--skinny-reps", type=int, default=400, help="decode calls timed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB device copy (a known-size reference for HBM counters)")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload family (one JSON line each) instead of the headline")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
@@ -164,10 +166,88 @@ def cpu_baseline(budget_s=15.0):
                       f"full K), {dt:.1f} s"}
 
 
+# The five workload families of the task, as (name, M, N, K, B layout); the
+# configurations sweep times each one (not the headline line).
+CONFIGS = [
+    ("edge_130x70x65", 130, 70, 65, "row"), ("edge_130x70x65_bt", 130, 70, 65, "col"),
+    ("square_256", 256, 256, 256, "row"), ("square_1024", 1024, 1024, 1024, "row"),
+    ("square_4096", 4096, 4096, 4096, "row"), ("square_8192", 8192, 8192, 8192, "row"),
+    ("skinny_m1", 1, 2048, 7168, "row"), ("skinny_m16", 16, 2048, 7168, "row"),
+    ("skinny_m64", 64, 2048, 7168, "row"), ("splitk_512x512x65536", 512, 512, 65536, "row"),
+    ("moe_131072x2048x7168", 131072, 2048, 7168, "row"),
+    ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col"),
+]
+
+
+def configs_sweep():
+    """One JSON line per configuration: GPU time per call and the rate
+    against the roofline its arithmetic intensity selects.  Working sets
+    under 1 GiB rotate over copies (up to 64) so calls do not run from the
+    previous call's caches; calls are captured in a graph so per-call host
+    cost is not timed."""
+    import numpy as np
+    import torch
+
+    import dense_tiled_gemm_fp16_amd as g
+    import synth
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+
+    for i, (name, m, n, k, bl) in enumerate(CONFIGS):
+        a0 = to_dev(synth.matrix(m, k, 7000 + i, synth.TENSOR_A))
+        bt = synth.matrix(k, n, 7000 + i, synth.TENSOR_B, order="col" if bl == "col" else "row")
+        b0 = to_dev(bt).t() if bl == "col" else to_dev(bt)
+        byts = 2.0 * (m * k + k * n + m * n)
+        copies = int(min(64, max(1, -(-(1 << 30) // int(byts)))))
+        As = [a0] + [a0.clone() for _ in range(copies - 1)]
+        Bs = [b0] + [(b0.t().clone().t() if bl == "col" else b0.clone()) for _ in range(copies - 1)]
+        c = torch.empty((m, n), dtype=torch.float16, device=dev)
+        p = g.plan(a0, b0, c)
+        ws = (torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+              if p["workspace_bytes"] else None)
+        cap = torch.cuda.Stream(dev)
+        with torch.cuda.stream(cap):
+            g.gemm(a0, b0, out=c, workspace=ws, stream=cap)
+        torch.cuda.synchronize()
+        reps = copies if byts * copies >= (1 << 28) else max(copies, 64)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for r in range(reps):
+                g.gemm(As[r % copies], Bs[r % copies], out=c, workspace=ws, stream=cap)
+        times = []
+        for r in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            e1.synchronize()
+            if r >= 1:
+                times.append(e0.elapsed_time(e1) / reps)
+        ms = sorted(times)[len(times) // 2]
+        flops = 2.0 * m * n * k
+        ai = flops / byts
+        tf, gbs = flops / (ms * 1e-3) / 1e12, byts / (ms * 1e-3) / 1e9
+        bound = "mfma" if ai >= PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+        print(json.dumps({"config": name, "M": m, "N": n, "K": k, "b_layout": bl,
+                          "plan": {q: p[q] for q in ("variant", "tile_id", "split_k", "grid")},
+                          "us_per_call": ms * 1e3, "TFLOPS": tf, "GBps": gbs, "AI": ai,
+                          "bound": bound,
+                          "frac": tf / PEAK_F16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS,
+                          "copies": copies}), flush=True)
+        del As, Bs, a0, b0, c, ws, graph
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.configs:
+        configs_sweep()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this GEMM build "

@@ -224,7 +224,9 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
       }
       break;
     case GEMM_VARIANT_SPLITK:
-      p.tile_id = want_tile ? want_tile : TILE_T128;
+      // The 256x256 full-line-A tile once the output holds a whole one (it
+      // falls back to 128x128 for layouts it does not take).
+      p.tile_id = want_tile ? want_tile : ((c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128);
       break;
     case GEMM_VARIANT_TILE64X32:
       if (want_tile && want_tile != TILE_T64X32) return GEMM_ERR_OPTS;
@@ -284,7 +286,13 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     int64_t s = want_split;
     if (s == 0) {
       if ((rc = need_cus())) return rc;
-      s = cdiv(2 * (int64_t)cus, T);
+      // Workgroups per compute unit: two for split-K on 128x128 tiles; one
+      // for skinny tiles, where every K range adds S x M x N x 4 bytes of
+      // partials against the 2KN bytes of B (M = 32..64 ran fastest at one);
+      // one half for the 256x256 tile, whose partials are 4x larger per
+      // workgroup (512 x 512 x 65536 ran fastest there).
+      const int64_t per_cu2 = p.variant == GEMM_VARIANT_SKINNY ? 2 : (ti.bm >= 256 ? 1 : 4);
+      s = cdiv(per_cu2 * (int64_t)cus, 2 * T);
       const int64_t max_by_k = cdiv(c.K, 2 * ti.bk);  // at least two K steps per split
       if (s > max_by_k) s = max_by_k;
       if (s > 64) s = 64;
