@@ -70,6 +70,9 @@ def measured_traffic(kind):
 
 
 COPY_KIB = float(1 << 20)      # the calibration copy reads and writes 1 GiB
+# The fp16 main-kernel instantiation that the 131072x2048x7168 plan runs
+# (N-contiguous B, one K range, not grouped).
+MAIN_KERNEL = "void gemmf16::gemm_dma_a128_kernel<gemmf16::DmaA128Cfg<4, 2>, false, false, false, 0>"
 
 
 def summarize_pmc(fetch_csv, write_csv):
@@ -96,8 +99,10 @@ def summarize_pmc(fetch_csv, write_csv):
     fetch, f_scale = load(fetch_csv, "FETCH_SIZE")
     write, w_scale = load(write_csv, "WRITE_SIZE")
 
-    def kernel(substr):
-        names = [k for k in fetch if substr in k]
+    def kernel(prefix):
+        # The instantiation itself: the grouped and bfloat16 launches of the
+        # same kernel template run in the same process.
+        names = [k for k in fetch if k.startswith(prefix)]
         if not names:
             return None
         name = max(names, key=lambda k: statistics.mean(fetch[k]))
@@ -108,9 +113,9 @@ def summarize_pmc(fetch_csv, write_csv):
     out = {"calibration": {"copy_bytes": COPY_KIB * 1024, "fetch_scale": f_scale,
                            "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer"},
            "source_hash": kernel_source_hash()}
-    alg = {"main_131072x2048x7168": ("gemm_dma", 2.0 * (M * K + K * N), 2.0 * M * N),
-           "skinny_m1_partials": ("gemv_kernel", 2.0 * (K + K * N), None),
-           "skinny_m1_reduce": ("splitk_reduce", None, 2.0 * N)}
+    alg = {"main_131072x2048x7168": (MAIN_KERNEL, 2.0 * (M * K + K * N), 2.0 * M * N),
+           "skinny_m1_partials": ("void gemmf16::gemv_kernel<1, 8, 0>", 2.0 * (K + K * N), None),
+           "skinny_m1_reduce": ("void gemmf16::splitk_reduce<16, 0>", None, 2.0 * N)}
     for key, (sub, alg_read, alg_write) in alg.items():
         k = kernel(sub)
         if k is None:
