@@ -1,8 +1,8 @@
 // LDS-DMA main kernel with full-line A rows (gfx950).
 //
-// The same method and k-step schedule as dma_kernel.hpp (one workgroup per
-// 256 x 256 tile, 32-k steps, MFMA 32x32x16, counted waits and a raw
-// barrier), with one change in how A reaches LDS.  There, a 32-k step of a
+// The same tile as dma_kernel.hpp (one workgroup per 256 x 256 tile, 32-k
+// steps, MFMA 32x32x16, counted waits and raw barriers), with two changes:
+// how A reaches LDS, and a ping-pong schedule of the two wave groups.  There, a 32-k step of a
 // K-contiguous A row is 64 bytes, so each global_load_lds_dwordx4 touches
 // sixteen half-used 128-byte lines, and the load path's cost follows the
 // number of lines touched rather than the bytes moved.  Here A is staged 64 k
@@ -10,11 +10,16 @@
 // eight whole lines, half as many per byte.
 //
 // LDS: three A super-slots of 256 x 64 (32 KiB each) and four B stages of
-// 32 x 256 (16 KiB each), 160 KiB in all.  In k-step t = 2u + h a wave issues
-// half h of A super-step u + 2 and all of its B k-step t + 3, so every step
-// issues the same four instructions and "all but this step's" is one fixed
-// vmcnt.  Super-step u + 2 overwrites the slot of super-step u - 1, whose
-// last reads were before the barrier that ended step 2u - 1.
+// 32 x 256 (16 KiB each), 160 KiB in all.  In k-step t = 2u + h a wave
+// issues half h of A super-step u + 2 and all of its B k-step t + 3, so
+// every step issues the same four instructions and "all but this step's" is
+// one fixed vmcnt.
+//
+// Schedule: the two halves of the workgroup (one wave of each per SIMD)
+// alternate between a memory phase (LDS fragment reads, DMA issue) and a
+// compute phase (MFMAs), one phase apart, so the matrix core of a SIMD is fed
+// by one wave while the other loads.  Phases end at workgroup barriers; the
+// loop states which barrier frees or publishes which slot.
 //
 // A slot layout: row r at r * 128 bytes; its octet c (k 8c .. 8c+7 of the
 // super-step) in 16-byte slot c ^ f8(r), with f8(r) = (r ^ (r >> 3)) & 7, so
@@ -25,6 +30,8 @@
 // and/or a K tail) is filled by masked register loads with zero fill after
 // the pipelined loop.
 #pragma once
+
+#include <type_traits>
 
 #include "dma_kernel.hpp"
 
@@ -98,53 +105,54 @@ struct ASource128 {
   }
 };
 
-// Fragments of k-substep ks of the 32-k step in half H of a super-step.  B
-// stages are laid out as in dma_kernel.hpp: N-major 512-byte k-rows, or,
-// for a K-contiguous B (BKMAJOR), 64-byte n-rows like its A tiles.
+// One fragment of k-substep ks of the 32-k step in half H of a super-step:
+// piece q < FM is A fragment q, piece FM + i is B fragment i.  B stages are
+// laid out as in dma_kernel.hpp: N-major 512-byte k-rows, or, for a
+// K-contiguous B (BKMAJOR), 64-byte n-rows like its A tiles.
 template <class CF, int H, bool BKMAJOR>
-__device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta, const char* tb,
-                                                int ks, int wm, int wn, int lane) {
+__device__ __forceinline__ void read_piece_a128(DmaFrags<CF>& f, const char* ta, const char* tb,
+                                                int ks, int wm, int wn, int lane, int q) {
   const int lr = lane % 32, lo = lane / 32;
-  const int c = 4 * H + 2 * ks + lo;
-#pragma unroll
-  for (int j = 0; j < CF::FM; ++j) {
-    const int r = wm * CF::WTM + j * 32 + lr;
-    f.fb_[j] = *reinterpret_cast<const f16x8*>(ta + r * 128 + ((c ^ f8(r)) * 16));
-  }
-  if constexpr (BKMAJOR) {
+  if (q < CF::FM) {
+    const int c = 4 * H + 2 * ks + lo;
+    const int r = wm * CF::WTM + q * 32 + lr;
+    f.fb_[q] = *reinterpret_cast<const f16x8*>(ta + r * 128 + ((c ^ f8(r)) * 16));
+  } else if constexpr (BKMAJOR) {
     const int cb = ks * 2 + lo;
-#pragma unroll
-    for (int i = 0; i < CF::FN; ++i) {
-      const int r = wn * CF::WTN + i * 32 + lr;
-      f.fa_[i] = *reinterpret_cast<const f16x8*>(tb + r * 64 + ((cb ^ fa(r)) * 16));
-    }
+    const int r = wn * CF::WTN + (q - CF::FM) * 32 + lr;
+    f.fa_[q - CF::FM] = *reinterpret_cast<const f16x8*>(tb + r * 64 + ((cb ^ fa(r)) * 16));
   } else {
     const int g = lane / 16, s = lane % 16;
     const int kr = ks * 16 + 8 * (g / 2) + s / 4;
-#pragma unroll
-    for (int i = 0; i < CF::FN; ++i) {
-      const int n = wn * CF::WTN + i * 32 + 16 * (g % 2);
-      const char* p0 = tb + kr * 512 + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
-      f.fa_[i] = read_tr_pair(p0, p0 + 4 * 512);
-    }
+    const int n = wn * CF::WTN + (q - CF::FM) * 32 + 16 * (g % 2);
+    const char* p0 = tb + kr * 512 + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
+    f.fa_[q - CF::FM] = read_tr_pair(p0, p0 + 4 * 512);
   }
 }
 
-template <class CF, int H, int DT, class SA, class SB>
-__device__ __forceinline__ void mma_frags_dma_a128(const DmaFrags<CF>& f,
-                                                   f32x16 (&acc)[CF::FN][CF::FM], SA& sa,
-                                                   SB& sb, uint32_t la, uint32_t lb, int64_t ua,
-                                                   int64_t tb) {
-  constexpr int NQ = CF::FN * CF::FM;
+template <class CF, int H, bool BKMAJOR>
+__device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta, const char* tb,
+                                                int ks, int wm, int wn, int lane) {
 #pragma unroll
-  for (int i = 0; i < CF::FN; ++i)
+  for (int q = 0; q < CF::FM + CF::FN; ++q) read_piece_a128<CF, H, BKMAJOR>(f, ta, tb, ks, wm, wn, lane, q);
+}
+
+// The MFMAs of `cur` with the reads of `nxt` (k-substep ks, super-step half
+// H) placed one fragment after each of the first FM + FN MFMAs, so the reads
+// issue in the shadow of matrix work.  `nxt` may be the registers of a
+// fragment set consumed earlier in program order.
+template <class CF, int H, bool BKMAJOR, int DT>
+__device__ __forceinline__ void mma_and_read(const DmaFrags<CF>& cur, DmaFrags<CF>& nxt,
+                                             f32x16 (&acc)[CF::FN][CF::FM], const char* ta,
+                                             const char* tb, int ks, int wm, int wn, int lane) {
+  static_assert(CF::FM + CF::FN <= CF::FN * CF::FM, "one read per MFMA at most");
 #pragma unroll
-    for (int j = 0; j < CF::FM; ++j) {
-      acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
-      const int q = i * CF::FM + j;
-      if (q == NQ / 4 - 1) sa.template issue_half<H>(la, ua);
-      if (q == 3 * NQ / 4 - 1) sb.issue_batch(lb, tb);
-    }
+  for (int q = 0; q < CF::FN * CF::FM; ++q) {
+    const int i = q / CF::FM, j = q % CF::FM;
+    acc[i][j] = mfma<32, DT>(cur.fa_[i], cur.fb_[j], acc[i][j]);
+    if (q < CF::FM + CF::FN) read_piece_a128<CF, H, BKMAJOR>(nxt, ta, tb, ks, wm, wn, lane, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
@@ -202,8 +210,28 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   DmaFrags<CF> f0, f1;
 
   if (nsup > 0) {
-    // Prologue: A super-steps 0 and 1, B steps 0, 1, 2 (clamped); then A(0),
-    // B(0) and B(1) complete (only A(1) and B(2) may still be in flight).
+    // Two groups of waves take turns on the matrix cores.  Waves w and
+    // w + NW/2 share a SIMD; group 0 is waves 0 .. NW/2-1 (tile rows 0..127),
+    // group 1 the rest.  Each 32-k step t of a group has a memory phase M(t)
+    // (second k-substep fragments of step t, this wave's DMA of step t + 3)
+    // and a compute phase C(t) (the 16 MFMAs of step t, with the first
+    // k-substep fragments of step t + 1 read under the second eight).
+    // Group 1 runs one phase behind group 0, so while one wave of a SIMD
+    // issues MFMAs the other issues its loads.  Every phase ends at a
+    // workgroup barrier; barrier b ends phase b - 1 of group 0 and phase
+    // b - 2 of group 1 (group 1 passes barrier 1 before its first phase).
+    //
+    // Invariants (D = 3 steps of prefetch, 4 B stages, 3 A super-slots):
+    //  - a wave's reads are complete when it leaves its memory phase
+    //    (lgkmcnt 0), so what group 1 reads of step t, in C(t-1) and M(t),
+    //    is free after barrier 2t + 2.  That barrier precedes group 0's
+    //    M(t + 1), the first phase to issue a DMA into that B stage (step
+    //    t + 4) or, when t ends a super-step, into that A super-slot;
+    //  - a wave leaves C(t) with only M(t)'s DMA outstanding (vmcnt), so
+    //    step t + 2 and its super-step have landed, for every wave, before
+    //    barrier 2t + 3, which precedes the first read of them (group 0's
+    //    C(t + 1)).
+    const bool g1 = wave >= CF::NW / 2;
     const int64_t u1 = nsup > 1 ? 1 : 0;
     sa.template issue_half<0>(lds_a(0, 0), 0);
     sa.template issue_half<1>(lds_a(0, 1), 0);
@@ -212,48 +240,42 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     sa.template issue_half<0>(lds_a(1, 0), u1);
     sa.template issue_half<1>(lds_a(1, 1), u1);
     sb.issue_batch(lds_b(2), nfull2 > 2 ? 2 : nfull2 - 1);
-    wait_vmcnt<CF::DMA_A + CF::DMA_B>();
+    wait_vmcnt<CF::DMA_A + CF::DMA_B>();   // A(0), B(0) and B(1) landed
     wg_barrier();
     read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(0), stage_b(0), 0, wm, wn, lane);
+    if (g1) wg_barrier();
 
+    // One step: H is the step's half of its super-step u; the DMA of step
+    // t + 3 carries half H of super-step u + 2 (clamped to the last one).
+    auto step = [&](auto h_tag, int64_t u, int64_t t, int64_t ua) {
+      constexpr int H = decltype(h_tag)::value;
+      const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
+      // M(t)
+      read_frags_a128<CF, H, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
+      sa.template issue_half<H>(lds_a(u + 2, H), ua);
+      sb.issue_batch(lds_b(t + 3), tb);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // C(t); the reads for step t + 1 fetch unused bytes of free slots on
+      // the last step.
+      mma_frags<CF, DT>(f0, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_and_read<CF, 1 - H, BKMAJOR, DT>(f1, f0, acc, slot_a(H ? u + 1 : u), stage_b(t + 1), 0,
+                                           wm, wn, lane);
+      wait_vmcnt<CF::DMA_PER_STEP>();
+      __builtin_amdgcn_sched_barrier(0);
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
     for (int64_t u = 0; u < nsup; ++u) {
       const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
-      // ---- step t = 2u (first half of super-step u)
-      {
-        const int64_t t = 2 * u;
-        const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
-        const uint32_t la = lds_a(u + 2, 0), lb = lds_b(t + 3);
-        read_frags_a128<CF, 0, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags_dma_a128<CF, 0, DT>(f0, acc, sa, sb, la, lb, ua, tb);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags_a128<CF, 1, BKMAJOR>(f0, slot_a(u), stage_b(t + 1), 0, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags<CF, DT>(f1, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<CF::DMA_PER_STEP>();
-        wg_barrier();
-      }
-      // ---- step t = 2u + 1 (second half)
-      {
-        const int64_t t = 2 * u + 1;
-        const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
-        const uint32_t la = lds_a(u + 2, 1), lb = lds_b(t + 3);
-        read_frags_a128<CF, 1, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags_dma_a128<CF, 1, DT>(f0, acc, sa, sb, la, lb, ua, tb);
-        __builtin_amdgcn_sched_barrier(0);
-        // First fragments of step t+1 (super-step u+1; stale and unused on
-        // the last step).
-        read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(u + 1), stage_b(t + 1), 0, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags<CF, DT>(f1, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<CF::DMA_PER_STEP>();
-        wg_barrier();
-      }
+      step(std::integral_constant<int, 0>{}, u, 2 * u, ua);
+      step(std::integral_constant<int, 1>{}, u, 2 * u + 1, ua);
     }
-    wait_vmcnt<0>();   // no LDS transfer may still be in flight past this point
+    if (!g1) wg_barrier();   // pairs with group 1's extra first barrier
+    wait_vmcnt<0>();         // no LDS transfer may still be in flight past this point
   }
   if (rem > 0) {
     // Remainder (< 64 k): masked fill of A super-slot nsup and B stages of
