@@ -141,18 +141,32 @@ __device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta,
 // H) placed one fragment after each of the first FM + FN MFMAs, so the reads
 // issue in the shadow of matrix work.  `nxt` may be the registers of a
 // fragment set consumed earlier in program order.
-template <class CF, int H, bool BKMAJOR, int DT>
+// EDGE: a wave of an edge tile skips the MFMAs of 32 x 32 blocks that lie
+// wholly past N (i >= fnv) or past M (j >= fmv); their outputs are never
+// stored.  fnv and fmv are uniform over the wave.
+template <class CF, int H, bool BKMAJOR, int DT, bool EDGE>
 __device__ __forceinline__ void mma_and_read(const DmaFrags<CF>& cur, DmaFrags<CF>& nxt,
                                              f32x16 (&acc)[CF::FN][CF::FM], const char* ta,
-                                             const char* tb, int ks, int wm, int wn, int lane) {
+                                             const char* tb, int ks, int wm, int wn, int lane,
+                                             int fnv, int fmv) {
   static_assert(CF::FM + CF::FN <= CF::FN * CF::FM, "one read per MFMA at most");
 #pragma unroll
   for (int q = 0; q < CF::FN * CF::FM; ++q) {
     const int i = q / CF::FM, j = q % CF::FM;
-    acc[i][j] = mfma<32, DT>(cur.fa_[i], cur.fb_[j], acc[i][j]);
+    if (!EDGE || (i < fnv && j < fmv)) acc[i][j] = mfma<32, DT>(cur.fa_[i], cur.fb_[j], acc[i][j]);
     if (q < CF::FM + CF::FN) read_piece_a128<CF, H, BKMAJOR>(nxt, ta, tb, ks, wm, wn, lane, q);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+template <class CF, int DT, bool EDGE>
+__device__ __forceinline__ void mma_frags_a128(const DmaFrags<CF>& f, f32x16 (&acc)[CF::FN][CF::FM],
+                                               int fnv, int fmv) {
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j)
+      if (!EDGE || (i < fnv && j < fmv)) acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
 }
 
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
@@ -181,6 +195,12 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
   const int64_t kb = split * a.k_split;
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
+  // 32-wide blocks of this wave's sub-tile that hold any output (all of
+  // them except in the last tile row or column).
+  const int64_t nrem = a.N - (n0 + wn * CF::WTN), mrem = a.M - (m0 + wm * CF::WTM);
+  const int fnv = nrem <= 0 ? 0 : (nrem >= CF::WTN ? CF::FN : (int)((nrem + 31) / 32));
+  const int fmv = mrem <= 0 ? 0 : (mrem >= CF::WTM ? CF::FM : (int)((mrem + 31) / 32));
+  const bool edge = fnv < CF::FN || fmv < CF::FM;
 
   ASource128<CF::DMA_A> sa;
   DmaSource<CF::DMA_B, BKMAJOR> sb;
@@ -247,8 +267,9 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
 
     // One step: H is the step's half of its super-step u; the DMA of step
     // t + 3 carries half H of super-step u + 2 (clamped to the last one).
-    auto step = [&](auto h_tag, int64_t u, int64_t t, int64_t ua) {
+    auto step = [&](auto h_tag, auto e_tag, int64_t u, int64_t t, int64_t ua) {
       constexpr int H = decltype(h_tag)::value;
+      constexpr bool EDGE = decltype(e_tag)::value;
       const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
       // M(t)
       read_frags_a128<CF, H, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
@@ -260,20 +281,27 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       // C(t); the reads for step t + 1 fetch unused bytes of free slots on
       // the last step.
-      mma_frags<CF, DT>(f0, acc);
+      mma_frags_a128<CF, DT, EDGE>(f0, acc, fnv, fmv);
       __builtin_amdgcn_sched_barrier(0);
-      mma_and_read<CF, 1 - H, BKMAJOR, DT>(f1, f0, acc, slot_a(H ? u + 1 : u), stage_b(t + 1), 0,
-                                           wm, wn, lane);
+      mma_and_read<CF, 1 - H, BKMAJOR, DT, EDGE>(f1, f0, acc, slot_a(H ? u + 1 : u), stage_b(t + 1),
+                                                 0, wm, wn, lane, fnv, fmv);
       wait_vmcnt<CF::DMA_PER_STEP>();
       __builtin_amdgcn_sched_barrier(0);
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
-    for (int64_t u = 0; u < nsup; ++u) {
-      const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
-      step(std::integral_constant<int, 0>{}, u, 2 * u, ua);
-      step(std::integral_constant<int, 1>{}, u, 2 * u + 1, ua);
-    }
+    // Both loops pass the same barriers; the edge one skips empty blocks.
+    auto run = [&](auto e_tag) {
+      for (int64_t u = 0; u < nsup; ++u) {
+        const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
+        step(std::integral_constant<int, 0>{}, e_tag, u, 2 * u, ua);
+        step(std::integral_constant<int, 1>{}, e_tag, u, 2 * u + 1, ua);
+      }
+    };
+    if (edge)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
     if (!g1) wg_barrier();   // pairs with group 1's extra first barrier
     wait_vmcnt<0>();         // no LDS transfer may still be in flight past this point
   }
@@ -286,13 +314,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     __syncthreads();
     read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(nsup), stage_b(nfull2), 0, wm, wn, lane);
     read_frags_a128<CF, 0, BKMAJOR>(f1, slot_a(nsup), stage_b(nfull2), 1, wm, wn, lane);
-    mma_frags<CF, DT>(f0, acc);
-    mma_frags<CF, DT>(f1, acc);
+    mma_frags_a128<CF, DT, true>(f0, acc, fnv, fmv);
+    mma_frags_a128<CF, DT, true>(f1, acc, fnv, fmv);
     if (rem > 32) {
       read_frags_a128<CF, 1, BKMAJOR>(f0, slot_a(nsup), stage_b(nfull2 + 1), 0, wm, wn, lane);
       read_frags_a128<CF, 1, BKMAJOR>(f1, slot_a(nsup), stage_b(nfull2 + 1), 1, wm, wn, lane);
-      mma_frags<CF, DT>(f0, acc);
-      mma_frags<CF, DT>(f1, acc);
+      mma_frags_a128<CF, DT, true>(f0, acc, fnv, fmv);
+      mma_frags_a128<CF, DT, true>(f1, acc, fnv, fmv);
     }
   }
 

@@ -181,6 +181,23 @@ def test_dma_tiles_k_remainders(tile, K, b_layout):
             check(run(a, b, Out(M, N), **kw), ref, mode, f"dma tile K={K} {mode} {kw}")
 
 
+@pytest.mark.parametrize("b_layout", ["row", "col"])
+def test_main_tile_edge_blocks(b_layout):
+    # Last tile row / column of the 256x256 tile with every count of live
+    # 32-wide blocks per wave (a wave owns 64 rows x 128 columns): rows past
+    # M and columns past N are skipped by the edge tiles' MFMA predicate.
+    K = 96
+    for M in (257, 321, 449):
+        for N in (264, 296, 352, 424, 488):
+            A = synth.matrix(M, K, 8500 + M, 0, "int")
+            B = synth.matrix(K, N, 8500 + N, 1, "int")
+            ref = reference(A, B)
+            a, b = to_dev(A), (to_dev(B) if b_layout == "row" else place(B, "col"))
+            assert g.plan(a, b, variant="main", tile=14)["tile_id"] == 14
+            for kw in (dict(variant="main", tile=14), dict(variant="splitk", tile=14, split_k=2)):
+                check(run(a, b, Out(M, N), **kw), ref, "int", f"edge blocks {M}x{N} {kw}")
+
+
 # ------------------------------------------------------------------ skinny / decode
 
 @pytest.mark.parametrize("M", [1, 7, 16, 33, 64])
