@@ -180,7 +180,9 @@ CONFIGS = [
     ("skinny_m1", 1, 2048, 7168, "row"), ("skinny_m16", 16, 2048, 7168, "row"),
     ("skinny_m64", 64, 2048, 7168, "row"), ("splitk_512x512x65536", 512, 512, 65536, "row"),
     ("moe_131072x2048x7168", 131072, 2048, 7168, "row"),
-    ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col"),
+    ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col", ("main",)),
+    # not a task workload: 17 x 16 tiles, a final wave of 16 tiles on 256 CUs
+    ("tail_4352x4096x8192", 4352, 4096, 8192, "row", ("main",)),
 ]
 
 
@@ -201,49 +203,60 @@ def configs_sweep():
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
 
-    for i, (name, m, n, k, bl) in enumerate(CONFIGS):
-        a0 = to_dev(synth.matrix(m, k, 7000 + i, synth.TENSOR_A))
-        bt = synth.matrix(k, n, 7000 + i, synth.TENSOR_B, order="col" if bl == "col" else "row")
-        b0 = to_dev(bt).t() if bl == "col" else to_dev(bt)
-        byts = 2.0 * (m * k + k * n + m * n)
-        copies = int(min(64, max(1, -(-(1 << 30) // int(byts)))))
-        As = [a0] + [a0.clone() for _ in range(copies - 1)]
-        Bs = [b0] + [(b0.t().clone().t() if bl == "col" else b0.clone()) for _ in range(copies - 1)]
-        c = torch.empty((m, n), dtype=torch.float16, device=dev)
-        p = g.plan(a0, b0, c)
-        ws = (torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
-              if p["workspace_bytes"] else None)
-        cap = torch.cuda.Stream(dev)
-        with torch.cuda.stream(cap):
-            g.gemm(a0, b0, out=c, workspace=ws, stream=cap)
-        torch.cuda.synchronize()
-        reps = copies if byts * copies >= (1 << 28) else max(copies, 64)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            for r in range(reps):
-                g.gemm(As[r % copies], Bs[r % copies], out=c, workspace=ws, stream=cap)
-        times = []
-        for r in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            graph.replay()
-            e1.record()
-            e1.synchronize()
-            if r >= 1:
-                times.append(e0.elapsed_time(e1) / reps)
-        ms = sorted(times)[len(times) // 2]
-        flops = 2.0 * m * n * k
-        ai = flops / byts
-        tf, gbs = flops / (ms * 1e-3) / 1e12, byts / (ms * 1e-3) / 1e9
-        bound = "mfma" if ai >= PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
-        print(json.dumps({"config": name, "M": m, "N": n, "K": k, "b_layout": bl,
-                          "plan": {q: p[q] for q in ("variant", "tile_id", "split_k", "grid")},
-                          "us_per_call": ms * 1e3, "TFLOPS": tf, "GBps": gbs, "AI": ai,
-                          "bound": bound,
-                          "frac": tf / PEAK_F16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS,
-                          "copies": copies}), flush=True)
-        del As, Bs, a0, b0, c, ws, graph
-        torch.cuda.empty_cache()
+    for i, cfg in enumerate(CONFIGS):
+        name, m, n, k, bl = cfg[:5]
+        for variant in ("auto",) + (cfg[5] if len(cfg) > 5 else ()):
+            sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant)
+
+
+def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant):
+    """Time one configuration under one plan (see configs_sweep)."""
+    import torch
+    a0 = to_dev(synth.matrix(m, k, 7000 + i, synth.TENSOR_A))
+    bt = synth.matrix(k, n, 7000 + i, synth.TENSOR_B, order="col" if bl == "col" else "row")
+    b0 = to_dev(bt).t() if bl == "col" else to_dev(bt)
+    byts = 2.0 * (m * k + k * n + m * n)
+    copies = int(min(64, max(1, -(-(1 << 30) // int(byts)))))
+    As = [a0] + [a0.clone() for _ in range(copies - 1)]
+    Bs = [b0] + [(b0.t().clone().t() if bl == "col" else b0.clone()) for _ in range(copies - 1)]
+    c = torch.empty((m, n), dtype=torch.float16, device=dev)
+    p = g.plan(a0, b0, c, variant=variant)
+    ws = (torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+          if p["workspace_bytes"] else None)
+    cap = torch.cuda.Stream(dev)
+    with torch.cuda.stream(cap):
+        g.gemm(a0, b0, out=c, workspace=ws, stream=cap, variant=variant)
+    torch.cuda.synchronize()
+    reps = copies if byts * copies >= (1 << 28) else max(copies, 64)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for r in range(reps):
+            g.gemm(As[r % copies], Bs[r % copies], out=c, workspace=ws, stream=cap,
+                   variant=variant)
+    times = []
+    for r in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        e1.synchronize()
+        if r >= 1:
+            times.append(e0.elapsed_time(e1) / reps)
+    ms = sorted(times)[len(times) // 2]
+    flops = 2.0 * m * n * k
+    ai = flops / byts
+    tf, gbs = flops / (ms * 1e-3) / 1e12, byts / (ms * 1e-3) / 1e9
+    bound = "mfma" if ai >= PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    print(json.dumps({"config": name, "M": m, "N": n, "K": k, "b_layout": bl,
+                      "forced": variant,
+                      "plan": {q: p[q] for q in ("variant", "tile_id", "split_k", "grid",
+                                                 "sk_tiles")},
+                      "us_per_call": ms * 1e3, "TFLOPS": tf, "GBps": gbs, "AI": ai,
+                      "bound": bound,
+                      "frac": tf / PEAK_F16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS,
+                      "copies": copies}), flush=True)
+    del As, Bs, a0, b0, c, ws, graph
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -255,8 +268,8 @@ def main():
         configs_sweep()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this GEMM build "
-              "has no multi-GPU path; see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
+              "no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -14,8 +14,9 @@ GEMM_OK = 0
 STATUS = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_SHAPE", -3: "GEMM_ERR_STRIDE",
           -4: "GEMM_ERR_LDC", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_WORKSPACE",
           -7: "GEMM_ERR_OPTS", -8: "GEMM_ERR_HIP"}
-VARIANT_AUTO, VARIANT_MAIN, VARIANT_SKINNY, VARIANT_SPLITK, VARIANT_TILE64X32 = 0, 1, 2, 3, 4
-VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4}
+VARIANT_AUTO, VARIANT_MAIN, VARIANT_SKINNY, VARIANT_SPLITK, VARIANT_TILE64X32, VARIANT_STREAMK = \
+    0, 1, 2, 3, 4, 5
+VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4, "streamk": 5}
 PATHS = {0: "gather", 1: "kvec", 2: "rvec"}
 
 EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes",
@@ -32,7 +33,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", i32), ("tile_m", i32), ("tile_n", i32), ("tile_k", i32),
                 ("split_k", i32), ("panel", i32), ("a_path", i32), ("b_path", i32),
                 ("tile_id", i32), ("grid", i64), ("grid2", i64),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("sk_tiles", i64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -183,8 +183,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   int64_t w = blockIdx.x;
   int64_t split = 0;
   if constexpr (PARTIAL) {
-    split = w / T;
-    w -= split * T;
+    if (a.sk_tiles > 0) {            // stream-K tail: see KArgs
+      split = w / a.sk_tiles;
+      w = a.sk_first + (w - split * a.sk_tiles);
+    } else {
+      split = w / T;
+      w -= split * T;
+    }
   }
   int64_t pm, pn;
   if constexpr (GROUPED) {
@@ -336,9 +341,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
         const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
         const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
         const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if constexpr (PARTIAL)
-          store4_f32(a, split, m, n, v0, v1, v2, v3);
-        else
+        if constexpr (PARTIAL) {
+          if (a.sk_tiles > 0)
+            store4_tile<CF::BM, CF::BN>(a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN), m - m0, n - n0,
+                                        v0, v1, v2, v3);
+          else
+            store4_f32(a, split, m, n, v0, v1, v2, v3);
+        } else
           store4_out<DT>(a, m, n, v0, v1, v2, v3);
       }
     }

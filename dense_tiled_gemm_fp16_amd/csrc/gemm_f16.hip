@@ -97,6 +97,7 @@ struct Plan {
   int gemv_mt;  // > 0: the decode-shaped VALU kernel with this many A rows
   int red_lanes;  // lanes per output quad in the split reduction
   int64_t GM, GN, grid, grid2, k_split;
+  int64_t sk_tiles;  // STREAMK: tiles split over K after the whole waves
   size_t ws;
 };
 
@@ -130,7 +131,7 @@ int spans(Call& c) {
 
 int check_opts(const gemm_f16_opts* o) {
   if (!o) return GEMM_OK;
-  if (o->variant < GEMM_VARIANT_AUTO || o->variant > GEMM_VARIANT_TILE64X32) return GEMM_ERR_OPTS;
+  if (o->variant < GEMM_VARIANT_AUTO || o->variant > GEMM_VARIANT_STREAMK) return GEMM_ERR_OPTS;
   if (o->split_k < 0 || o->split_k > 256) return GEMM_ERR_OPTS;
   if (!(o->panel == -1 || (o->panel >= 0 && o->panel <= 4096))) return GEMM_ERR_OPTS;
   if (o->tile < 0 || o->tile > TILE_MAX) return GEMM_ERR_OPTS;
@@ -187,6 +188,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     return device_cus(&cus);
   };
 
+  p.sk_tiles = 0;
   p.variant = variant;
   if (p.variant == GEMM_VARIANT_AUTO) {
     if ((rc = need_cus())) return rc;
@@ -227,6 +229,10 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
       // The 256x256 full-line-A tile once the output holds a whole one (it
       // falls back to 128x128 for layouts it does not take).
       p.tile_id = want_tile ? want_tile : ((c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128);
+      break;
+    case GEMM_VARIANT_STREAMK:
+      if (want_tile && want_tile != TILE_DMA256A128) return GEMM_ERR_OPTS;
+      p.tile_id = TILE_DMA256A128;
       break;
     case GEMM_VARIANT_TILE64X32:
       if (want_tile && want_tile != TILE_T64X32) return GEMM_ERR_OPTS;
@@ -280,6 +286,41 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   p.GM = cdiv(c.M, ti.bm);
   p.GN = cdiv(c.N, ti.bn);
   const int64_t T = p.GM * p.GN;
+  if (p.variant == GEMM_VARIANT_STREAMK && p.tile_id != TILE_DMA256A128) return GEMM_ERR_OPTS;
+  if (variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN && !want_tile &&
+      p.tile_id == TILE_DMA256A128 && c.K >= 2048) {
+    // A final wave at most half full goes to the stream-K tail (one 256x256
+    // workgroup fits a compute unit, so a wave is `cus` tiles).
+    if ((rc = need_cus())) return rc;
+    const int64_t tail = T % cus;
+    if (T >= cus && tail > 0 && 2 * tail <= cus) p.variant = GEMM_VARIANT_STREAMK;
+  }
+  if (p.variant == GEMM_VARIANT_STREAMK) {
+    if ((rc = need_cus())) return rc;
+    // Tail tiles: the partial last wave; when the tiles fill whole waves (a
+    // forced plan), the last whole wave, or every tile if there is less.
+    int64_t L = T % cus;
+    if (L == 0) L = T < cus ? T : cus;
+    int64_t s = want_split;
+    if (s == 0) {
+      s = cus / L;                                  // fill the idle compute units
+      if (s > cdiv(c.K, 512)) s = cdiv(c.K, 512);   // at least 512 k per range
+      if (s > 64) s = 64;
+      if (s < 1) s = 1;
+    }
+    set_split(p, c.K, 64, s);   // whole 64-k super-steps per range
+    p.sk_tiles = L;
+    p.grid = T - L;
+    p.grid2 = L * (ti.bm * ti.bn / 1024);
+    p.panel = want_panel != 0 ? want_panel : 4;
+    p.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
+    p.red_lanes = 1;
+    int64_t bytes;
+    if (__builtin_mul_overflow(L * p.split, (int64_t)ti.bm * ti.bn * 4, &bytes) || bytes > INT64_MAX - 256)
+      return GEMM_ERR_SHAPE;
+    p.ws = (size_t)((bytes + 255) / 256 * 256);
+    return GEMM_OK;
+  }
 
   // K split.
   if (p.variant == GEMM_VARIANT_SPLITK || p.variant == GEMM_VARIANT_SKINNY) {
@@ -334,6 +375,7 @@ void fill_info(const Plan& p, gemm_f16_plan_info* info) {
   info->grid = p.grid;
   info->grid2 = p.grid2;
   info->workspace_bytes = p.ws;
+  info->sk_tiles = p.sk_tiles;
 }
 
 // Second launch of a split plan: sum the partials in ws into C.
@@ -379,6 +421,35 @@ int launch_gemv(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   return launch_reduce(c, p, ws, stream);
 }
 
+// Stream-K plan: whole waves of tiles (raster ids 0 .. grid-1) with the
+// final kernel, the tail tiles' K ranges with the partial kernel into the
+// workspace, then the fixed-order fix-up into C.
+int launch_streamk(const Call& c, const Plan& p, KArgs a, kfn_t final_fn, kfn_t partial_fn, void* ws,
+                   hipStream_t stream) {
+  const TileInfo& ti = tile_info(p.tile_id);
+  void* args[] = {&a};
+  a.k_split = c.K;   // whole waves: every tile over all of K
+  if (p.grid > 0 &&
+      hipLaunchKernel((const void*)final_fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  a.k_split = p.k_split;
+  a.W = (float*)ws;
+  a.sk_first = p.grid;
+  a.sk_tiles = p.sk_tiles;
+  if (hipLaunchKernel((const void*)partial_fn, dim3((unsigned)(p.sk_tiles * p.split)), dim3(ti.nt), args, 0,
+                      stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  const float* W = (const float*)ws;
+  int S = p.split, panel = p.panel, bm = ti.bm, bn = ti.bn, cv = p.c_vec;
+  int64_t L = p.sk_tiles, first = p.grid, GM = p.GM, GN = p.GN, M = c.M, N = c.N, ldc = c.ldc;
+  uint16_t* C = (uint16_t*)c.C;
+  void* fargs[] = {&W, &S, &L, &first, &GM, &GN, &panel, &bm, &bn, &M, &N, &C, &ldc, &cv};
+  const void* fix = c.dt == DT_F16 ? (const void*)sk_fixup<DT_F16> : (const void*)sk_fixup<DT_BF16>;
+  if (hipLaunchKernel(fix, dim3((unsigned)p.grid2), dim3(256), fargs, 0, stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
 int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   if (p.gemv_mt) return launch_gemv(c, p, ws, stream);
   const TileInfo& ti = tile_info(p.tile_id);
@@ -404,7 +475,11 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   a.g_tiles = nullptr;
   a.ldb_g = 0;
   a.G = 0;
+  a.sk_first = 0;
+  a.sk_tiles = 0;
   const int sel = p.a_path * 3 + p.b_path;
+  if (p.variant == GEMM_VARIANT_STREAMK) return launch_streamk(c, p, a, ti.final_fn[c.dt][sel],
+                                                               ti.partial_fn[c.dt][sel], ws, stream);
   kfn_t fn = (p.split > 1) ? ti.partial_fn[c.dt][sel] : ti.final_fn[c.dt][sel];
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
@@ -560,6 +635,8 @@ int launch_grouped(const GroupCall& c, int tile_id, kfn_t fn, int64_t grid, void
   a.g_tiles = tiles;
   a.ldb_g = c.ldb_g;
   a.G = c.G;
+  a.sk_first = 0;
+  a.sk_tiles = 0;
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(ti.nt), args, 0, s) != hipSuccess)
     return GEMM_ERR_HIP;

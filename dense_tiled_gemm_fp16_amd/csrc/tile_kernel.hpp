@@ -66,6 +66,12 @@ struct KArgs {
   const int64_t* g_tiles;
   int64_t ldb_g;
   int32_t G;
+  // Stream-K tail launches only (sk_tiles > 0, PARTIAL kernels of the
+  // full-line-A tile): workgroup w takes K range w / sk_tiles of the tile
+  // that raster id sk_first + w % sk_tiles maps to, and writes its partial
+  // tile densely to W at slot w (BM x BN floats, row-major).
+  int64_t sk_first;
+  int64_t sk_tiles;
 };
 
 // Grouped product (TileLang tutorial ch. 14, section 4.3: one launch over
@@ -151,6 +157,14 @@ __device__ __forceinline__ void store4_f32(const KArgs& a, int64_t split, int64_
     for (int e = 0; e < 4; ++e)
       if (n + e < a.N) p[e] = v[e];
   }
+}
+
+// Four consecutive fp32 partials of a dense BM x BN tile slot (row r,
+// columns c .. c+3 of the tile; whole tile written, edges included).
+template <int BM, int BN>
+__device__ __forceinline__ void store4_tile(float* slot, int64_t r, int64_t c, float v0, float v1,
+                                            float v2, float v3) {
+  *reinterpret_cast<f32x4*>(slot + r * BN + c) = f32x4{v0, v1, v2, v3};
 }
 
 // MFMAs of one BK step from one LDS stage.  Operand fragments are double

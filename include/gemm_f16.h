@@ -62,19 +62,34 @@ enum gemm_status {
   GEMM_ERR_HIP = -8        /* a HIP runtime call failed (no device, launch, ...) */
 };
 
-/* Kernel families (gemm_f16_opts.variant / gemm_f16_plan_info.variant). */
+/* Kernel families (gemm_f16_opts.variant / gemm_f16_plan_info.variant).
+ *
+ * STREAMK is the tail-wave scheduling of the TileLang tutorial, ch. 14,
+ * section 4.2 (stream-K: spread the K iterations evenly over the compute
+ * units instead of whole tiles), in a deterministic form: the tiles that
+ * fill whole waves of the 256x256 tile run as in MAIN; the last sk_tiles
+ * tiles, which would leave most compute units idle in a final partial wave,
+ * are split into split_k K ranges each, written as fp32 partials to the
+ * workspace, and a fix-up launch sums each output's ranges in ascending
+ * order (no atomics, bit-reproducible for a given plan).  It needs the
+ * 256x256 LDS-DMA tile (K-contiguous A; N-contiguous B with N % 8 == 0, or
+ * K-contiguous B); forcing it for other layouts returns GEMM_ERR_OPTS.
+ * AUTO picks it when the partial wave is at most half full and K >= 2048. */
 enum gemm_variant {
   GEMM_VARIANT_AUTO = 0,    /* choose from the shape (the default)                */
   GEMM_VARIANT_MAIN = 1,    /* one workgroup per output tile, whole K            */
   GEMM_VARIANT_SKINNY = 2,  /* M <= 64: B streamed once, K split, fixed-order sum */
   GEMM_VARIANT_SPLITK = 3,  /* tiles x K ranges into fp32 partials, then a       */
                             /* second pass sums the ranges in fixed order        */
-  GEMM_VARIANT_TILE64X32 = 4 /* main structure with the pages' 64x32x32 tile    */
+  GEMM_VARIANT_TILE64X32 = 4, /* main structure with the pages' 64x32x32 tile   */
+  GEMM_VARIANT_STREAMK = 5   /* main tiles in whole waves, then the last        */
+                             /* sk_tiles tiles split over K across the idle     */
+                             /* compute units, summed by a fixed-order fix-up   */
 };
 
 typedef struct gemm_f16_opts {
   int32_t variant; /* enum gemm_variant                                          */
-  int32_t split_k; /* K ranges for SPLITK/SKINNY; 0 = choose; 1..256              */
+  int32_t split_k; /* K ranges for SPLITK/SKINNY/STREAMK; 0 = choose; 1..256      */
   int32_t panel;   /* raster group height in tiles; 0 = choose; -1 = plain       */
                    /* row-major tile order without XCD remapping; 1..4096        */
   int32_t tile;    /* main-kernel tile id (0 = choose; see gemm_f16_plan_info)   */
@@ -91,6 +106,7 @@ typedef struct gemm_f16_plan_info {
   int64_t grid;             /* workgroups in the first launch                    */
   int64_t grid2;            /* workgroups in the reduction launch (0 = none)     */
   uint64_t workspace_bytes; /* device workspace the call needs (0 = none)        */
+  int64_t sk_tiles;         /* STREAMK: tiles split over K (0 otherwise)         */
 } gemm_f16_plan_info;
 
 /*

@@ -74,6 +74,10 @@ def test_option_errors():
     # skinny is only for M <= 64; main takes no K split
     assert call(M=65, opts=_lib.Opts(2, 4, -1, 0)) == -7
     assert call(opts=_lib.Opts(1, 4, 8, 0)) == -7
+    # stream-K runs on the 256x256 LDS-DMA tile only, and variants end at 5
+    assert call(opts=_lib.Opts(6, 0, 0, 0)) == -7
+    assert call(opts=_lib.Opts(5, 0, 0, 1)) == -7
+    assert call(lda_m=1, lda_k=64, opts=_lib.Opts(5, 0, 0, 0)) == -7   # A not K-contiguous
 
 
 def test_workspace_errors():

@@ -295,7 +295,8 @@ def test_int64_stride_integer_slice_exact():
     assert a.stride() == (Kfull, 1) and b.stride() == (1, Kfull)
     rows = np.array([0, 1, 131071, 131072, 262143, 262144, 262145, M - 1])
     ref = reference(A, np.ascontiguousarray(Bt.T), rows)
-    for kw in (dict(variant="auto"), dict(variant="splitk", split_k=2)):
+    for kw in (dict(variant="auto"), dict(variant="splitk", split_k=2),
+               dict(variant="streamk", split_k=2)):
         gpu = run(a, b, **kw)
         check(gpu[rows], ref, "int", f"int64 slice {kw}")
 
