@@ -1,4 +1,5 @@
-"""CPU oracle for C = A.B with fp16 (or bfloat16) inputs and output.
+"""CPU oracle for C = A.B with fp16 (or bfloat16) inputs and output, and
+with FP8 (E4M3 / E5M2) inputs and fp16 output.
 
 TEST INFRASTRUCTURE ONLY.  Only `tests/`, the smoke check in
 `__graft_entry__.py` and the CPU-baseline leg of `bench.py` may import this
@@ -68,6 +69,13 @@ def _load():
         lib.orc_bf16_to_f64_array.argtypes = [vp, vp, i64]
         lib.orc_f64_to_bf16_array.restype = None
         lib.orc_f64_to_bf16_array.argtypes = [vp, vp, i64]
+        lib.orc_gemm_f8.restype = ctypes.c_int
+        lib.orc_gemm_f8.argtypes = lib.orc_gemm_f16.argtypes[:-1] + [ctypes.c_int] * 3
+        lib.orc_gemm_f8_points.restype = ctypes.c_int
+        lib.orc_gemm_f8_points.argtypes = lib.orc_gemm_f16_points.argtypes[:-1] + [ctypes.c_int] * 3
+        for name in ("orc_e4m3_to_f64_array", "orc_e5m2_to_f64_array"):
+            getattr(lib, name).restype = None
+            getattr(lib, name).argtypes = [vp, vp, i64]
         _lib = lib
     return _lib
 
@@ -105,6 +113,24 @@ def f64_to_bf16(x):
     return out
 
 
+F8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def f8_to_f64(bits, fmt):
+    """Decode FP8 bytes (uint8 array) of format "e4m3" (OCP E4M3FN) or "e5m2"."""
+    wide = np.ascontiguousarray(bits, dtype=np.uint8).astype(np.uint16)
+    out = np.empty(wide.shape, dtype=np.float64)
+    fn = {"e4m3": _load().orc_e4m3_to_f64_array, "e5m2": _load().orc_e5m2_to_f64_array}[fmt]
+    fn(wide.ctypes.data, out.ctypes.data, wide.size)
+    return out
+
+
+def _widen_f8(buf, name):
+    if not (isinstance(buf, np.ndarray) and buf.dtype == np.uint8 and buf.flags["C_CONTIGUOUS"]):
+        raise TypeError(f"{name} must be a C-contiguous uint8 numpy array of FP8 bytes")
+    return buf.astype(np.uint16)
+
+
 def _span(off, rows, cols, rs, cs):
     """Largest element offset touched by a rows x cols view (strides >= 0)."""
     return off + (rows - 1) * rs + (cols - 1) * cs
@@ -116,13 +142,17 @@ def _check_buf(buf, name):
 
 
 def gemm(A, lda, B, ldb, M, N, K, a_off=0, b_off=0, C=None, ldc=None, c_off=0,
-         exact=False, nthreads=None, dtype="f16"):
+         exact=False, nthreads=None, dtype="f16", fmt_a="e4m3", fmt_b="e4m3"):
     """C[i,j] = rne(sum_k A[i,k] B[k,j]) for the strided views
         A[i,k] = A.flat[a_off + i*lda[0] + k*lda[1]]
         B[k,j] = B.flat[b_off + k*ldb[0] + j*ldb[1]]
     written to C.flat[c_off + i*ldc + j] (a fresh (M, N) array when C is None).
-    dtype "f16" (binary16) or "bf16" (bfloat16) for inputs and output.
+    dtype "f16" (binary16) or "bf16" (bfloat16) for inputs and output, or
+    "f8": A and B are uint8 FP8 bytes of formats fmt_a / fmt_b ("e4m3" or
+    "e5m2") and C is binary16.
     Returns C, or (C, S) with S the unrounded binary64 sums when exact=True."""
+    if dtype == "f8":
+        A, B = _widen_f8(A, "A"), _widen_f8(B, "B")
     _check_buf(A, "A")
     _check_buf(B, "B")
     if min(M, N, K) <= 0:
@@ -140,11 +170,13 @@ def gemm(A, lda, B, ldb, M, N, K, a_off=0, b_off=0, C=None, ldc=None, c_off=0,
     if _span(c_off, M, N, ldc, 1) >= C.size:
         raise ValueError("output view reaches past its buffer")
     S = np.empty((M, N), dtype=np.float64) if exact else None
-    fn = {"f16": _load().orc_gemm_f16, "bf16": _load().orc_gemm_bf16}[dtype]
-    rc = fn(
-        A.ctypes.data + 2 * a_off, lda[0], lda[1], B.ctypes.data + 2 * b_off, ldb[0], ldb[1],
-        C.ctypes.data + 2 * c_off, ldc, None if S is None else S.ctypes.data, M, N, K,
-        nthreads or threads())
+    args = (A.ctypes.data + 2 * a_off, lda[0], lda[1], B.ctypes.data + 2 * b_off, ldb[0], ldb[1],
+            C.ctypes.data + 2 * c_off, ldc, None if S is None else S.ctypes.data, M, N, K)
+    if dtype == "f8":
+        rc = _load().orc_gemm_f8(*args, F8_FORMATS[fmt_a], F8_FORMATS[fmt_b], nthreads or threads())
+    else:
+        fn = {"f16": _load().orc_gemm_f16, "bf16": _load().orc_gemm_bf16}[dtype]
+        rc = fn(*args, nthreads or threads())
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return (C, S) if exact else C
@@ -173,9 +205,11 @@ def gemm_grouped(A, Bs, offsets, N, K, C=None, nthreads=None, dtype="f16"):
 
 
 def gemm_points(A, lda, B, ldb, K, rows, cols, a_off=0, b_off=0, exact=False, nthreads=None,
-                dtype="f16"):
+                dtype="f16", fmt_a="e4m3", fmt_b="e4m3"):
     """Selected outputs C[rows[t], cols[t]] of the same product, each computed
     on its own.  Returns output bits (and the unrounded sums when exact=True)."""
+    if dtype == "f8":
+        A, B = _widen_f8(A, "A"), _widen_f8(B, "B")
     _check_buf(A, "A")
     _check_buf(B, "B")
     rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -192,11 +226,15 @@ def gemm_points(A, lda, B, ldb, K, rows, cols, a_off=0, b_off=0, exact=False, nt
             raise ValueError("point reaches past its buffer")
     out = np.empty(rows.size, dtype=np.uint16)
     S = np.empty(rows.size, dtype=np.float64) if exact else None
-    fn = {"f16": _load().orc_gemm_f16_points, "bf16": _load().orc_gemm_bf16_points}[dtype]
-    rc = fn(
-        A.ctypes.data + 2 * a_off, lda[0], lda[1], B.ctypes.data + 2 * b_off, ldb[0], ldb[1], K,
-        rows.ctypes.data, cols.ctypes.data, rows.size, out.ctypes.data,
-        None if S is None else S.ctypes.data, nthreads or threads())
+    args = (A.ctypes.data + 2 * a_off, lda[0], lda[1], B.ctypes.data + 2 * b_off, ldb[0], ldb[1], K,
+            rows.ctypes.data, cols.ctypes.data, rows.size, out.ctypes.data,
+            None if S is None else S.ctypes.data)
+    if dtype == "f8":
+        rc = _load().orc_gemm_f8_points(*args, F8_FORMATS[fmt_a], F8_FORMATS[fmt_b],
+                                        nthreads or threads())
+    else:
+        fn = {"f16": _load().orc_gemm_f16_points, "bf16": _load().orc_gemm_bf16_points}[dtype]
+        rc = fn(*args, nthreads or threads())
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return (out, S) if exact else out

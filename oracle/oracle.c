@@ -145,16 +145,59 @@ uint16_t orc_f64_to_bf16(double x) {
   return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)(q - 128));
 }
 
+/* ---- 8-bit floating-point formats (OCP FP8), decode only ----------------
+ * Inputs arrive one byte per uint16_t element (the upper byte zero).
+ * E4M3 ("FN" variant): 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-9
+ *   exponent 1..15  : normal,    value = (8 + fraction) * 2^(exponent-10)
+ *   exponent 15 with fraction 7 is NaN; there are no infinities (max 448).
+ * E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-16
+ *   exponent 1..30  : normal,    value = (4 + fraction) * 2^(exponent-17)
+ *   exponent 31     : fraction 0 -> infinity, otherwise NaN (max 57344). */
+
+static double orc_nan(void) {
+  uint64_t bits = 0x7FF8000000000000ull;
+  double d;
+  memcpy(&d, &bits, sizeof d);
+  return d;
+}
+
+double orc_e4m3_to_f64(uint16_t v) {
+  const int s = (v >> 7) & 1, e = (v >> 3) & 0xF, f = v & 7;
+  double out;
+  if (e == 15 && f == 7) return orc_nan();
+  if (e == 0)
+    out = (double)f * 0x1p-9;
+  else
+    out = (double)(8 + f) * (double)(1u << e) * 0x1p-10;   /* exact */
+  return s ? -out : out;
+}
+
+double orc_e5m2_to_f64(uint16_t v) {
+  const int s = (v >> 7) & 1, e = (v >> 2) & 0x1F, f = v & 3;
+  double out;
+  if (e == 31) {
+    if (f) return orc_nan();
+    out = 1.0 / 0.0;
+  } else if (e == 0) {
+    out = (double)f * 0x1p-16;
+  } else {
+    out = (double)(4 + f) * (double)(1u << e) * 0x1p-17;   /* exact */
+  }
+  return s ? -out : out;
+}
+
 typedef double (*orc_dec_fn)(uint16_t);
 typedef uint16_t (*orc_enc_fn)(double);
 
 /* One output element: the defining sum, ascending k, binary64. */
 static double orc_dot(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
                       int64_t ldb_k, int64_t ldb_n, int64_t i, int64_t j, int64_t K,
-                      orc_dec_fn dec) {
+                      orc_dec_fn dec_a, orc_dec_fn dec_b) {
   double s = 0.0;
   for (int64_t k = 0; k < K; ++k)
-    s += dec(A[i * lda_m + k * lda_k]) * dec(B[k * ldb_k + j * ldb_n]);
+    s += dec_a(A[i * lda_m + k * lda_k]) * dec_b(B[k * ldb_k + j * ldb_n]);
   return s;
 }
 
@@ -167,16 +210,18 @@ typedef struct {
   const int64_t* pi;         /* point mode: output coordinates */
   const int64_t* pj;
   int64_t npts;
-  orc_dec_fn dec;            /* element format: binary16 or bfloat16 */
-  orc_enc_fn enc;
+  orc_dec_fn dec;            /* element format of A: binary16, bfloat16, E4M3, E5M2 */
+  orc_enc_fn enc;            /* output format: binary16 or bfloat16 */
   int nthreads, tid;
+  orc_dec_fn dec_b;          /* element format of B (NULL: the same as A) */
 } orc_job;
 
 static void* orc_rows(void* p) {
   orc_job* j = (orc_job*)p;
   for (int64_t i = j->tid; i < j->M; i += j->nthreads)
     for (int64_t c = 0; c < j->N; ++c) {
-      double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, i, c, j->K, j->dec);
+      double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, i, c, j->K, j->dec,
+                         j->dec_b ? j->dec_b : j->dec);
       j->C[i * j->ldc + c] = j->enc(s);
       if (j->S) j->S[i * j->N + c] = s;
     }
@@ -187,7 +232,7 @@ static void* orc_points(void* p) {
   orc_job* j = (orc_job*)p;
   for (int64_t t = j->tid; t < j->npts; t += j->nthreads) {
     double s = orc_dot(j->A, j->lda_m, j->lda_k, j->B, j->ldb_k, j->ldb_n, j->pi[t], j->pj[t], j->K,
-                       j->dec);
+                       j->dec, j->dec_b ? j->dec_b : j->dec);
     j->C[t] = j->enc(s);
     if (j->S) j->S[t] = s;
   }
@@ -255,6 +300,43 @@ int orc_gemm_bf16_points(const uint16_t* A, int64_t lda_m, int64_t lda_k, const 
                orc_bf16_to_f64, orc_f64_to_bf16, nthreads, 0};
   orc_run(&j, orc_points);
   return 0;
+}
+
+/* FP8 inputs (fmt 0 = E4M3, 1 = E5M2, per operand; one byte per uint16_t
+ * element), binary64 sum, one rounding to binary16. */
+static orc_dec_fn orc_f8_dec(int fmt) {
+  return fmt == 0 ? orc_e4m3_to_f64 : (fmt == 1 ? orc_e5m2_to_f64 : NULL);
+}
+
+int orc_gemm_f8(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                int64_t ldb_k, int64_t ldb_n, uint16_t* C, int64_t ldc, double* S,
+                int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, int nthreads) {
+  if (!A || !B || !C || M <= 0 || N <= 0 || K <= 0) return -1;
+  if (!orc_f8_dec(fmt_a) || !orc_f8_dec(fmt_b)) return -1;
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, S, M, N, K, NULL, NULL, 0,
+               orc_f8_dec(fmt_a), orc_f64_to_f16, nthreads, 0, orc_f8_dec(fmt_b)};
+  orc_run(&j, orc_rows);
+  return 0;
+}
+
+int orc_gemm_f8_points(const uint16_t* A, int64_t lda_m, int64_t lda_k, const uint16_t* B,
+                       int64_t ldb_k, int64_t ldb_n, int64_t K, const int64_t* pi,
+                       const int64_t* pj, int64_t npts, uint16_t* out, double* S, int fmt_a,
+                       int fmt_b, int nthreads) {
+  if (!A || !B || !out || !pi || !pj || K <= 0 || npts < 0) return -1;
+  if (!orc_f8_dec(fmt_a) || !orc_f8_dec(fmt_b)) return -1;
+  orc_job j = {A, lda_m, lda_k, B, ldb_k, ldb_n, out, 0, S, 0, 0, K, pi, pj, npts,
+               orc_f8_dec(fmt_a), orc_f64_to_f16, nthreads, 0, orc_f8_dec(fmt_b)};
+  orc_run(&j, orc_points);
+  return 0;
+}
+
+void orc_e4m3_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t t = 0; t < n; ++t) out[t] = orc_e4m3_to_f64(in[t]);
+}
+
+void orc_e5m2_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t t = 0; t < n; ++t) out[t] = orc_e5m2_to_f64(in[t]);
 }
 
 /* Array forms of the codec, for the tests that sweep all 65536 patterns. */

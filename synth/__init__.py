@@ -27,7 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gen.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 MODES = {"uniform": 0, "int": 1}
-FORMATS = {"f16": 0, "bf16": 2}
+FORMATS = {"f16": 0, "bf16": 2, "e4m3": 4, "e5m2": 8}
+F8 = ("e4m3", "e5m2")
 TENSOR_A, TENSOR_B = 0, 1
 
 _lib = None
@@ -66,8 +67,9 @@ def fill(dst, rows, cols, rs, cs, seed, tensor, mode="uniform", row0=0, row_inde
     dst.flat[r*rs + c*cs] for r in [0, rows).  The logical row is
     row_index[r] when row_index is given, else row0 + r.  `dst` is a
     uint16 numpy array (any shape, C-contiguous storage is addressed flat).
-    fmt "f16" writes binary16 bits, "bf16" bfloat16 bits of the same value."""
-    assert dst.dtype == np.uint16 and dst.flags["C_CONTIGUOUS"]
+    fmt "f16" writes binary16 bits, "bf16" bfloat16 bits of the same value;
+    "e4m3" / "e5m2" write OCP FP8 bytes into a uint8 array."""
+    assert dst.dtype == (np.uint8 if fmt in F8 else np.uint16) and dst.flags["C_CONTIGUOUS"]
     if rows > 0 and cols > 0:
         last = (rows - 1) * rs + (cols - 1) * cs
         assert 0 <= last < dst.size, "fill would write outside dst"
@@ -90,11 +92,12 @@ def matrix(rows, cols, seed, tensor, mode="uniform", order="row", nthreads=None,
     order="row": returned array has shape (rows, cols) (row-major storage).
     order="col": returned array has shape (cols, rows) and holds the
     transpose, i.e. the storage of a transposed view with strides (1, rows)."""
+    dt = np.uint8 if fmt in F8 else np.uint16
     if order == "row":
-        out = np.empty((rows, cols), dtype=np.uint16)
+        out = np.empty((rows, cols), dtype=dt)
         return fill(out, rows, cols, cols, 1, seed, tensor, mode, nthreads=nthreads, fmt=fmt)
     if order == "col":
-        out = np.empty((cols, rows), dtype=np.uint16)
+        out = np.empty((cols, rows), dtype=dt)
         return fill(out, rows, cols, 1, rows, seed, tensor, mode, nthreads=nthreads, fmt=fmt)
     raise ValueError(order)
 
@@ -102,7 +105,7 @@ def matrix(rows, cols, seed, tensor, mode="uniform", order="row", nthreads=None,
 def rows_of(row_index, cols, seed, tensor, mode="uniform", nthreads=None, fmt="f16"):
     """Selected logical rows (len(row_index), cols) of the (seed, tensor) matrix."""
     idx = np.ascontiguousarray(row_index, dtype=np.int64)
-    out = np.empty((idx.size, cols), dtype=np.uint16)
+    out = np.empty((idx.size, cols), dtype=np.uint8 if fmt in F8 else np.uint16)
     return fill(out, idx.size, cols, cols, 1, seed, tensor, mode, row_index=idx,
                 nthreads=nthreads, fmt=fmt)
 
@@ -148,4 +151,8 @@ def reference_rows(row_index, cols, seed, tensor, mode="uniform", fmt="f16"):
     if fmt == "bf16":   # float32 -> bfloat16, ties to even, by torch (values exact in float32)
         import torch
         return torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if fmt in F8:       # float32 -> OCP FP8, ties to even, by torch
+        import torch
+        dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+        return torch.from_numpy(vals).to(dt).view(torch.uint8).numpy()
     return vals.astype(np.float16).view(np.uint16)

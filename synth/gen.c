@@ -18,7 +18,9 @@
  *                  element is x rounded to binary16 (ties to even).
  *   SYNTH_INT:     (h >> 40) % 9 - 4, an integer in [-4, 4] (exact in fp16).
  * With SYNTH_BF16 added to the mode the same value is rounded to bfloat16
- * (ties to even) instead of binary16.
+ * (ties to even) instead of binary16.  With SYNTH_E4M3 or SYNTH_E5M2 it is
+ * rounded (ties to even) to that OCP FP8 format and the destination holds
+ * one byte per element.
  */
 #include <math.h>
 #include <pthread.h>
@@ -28,6 +30,8 @@
 #define SYNTH_UNIFORM 0
 #define SYNTH_INT 1
 #define SYNTH_BF16 2
+#define SYNTH_E4M3 4
+#define SYNTH_E5M2 8
 
 static inline uint64_t sm_step(uint64_t x) {
   uint64_t z = x + 0x9E3779B97F4A7C15ull;
@@ -82,16 +86,43 @@ static uint16_t synth_to_bf16(double x) {
   return (uint16_t)(sign | (uint16_t)((ev + 127) << 7) | mant);
 }
 
+/* Round a finite double to an OCP FP8 format with `mbits` fraction bits,
+ * exponent bias `bias`, ties to even: scale to the quantum, nearbyint,
+ * re-encode.  E4M3 (mbits 3, bias 7) has no infinity and its largest finite
+ * value is 448; a larger rounded magnitude gives its NaN (0x7F).  E5M2
+ * (mbits 2, bias 15) overflows past 57344 to infinity (0x7C). */
+static uint8_t synth_to_f8(double x, int mbits, int bias) {
+  const int e4m3 = mbits == 3;
+  uint8_t sign = signbit(x) ? 0x80u : 0u;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  const double maxv = e4m3 ? 448.0 : 57344.0;
+  const int emin = 1 - bias;                 /* exponent of the smallest normal */
+  int e2;
+  frexp(a, &e2);
+  int ex = e2 - 1;
+  if (ex < emin) ex = emin;                  /* subnormals share the quantum */
+  double q = ldexp(1.0, ex - mbits);
+  if (ex > 20) return (uint8_t)(sign | (e4m3 ? 0x7Fu : 0x7Cu));
+  double m = nearbyint(a / q);
+  double v = m * q;
+  if (v > maxv) return (uint8_t)(sign | (e4m3 ? 0x7Fu : 0x7Cu));
+  if (v < ldexp(1.0, emin)) return (uint8_t)(sign | (uint8_t)(v / ldexp(1.0, emin - mbits)));
+  frexp(v, &e2);
+  int ev = e2 - 1;
+  uint8_t mant = (uint8_t)(v / ldexp(1.0, ev - mbits) - (double)(1 << mbits));
+  return (uint8_t)(sign | (uint8_t)((ev + bias) << mbits) | mant);
+}
+
+static inline double synth_draw(uint64_t h, int mode) {
+  if ((mode & 1) == SYNTH_INT) return (double)((int)((h >> 40) % 9u) - 4);
+  int64_t u = (int64_t)(h >> 40);
+  return (double)(2 * u + 1 - (1ll << 24)) * 0x1p-24;
+}
+
 static inline uint16_t synth_value(uint64_t h, int mode) {
-  const int bf = mode & SYNTH_BF16;
-  double x;
-  if ((mode & 1) == SYNTH_INT) {
-    x = (double)((int)((h >> 40) % 9u) - 4);
-  } else {
-    int64_t u = (int64_t)(h >> 40);
-    x = (double)(2 * u + 1 - (1ll << 24)) * 0x1p-24;
-  }
-  return bf ? synth_to_bf16(x) : synth_to_half(x);
+  const double x = synth_draw(h, mode);
+  return (mode & SYNTH_BF16) ? synth_to_bf16(x) : synth_to_half(x);
 }
 
 typedef struct {
@@ -109,6 +140,14 @@ static void* synth_worker(void* p) {
   for (int64_t r = j->tid; r < j->rows; r += j->nthreads) {
     int64_t lr = j->row_index ? j->row_index[r] : j->row0 + r;
     uint64_t base_r = sm_step(base_t ^ (uint64_t)lr);
+    if (j->mode & (SYNTH_E4M3 | SYNTH_E5M2)) {
+      const int e4 = (j->mode & SYNTH_E4M3) != 0;
+      uint8_t* row8 = (uint8_t*)j->dst + r * j->rs;
+      for (int64_t c = 0; c < j->cols; ++c)
+        row8[c * j->cs] = synth_to_f8(synth_draw(sm_step(base_r ^ (uint64_t)c), j->mode),
+                                      e4 ? 3 : 2, e4 ? 7 : 15);
+      continue;
+    }
     uint16_t* row = j->dst + r * j->rs;
     for (int64_t c = 0; c < j->cols; ++c)
       row[c * j->cs] = synth_value(sm_step(base_r ^ (uint64_t)c), j->mode);
@@ -119,12 +158,17 @@ static void* synth_worker(void* p) {
 /*
  * Fill dst[r*rs + c*cs] = element (logical row, logical col c) for r in
  * [0, rows), where the logical row is row_index[r] if row_index is not NULL,
- * else row0 + r.  Strides are in elements.  Returns 0, or -1 on bad args.
+ * else row0 + r.  Strides are in elements; dst holds uint16_t elements, or
+ * bytes for the FP8 modes.  Returns 0, or -1 on bad args.
  */
 int synth_fill(uint16_t* dst, int64_t rows, int64_t cols, int64_t rs, int64_t cs,
                int64_t row0, const int64_t* row_index, uint64_t seed, uint64_t tensor,
                int mode, int nthreads) {
-  if (!dst || rows < 0 || cols < 0 || mode < 0 || mode > (SYNTH_INT | SYNTH_BF16)) return -1;
+  if (!dst || rows < 0 || cols < 0 || mode < 0 || mode > (SYNTH_INT | SYNTH_E5M2)) return -1;
+  {
+    const int fmts = (mode & SYNTH_BF16 ? 1 : 0) + (mode & SYNTH_E4M3 ? 1 : 0) + (mode & SYNTH_E5M2 ? 1 : 0);
+    if (fmts > 1) return -1;
+  }
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if (rows < nthreads) nthreads = rows > 0 ? (int)rows : 1;

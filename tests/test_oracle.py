@@ -413,3 +413,102 @@ def test_bf16_brute_force_small_products():
         B = _torch_bf16_from_f32(Bi)
         got = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, dtype="bf16")
         assert np.array_equal(got, _torch_bf16_from_f32(Ai @ Bi))
+
+
+# ------------------------------------------------------------------ FP8 inputs
+# TileLang tutorial ch. 14, section 5 (low precision): FP8 operands in the
+# E4M3 and E5M2 formats with wider accumulation.  The decoders are pinned to
+# torch's float8 types (another implementation of the OCP definitions) on
+# all 256 patterns, to closed forms, and the products to exact sums.
+
+def _torch_f8(fmt):
+    import torch
+    return torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_f8_decode_all_patterns_matches_torch(fmt):
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.f8_to_f64(bits, fmt)
+    ref = torch.from_numpy(bits).view(_torch_f8(fmt)).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f8_closed_forms():
+    e4 = oracle.f8_to_f64(np.array([0x7E, 0x01, 0x08, 0x38, 0x7F, 0xFF, 0x80, 0x44], np.uint8), "e4m3")
+    assert e4[0] == 448.0 and e4[1] == 2.0 ** -9 and e4[2] == 2.0 ** -6 and e4[3] == 1.0
+    assert np.isnan(e4[4]) and np.isnan(e4[5]) and e4[6] == 0.0 and np.signbit(e4[6])
+    assert e4[7] == 3.0
+    e5 = oracle.f8_to_f64(np.array([0x7B, 0x01, 0x04, 0x3C, 0x7C, 0xFC, 0x7D, 0x3E], np.uint8), "e5m2")
+    assert e5[0] == 57344.0 and e5[1] == 2.0 ** -16 and e5[2] == 2.0 ** -14 and e5[3] == 1.0
+    assert e5[4] == np.inf and e5[5] == -np.inf and np.isnan(e5[6]) and e5[7] == 1.5
+
+
+def _fraction_to_f16_bits(x):
+    """Exact rational -> binary16 bits, ties to even (written from the format:
+    quantum 2^(e-10) for 2^e <= |x| < 2^(e+1), e >= -14; overflow to inf)."""
+    sign = 0x8000 if x < 0 else 0
+    a = abs(x)
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (max(e, -14) - 10)
+    m, r = divmod(a, q)
+    m = int(m)
+    if r > q / 2 or (r == q / 2 and m % 2 == 1):
+        m += 1
+    v = m * q
+    if v >= 65520:
+        return sign | 0x7C00
+    if v < Fraction(2) ** -14:
+        return sign | int(v / Fraction(2) ** -24)
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    return sign | ((e + 15) << 10) | int(v / Fraction(2) ** (e - 10) - 1024)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"),
+                                   ("e5m2", "e5m2")])
+def test_f8_brute_force_exact_sums(fa, fb):
+    # Random FP8 operands (finite patterns), each output the exact rational sum
+    # rounded once to binary16; mixed formats decode each operand by its own.
+    rng = np.random.default_rng(17)
+    for M, N, K in itertools.product((1, 3), (1, 4), (1, 5, 33)):
+        A = rng.integers(0, 256, (M, K)).astype(np.uint8)
+        B = rng.integers(0, 256, (K, N)).astype(np.uint8)
+        av, bv = oracle.f8_to_f64(A, fa), oracle.f8_to_f64(B, fb)
+        A[~np.isfinite(av)] = 0
+        B[~np.isfinite(bv)] = 0
+        av, bv = oracle.f8_to_f64(A, fa), oracle.f8_to_f64(B, fb)
+        got = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, dtype="f8", fmt_a=fa, fmt_b=fb)
+        for i in range(M):
+            for j in range(N):
+                s = sum(Fraction(av[i, k]) * Fraction(bv[k, j]) for k in range(K))
+                assert got[i, j] == _fraction_to_f16_bits(s), (i, j, float(s))
+
+
+def test_f8_integer_product_equals_the_f16_product():
+    # Integers in [-4, 4] are exact in both FP8 formats and in binary16, so the
+    # FP8 product must equal the binary16 product of the same values.
+    for fmt in ("e4m3", "e5m2"):
+        A8 = synth.matrix(40, 70, 5, 0, "int", fmt=fmt)
+        B8 = synth.matrix(70, 30, 5, 1, "int", fmt=fmt)
+        A16 = oracle.f64_to_f16(oracle.f8_to_f64(A8, fmt))
+        B16 = oracle.f64_to_f16(oracle.f8_to_f64(B8, fmt))
+        want = oracle.gemm(A16, (70, 1), B16, (30, 1), 40, 30, 70)
+        got = oracle.gemm(A8, (70, 1), B8, (30, 1), 40, 30, 70, dtype="f8", fmt_a=fmt, fmt_b=fmt)
+        assert np.array_equal(got, want)
+        pts = oracle.gemm_points(A8, (70, 1), B8, (30, 1), 70, [0, 39, 7], [0, 29, 11], dtype="f8",
+                                 fmt_a=fmt, fmt_b=fmt)
+        assert pts.tolist() == [want[0, 0], want[39, 29], want[7, 11]]

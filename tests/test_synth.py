@@ -53,3 +53,15 @@ def test_bf16_format_matches_the_numpy_torch_restatement(mode):
     f16 = synth.rows_of(rows, 300, 77, 3, mode).view(np.float16).astype(np.float64)
     bf = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.all(np.abs(bf - f16) <= np.abs(f16) * 2.0 ** -8 + 2.0 ** -24)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("mode", ["uniform", "int"])
+def test_f8_formats_match_the_torch_restatement(fmt, mode):
+    rows = np.array([0, 1, 7, 1000, 123456])
+    got = synth.rows_of(rows, 300, 78, 3, mode, fmt=fmt)
+    assert got.dtype == np.uint8
+    assert np.array_equal(got, synth.reference_rows(rows, 300, 78, 3, mode, fmt=fmt))
+    a = synth.matrix(50, 20, 78, 3, mode, fmt=fmt)
+    at = synth.matrix(50, 20, 78, 3, mode, fmt=fmt, order="col")
+    assert np.array_equal(a, at.T)
