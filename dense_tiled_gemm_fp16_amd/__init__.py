@@ -4,7 +4,8 @@ The computation runs in libgemmf16.so (hand-written HIP, C-ABI in
 include/gemm_f16.h).  This package only marshals arguments: torch supplies
 device memory and the current stream.
 
-    gemm(a, b, out=None, ...)      -> C ([M, N], float16 or bfloat16 like a and b)
+    gemm(a, b, out=None, ...)      -> C ([M, N], float16 or bfloat16 like a and b;
+                                      float16 for float8_e4m3fn / float8_e5m2 inputs)
     gemm_grouped(a, b, offsets)    -> C, group g: C[off[g]:off[g+1]] = A[...] @ b[g]
     plan(a, b, out=None, ...)      -> dict describing the kernel that would run
     workspace_bytes(M, N, K, ...)  -> bytes of split-K workspace needed
@@ -33,8 +34,14 @@ def _check(a, b, out):
         raise ValueError("expected two matrices")
     if not a.is_cuda or not b.is_cuda or a.device != b.device:
         raise ValueError("inputs must share one GPU device")
-    if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
-        raise TypeError("inputs must both be float16 or both bfloat16")
+    if a.dtype in F8_FORMATS or b.dtype in F8_FORMATS:
+        if a.dtype not in F8_FORMATS or b.dtype not in F8_FORMATS:
+            raise TypeError("FP8 inputs must both be float8_e4m3fn or float8_e5m2")
+        out_dtype = torch.float16
+    elif a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
+        raise TypeError("inputs must both be float16, both bfloat16, or both FP8")
+    else:
+        out_dtype = a.dtype
     m, k = a.shape
     kb, n = b.shape
     if k != kb or min(m, n, k) <= 0:
@@ -42,10 +49,10 @@ def _check(a, b, out):
     if min(a.stride() + b.stride()) <= 0:
         raise ValueError("strides must be positive")
     if out is None:
-        out = torch.empty((m, n), device=a.device, dtype=a.dtype)
+        out = torch.empty((m, n), device=a.device, dtype=out_dtype)
     else:
-        if out.dtype != a.dtype or out.device != a.device or out.shape != (m, n):
-            raise ValueError("out must be an [M, N] tensor of the inputs' dtype and device")
+        if out.dtype != out_dtype or out.device != a.device or out.shape != (m, n):
+            raise ValueError("out must be an [M, N] tensor of the output dtype on the inputs' device")
         if out.stride(1) != 1 or out.stride(0) < n:
             raise ValueError("out must be row-major with unit column stride")
     return m, n, k, out
@@ -59,7 +66,20 @@ def gemm_raw(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream=0, worksp
                            workspace, workspace_bytes, ctypes.byref(o) if o is not None else None)
 
 
-def _fn(a, name):
+# OCP FP8 formats of the inputs -> format codes of gemm_f8* (0 E4M3, 1 E5M2).
+F8_FORMATS = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
+
+
+def _fn(a, name, b=None):
+    """The entry point for the inputs' format.  For FP8 inputs the returned
+    callable appends the two format codes after K (the gemm_f8* layout)."""
+    if a.dtype in F8_FORMATS:
+        f = getattr(lib, name.replace("gemm_f16", "gemm_f8"))
+        fa, fb = F8_FORMATS[a.dtype], F8_FORMATS[(b if b is not None else a).dtype]
+
+        def call(*args):
+            return f(*args[:11], fa, fb, *args[11:])
+        return call
     return getattr(lib, name if a.dtype == torch.float16 else name.replace("gemm_f16", "gemm_bf16"))
 
 
@@ -75,7 +95,7 @@ def gemm(a, b, out=None, workspace=None, variant="auto", split_k=0, panel=0, til
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(a.device):
-        rc = _fn(a, "gemm_f16_ex")(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
+        rc = _fn(a, "gemm_f16_ex", b)(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
                                    b.stride(0), b.stride(1), out.data_ptr(), out.stride(0), m, n,
                                    k, stream.cuda_stream, ws_ptr, ws_bytes, ctypes.byref(opts))
     if rc != GEMM_OK:
@@ -125,7 +145,7 @@ def plan(a, b, out=None, variant="auto", split_k=0, panel=0, tile=0):
     opts = make_opts(variant, split_k, panel, tile)
     info = PlanInfo()
     with torch.cuda.device(a.device):
-        rc = _fn(a, "gemm_f16_plan")(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
+        rc = _fn(a, "gemm_f16_plan", b)(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
                                      b.stride(0), b.stride(1), out.data_ptr(), out.stride(0), m, n,
                                      k, ctypes.byref(opts), ctypes.byref(info))
     if rc != GEMM_OK:

@@ -13,7 +13,7 @@ i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_siz
 GEMM_OK = 0
 STATUS = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_SHAPE", -3: "GEMM_ERR_STRIDE",
           -4: "GEMM_ERR_LDC", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_WORKSPACE",
-          -7: "GEMM_ERR_OPTS", -8: "GEMM_ERR_HIP"}
+          -7: "GEMM_ERR_OPTS", -8: "GEMM_ERR_HIP", -9: "GEMM_ERR_LAYOUT"}
 VARIANT_AUTO, VARIANT_MAIN, VARIANT_SKINNY, VARIANT_SPLITK, VARIANT_TILE64X32, VARIANT_STREAMK = \
     0, 1, 2, 3, 4, 5
 VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4, "streamk": 5}
@@ -21,6 +21,7 @@ PATHS = {0: "gather", 1: "kvec", 2: "rvec"}
 
 EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes",
            "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_plan", "gemm_bf16_workspace_bytes",
+           "gemm_f8", "gemm_f8_ex", "gemm_f8_plan", "gemm_f8_workspace_bytes",
            "gemm_f16_grouped", "gemm_f16_grouped_workspace_bytes",
            "gemm_f16_status_string", "gemm_f16_version"]
 
@@ -62,6 +63,16 @@ def _load():
         getattr(lib, pre + "_plan").restype = ctypes.c_int
         getattr(lib, pre + "_workspace_bytes").argtypes = lib.gemm_f16_workspace_bytes.argtypes
         getattr(lib, pre + "_workspace_bytes").restype = sz
+    args14 = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i32, i32, vp]
+    lib.gemm_f8.argtypes = args14
+    lib.gemm_f8.restype = ctypes.c_int
+    lib.gemm_f8_ex.argtypes = args14 + [vp, sz, ctypes.POINTER(Opts)]
+    lib.gemm_f8_ex.restype = ctypes.c_int
+    lib.gemm_f8_plan.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i32, i32,
+                                 ctypes.POINTER(Opts), ctypes.POINTER(PlanInfo)]
+    lib.gemm_f8_plan.restype = ctypes.c_int
+    lib.gemm_f8_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(Opts)]
+    lib.gemm_f8_workspace_bytes.restype = sz
     lib.gemm_f16_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, i64, vp, i32,
                                      i64, i64, i64, vp, vp, sz]
     lib.gemm_f16_grouped.restype = ctypes.c_int

@@ -45,7 +45,7 @@ const TileInfo& tile_info(int id) {
       TileInfo{},           tile_info_t128(),     tile_info_t64x32(), tile_info_s16(),
       tile_info_s32(),      tile_info_s64(),      tile_info_t256(),   tile_info_t256x128(),
       tile_info_t128x256(),   tile_info_t256w8a(), tile_info_t256w8b(), tile_info_dma256(),
-      tile_info_dma256w8a(), tile_info_dma256w8b(), tile_info_dma256a128()};
+      tile_info_dma256w8a(), tile_info_dma256w8b(), tile_info_dma256a128(), tile_info_f8()};
   return table[id];
 }
 
@@ -116,13 +116,16 @@ int validate(const Call& c) {
   return GEMM_OK;
 }
 
+// Bytes per A and B element (C is always 16-bit).
+uintptr_t in_bytes(const Call& c) { return c.dt >= DT_F8 ? 1 : 2; }
+
 int spans(Call& c) {
   if (!view_span(c.M, c.K, c.lda_m, c.lda_k, &c.spanA) ||
       !view_span(c.K, c.N, c.ldb_k, c.ldb_n, &c.spanB) ||
       !view_span(c.M, c.N, c.ldc, 1, &c.spanC))
     return GEMM_ERR_SHAPE;
-  const uintptr_t a0 = (uintptr_t)c.A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
-  const uintptr_t b0 = (uintptr_t)c.B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+  const uintptr_t a0 = (uintptr_t)c.A, a1 = a0 + in_bytes(c) * (uintptr_t)(c.spanA + 1);
+  const uintptr_t b0 = (uintptr_t)c.B, b1 = b0 + in_bytes(c) * (uintptr_t)(c.spanB + 1);
   const uintptr_t c0 = (uintptr_t)c.C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
   if (a1 < a0 || b1 < b0 || c1 < c0) return GEMM_ERR_SHAPE;
   if (ranges_overlap(c0, c1, a0, a1) || ranges_overlap(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
@@ -169,6 +172,7 @@ int plan_partials(const Call& c, Plan& p) {
 }
 
 bool has_format(const TileInfo& t, int dt) {
+  if (dt < 0 || dt >= NDT) return false;
   for (int i = 0; i < 9; ++i)
     if (t.final_fn[dt][i]) return true;
   return false;
@@ -188,11 +192,23 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     return device_cus(&cus);
   };
 
+  // FP8 operands: K-contiguous A and B with 16-byte aligned rows, on the FP8
+  // tile, in the main, split-K and stream-K families only.
+  const bool f8 = c.dt >= DT_F8;
+  if (f8) {
+    if (c.lda_k != 1 || c.lda_m % 16 != 0 || ((uintptr_t)c.A & 15u) || c.ldb_k != 1 ||
+        c.ldb_n % 16 != 0 || ((uintptr_t)c.B & 15u))
+      return GEMM_ERR_LAYOUT;
+    if (variant == GEMM_VARIANT_SKINNY || variant == GEMM_VARIANT_TILE64X32 ||
+        (want_tile && want_tile != TILE_F8))
+      return GEMM_ERR_OPTS;
+  }
+
   p.sk_tiles = 0;
   p.variant = variant;
   if (p.variant == GEMM_VARIANT_AUTO) {
     if ((rc = need_cus())) return rc;
-    if (c.M <= 64) {
+    if (c.M <= 64 && !f8) {
       p.variant = GEMM_VARIANT_SKINNY;
     } else {
       const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
@@ -210,13 +226,15 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     return GEMM_ERR_OPTS;
   if (p.variant == GEMM_VARIANT_SKINNY && c.M > 64) return GEMM_ERR_OPTS;
 
-  p.a_path = classify(c.A, c.lda_m, c.lda_k);
-  p.b_path = classify(c.B, c.ldb_n, c.ldb_k);
+  p.a_path = f8 ? PATH_KVEC : classify(c.A, c.lda_m, c.lda_k);
+  p.b_path = f8 ? PATH_KVEC : classify(c.B, c.ldb_n, c.ldb_k);
 
   // Tile.
   switch (p.variant) {
     case GEMM_VARIANT_MAIN:
-      if (want_tile) {
+      if (f8) {
+        p.tile_id = TILE_F8;
+      } else if (want_tile) {
         p.tile_id = want_tile;
       } else {
         // 256x256 tiles once they give at least half a wave of workgroups.
@@ -228,11 +246,12 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     case GEMM_VARIANT_SPLITK:
       // The 256x256 full-line-A tile once the output holds a whole one (it
       // falls back to 128x128 for layouts it does not take).
-      p.tile_id = want_tile ? want_tile : ((c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128);
+      p.tile_id = f8 ? TILE_F8
+                     : (want_tile ? want_tile : ((c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128));
       break;
     case GEMM_VARIANT_STREAMK:
-      if (want_tile && want_tile != TILE_DMA256A128) return GEMM_ERR_OPTS;
-      p.tile_id = TILE_DMA256A128;
+      if (!f8 && want_tile && want_tile != TILE_DMA256A128) return GEMM_ERR_OPTS;
+      p.tile_id = f8 ? TILE_F8 : TILE_DMA256A128;
       break;
     case GEMM_VARIANT_TILE64X32:
       if (want_tile && want_tile != TILE_T64X32) return GEMM_ERR_OPTS;
@@ -286,9 +305,10 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   p.GM = cdiv(c.M, ti.bm);
   p.GN = cdiv(c.N, ti.bn);
   const int64_t T = p.GM * p.GN;
-  if (p.variant == GEMM_VARIANT_STREAMK && p.tile_id != TILE_DMA256A128) return GEMM_ERR_OPTS;
-  if (variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN && !want_tile &&
-      p.tile_id == TILE_DMA256A128 && c.K >= 2048) {
+  const bool sk_tile = p.tile_id == TILE_DMA256A128 || p.tile_id == TILE_F8;
+  if (p.variant == GEMM_VARIANT_STREAMK && !sk_tile) return GEMM_ERR_OPTS;
+  if (variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN && (!want_tile || f8) &&
+      sk_tile && c.K >= 2048) {
     // A final wave at most half full goes to the stream-K tail (one 256x256
     // workgroup fits a compute unit, so a wave is `cus` tiles).
     if ((rc = need_cus())) return rc;
@@ -304,11 +324,11 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     int64_t s = want_split;
     if (s == 0) {
       s = cus / L;                                  // fill the idle compute units
-      if (s > cdiv(c.K, 512)) s = cdiv(c.K, 512);   // at least 512 k per range
+      if (s > cdiv(c.K, 16 * ti.bk)) s = cdiv(c.K, 16 * ti.bk);   // at least 8 super-steps per range
       if (s > 64) s = 64;
       if (s < 1) s = 1;
     }
-    set_split(p, c.K, 64, s);   // whole 64-k super-steps per range
+    set_split(p, c.K, 2 * ti.bk, s);   // whole super-steps per range
     p.sk_tiles = L;
     p.grid = T - L;
     p.grid2 = L * (ti.bm * ti.bn / 1024);
@@ -338,7 +358,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
       if (s > max_by_k) s = max_by_k;
       if (s > 64) s = 64;
     }
-    set_split(p, c.K, ti.bk, s);
+    set_split(p, c.K, f8 ? 2 * ti.bk : ti.bk, s);   // FP8: whole 128-k super-steps
   } else {
     if (want_split > 1) return GEMM_ERR_OPTS;
     set_split(p, c.K, ti.bk, 1);
@@ -386,7 +406,7 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   int64_t M = c.M, N = c.N, ldc = c.ldc;
   uint16_t* C = (uint16_t*)c.C;
   int cv = p.c_vec;
-  kfn_reduce fn = c.dt == DT_F16
+  kfn_reduce fn = c.dt != DT_BF16   // binary16 output for the fp16 and FP8 formats
       ? (p.red_lanes == 16 ? splitk_reduce<16, DT_F16> : (p.red_lanes == 4 ? splitk_reduce<4, DT_F16> : splitk_reduce<1, DT_F16>))
       : (p.red_lanes == 16 ? splitk_reduce<16, DT_BF16> : (p.red_lanes == 4 ? splitk_reduce<4, DT_BF16> : splitk_reduce<1, DT_BF16>));
   void* rargs[] = {&W, &S, &M, &N, &C, &ldc, &cv};
@@ -444,7 +464,7 @@ int launch_streamk(const Call& c, const Plan& p, KArgs a, kfn_t final_fn, kfn_t 
   int64_t L = p.sk_tiles, first = p.grid, GM = p.GM, GN = p.GN, M = c.M, N = c.N, ldc = c.ldc;
   uint16_t* C = (uint16_t*)c.C;
   void* fargs[] = {&W, &S, &L, &first, &GM, &GN, &panel, &bm, &bn, &M, &N, &C, &ldc, &cv};
-  const void* fix = c.dt == DT_F16 ? (const void*)sk_fixup<DT_F16> : (const void*)sk_fixup<DT_BF16>;
+  const void* fix = c.dt != DT_BF16 ? (const void*)sk_fixup<DT_F16> : (const void*)sk_fixup<DT_BF16>;
   if (hipLaunchKernel(fix, dim3((unsigned)p.grid2), dim3(256), fargs, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
   return GEMM_OK;
@@ -514,8 +534,8 @@ int ex_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, 
   if (workspace) {
     if (workspace_bytes < p.ws || ((uintptr_t)workspace & 255u)) return GEMM_ERR_WORKSPACE;
     const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + p.ws;
-    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
-    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + in_bytes(c) * (uintptr_t)(c.spanA + 1);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + in_bytes(c) * (uintptr_t)(c.spanB + 1);
     const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
     if (ranges_overlap(w0, w1, a0, a1) || ranges_overlap(w0, w1, b0, b1) ||
         ranges_overlap(w0, w1, c0, c1))
@@ -532,8 +552,11 @@ int ex_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, 
 size_t ws_impl(int dt, int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
   // Shape-only plan on non-overlapping, aligned stand-in addresses.
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  Call c{dt, (const void*)0x100000000000ull, (const void*)0x200000000000ull,
-         (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
+  const int64_t Kp = (K + 15) / 16 * 16;   // FP8: K-contiguous A and B rows
+  Call c = dt >= DT_F8 ? Call{dt, (const void*)0x100000000000ull, (const void*)0x200000000000ull,
+                              (const void*)0x300000000000ull, Kp, 1, 1, Kp, N, M, N, K, 0, 0, 0}
+                       : Call{dt, (const void*)0x100000000000ull, (const void*)0x200000000000ull,
+                              (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
   if (spans(c)) return 0;
   Plan p;
   if (make_plan(c, opts, p)) return 0;
@@ -729,6 +752,40 @@ size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16
   return ws_impl(DT_BF16, M, N, K, opts);
 }
 
+static int f8_dt(int32_t fmt_a, int32_t fmt_b) {
+  if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return -1;
+  return DT_F8 + 2 * fmt_a + fmt_b;
+}
+
+int gemm_f8_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                 int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                 int32_t fmt_a, int32_t fmt_b, const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
+  const int dt = f8_dt(fmt_a, fmt_b);
+  if (dt < 0) return GEMM_ERR_OPTS;
+  return plan_impl(dt, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info);
+}
+
+int gemm_f8_ex(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+               int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t fmt_a,
+               int32_t fmt_b, void* stream, void* workspace, size_t workspace_bytes,
+               const gemm_f16_opts* opts) {
+  const int dt = f8_dt(fmt_a, fmt_b);
+  if (dt < 0) return GEMM_ERR_OPTS;
+  return ex_impl(dt, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream, workspace,
+                 workspace_bytes, opts);
+}
+
+int gemm_f8(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+            int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t fmt_a,
+            int32_t fmt_b, void* stream) {
+  return gemm_f8_ex(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, fmt_a, fmt_b, stream,
+                    nullptr, 0, nullptr);
+}
+
+size_t gemm_f8_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
+  return ws_impl(DT_F8, M, N, K, opts);   // the same for every format pair
+}
+
 const char* gemm_f16_status_string(int status) {
   switch (status) {
     case GEMM_OK: return "success";
@@ -740,6 +797,7 @@ const char* gemm_f16_status_string(int status) {
     case GEMM_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case GEMM_ERR_OPTS: return "invalid options (variant, split, panel or tile)";
     case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_LAYOUT: return "operand layout not taken for this format (FP8: K-contiguous A and B, 16-byte aligned rows)";
     default: return "unknown status";
   }
 }

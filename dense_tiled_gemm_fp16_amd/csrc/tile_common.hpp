@@ -48,6 +48,10 @@ enum LoadPath { PATH_GATHER = 0, PATH_KVEC = 1, PATH_RVEC = 2 };
 // LDS staging move 16-bit elements whatever the format; only the MFMA, the
 // VALU decode of inputs and the final conversion differ.
 enum DType { DT_F16 = 0, DT_BF16 = 1 };
+// Operand formats of a call: the two 16-bit formats, then the four pairs of
+// FP8 formats (A, B) = (E4M3|E5M2, E4M3|E5M2) at DT_F8 + 2 * fmt_a + fmt_b
+// (binary16 output).
+constexpr int DT_F8 = 2, NDT = 6;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // fp32 -> output element, round to nearest even (v_cvt_f16_f32 /

@@ -5,6 +5,7 @@
 
 #include "dma_a128_kernel.hpp"
 #include "dma_kernel.hpp"
+#include "f8_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace gemmf16 {
@@ -29,15 +30,15 @@ enum TileId {
   TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5,
   TILE_T256 = 6, TILE_T256X128 = 7, TILE_T128X256 = 8, TILE_T256W8A = 9,
   TILE_T256W8B = 10, TILE_DMA256 = 11, TILE_DMA256W8A = 12,
-  TILE_DMA256W8B = 13, TILE_DMA256A128 = 14, TILE_MAX = 14
+  TILE_DMA256W8B = 13, TILE_DMA256A128 = 14, TILE_F8 = 15, TILE_MAX = 15
 };
 
 typedef void (*kfn_t)(KArgs);
 
 struct TileInfo {
   int id, bm, bn, bk, nt;
-  kfn_t final_fn[2][9];    // [format][a_path * 3 + b_path]; nullptr = not supported
-  kfn_t partial_fn[2][9];
+  kfn_t final_fn[NDT][9];  // [format][a_path * 3 + b_path]; nullptr = not supported
+  kfn_t partial_fn[NDT][9];
   kfn_t grouped_fn[9];     // grouped launches, fp16 (nullptr: not instantiated)
   int fallback;         // tile used for layouts this one does not support
   int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
@@ -57,7 +58,7 @@ void fill_fns(kfn_t* f) {
 }
 
 inline void clear_fns(TileInfo& t) {
-  for (int d = 0; d < 2; ++d)
+  for (int d = 0; d < NDT; ++d)
     for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
   for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
 }
@@ -128,6 +129,31 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   return t;
 }
 
+// The FP8 tile: K-contiguous A and B (B given as [N, K] rows), the four
+// format pairs; it takes no other layout and no 16-bit format.
+template <int FA, int FB>
+void fill_f8(TileInfo& t) {
+  t.final_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_KVEC] = gemm_f8_kernel<FA, FB, false>;
+  t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_KVEC] = gemm_f8_kernel<FA, FB, true>;
+}
+
+inline TileInfo make_f8_info(int id) {
+  TileInfo t;
+  t.id = id;
+  t.bm = F8Cfg::BM;
+  t.bn = F8Cfg::BN;
+  t.bk = F8Cfg::BK;
+  t.nt = F8Cfg::NT;
+  clear_fns(t);
+  fill_f8<F8_E4M3, F8_E4M3>(t);
+  fill_f8<F8_E4M3, F8_E5M2>(t);
+  fill_f8<F8_E5M2, F8_E4M3>(t);
+  fill_f8<F8_E5M2, F8_E5M2>(t);
+  t.fallback = id;
+  t.n_mult = 0;
+  return t;
+}
+
 // Defined in tile_<id>.hip.
 TileInfo tile_info_t128();
 TileInfo tile_info_t64x32();
@@ -143,5 +169,6 @@ TileInfo tile_info_dma256();
 TileInfo tile_info_dma256w8a();
 TileInfo tile_info_dma256w8b();
 TileInfo tile_info_dma256a128();
+TileInfo tile_info_f8();
 
 }  // namespace gemmf16

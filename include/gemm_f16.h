@@ -59,7 +59,8 @@ enum gemm_status {
   GEMM_ERR_ALIAS = -5,     /* C's byte range overlaps A's or B's                 */
   GEMM_ERR_WORKSPACE = -6, /* the workspace given is smaller than required       */
   GEMM_ERR_OPTS = -7,      /* invalid forced variant, split, panel or tile       */
-  GEMM_ERR_HIP = -8        /* a HIP runtime call failed (no device, launch, ...) */
+  GEMM_ERR_HIP = -8,       /* a HIP runtime call failed (no device, launch, ...) */
+  GEMM_ERR_LAYOUT = -9     /* operand layout not taken for the format (FP8 below) */
 };
 
 /* Kernel families (gemm_f16_opts.variant / gemm_f16_plan_info.variant).
@@ -176,6 +177,40 @@ int gemm_bf16_plan(const void* A, int64_t lda_m, int64_t lda_k,
                    int64_t M, int64_t N, int64_t K,
                    const gemm_f16_opts* opts, gemm_f16_plan_info* info);
 size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
+
+/*
+ * C := A.B with OCP FP8 operands, fp32 accumulation and binary16 output
+ * (round to nearest even): the FP8 variant of the TileLang tutorial, ch. 14,
+ * section 5 (E4M3 and E5M2 operands with wider accumulation, the GEMM
+ * skeleton kept, a K step of 64).  fmt_a and fmt_b give each operand's
+ * format: 0 = E4M3 (the "FN" variant: no infinities, 448 the largest
+ * finite value), 1 = E5M2; anything else is GEMM_ERR_OPTS.  A and B are one
+ * byte per element; strides are in elements as for the 16-bit calls; C is
+ * binary16 with row stride ldc.
+ *
+ * Layout: A must be K-contiguous (lda_k == 1) and B must be K-contiguous
+ * (ldb_k == 1: the [N, K] weight layout, seen as a transposed view), with
+ * lda_m and ldb_n multiples of 16 and A and B 16-byte aligned; any other
+ * layout returns GEMM_ERR_LAYOUT before anything is enqueued.  M, N and K are
+ * masked as in the 16-bit calls (zero fill on K).  Variants: AUTO, MAIN,
+ * SPLITK and STREAMK (SKINNY and TILE64X32 return GEMM_ERR_OPTS); the tile
+ * is 256 x 256 x 64.  Workspace contract and other return codes as above.
+ */
+int gemm_f8(const void* A, int64_t lda_m, int64_t lda_k,
+            const void* B, int64_t ldb_k, int64_t ldb_n,
+            void* C, int64_t ldc,
+            int64_t M, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b, void* stream);
+int gemm_f8_ex(const void* A, int64_t lda_m, int64_t lda_k,
+               const void* B, int64_t ldb_k, int64_t ldb_n,
+               void* C, int64_t ldc,
+               int64_t M, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b, void* stream,
+               void* workspace, size_t workspace_bytes, const gemm_f16_opts* opts);
+int gemm_f8_plan(const void* A, int64_t lda_m, int64_t lda_k,
+                 const void* B, int64_t ldb_k, int64_t ldb_n,
+                 const void* C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b,
+                 const gemm_f16_opts* opts, gemm_f16_plan_info* info);
+size_t gemm_f8_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
 
 /*
  * Grouped product, one launch over G products that share N and K (the

@@ -22,7 +22,8 @@ PA, PB, PC, PW = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_b?f16\w*)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_(?:b?f16|f8)\w*)\s*\(", text,
+                                 re.M)))
 
 
 def test_header_declares_the_binding_list():
@@ -179,3 +180,41 @@ def test_bf16_options_and_plans():
                               ctypes.byref(info))
     assert rc == 0 and info.split_k == 4 and info.workspace_bytes == 4 * 16 * 32 * 4
     assert g.lib.gemm_bf16_workspace_bytes(16, 32, 1024, ctypes.byref(o)) == 4 * 16 * 32 * 4
+
+
+def f8call(A=PA, lda_m=64, lda_k=1, B=PB, ldb_k=1, ldb_n=64, C=PC, ldc=32, M=16, N=32, K=64,
+           fa=0, fb=0, opts=None):
+    return g.lib.gemm_f8_ex(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, fa, fb, 0, 0, 0,
+                            ctypes.byref(opts) if opts is not None else None)
+
+
+def test_f8_rejected_before_any_device_work():
+    # Layout: K-contiguous A and B with 16-byte aligned rows only.
+    assert f8call(lda_m=1, lda_k=64) == -9              # A not K-contiguous
+    assert f8call(ldb_k=32, ldb_n=1) == -9              # B N-contiguous
+    assert f8call(lda_m=72) == -9                       # A rows not 16-byte aligned
+    assert f8call(ldb_n=40) == -9
+    assert f8call(A=PA + 8) == -9
+    assert f8call(fa=2) == -7 and f8call(fb=-1) == -7   # formats 0 (E4M3) and 1 (E5M2)
+    assert f8call(opts=_lib.Opts(2, 0, 0, 0)) == -7     # no skinny FP8 path
+    assert f8call(opts=_lib.Opts(4, 0, 0, 0)) == -7
+    assert f8call(opts=_lib.Opts(1, 0, 0, 14)) == -7    # the FP8 tile only
+    assert f8call(M=0) == -2 and f8call(ldc=31) == -4 and f8call(A=0) == -1
+    # byte-sized A and B: C may start right after A's last byte
+    assert f8call(C=PA + 15 * 64 + 64) != -5
+    assert f8call(C=PA + 15 * 64 + 62) == -5
+
+
+def test_f8_plans():
+    info = _lib.PlanInfo()
+    for fa, fb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+        rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 1, 704, PC, 520, 600, 520, 700, fa, fb,
+                                ctypes.byref(_lib.Opts(1, 0, 4, 0)), ctypes.byref(info))
+        assert rc == 0
+        assert (info.tile_id, info.tile_m, info.tile_n, info.tile_k) == (15, 256, 256, 64)
+        assert (info.split_k, info.grid, info.workspace_bytes) == (1, 9, 0)
+    rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 1, 704, PC, 520, 600, 520, 700, 0, 0,
+                            ctypes.byref(_lib.Opts(3, 3, -1, 0)), ctypes.byref(info))
+    assert rc == 0 and info.split_k == 3 and info.workspace_bytes == 3 * 600 * 520 * 4
+    assert g.lib.gemm_f8_workspace_bytes(600, 520, 700, ctypes.byref(_lib.Opts(3, 3, -1, 0))) \
+        == info.workspace_bytes

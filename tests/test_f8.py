@@ -1,0 +1,111 @@
+"""GPU parity of the FP8 entry points (gemm_f8*, TileLang tutorial ch. 14,
+section 5): OCP E4M3 / E5M2 operands, fp32 accumulation, binary16 output,
+against the oracle's FP8 product on the same seeded inputs.  Acceptance as
+for fp16: bit-exact on integer inputs (exact in both FP8 formats, sums exact
+in fp32), the elementwise tolerance 1e-2 + 2e-3 |C| on U(-1, 1) inputs
+rounded to FP8.  Operand rows are padded with the NaN byte 0x7F (NaN in both
+formats), which must never reach an output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_gemm_fp16_amd as g
+import oracle
+import synth
+from gpu_util import DEV, ORACLE_THREADS, Out, assert_bits_equal, assert_close, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+TORCH_F8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+PAIRS = [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
+
+
+def f8_rows(bits, fmt, pad=None):
+    """uint8 [R, K] -> FP8 device view [R, K] whose rows are padded to a
+    multiple of 16 bytes (at least 16 more) with 0x7F."""
+    R, K = bits.shape
+    pad = (-K) % 16 + 16 if pad is None else pad
+    buf = np.full((R, K + pad), 0x7F, dtype=np.uint8)
+    buf[:, :K] = bits
+    return torch.from_numpy(buf).to(DEV).view(TORCH_F8[fmt])[:, :K]
+
+
+def inputs(M, N, K, seed, mode, fa, fb):
+    A = synth.matrix(M, K, seed, 0, mode, fmt=fa)
+    Bt = synth.matrix(K, N, seed, 1, mode, fmt=fb, order="col")    # stored [N][K]
+    return A, Bt
+
+
+def reference(A, Bt, fa, fb, rows=None):
+    K = A.shape[1]
+    B = np.ascontiguousarray(Bt.T)
+    if rows is not None:
+        A = np.ascontiguousarray(A[rows])
+    return oracle.gemm(A, (K, 1), B, (B.shape[1], 1), A.shape[0], B.shape[1], K, dtype="f8",
+                       fmt_a=fa, fmt_b=fb, nthreads=ORACLE_THREADS)
+
+
+def run(a, b, out, **kw):
+    say(f"gemm_f8 M={a.shape[0]} N={b.shape[1]} K={a.shape[1]} {a.dtype}/{b.dtype} "
+        f"a.stride={a.stride()} b.stride={b.stride()} opts={kw}")
+    g.gemm(a, b, out=out.view, **kw)
+    torch.cuda.synchronize()
+    return out.result()
+
+
+@pytest.mark.parametrize("mode", ["int", "uniform"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_f8_parity_ragged(fa, fb, mode):
+    M, N, K = 600, 520, 700
+    A, Bt = inputs(M, N, K, 14000, mode, fa, fb)
+    ref = reference(A, Bt, fa, fb)
+    a, b = f8_rows(A, fa), f8_rows(Bt, fb).t()
+    for kw in (dict(variant="main"), dict(variant="splitk", split_k=3),
+               dict(variant="streamk", split_k=2)):
+        got = run(a, b, Out(M, N), **kw)
+        what = f"f8 {fa}x{fb} {mode} {kw}"
+        if mode == "int":
+            assert_bits_equal(got, ref, what)
+        else:
+            assert_close(got, ref, what)
+
+
+@pytest.mark.parametrize("K", [1, 33, 64, 100, 128, 192, 255, 384])
+def test_f8_k_tails(K):
+    # Whole 128-k super-steps, an odd 64-k step and ragged tails, byte by byte.
+    M, N = 300, 264
+    A, Bt = inputs(M, N, K, 14100 + K, "int", "e4m3", "e4m3")
+    ref = reference(A, Bt, "e4m3", "e4m3")
+    got = run(f8_rows(A, "e4m3"), f8_rows(Bt, "e4m3").t(), Out(M, N), variant="main")
+    assert_bits_equal(got, ref, f"f8 K={K}")
+
+
+def test_f8_edge_blocks():
+    # Last tile row / column with every count of live 32-wide blocks.
+    K = 192
+    for M in (257, 321, 449):
+        for N in (264, 296, 352, 424, 488):
+            A, Bt = inputs(M, N, K, 14200 + M + N, "int", "e5m2", "e4m3")
+            ref = reference(A, Bt, "e5m2", "e4m3")
+            got = run(f8_rows(A, "e5m2"), f8_rows(Bt, "e4m3").t(), Out(M, N), variant="main")
+            assert_bits_equal(got, ref, f"f8 edge blocks {M}x{N}")
+
+
+def test_f8_moe_shape_sampled():
+    # The 131072 x 2048 x 7168 product with E4M3 operands (B as [N, K]
+    # weights); sampled rows of every tile row band against the oracle.
+    M, N, K = 131072, 2048, 7168
+    say("f8 MoE: generating inputs")
+    A, Bt = inputs(M, N, K, 14300, "uniform", "e4m3", "e4m3")
+    a = torch.from_numpy(A).to(DEV).view(torch.float8_e4m3fn)
+    b = torch.from_numpy(Bt).to(DEV).view(torch.float8_e4m3fn).t()
+    p = g.plan(a, b)
+    assert p["tile_id"] == 15
+    say(f"f8 MoE: launch {p}")
+    c = g.gemm(a, b)
+    torch.cuda.synchronize()
+    got = to_host(c)
+    rng = np.random.default_rng(14300)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
+    assert_close(got[rows], reference(A, Bt, "e4m3", "e4m3", rows), "f8 MoE sampled rows")
