@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOPS & %MFMA peak, fp16 GEMM 131072x2048x7168; GB/s at M=1"
 PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_F8_TFLOPS = 5033.2       # MI355X dense FP8 MFMA (twice the fp16 rate)
 PAGES_TFLOPS = 117.250897     # the pages' TileLang kernel on MetaX C500, same workload
 M, N, K = 131072, 2048, 7168
 
@@ -400,6 +401,24 @@ def main():
             "timing": "HIP events around each call"}
     del ab, bb
 
+    # ---- FP8: the same product with E4M3 operands (B as [N, K] weights), fp16 out
+    af = torch.from_numpy(synth.matrix(M, K, 4001, synth.TENSOR_A, fmt="e4m3")).to(dev).view(
+        torch.float8_e4m3fn)
+    bf = torch.from_numpy(synth.matrix(K, N, 4001, synth.TENSOR_B, fmt="e4m3", order="col")).to(
+        dev).view(torch.float8_e4m3fn).t()
+
+    def step_f():
+        g.gemm(af, bf, out=c, stream=stream)
+
+    df, _ = timed_launches(step_f, stream, max(5, args.steps // 5), 2)
+    msf = sum(df) / len(df)
+    f8 = {"workload": f"{M}x{N}x{K}, E4M3 inputs (B as [N, K] weights), fp32 accumulation, fp16 out",
+          "plan": {k: g.plan(af, bf, c)[k] for k in ("variant", "tile_id", "split_k")},
+          "ms": msf, "TFLOPS": flops / (msf * 1e-3) / 1e12,
+          "frac": flops / (msf * 1e-3) / 1e12 / PEAK_F8_TFLOPS, "peak": PEAK_F8_TFLOPS,
+          "timing": "HIP events around each call"}
+    del af, bf
+
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -420,6 +439,7 @@ def main():
         "skinny_m1": skinny,
         "grouped_moe": grouped,
         "bf16": bf16,
+        "f8": f8,
         "vs_baseline_ref": "pages' TileLang kernel on MetaX C500, 117.25 TFLOPS (context only)",
     }
     if not args.no_cpu_baseline:
