@@ -7,6 +7,7 @@ device memory and the current stream.
     gemm(a, b, out=None, ...)      -> C ([M, N], float16 or bfloat16 like a and b;
                                       float16 for float8_e4m3fn / float8_e5m2 inputs)
     gemm_grouped(a, b, offsets)    -> C, group g: C[off[g]:off[g+1]] = A[...] @ b[g]
+    pack_b(b) / gemm_packed(a, p)  -> a static fp16 B packed once, then C = a @ B
     plan(a, b, out=None, ...)      -> dict describing the kernel that would run
     workspace_bytes(M, N, K, ...)  -> bytes of split-K workspace needed
 """
@@ -17,7 +18,8 @@ import torch
 from ._lib import (GEMM_OK, LIB_PATH, PATHS, STATUS, VARIANTS, Opts, PlanInfo, lib, make_opts,
                    status_string)
 
-__all__ = ["gemm", "gemm_raw", "gemm_grouped", "plan", "workspace_bytes", "GemmError", "LIB_PATH",
+__all__ = ["gemm", "gemm_raw", "gemm_grouped", "pack_b", "gemm_packed", "PackedB", "plan",
+           "workspace_bytes", "GemmError", "LIB_PATH",
            "VARIANTS"]
 
 
@@ -159,3 +161,50 @@ def plan(a, b, out=None, variant="auto", split_k=0, panel=0, tile=0):
 def workspace_bytes(M, N, K, variant="auto", split_k=0, panel=0, tile=0):
     opts = make_opts(variant, split_k, panel, tile)
     return int(lib.gemm_f16_workspace_bytes(M, N, K, ctypes.byref(opts)))
+
+
+class PackedB:
+    """A float16 B [K, N] packed by gemm_f16_pack_b (opaque bytes on its GPU)."""
+
+    def __init__(self, data, K, N):
+        self.data, self.K, self.N = data, K, N
+
+
+def pack_b(b, stream=None):
+    """Pack a static float16 B [K, N] (any positive strides) for gemm_packed."""
+    if b.ndim != 2 or not b.is_cuda or b.dtype != torch.float16:
+        raise ValueError("expected a float16 [K, N] matrix on a GPU")
+    K, N = b.shape
+    nbytes = int(lib.gemm_f16_packed_b_bytes(K, N))
+    if nbytes == 0:
+        raise ValueError("empty or oversized shape")
+    data = torch.empty(nbytes, dtype=torch.uint8, device=b.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(b.device)
+    with torch.cuda.device(b.device):
+        rc = lib.gemm_f16_pack_b(b.data_ptr(), b.stride(0), b.stride(1), K, N, data.data_ptr(),
+                                 stream.cuda_stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return PackedB(data, K, N)
+
+
+def gemm_packed(a, packed, out=None, stream=None):
+    """C = a @ B for a float16 a [M, K] (K-contiguous rows) and B packed by pack_b."""
+    if a.ndim != 2 or not a.is_cuda or a.dtype != torch.float16:
+        raise ValueError("expected a float16 [M, K] matrix on a GPU")
+    if packed.data.device != a.device or a.shape[1] != packed.K:
+        raise ValueError("a and the packed B must share the GPU and K")
+    m, n = a.shape[0], packed.N
+    if out is None:
+        out = torch.empty((m, n), device=a.device, dtype=torch.float16)
+    elif out.dtype != torch.float16 or out.shape != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be a row-major float16 [M, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        rc = lib.gemm_f16_packed(a.data_ptr(), a.stride(0), a.stride(1), packed.data.data_ptr(),
+                                 out.data_ptr(), out.stride(0), m, n, packed.K, stream.cuda_stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return out

@@ -105,6 +105,36 @@ struct ASource128 {
   }
 };
 
+// B pre-packed into the LDS image of its K-major stages (see
+// gemm_f16_pack_b): 256-column panels of ceil(K/32) 16 KiB blocks, zero
+// padded past N and K, so every DMA instruction reads 1 KiB of consecutive
+// bytes and the K tail needs no masks.  s_r is the panel stride in elements.
+template <int NI>
+struct PackedBSource {
+  const uint16_t* p[NI];
+  static constexpr int64_t step = 8192;  // elements per 32-k block
+
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t s_r, int64_t, int64_t,
+                                       int64_t r0, int64_t kb, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      p[i] = base + (r0 / 256) * s_r + (kb / 32) * step + (NI * wave + i) * 512 + lane * 8;
+  }
+
+  __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
+    dma16_batch<NI>(p, t * step, lds_wave);
+  }
+
+  // The block of step t as it lies (its K tail is already zero).
+  __device__ __forceinline__ void fill_masked(char* lds_op, int wave, int lane, int64_t t, int64_t,
+                                              int64_t, int64_t) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<u32x4*>(lds_op + (NI * wave + i) * 1024 + lane * 16) =
+          *reinterpret_cast<const u32x4*>(p[i] + t * step);
+  }
+};
+
 // One fragment of k-substep ks of the 32-k step in half H of a super-step:
 // piece q < FM is A fragment q, piece FM + i is B fragment i.  B stages are
 // laid out as in dma_kernel.hpp: N-major 512-byte k-rows, or, for a
@@ -170,8 +200,11 @@ __device__ __forceinline__ void mma_frags_a128(const DmaFrags<CF>& f, f32x16 (&a
 }
 
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
-template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false, int DT = DT_F16>
+// BPACK: B comes pre-packed (PackedBSource; read as a K-major B).
+template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false, int DT = DT_F16,
+          bool BPACK = false>
 __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
+  static_assert(!BPACK || BKMAJOR, "packed B stages are K-major");
   static_assert(!(PARTIAL && GROUPED), "grouped launches are never split");
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
@@ -208,7 +241,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   const bool edge = fnv < CF::FN || fmv < CF::FM;
 
   ASource128<CF::DMA_A> sa;
-  DmaSource<CF::DMA_B, BKMAJOR> sb;
+  std::conditional_t<BPACK, PackedBSource<CF::DMA_B>, DmaSource<CF::DMA_B, BKMAJOR>> sb;
   sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, kb, wave, lane);
   sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, kb, wave, lane);
 

@@ -24,6 +24,7 @@
 #include "../../include/gemm_f16.h"
 #include "gemv_kernel.hpp"
 #include "group_kernel.hpp"
+#include "pack_kernel.hpp"
 #include "reduce_kernel.hpp"
 #include "tiles.hpp"
 
@@ -750,6 +751,95 @@ int gemm_bf16(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_
 
 size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
   return ws_impl(DT_BF16, M, N, K, opts);
+}
+
+// ---- pre-packed B
+static int64_t packed_blocks(int64_t K, int64_t N, int64_t* S) {
+  *S = cdiv(K, 32);
+  return cdiv(N, 256) * *S;
+}
+
+size_t gemm_f16_packed_b_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0 || K > (INT64_C(1) << 40) || N > (INT64_C(1) << 40)) return 0;
+  int64_t S;
+  const int64_t blocks = packed_blocks(K, N, &S);
+  int64_t bytes;
+  if (__builtin_mul_overflow(blocks, (int64_t)16384, &bytes)) return 0;
+  return (size_t)bytes;
+}
+
+int gemm_f16_pack_b(const void* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int64_t N, void* Bp,
+                    void* stream) {
+  if (!B || !Bp) return GEMM_ERR_NULL;
+  if (K <= 0 || N <= 0) return GEMM_ERR_SHAPE;
+  if (ldb_k <= 0 || ldb_n <= 0) return GEMM_ERR_STRIDE;
+  int64_t spanB;
+  if (!view_span(K, N, ldb_k, ldb_n, &spanB)) return GEMM_ERR_SHAPE;
+  const size_t bytes = gemm_f16_packed_b_bytes(K, N);
+  if (bytes == 0) return GEMM_ERR_SHAPE;
+  if (((uintptr_t)Bp & 255u) != 0) return GEMM_ERR_WORKSPACE;
+  const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(spanB + 1);
+  if (ranges_overlap(b0, b1, (uintptr_t)Bp, (uintptr_t)Bp + bytes)) return GEMM_ERR_ALIAS;
+  int64_t S;
+  packed_blocks(K, N, &S);
+  int64_t slots = (int64_t)(bytes / 16);
+  const uint16_t* src = (const uint16_t*)B;
+  uint16_t* dst = (uint16_t*)Bp;
+  void* args[] = {&src, &ldb_k, &ldb_n, &K, &N, &S, &slots, &dst};
+  if (hipLaunchKernel((const void*)pack_b_kernel, dim3((unsigned)cdiv(slots, 256)), dim3(256), args, 0,
+                      (hipStream_t)stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+int gemm_f16_packed(const void* A, int64_t lda_m, int64_t lda_k, const void* Bp, void* C, int64_t ldc,
+                    int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!A || !Bp || !C) return GEMM_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0) return GEMM_ERR_SHAPE;
+  if (lda_m <= 0 || lda_k <= 0) return GEMM_ERR_STRIDE;
+  if (ldc < N) return GEMM_ERR_LDC;
+  int64_t spanA, spanC;
+  if (!view_span(M, K, lda_m, lda_k, &spanA) || !view_span(M, N, ldc, 1, &spanC)) return GEMM_ERR_SHAPE;
+  const size_t bytes = gemm_f16_packed_b_bytes(K, N);
+  if (bytes == 0) return GEMM_ERR_SHAPE;
+  // The full-line-A tile's A path: K-contiguous, 16-byte aligned rows.
+  if (classify(A, lda_m, lda_k) != PATH_KVEC || ((uintptr_t)Bp & 255u) != 0) return GEMM_ERR_LAYOUT;
+  const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(spanA + 1);
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(spanC + 1);
+  const uintptr_t p0 = (uintptr_t)Bp, p1 = p0 + bytes;
+  if (ranges_overlap(c0, c1, a0, a1) || ranges_overlap(c0, c1, p0, p1)) return GEMM_ERR_ALIAS;
+  const TileInfo& ti = tile_info(TILE_DMA256A128);
+  KArgs a;
+  a.A = (const uint16_t*)A;
+  a.lda_m = lda_m;
+  a.lda_k = lda_k;
+  a.B = (const uint16_t*)Bp;
+  a.ldb_k = 1;
+  a.ldb_n = cdiv(K, 32) * 8192;   // elements per 256-column panel
+  a.C = (uint16_t*)C;
+  a.ldc = ldc;
+  a.W = nullptr;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.k_split = K;
+  a.GM = cdiv(M, ti.bm);
+  a.GN = cdiv(N, ti.bn);
+  a.panel = 4;
+  a.c_vec = (((uintptr_t)C & 7u) == 0 && (ldc & 3) == 0) ? 1 : 0;
+  a.g_off = nullptr;
+  a.g_tiles = nullptr;
+  a.ldb_g = 0;
+  a.G = 0;
+  a.sk_first = 0;
+  a.sk_tiles = 0;
+  int64_t grid;
+  if (__builtin_mul_overflow(a.GM, a.GN, &grid) || grid > INT32_MAX) return GEMM_ERR_SHAPE;
+  void* args[] = {&a};
+  if (hipLaunchKernel((const void*)ti.packed_fn, dim3((unsigned)grid), dim3(ti.nt), args, 0,
+                      (hipStream_t)stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
 }
 
 static int f8_dt(int32_t fmt_a, int32_t fmt_b) {

@@ -1,0 +1,33 @@
+// Pre-packing of a static B (the "interleave4" weight packing of the C500
+// log, done once outside the timed region) into the layout the main
+// kernel's K-major B stages have in LDS.  Included by the host translation
+// unit only (non-inline kernel).
+#pragma once
+
+#include "dma_kernel.hpp"
+
+namespace gemmf16 {
+
+// Bp: ceil(N/256) panels x ceil(K/32) blocks of 16 KiB.  Byte o of block
+// (p, s) holds, for row r = o / 64 (n = 256 p + r) and 16-byte slot
+// q = (o % 64) / 16, the 8 elements k = 32 s + 8 (q ^ fa(r)) + e, e = 0..7
+// (zero past N or K): the bytes a DMA of a K-major B stage writes to LDS.
+// One thread per 16-byte slot; B is read through its element strides.
+__global__ __launch_bounds__(256) void pack_b_kernel(const uint16_t* B, int64_t ldb_k, int64_t ldb_n,
+                                                     int64_t K, int64_t N, int64_t S, int64_t slots,
+                                                     uint16_t* Bp) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= slots) return;
+  const int64_t blk = q / 1024, o = (q % 1024) * 16;
+  const int64_t pnl = blk / S, s = blk - pnl * S;
+  const int r = (int)(o / 64), c = (int)((o % 64) / 16) ^ fa(r);
+  const int64_t n = 256 * pnl + r, k0 = 32 * s + 8 * c;
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    h[e] = (n < N && k0 + e < K) ? (uint32_t)B[(k0 + e) * ldb_k + n * ldb_n] : 0u;
+  *reinterpret_cast<u32x4*>(Bp + q * 8) =
+      u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+}  // namespace gemmf16

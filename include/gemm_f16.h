@@ -213,6 +213,27 @@ int gemm_f8_plan(const void* A, int64_t lda_m, int64_t lda_k,
 size_t gemm_f8_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
 
 /*
+ * Pre-packed static B: the C500 log's weight packing (B re-laid once,
+ * outside the timed region, into the order the matrix instructions read
+ * it), reported beside the general-stride path and never instead of it.
+ * gemm_f16_pack_b reads B [K, N] through its element strides (any positive
+ * strides) and writes Bp, an opaque device buffer of
+ * gemm_f16_packed_b_bytes(K, N) bytes (256-byte aligned, not overlapping B):
+ * 256-column panels of ceil(K/32) blocks of 16 KiB, each block the LDS image
+ * of one K-major B stage of the 256 x 256 LDS-DMA tile, zero past N and K.
+ * gemm_f16_packed computes C := A.B from A (K-contiguous, 16-byte aligned
+ * rows: GEMM_ERR_LAYOUT otherwise) and Bp packed for the same K and N, on
+ * the main variant of that tile (no split, no workspace).  Both are
+ * asynchronous on `stream`; other return codes as gemm_f16.  The packed
+ * buffer's layout is private to this library version.
+ */
+size_t gemm_f16_packed_b_bytes(int64_t K, int64_t N);
+int gemm_f16_pack_b(const void* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int64_t N, void* Bp,
+                    void* stream);
+int gemm_f16_packed(const void* A, int64_t lda_m, int64_t lda_k, const void* Bp,
+                    void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Grouped product, one launch over G products that share N and K (the
  * TileLang tutorial, ch. 14, section 4.3: grouped GEMM with per-group row
  * counts, as for the experts of a mixture-of-experts layer):

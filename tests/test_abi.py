@@ -218,3 +218,20 @@ def test_f8_plans():
     assert rc == 0 and info.split_k == 3 and info.workspace_bytes == 3 * 600 * 520 * 4
     assert g.lib.gemm_f8_workspace_bytes(600, 520, 700, ctypes.byref(_lib.Opts(3, 3, -1, 0))) \
         == info.workspace_bytes
+
+
+def test_packed_b_rejected_before_any_device_work():
+    nb = g.lib.gemm_f16_packed_b_bytes(100, 300)
+    assert nb == 2 * 4 * 16384                                      # 2 panels x 4 blocks of 32 k
+    assert g.lib.gemm_f16_packed_b_bytes(0, 5) == 0
+    pack = g.lib.gemm_f16_pack_b
+    assert pack(0, 300, 1, 100, 300, PW, 0) == -1
+    assert pack(PB, 300, 1, 0, 300, PW, 0) == -2
+    assert pack(PB, 0, 1, 100, 300, PW, 0) == -3
+    assert pack(PB, 300, 1, 100, 300, PW + 16, 0) == -6             # Bp not 256-byte aligned
+    assert pack(PB, 300, 1, 100, 300, PB + 256, 0) == -5            # Bp overlaps B
+    run = g.lib.gemm_f16_packed
+    assert run(PA, 100, 1, PW, PC, 300, 50, 300, 100, 0) == -9      # A rows not 16-byte multiples
+    assert run(PA, 1, 50, PW, PC, 300, 50, 300, 100, 0) == -9       # A not K-contiguous
+    assert run(PA, 112, 1, PW, PC, 299, 50, 300, 100, 0) == -4
+    assert run(PA, 112, 1, PW, PW + 1024, 300, 50, 300, 100, 0) == -5   # C overlaps Bp
