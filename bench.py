@@ -73,7 +73,7 @@ def measured_traffic(kind):
 COPY_KIB = float(1 << 20)      # the calibration copy reads and writes 1 GiB
 # The fp16 main-kernel instantiation that the 131072x2048x7168 plan runs
 # (N-contiguous B, one K range, not grouped).
-MAIN_KERNEL = "void gemmf16::gemm_dma_a128_kernel<gemmf16::DmaA128Cfg<4, 2>, false, false, false, 0>"
+MAIN_KERNEL = "void gemmf16::gemm_dma_a128_kernel<gemmf16::DmaA128Cfg<4, 2>, false, false, false, 0, false>"
 
 
 def summarize_pmc(fetch_csv, write_csv):
