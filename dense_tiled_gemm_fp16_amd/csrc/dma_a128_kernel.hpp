@@ -29,6 +29,14 @@
 // A ragged remainder of fewer than 64 k (an odd number of full 32-k steps
 // and/or a K tail) is filled by masked register loads with zero fill after
 // the pipelined loop.
+//
+// Issue economy: a wave's memory phase is short of issue slots, not of
+// bandwidth, so the loop keeps its bookkeeping cheap.  LDS slot indices
+// rotate in 32-bit scalar registers, and the DMA uses the SGPR-base form of
+// global_load_lds_dwordx4 (a uniform 64-bit base advanced once per step, a
+// fixed 32-bit offset per lane), which takes no per-instruction 64-bit vector
+// adds.  Lane offsets span at most 255 rows of an operand, so the host sends
+// operands whose row stride exceeds 2^23 elements to another tile.
 #pragma once
 
 #include <type_traits>
@@ -101,6 +109,145 @@ struct ASource128 {
       const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
       const u32x4 v = load_partial8(p[i] + (nk > 0 ? u * step : 0), s_k, nk);
       *reinterpret_cast<u32x4*>(slot + (NI * wave + i) * 1024 + lane * 16) = v;
+    }
+  }
+};
+
+// global_load_lds_dwordx4 in its SGPR-base form: a uniform 64-bit base and a
+// 32-bit per-lane byte offset, so a step's DMA needs no 64-bit VALU address
+// arithmetic.  As in dma16_batch, the instruction offset (1024 j for the j-th
+// instruction of a batch) is added to both addresses; the per-lane offsets
+// carry the matching -1024 j.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+template <int NI>
+__device__ __forceinline__ void dma16s_batch(const uint32_t* off, const char* base, uint32_t lds) {
+  static_assert(NI == 2 || NI == 4, "batch size");
+  if constexpr (NI == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, %5 offset:3072"
+        :
+        : "s"(lds), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "global_load_lds_dwordx4 %2, %3 offset:1024"
+        :
+        : "s"(lds), "v"(off[0]), "v"(off[1]), "s"(base)
+        : "memory", "m0");
+  }
+}
+
+// Bytes below a source's base that its offsets start from, so that the
+// biased offsets (down to -3072) stay non-negative.
+constexpr int kSBias = 4096;
+
+// ASource128 in SGPR-base form (same rows, slots and clamping).
+template <int NI>
+struct ASourceS {
+  const char* base;  // byte address of (row r0, k kb) less kSBias
+  uint32_t off[NI];
+  int64_t step;      // bytes per 64-k super-step
+
+  __device__ __forceinline__ void init(const uint16_t* A, int64_t s_r, int64_t s_k, int64_t R_tot,
+                                       int64_t r0, int64_t kb, int wave, int lane) {
+    base = uniform_ptr((const char*)(A + r0 * s_r + kb * s_k) - kSBias);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (NI * wave + i) * 8 + lane / 8;
+      const int c = (lane % 8) ^ f8(r);
+      int64_t rr = r0 + r;
+      if (rr > R_tot - 1) rr = R_tot - 1;
+      off[i] = (uint32_t)(((rr - r0) * s_r + 8 * c * s_k) * 2 + kSBias - 1024 * (i % (NI / 2)));
+    }
+    step = (int64_t)128 * s_k;
+  }
+  template <int H>
+  __device__ __forceinline__ void issue_half(uint32_t lds, int64_t u) {
+    dma16s_batch<NI / 2>(&off[H * (NI / 2)], base + u * step, lds);
+  }
+  __device__ __forceinline__ const uint16_t* ptr(int i, int64_t u) const {
+    return (const uint16_t*)(base + u * step + off[i] + 1024 * (i % (NI / 2)));
+  }
+  __device__ __forceinline__ void fill_masked(char* slot, int wave, int lane, int64_t u, int64_t kb,
+                                              int64_t k_end, int64_t s_k) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (NI * wave + i) * 8 + lane / 8;
+      const int c = (lane % 8) ^ f8(r);
+      const int64_t kk = kb + u * 64 + 8 * c;
+      const int64_t d = k_end - kk;
+      const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
+      const u32x4 v = load_partial8(ptr(i, nk > 0 ? u : 0), s_k, nk);
+      *reinterpret_cast<u32x4*>(slot + (NI * wave + i) * 1024 + lane * 16) = v;
+    }
+  }
+};
+
+// DmaSource in SGPR-base form (same rows, slots and clamping).
+template <int NI, bool KMAJOR>
+struct BSourceS {
+  const char* base;  // byte address of (row r0, k kb) less kSBias
+  uint32_t off[NI];
+  int64_t step;      // bytes per 32-k step
+
+  __device__ __forceinline__ void init(const uint16_t* B, int64_t s_r, int64_t s_k, int64_t R_tot,
+                                       int64_t r0, int64_t kb, int wave, int lane) {
+    base = uniform_ptr((const char*)(B + r0 * s_r + kb * s_k) - kSBias);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      int64_t e;
+      if constexpr (KMAJOR) {
+        const int r = (NI * wave + i) * 16 + lane / 4;
+        const int c = (lane % 4) ^ fa(r);
+        int64_t rr = r0 + r;
+        if (rr > R_tot - 1) rr = R_tot - 1;
+        e = (rr - r0) * s_r + 8 * c * s_k;
+      } else {
+        const int k = (NI * wave + i) * 2 + lane / 32;
+        const int slot = lane % 32;
+        const int b = (slot / 2) ^ hb(k);
+        int64_t n = r0 + b * 16 + (slot % 2) * 8;
+        if (n > R_tot - 8) n = R_tot - 8;
+        e = (n - r0) * s_r + k * s_k;
+      }
+      off[i] = (uint32_t)(e * 2 + kSBias - 1024 * i);
+    }
+    step = (int64_t)64 * s_k;
+  }
+  __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
+    dma16s_batch<NI>(off, base + t * step, lds_wave);
+  }
+  __device__ __forceinline__ void fill_masked(char* lds_op, int wave, int lane, int64_t t,
+                                              int64_t kb, int64_t k_end, int64_t s_k) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint16_t* q = (const uint16_t*)(base + t * step + off[i] + 1024 * i);
+      u32x4 v;
+      if constexpr (KMAJOR) {
+        const int r = (NI * wave + i) * 16 + lane / 4;
+        const int c = (lane % 4) ^ fa(r);
+        const int64_t kk = kb + t * 32 + 8 * c;
+        const int64_t d = k_end - kk;
+        const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
+        v = load_partial8(q, s_k, nk);
+      } else {
+        const int k = (NI * wave + i) * 2 + lane / 32;
+        const bool ok = kb + t * 32 + k < k_end;
+        v = ok ? *reinterpret_cast<const u32x4*>(q) : zero4();
+      }
+      *reinterpret_cast<u32x4*>(lds_op + (NI * wave + i) * 1024 + lane * 16) = v;
     }
   }
 };
@@ -240,8 +387,8 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   const int fmv = mrem <= 0 ? 0 : (mrem >= CF::WTM ? CF::FM : (int)((mrem + 31) / 32));
   const bool edge = fnv < CF::FN || fmv < CF::FM;
 
-  ASource128<CF::DMA_A> sa;
-  std::conditional_t<BPACK, PackedBSource<CF::DMA_B>, DmaSource<CF::DMA_B, BKMAJOR>> sb;
+  ASourceS<CF::DMA_A> sa;
+  std::conditional_t<BPACK, PackedBSource<CF::DMA_B>, BSourceS<CF::DMA_B, BKMAJOR>> sb;
   sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, kb, wave, lane);
   sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, kb, wave, lane);
 
@@ -303,16 +450,25 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     read_frags_a128<CF, 0, BKMAJOR>(f0, slot_a(0), stage_b(0), 0, wm, wn, lane);
     if (g1) wg_barrier();
 
-    // One step: H is the step's half of its super-step u; the DMA of step
-    // t + 3 carries half H of super-step u + 2 (clamped to the last one).
-    auto step = [&](auto h_tag, auto e_tag, int64_t u, int64_t t, int64_t ua) {
+    // One step: H is the step's half of its super-step u, whose A super-slot
+    // is iu (i1, i2: those of u + 1 and u + 2); the DMA of step t + 3 carries
+    // half H of super-step u + 2 (clamped to the last one).  Slot indices
+    // rotate in 32-bit registers: a 64-bit modulo per step costs more issue
+    // slots than the memory phase has to spare.
+    const int ns = (int)nsup, nf2 = 2 * ns;
+    auto sl_a = [&](int i) { return smem + i * CF::A_SLOT; };
+    auto st_b = [&](int t) { return smem + CF::B_BASE + (t & (CF::B_STAGES - 1)) * CF::B_STAGE; };
+    const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::DMA_A * wave * 1024);
+    const uint32_t lb0 =
+        __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::B_BASE + CF::DMA_B * wave * 1024);
+    auto step = [&](auto h_tag, auto e_tag, int iu, int i1, int i2, int t, int ua) {
       constexpr int H = decltype(h_tag)::value;
       constexpr bool EDGE = decltype(e_tag)::value;
-      const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
+      const int tb = (t + 3 < nf2) ? t + 3 : nf2 - 1;
       // M(t)
-      read_frags_a128<CF, H, BKMAJOR>(f1, slot_a(u), stage_b(t), 1, wm, wn, lane);
-      sa.template issue_half<H>(lds_a(u + 2, H), ua);
-      sb.issue_batch(lds_b(t + 3), tb);
+      read_frags_a128<CF, H, BKMAJOR>(f1, sl_a(iu), st_b(t), 1, wm, wn, lane);
+      sa.template issue_half<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, ua);
+      sb.issue_batch(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, tb);
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
       wg_barrier();
@@ -321,8 +477,8 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
       // the last step.
       mma_frags_a128<CF, DT, EDGE>(f0, acc, fnv, fmv);
       __builtin_amdgcn_sched_barrier(0);
-      mma_and_read<CF, 1 - H, BKMAJOR, DT, EDGE>(f1, f0, acc, slot_a(H ? u + 1 : u), stage_b(t + 1),
-                                                 0, wm, wn, lane, fnv, fmv);
+      mma_and_read<CF, 1 - H, BKMAJOR, DT, EDGE>(f1, f0, acc, sl_a(H ? i1 : iu), st_b(t + 1), 0,
+                                                 wm, wn, lane, fnv, fmv);
       wait_vmcnt<CF::DMA_PER_STEP>();
       __builtin_amdgcn_sched_barrier(0);
       wg_barrier();
@@ -330,10 +486,14 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     };
     // Both loops pass the same barriers; the edge one skips empty blocks.
     auto run = [&](auto e_tag) {
-      for (int64_t u = 0; u < nsup; ++u) {
-        const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
-        step(std::integral_constant<int, 0>{}, e_tag, u, 2 * u, ua);
-        step(std::integral_constant<int, 1>{}, e_tag, u, 2 * u + 1, ua);
+      static_assert(CF::A_SLOTS == 3, "slot rotation");
+      int iu = 0;
+      for (int u = 0; u < ns; ++u) {
+        const int i1 = iu == 2 ? 0 : iu + 1, i2 = iu == 0 ? 2 : iu - 1;
+        const int ua = (u + 2 < ns) ? u + 2 : ns - 1;
+        step(std::integral_constant<int, 0>{}, e_tag, iu, i1, i2, 2 * u, ua);
+        step(std::integral_constant<int, 1>{}, e_tag, iu, i1, i2, 2 * u + 1, ua);
+        iu = i1;
       }
     };
     if (edge)

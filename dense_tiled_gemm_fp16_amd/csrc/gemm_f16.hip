@@ -16,6 +16,7 @@
 // bandwidth-bound problem).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -179,6 +180,10 @@ bool has_format(const TileInfo& t, int dt) {
   return false;
 }
 
+int64_t max_stride(const Call& c) {
+  return std::max(std::max(c.lda_m, c.lda_k), std::max(c.ldb_k, c.ldb_n));
+}
+
 int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   int rc = check_opts(o);
   if (rc) return rc;
@@ -296,7 +301,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   for (;;) {
     const TileInfo& t = tile_info(p.tile_id);
     const bool ok = t.final_fn[c.dt][p.a_path * 3 + p.b_path] != nullptr &&
-                    !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult));
+                    !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult)) &&
+                    !(t.max_k && c.K > t.max_k) && !(t.max_ld && max_stride(c) > t.max_ld);
     if (ok) break;
     // fp16 tiles hand over along their fallback chain; bfloat16 goes straight
     // to the 128x128 tile, which covers every layout in both formats.
@@ -611,7 +617,8 @@ int grouped_plan(const GroupCall& c, int* tile_id, kfn_t* fn, int64_t* grid) {
   int id = TILE_T128;
   const TileInfo& d = tile_info(TILE_DMA256A128);
   if (ldb_g_ok && c.M >= (int64_t)256 * c.G && d.grouped_fn[a_path * 3 + b_path] &&
-      !(b_path == PATH_RVEC && (c.N % d.n_mult != 0 || c.N < d.n_mult)))
+      !(b_path == PATH_RVEC && (c.N % d.n_mult != 0 || c.N < d.n_mult)) && !(c.K > d.max_k) &&
+      !(std::max(std::max(c.lda_m, c.lda_k), std::max(c.ldb_k, c.ldb_n)) > d.max_ld))
     id = TILE_DMA256A128;
   const TileInfo& ti = tile_info(id);
   // Layout classes were taken on group 0's B; other groups share them only if
@@ -776,7 +783,7 @@ int gemm_f16_pack_b(const void* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int6
   int64_t spanB;
   if (!view_span(K, N, ldb_k, ldb_n, &spanB)) return GEMM_ERR_SHAPE;
   const size_t bytes = gemm_f16_packed_b_bytes(K, N);
-  if (bytes == 0) return GEMM_ERR_SHAPE;
+  if (bytes == 0 || K > tile_info(TILE_DMA256A128).max_k) return GEMM_ERR_SHAPE;
   if (((uintptr_t)Bp & 255u) != 0) return GEMM_ERR_WORKSPACE;
   const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(spanB + 1);
   if (ranges_overlap(b0, b1, (uintptr_t)Bp, (uintptr_t)Bp + bytes)) return GEMM_ERR_ALIAS;
@@ -801,9 +808,11 @@ int gemm_f16_packed(const void* A, int64_t lda_m, int64_t lda_k, const void* Bp,
   int64_t spanA, spanC;
   if (!view_span(M, K, lda_m, lda_k, &spanA) || !view_span(M, N, ldc, 1, &spanC)) return GEMM_ERR_SHAPE;
   const size_t bytes = gemm_f16_packed_b_bytes(K, N);
-  if (bytes == 0) return GEMM_ERR_SHAPE;
+  if (bytes == 0 || K > tile_info(TILE_DMA256A128).max_k) return GEMM_ERR_SHAPE;
   // The full-line-A tile's A path: K-contiguous, 16-byte aligned rows.
-  if (classify(A, lda_m, lda_k) != PATH_KVEC || ((uintptr_t)Bp & 255u) != 0) return GEMM_ERR_LAYOUT;
+  if (classify(A, lda_m, lda_k) != PATH_KVEC || ((uintptr_t)Bp & 255u) != 0 ||
+      lda_m > tile_info(TILE_DMA256A128).max_ld)
+    return GEMM_ERR_LAYOUT;
   const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(spanA + 1);
   const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(spanC + 1);
   const uintptr_t p0 = (uintptr_t)Bp, p1 = p0 + bytes;

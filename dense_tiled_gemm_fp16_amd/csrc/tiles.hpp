@@ -43,6 +43,8 @@ struct TileInfo {
   kfn_t packed_fn;         // pre-packed B, K-contiguous A, fp16 (nullptr: none)
   int fallback;         // tile used for layouts this one does not support
   int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
+  int64_t max_k;        // largest K the tile's 32-bit step counters cover (0 = any)
+  int64_t max_ld;       // largest element stride its 32-bit lane offsets cover (0 = any)
 };
 
 template <class CF, bool P, bool G = false, int DT = DT_F16>
@@ -59,6 +61,8 @@ void fill_fns(kfn_t* f) {
 }
 
 inline void clear_fns(TileInfo& t) {
+  t.max_k = 0;
+  t.max_ld = 0;
   for (int d = 0; d < NDT; ++d)
     for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
   for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
@@ -129,6 +133,8 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   t.packed_fn = gemm_dma_a128_kernel<CF, true, false, false, DT_F16, true>;
   t.fallback = fallback;
   t.n_mult = 8;
+  t.max_k = INT64_C(1) << 36;   // 64-k super-steps counted in int
+  t.max_ld = INT64_C(1) << 23;  // 255 rows * 2^23 * 2 bytes + bias < 2^32
   return t;
 }
 

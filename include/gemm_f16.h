@@ -74,7 +74,8 @@ enum gemm_status {
  * workspace, and a fix-up launch sums each output's ranges in ascending
  * order (no atomics, bit-reproducible for a given plan).  It needs the
  * 256x256 LDS-DMA tile (K-contiguous A; N-contiguous B with N % 8 == 0, or
- * K-contiguous B); forcing it for other layouts returns GEMM_ERR_OPTS.
+ * K-contiguous B; every stride at most 2^23 elements); forcing it for other
+ * layouts returns GEMM_ERR_OPTS.
  * AUTO picks it when the partial wave is at most half full and K >= 2048. */
 enum gemm_variant {
   GEMM_VARIANT_AUTO = 0,    /* choose from the shape (the default)                */
@@ -222,8 +223,10 @@ size_t gemm_f8_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_o
  * 256-column panels of ceil(K/32) blocks of 16 KiB, each block the LDS image
  * of one K-major B stage of the 256 x 256 LDS-DMA tile, zero past N and K.
  * gemm_f16_packed computes C := A.B from A (K-contiguous, 16-byte aligned
- * rows: GEMM_ERR_LAYOUT otherwise) and Bp packed for the same K and N, on
- * the main variant of that tile (no split, no workspace).  Both are
+ * rows at most 2^23 elements apart: GEMM_ERR_LAYOUT otherwise) and Bp
+ * packed for the same K and N, on the main variant of that tile (no split,
+ * no workspace; K above 2^36 is GEMM_ERR_SHAPE, as that tile counts its
+ * 64-k steps in 32 bits).  Both are
  * asynchronous on `stream`; other return codes as gemm_f16.  The packed
  * buffer's layout is private to this library version.
  */

@@ -339,6 +339,46 @@ def test_offsets_of_2_pow_32_elements():
     assert torch.all(cbuf[N:N + 8] == 7.0) and torch.all(cbuf[big - 8:big] == 7.0)
 
 
+def _rows_at(bits, ld):
+    """fp16 bits [R, C] into a NaN buffer with row stride ld (elements)."""
+    R, C = bits.shape
+    buf = dev_nan((R - 1) * ld + C + 8)
+    v = torch.as_strided(buf, (R, C), (ld, 1))
+    v.copy_(to_dev(bits))
+    return buf, v
+
+
+@pytest.mark.parametrize("which", ["A", "B_n", "B_k"])
+def test_dma_tile_stride_limit(which):
+    """The 256x256 LDS-DMA tile addresses its operands with 32-bit lane
+    offsets over 256 rows: at a row stride of 2^23 elements (lane offsets up
+    to 255 * 2^24 bytes, just under 2^32) it still runs, with the last tile
+    row clamped; one step past the limit the plan hands over to another
+    tile.  Integer inputs, bit-exact against the oracle."""
+    M, N, K = 257, 264, 96
+    A = synth.matrix(M, K, 16000, 0, "int")
+    B = synth.matrix(K, N, 16001, 1, "int")
+    ref = reference(A, B)
+    lim = 1 << 23
+    for ld, dma in ((lim, True), (lim + 8, False)):
+        if which == "A":
+            buf, a = _rows_at(A, ld)
+            b = to_dev(B)
+        elif which == "B_n":           # N-contiguous B, k-rows ld apart
+            buf, b = _rows_at(B, ld)
+            a = to_dev(A)
+        else:                          # K-contiguous B stored [N, K], n-rows ld apart
+            buf, bt = _rows_at(np.ascontiguousarray(B.T), ld)
+            b = bt.t()
+            a = to_dev(A)
+        kw = dict(variant="main", tile=14)
+        p = g.plan(a, b, **kw)
+        assert (p["tile_id"] == 14) == dma, (which, ld, p)
+        check(run(a, b, **kw), ref, "int", f"{which} stride {ld} plan {p}")
+        del buf, a, b
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ properties
 
 def test_repeat_runs_are_bit_identical():
