@@ -258,18 +258,19 @@ struct BSourceS {
 // bytes and the K tail needs no masks.  s_r is the panel stride in elements.
 template <int NI>
 struct PackedBSource {
-  const uint16_t* p[NI];
-  static constexpr int64_t step = 8192;  // elements per 32-k block
+  const char* base;  // byte address of this tile's first block less kSBias
+  uint32_t off[NI];  // all equal: 1 KiB per instruction is the batch offset
+  static constexpr int64_t step = 16384;  // bytes per 32-k block
 
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t s_r, int64_t, int64_t,
+  __device__ __forceinline__ void init(const uint16_t* B, int64_t s_r, int64_t, int64_t,
                                        int64_t r0, int64_t kb, int wave, int lane) {
+    base = uniform_ptr((const char*)(B + (r0 / 256) * s_r + (kb / 32) * 8192) - kSBias);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      p[i] = base + (r0 / 256) * s_r + (kb / 32) * step + (NI * wave + i) * 512 + lane * 8;
+    for (int i = 0; i < NI; ++i) off[i] = (uint32_t)(NI * wave * 1024 + lane * 16 + kSBias);
   }
 
   __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
-    dma16_batch<NI>(p, t * step, lds_wave);
+    dma16s_batch<NI>(off, base + t * step, lds_wave);
   }
 
   // The block of step t as it lies (its K tail is already zero).
@@ -278,7 +279,7 @@ struct PackedBSource {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<u32x4*>(lds_op + (NI * wave + i) * 1024 + lane * 16) =
-          *reinterpret_cast<const u32x4*>(p[i] + t * step);
+          *reinterpret_cast<const u32x4*>(base + t * step + off[i] + 1024 * i);
   }
 };
 

@@ -135,8 +135,8 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
   const bool edge = fnv < CF::FN || fmv < CF::FM;
 
   // Byte-pair views for the DMA: strides and K offsets halve.
-  ASource128<CF::DMA_A> sa;
-  DmaSource<CF::DMA_B, true> sb;
+  ASourceS<CF::DMA_A> sa;
+  BSourceS<CF::DMA_B, true> sb;
   sa.init(a.A, a.lda_m / 2, 1, a.M, m0, kb / 2, wave, lane);
   sb.init(a.B, a.ldb_n / 2, 1, a.N, n0, kb / 2, wave, lane);
 
@@ -182,17 +182,24 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     f.fa_[1] = read_b_f8(stage_b(0), 1, wn, lane);
     if (g1) wg_barrier();
 
-    auto step = [&](auto h_tag, auto e_tag, int64_t u, int64_t t, int64_t ua) {
+    // Slot indices rotate in 32-bit registers, as in the fp16 kernel.
+    const int ns = (int)nsup, nf2 = 2 * ns;
+    auto sl_a = [&](int i) { return smem + i * CF::A_SLOT; };
+    auto st_b = [&](int t) { return smem + CF::B_BASE + (t & (CF::B_STAGES - 1)) * CF::B_STAGE; };
+    const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::DMA_A * wave * 1024);
+    const uint32_t lb0 =
+        __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::B_BASE + CF::DMA_B * wave * 1024);
+    auto step = [&](auto h_tag, auto e_tag, int iu, int i2, int t, int ua) {
       constexpr int H = decltype(h_tag)::value;
       constexpr bool EDGE = decltype(e_tag)::value;
-      const int64_t tb = (t + 3 < nfull2) ? t + 3 : nfull2 - 1;
+      const int tb = (t + 3 < nf2) ? t + 3 : nf2 - 1;
       // M(t)
-      f.fb_[0] = read_a_f8(slot_a(u), H, 0, wm, lane);
-      f.fb_[1] = read_a_f8(slot_a(u), H, 1, wm, lane);
-      f.fa_[2] = read_b_f8(stage_b(t), 2, wn, lane);
-      f.fa_[3] = read_b_f8(stage_b(t), 3, wn, lane);
-      sa.template issue_half<H>(lds_a(u + 2, H), ua);
-      sb.issue_batch(lds_b(t + 3), tb);
+      f.fb_[0] = read_a_f8(sl_a(iu), H, 0, wm, lane);
+      f.fb_[1] = read_a_f8(sl_a(iu), H, 1, wm, lane);
+      f.fa_[2] = read_b_f8(st_b(t), 2, wn, lane);
+      f.fa_[3] = read_b_f8(st_b(t), 3, wn, lane);
+      sa.template issue_half<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, ua);
+      sb.issue_batch(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, tb);
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
       wg_barrier();
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       // C(t); on the last step the reads fetch unused bytes of a free stage.
       mma_f8<FA, FB, EDGE>(f, acc, 0, 2, fnv, fmv);
       __builtin_amdgcn_sched_barrier(0);
-      const char* nb = stage_b(t + 1);
+      const char* nb = st_b(t + 1);
 #pragma unroll
       for (int i = 2; i < CF::FN; ++i)
 #pragma unroll
@@ -215,10 +222,14 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     auto run = [&](auto e_tag) {
-      for (int64_t u = 0; u < nsup; ++u) {
-        const int64_t ua = (u + 2 < nsup) ? u + 2 : nsup - 1;
-        step(std::integral_constant<int, 0>{}, e_tag, u, 2 * u, ua);
-        step(std::integral_constant<int, 1>{}, e_tag, u, 2 * u + 1, ua);
+      static_assert(CF::A_SLOTS == 3, "slot rotation");
+      int iu = 0;
+      for (int u = 0; u < ns; ++u) {
+        const int i1 = iu == 2 ? 0 : iu + 1, i2 = iu == 0 ? 2 : iu - 1;
+        const int ua = (u + 2 < ns) ? u + 2 : ns - 1;
+        step(std::integral_constant<int, 0>{}, e_tag, iu, i2, 2 * u, ua);
+        step(std::integral_constant<int, 1>{}, e_tag, iu, i2, 2 * u + 1, ua);
+        iu = i1;
       }
     };
     if (edge)

@@ -202,8 +202,10 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   // tile, in the main, split-K and stream-K families only.
   const bool f8 = c.dt >= DT_F8;
   if (f8) {
+    // Row strides up to 2^24 bytes: the DMA's 32-bit lane offsets span 255 rows.
     if (c.lda_k != 1 || c.lda_m % 16 != 0 || ((uintptr_t)c.A & 15u) || c.ldb_k != 1 ||
-        c.ldb_n % 16 != 0 || ((uintptr_t)c.B & 15u))
+        c.ldb_n % 16 != 0 || ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) ||
+        c.ldb_n > (INT64_C(1) << 24))
       return GEMM_ERR_LAYOUT;
     if (variant == GEMM_VARIANT_SKINNY || variant == GEMM_VARIANT_TILE64X32 ||
         (want_tile && want_tile != TILE_F8))

@@ -141,26 +141,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 
   for (int64_t c0 = kb; c0 < ke; c0 += kGemvChunk) {
     const int cl = (ke - c0 < kGemvChunk) ? (int)(ke - c0) : kGemvChunk;
+    const uint16_t* p0 = bcol + c0 * a.ldb_k;
+    // The chunk's first two passes of B are issued before A is staged, so
+    // the round trip of the A loads hides under the B stream instead of
+    // preceding it.
+    u32x4 v0[RPT], v1[RPT];
+    if (nvalid == 8) {
+      load_rows<RPT>(v0, p0, a.ldb_k, rg * RPT, cl);
+      load_rows<RPT>(v1, p0, a.ldb_k, rg * RPT + 8 * RPT, cl);
+    }
     if (c0 != kb) __syncthreads();  // the previous chunk's readers are done
 #pragma unroll
     for (int m = 0; m < MT; ++m)
       for (int j = tid; j < kGemvChunk; j += 256)
         As[m][j] = (m < a.M && j < cl) ? a.A[m * a.lda_m + (c0 + j) * a.lda_k] : (uint16_t)0;
     __syncthreads();
-
-    const uint16_t* p0 = bcol + c0 * a.ldb_k;
     if (nvalid == 8) {
-      // Two passes in flight: the next pass's loads are issued before this
-      // pass's arithmetic.
-      u32x4 v0[RPT], v1[RPT];
-      int j0 = rg * RPT;
-      load_rows<RPT>(v0, p0, a.ldb_k, j0, cl);
-      for (; j0 < cl; j0 += 16 * RPT) {
-        load_rows<RPT>(v1, p0, a.ldb_k, j0 + 8 * RPT, cl);
+      // Two passes in flight: the pass after next is issued before this
+      // pass's arithmetic.  Rows are added in ascending order.
+      for (int j0 = rg * RPT; j0 < cl; j0 += 16 * RPT) {
         fma_rows<MT, RPT, DT>(acc, v0, As, j0);
         if (j0 + 8 * RPT >= cl) break;
-        load_rows<RPT>(v0, p0, a.ldb_k, j0 + 16 * RPT, cl);
+        if (j0 + 16 * RPT < cl) load_rows<RPT>(v0, p0, a.ldb_k, j0 + 16 * RPT, cl);
         fma_rows<MT, RPT, DT>(acc, v1, As, j0 + 8 * RPT);
+        if (j0 + 24 * RPT < cl) load_rows<RPT>(v1, p0, a.ldb_k, j0 + 24 * RPT, cl);
       }
     } else if (nvalid > 0) {
       // The ragged last vector of a row: element loads, one pass at a time.

@@ -195,6 +195,8 @@ def test_f8_rejected_before_any_device_work():
     assert f8call(lda_m=72) == -9                       # A rows not 16-byte aligned
     assert f8call(ldb_n=40) == -9
     assert f8call(A=PA + 8) == -9
+    assert f8call(lda_m=(1 << 24) + 16) == -9           # rows over 2^24 bytes apart
+    assert f8call(ldb_n=(1 << 24) + 16) == -9
     assert f8call(fa=2) == -7 and f8call(fb=-1) == -7   # formats 0 (E4M3) and 1 (E5M2)
     assert f8call(opts=_lib.Opts(2, 0, 0, 0)) == -7     # no skinny FP8 path
     assert f8call(opts=_lib.Opts(4, 0, 0, 0)) == -7
@@ -233,5 +235,6 @@ def test_packed_b_rejected_before_any_device_work():
     run = g.lib.gemm_f16_packed
     assert run(PA, 100, 1, PW, PC, 300, 50, 300, 100, 0) == -9      # A rows not 16-byte multiples
     assert run(PA, 1, 50, PW, PC, 300, 50, 300, 100, 0) == -9       # A not K-contiguous
+    assert run(PA, (1 << 23) + 8, 1, PW, PC, 300, 50, 300, 100, 0) == -9   # rows over 2^23 apart
     assert run(PA, 112, 1, PW, PC, 299, 50, 300, 100, 0) == -4
     assert run(PA, 112, 1, PW, PW + 1024, 300, 50, 300, 100, 0) == -5   # C overlaps Bp

@@ -109,3 +109,20 @@ def test_f8_moe_shape_sampled():
     rng = np.random.default_rng(14300)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
     assert_close(got[rows], reference(A, Bt, "e4m3", "e4m3", rows), "f8 MoE sampled rows")
+
+
+def test_f8_stride_limit():
+    # A rows 2^24 bytes apart, the largest stride the FP8 tile takes: lane
+    # offsets of the DMA reach 255 * 2^24 bytes, just under 2^32; the last
+    # tile row is clamped (M = 257).  Integer inputs, bit-exact.
+    M, N, K = 257, 264, 192
+    A, Bt = inputs(M, N, K, 14400, "int", "e4m3", "e4m3")
+    ref = reference(A, Bt, "e4m3", "e4m3")
+    ld = 1 << 24
+    buf = torch.full(((M - 1) * ld + K + 16,), 0x7F, dtype=torch.uint8, device=DEV)
+    a8 = torch.as_strided(buf, (M, K), (ld, 1))
+    a8.copy_(torch.from_numpy(A).to(DEV))
+    a = a8.view(torch.float8_e4m3fn)
+    b = f8_rows(Bt, "e4m3").t()
+    got = run(a, b, Out(M, N), variant="main")
+    assert_bits_equal(got, ref, "f8 lda_m = 2^24")
