@@ -68,51 +68,6 @@ struct DmaA128Cfg {
 
 __device__ __forceinline__ int f8(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Per-lane sources of this wave's NI A instructions of a super-step:
-// instruction i covers rows (NI w + i) * 8 .. +8; lane l -> row +l/8, 16-byte
-// slot l%8 -> octet (l%8) ^ f8(row).  Rows past M read the last valid row.
-template <int NI>
-struct ASource128 {
-  const uint16_t* p[NI];
-  int64_t step;  // elements per 64-k super-step
-
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t s_r, int64_t s_k,
-                                       int64_t R_tot, int64_t r0, int64_t kb, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (NI * wave + i) * 8 + lane / 8;
-      const int c = (lane % 8) ^ f8(r);
-      int64_t rr = r0 + r;
-      if (rr > R_tot - 1) rr = R_tot - 1;
-      p[i] = base + rr * s_r + (kb + 8 * c) * s_k;
-    }
-    step = (int64_t)64 * s_k;
-  }
-
-  // Instructions H*NI/2 .. of super-step u into LDS at lds (the slot's byte
-  // address of the first of them for this wave).
-  template <int H>
-  __device__ __forceinline__ void issue_half(uint32_t lds, int64_t u) {
-    dma16_batch<NI / 2>(&p[H * (NI / 2)], u * step, lds);
-  }
-
-  // Masked register fill of the 64 k from k0 (k < k_end kept, zero fill)
-  // into the same LDS bytes the DMA would write.
-  __device__ __forceinline__ void fill_masked(char* slot, int wave, int lane, int64_t u, int64_t kb,
-                                              int64_t k_end, int64_t s_k) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (NI * wave + i) * 8 + lane / 8;
-      const int c = (lane % 8) ^ f8(r);
-      const int64_t kk = kb + u * 64 + 8 * c;
-      const int64_t d = k_end - kk;
-      const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
-      const u32x4 v = load_partial8(p[i] + (nk > 0 ? u * step : 0), s_k, nk);
-      *reinterpret_cast<u32x4*>(slot + (NI * wave + i) * 1024 + lane * 16) = v;
-    }
-  }
-};
-
 // global_load_lds_dwordx4 in its SGPR-base form: a uniform 64-bit base and a
 // 32-bit per-lane byte offset, so a step's DMA needs no 64-bit VALU address
 // arithmetic.  As in dma16_batch, the instruction offset (1024 j for the j-th
@@ -153,7 +108,9 @@ __device__ __forceinline__ void dma16s_batch(const uint32_t* off, const char* ba
 // biased offsets (down to -3072) stay non-negative.
 constexpr int kSBias = 4096;
 
-// ASource128 in SGPR-base form (same rows, slots and clamping).
+// Per-lane sources of this wave's NI A instructions of a super-step:
+// instruction i covers rows (NI w + i) * 8 .. +8; lane l -> row +l/8, 16-byte
+// slot l%8 -> octet (l%8) ^ f8(row).  Rows past M read the last valid row.
 template <int NI>
 struct ASourceS {
   const char* base;  // byte address of (row r0, k kb) less kSBias
@@ -176,6 +133,11 @@ struct ASourceS {
   template <int H>
   __device__ __forceinline__ void issue_half(uint32_t lds, int64_t u) {
     dma16s_batch<NI / 2>(&off[H * (NI / 2)], base + u * step, lds);
+  }
+  // Same, from a super-step base the caller advances (base + u * step).
+  template <int H>
+  __device__ __forceinline__ void issue_half_at(uint32_t lds, const char* b) {
+    dma16s_batch<NI / 2>(&off[H * (NI / 2)], b, lds);
   }
   __device__ __forceinline__ const uint16_t* ptr(int i, int64_t u) const {
     return (const uint16_t*)(base + u * step + off[i] + 1024 * (i % (NI / 2)));
@@ -229,6 +191,10 @@ struct BSourceS {
   __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
     dma16s_batch<NI>(off, base + t * step, lds_wave);
   }
+  // Same, from a step base the caller advances (base + t * step).
+  __device__ __forceinline__ void issue_batch_at(uint32_t lds_wave, const char* b) {
+    dma16s_batch<NI>(off, b, lds_wave);
+  }
   __device__ __forceinline__ void fill_masked(char* lds_op, int wave, int lane, int64_t t,
                                               int64_t kb, int64_t k_end, int64_t s_k) {
 #pragma unroll
@@ -271,6 +237,9 @@ struct PackedBSource {
 
   __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
     dma16s_batch<NI>(off, base + t * step, lds_wave);
+  }
+  __device__ __forceinline__ void issue_batch_at(uint32_t lds_wave, const char* b) {
+    dma16s_batch<NI>(off, b, lds_wave);
   }
 
   // The block of step t as it lies (its K tail is already zero).
@@ -462,14 +431,18 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::DMA_A * wave * 1024);
     const uint32_t lb0 =
         __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::B_BASE + CF::DMA_B * wave * 1024);
-    auto step = [&](auto h_tag, auto e_tag, int iu, int i1, int i2, int t, int ua) {
+    // DMA source bases of super-step u + 2 and step t + 3 (each clamped to
+    // the last one), advanced in place rather than multiplied out.
+    const char* pa = sa.base + (int64_t)(ns > 2 ? 2 : ns - 1) * sa.step;
+    const char* pb = sb.base + (int64_t)(nf2 > 3 ? 3 : nf2 - 1) * sb.step;
+    auto step = [&](auto h_tag, auto e_tag, int iu, int i1, int i2, int t) {
       constexpr int H = decltype(h_tag)::value;
       constexpr bool EDGE = decltype(e_tag)::value;
-      const int tb = (t + 3 < nf2) ? t + 3 : nf2 - 1;
       // M(t)
       read_frags_a128<CF, H, BKMAJOR>(f1, sl_a(iu), st_b(t), 1, wm, wn, lane);
-      sa.template issue_half<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, ua);
-      sb.issue_batch(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, tb);
+      sa.template issue_half_at<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, pa);
+      sb.issue_batch_at(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, pb);
+      if (t + 4 < nf2) pb += sb.step;
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
       wg_barrier();
@@ -491,9 +464,9 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
       int iu = 0;
       for (int u = 0; u < ns; ++u) {
         const int i1 = iu == 2 ? 0 : iu + 1, i2 = iu == 0 ? 2 : iu - 1;
-        const int ua = (u + 2 < ns) ? u + 2 : ns - 1;
-        step(std::integral_constant<int, 0>{}, e_tag, iu, i1, i2, 2 * u, ua);
-        step(std::integral_constant<int, 1>{}, e_tag, iu, i1, i2, 2 * u + 1, ua);
+        step(std::integral_constant<int, 0>{}, e_tag, iu, i1, i2, 2 * u);
+        step(std::integral_constant<int, 1>{}, e_tag, iu, i1, i2, 2 * u + 1);
+        if (u + 3 < ns) pa += sa.step;
         iu = i1;
       }
     };

@@ -189,17 +189,19 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::DMA_A * wave * 1024);
     const uint32_t lb0 =
         __builtin_amdgcn_readfirstlane(lds_addr(smem) + CF::B_BASE + CF::DMA_B * wave * 1024);
-    auto step = [&](auto h_tag, auto e_tag, int iu, int i2, int t, int ua) {
+    const char* pa = sa.base + (int64_t)(ns > 2 ? 2 : ns - 1) * sa.step;
+    const char* pb = sb.base + (int64_t)(nf2 > 3 ? 3 : nf2 - 1) * sb.step;
+    auto step = [&](auto h_tag, auto e_tag, int iu, int i2, int t) {
       constexpr int H = decltype(h_tag)::value;
       constexpr bool EDGE = decltype(e_tag)::value;
-      const int tb = (t + 3 < nf2) ? t + 3 : nf2 - 1;
       // M(t)
       f.fb_[0] = read_a_f8(sl_a(iu), H, 0, wm, lane);
       f.fb_[1] = read_a_f8(sl_a(iu), H, 1, wm, lane);
       f.fa_[2] = read_b_f8(st_b(t), 2, wn, lane);
       f.fa_[3] = read_b_f8(st_b(t), 3, wn, lane);
-      sa.template issue_half<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, ua);
-      sb.issue_batch(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, tb);
+      sa.template issue_half_at<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, pa);
+      sb.issue_batch_at(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, pb);
+      if (t + 4 < nf2) pb += sb.step;
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
       wg_barrier();
@@ -226,9 +228,9 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       int iu = 0;
       for (int u = 0; u < ns; ++u) {
         const int i1 = iu == 2 ? 0 : iu + 1, i2 = iu == 0 ? 2 : iu - 1;
-        const int ua = (u + 2 < ns) ? u + 2 : ns - 1;
-        step(std::integral_constant<int, 0>{}, e_tag, iu, i2, 2 * u, ua);
-        step(std::integral_constant<int, 1>{}, e_tag, iu, i2, 2 * u + 1, ua);
+        step(std::integral_constant<int, 0>{}, e_tag, iu, i2, 2 * u);
+        step(std::integral_constant<int, 1>{}, e_tag, iu, i2, 2 * u + 1);
+        if (u + 3 < ns) pa += sa.step;
         iu = i1;
       }
     };
