@@ -180,9 +180,27 @@ bool has_format(const TileInfo& t, int dt) {
   return false;
 }
 
+// Fewer 256x256 tiles than half a wave and a long K: every tile goes to the
+// stream-K tail, cut into about cus / tiles K ranges, rather than to the
+// 128x128 register-path tile (2048 x 2048 x 8192 ran 1.8x faster so; at
+// K = 2048 the main plan was still ahead).
+bool small_grid_streamk(const Call& c, int64_t t256, int cus) {
+  return 2 * t256 < cus && c.K >= 3072 && c.M >= 256 && c.N >= 256;
+}
+
 int64_t max_stride(const Call& c) {
   return std::max(std::max(c.lda_m, c.lda_k), std::max(c.ldb_k, c.ldb_n));
 }
+
+// Whether a tile's kernels take this call's format and layout (needs
+// p.a_path and p.b_path).
+bool tile_takes(const TileInfo& t, const Call& c, const Plan& p) {
+  return t.final_fn[c.dt][p.a_path * 3 + p.b_path] != nullptr &&
+         !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult)) &&
+         !(t.max_k && c.K > t.max_k) && !(t.max_ld && max_stride(c) > t.max_ld);
+}
+
+bool dma_tile_takes(const Call& c, const Plan& p) { return tile_takes(tile_info(TILE_DMA256A128), c, p); }
 
 int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   int rc = check_opts(o);
@@ -245,10 +263,13 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
       } else if (want_tile) {
         p.tile_id = want_tile;
       } else {
-        // 256x256 tiles once they give at least half a wave of workgroups.
+        // 256x256 tiles once they give at least half a wave of workgroups,
+        // or, with a long K, when the stream-K plan below spreads fewer of
+        // them over the compute units (the layout permitting).
         if ((rc = need_cus())) return rc;
         const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
-        p.tile_id = (2 * t256 >= cus) ? TILE_DMA256A128 : TILE_T128;
+        p.tile_id = (2 * t256 >= cus || (small_grid_streamk(c, t256, cus) && dma_tile_takes(c, p)))
+                        ? TILE_DMA256A128 : TILE_T128;
       }
       break;
     case GEMM_VARIANT_SPLITK:
@@ -302,10 +323,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   // N a multiple of 8).
   for (;;) {
     const TileInfo& t = tile_info(p.tile_id);
-    const bool ok = t.final_fn[c.dt][p.a_path * 3 + p.b_path] != nullptr &&
-                    !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult)) &&
-                    !(t.max_k && c.K > t.max_k) && !(t.max_ld && max_stride(c) > t.max_ld);
-    if (ok) break;
+    if (tile_takes(t, c, p)) break;
     // fp16 tiles hand over along their fallback chain; bfloat16 goes straight
     // to the 128x128 tile, which covers every layout in both formats.
     p.tile_id = c.dt == DT_F16 ? t.fallback : TILE_T128;
@@ -322,7 +340,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
     // workgroup fits a compute unit, so a wave is `cus` tiles).
     if ((rc = need_cus())) return rc;
     const int64_t tail = T % cus;
-    if (T >= cus && tail > 0 && 2 * tail <= cus) p.variant = GEMM_VARIANT_STREAMK;
+    if ((T >= cus && tail > 0 && 2 * tail <= cus) || small_grid_streamk(c, T, cus))
+      p.variant = GEMM_VARIANT_STREAMK;
   }
   if (p.variant == GEMM_VARIANT_STREAMK) {
     if ((rc = need_cus())) return rc;

@@ -76,7 +76,9 @@ enum gemm_status {
  * 256x256 LDS-DMA tile (K-contiguous A; N-contiguous B with N % 8 == 0, or
  * K-contiguous B; every stride at most 2^23 elements); forcing it for other
  * layouts returns GEMM_ERR_OPTS.
- * AUTO picks it when the partial wave is at most half full and K >= 2048. */
+ * AUTO picks it when the partial wave is at most half full and K >= 2048,
+ * and, with every tile in the tail, when all the 256x256 tiles together fill
+ * less than half a wave, K >= 3072 and M, N >= 256. */
 enum gemm_variant {
   GEMM_VARIANT_AUTO = 0,    /* choose from the shape (the default)                */
   GEMM_VARIANT_MAIN = 1,    /* one workgroup per output tile, whole K            */

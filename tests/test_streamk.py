@@ -118,3 +118,27 @@ def test_streamk_bf16():
     torch.cuda.synchronize()
     got = c.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     assert_bits_equal(got, ref, "stream-K bf16 integer inputs")
+
+
+def test_streamk_auto_small_grid():
+    # 6 x 6 = 36 tiles of 256 x 256, under half a wave, with a long K: the
+    # automatic plan sends every tile to the stream-K tail rather than to the
+    # 128 x 128 tile.  Integer inputs keep every fp32 sum exact (|sum| <= 16 K
+    # < 2^24), so the result must equal the main plan's and the oracle's bit
+    # for bit; sampled rows against the oracle, including the last tile row.
+    M, N, K = 1536, 1536, 8192
+    W = cus()
+    A = synth.matrix(M, K, 13400, 0, "int")
+    B = synth.matrix(K, N, 13401, 1, "int")
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    if 2 * 36 >= W:
+        pytest.skip(f"{W} compute units: 36 tiles are at least half a wave")
+    assert (p["variant"], p["tile_id"], p["sk_tiles"], p["grid"]) == ("streamk", 14, 36, 0), p
+    say(f"stream-K small-grid auto plan {p}")
+    got = to_host(g.gemm(a, b))
+    main = to_host(g.gemm(a, b, variant="main", tile=1))
+    torch.cuda.synchronize()
+    assert_bits_equal(got, main, "stream-K small grid vs 128x128 main")
+    rows = np.array([0, 1, 255, 256, 777, 1279, 1280, 1535])
+    assert_bits_equal(got[rows], reference(A, B, rows), "stream-K small grid sampled rows")
