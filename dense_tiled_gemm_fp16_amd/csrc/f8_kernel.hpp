@@ -204,10 +204,13 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       if (t + 4 < nf2) pb += sb.step;
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
+      // C(t), its first MFMA ahead of the barrier as in the fp16 kernel; on
+      // the last step the reads fetch unused bytes of a free stage.
+      if (!EDGE || (0 < fnv && 0 < fmv)) acc[0][0] = mfma_f8<FA, FB>(f.fa_[0], f.fb_[0], acc[0][0]);
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // C(t); on the last step the reads fetch unused bytes of a free stage.
-      mma_f8<FA, FB, EDGE>(f, acc, 0, 2, fnv, fmv);
+      if (!EDGE || (0 < fnv && 1 < fmv)) acc[0][1] = mfma_f8<FA, FB>(f.fa_[0], f.fb_[1], acc[0][1]);
+      mma_f8<FA, FB, EDGE>(f, acc, 1, 2, fnv, fmv);
       __builtin_amdgcn_sched_barrier(0);
       const char* nb = st_b(t + 1);
 #pragma unroll
