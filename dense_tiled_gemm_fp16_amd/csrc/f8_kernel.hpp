@@ -204,8 +204,10 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       if (t + 4 < nf2) pb += sb.step;
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
-      // C(t), its first MFMA ahead of the barrier as in the fp16 kernel; on
-      // the last step the reads fetch unused bytes of a free stage.
+      // C(t), at raised issue priority and with its first MFMA ahead of the
+      // barrier, as in the fp16 kernel; on the last step the reads fetch
+      // unused bytes of a free stage.
+      __builtin_amdgcn_s_setprio(1);
       if (!EDGE || (0 < fnv && 0 < fmv)) acc[0][0] = mfma_f8<FA, FB>(f.fa_[0], f.fb_[0], acc[0][0]);
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -223,6 +225,7 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
         }
       wait_vmcnt<CF::DMA_PER_STEP>();
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
