@@ -10,9 +10,11 @@
 // byte holds changes: a super-step is 128 k and a step 64 k, and each 32 x 32
 // block of a step is one v_mfma_f32_32x32x64_f8f6f4 (formats as immediates).
 //
-// Operands are K-contiguous (A [M, K] row-major; B given as [N, K] rows, i.e.
-// a transposed view), so the DMA moves pairs of bytes with the 16-bit
-// helpers (views with half the row stride).  A lane's 32 operand bytes are
+// A is K-contiguous (A [M, K] row-major).  B is K-contiguous (given as
+// [N, K] rows, i.e. a transposed view), when the DMA moves pairs of bytes
+// with the 16-bit helpers (views with half the row stride), or, in the BN
+// kernels, N-contiguous (B [K, N] row-major): 64 k-rows of 256 bytes per
+// stage, read back with the 8-bit transposing LDS read (read_b_f8_n).  A lane's 32 operand bytes are
 // k = 32 g .. 32 g + 31 of the step for lane group g = lane / 32, for A and B
 // alike: the matrix instruction pairs byte b of the A operand with byte b of
 // the B operand, so any assignment of k to bytes that both operands share is
@@ -74,6 +76,85 @@ __device__ __forceinline__ i32x8 read_b_f8(const char* tb, int i, int wn, int la
                *reinterpret_cast<const u32x4*>(row + (((c + 1) ^ fa(r)) * 16)));
 }
 
+// N-contiguous B (B [K, N] row-major, BN kernels).  A stage is 64 k-rows of
+// 256 bytes; the 16-byte chunk of columns 16c .. 16c+15 of k-row k sits at
+// chunk c ^ h8(k), so that the transposing reads of 8 consecutive k-rows hit
+// 16 distinct chunks (all 64 banks) per half wave.
+__device__ __forceinline__ int h8(int k) { return 2 * (k & 7); }
+
+// Per-lane sources of this wave's NI DMA instructions of an N-major B step:
+// instruction i covers k-rows (NI w + i) * 4 .. +4, lane l -> k-row +l/16,
+// LDS chunk l%16 <- global column chunk (l%16) ^ h8(k-row).  A chunk wholly
+// past N reads any valid chunk (N is a multiple of 16).  SGPR-base form as
+// ASourceS; B is addressed in bytes.
+template <int NI>
+struct BSourceN8 {
+  const char* base;  // byte address of (k kb, column n0) less kSBias
+  uint32_t off[NI];
+  int64_t step;      // bytes per 64-k step
+
+  __device__ __forceinline__ void init(const void* B, int64_t ldb_k, int64_t N, int64_t n0,
+                                       int64_t kb, int wave, int lane) {
+    base = uniform_ptr((const char*)B + kb * ldb_k + n0 - kSBias);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = (NI * wave + i) * 4 + lane / 16;
+      int64_t n = n0 + 16 * ((lane % 16) ^ h8(k));
+      if (n > N - 16) n = N - 16;
+      off[i] = (uint32_t)(k * ldb_k + (n - n0) + kSBias - 1024 * i);
+    }
+    step = 64 * ldb_k;
+  }
+  __device__ __forceinline__ void issue_batch(uint32_t lds_wave, int64_t t) {
+    dma16s_batch<NI>(off, base + t * step, lds_wave);
+  }
+  __device__ __forceinline__ void issue_batch_at(uint32_t lds_wave, const char* b) {
+    dma16s_batch<NI>(off, b, lds_wave);
+  }
+  // Step t past kb with k-rows at or past k_end zero (the K tail).
+  __device__ __forceinline__ void fill_masked(char* lds_op, int wave, int lane, int64_t t, int64_t kb,
+                                              int64_t k_end) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = (NI * wave + i) * 4 + lane / 16;
+      const bool ok = kb + t * 64 + k < k_end;
+      const char* q = base + t * step + off[i] + 1024 * i;
+      *reinterpret_cast<u32x4*>(lds_op + (NI * wave + i) * 1024 + lane * 16) =
+          ok ? *reinterpret_cast<const u32x4*>(q) : zero4();
+    }
+  }
+};
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ i32x2 read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+
+// B block i of an N-major stage with ds_read_b64_tr_b8: in each group of 16
+// lanes, lane j receives byte j%8 of the 8-byte reads of source lanes
+// 2q + j/8 (q = 0..7) as its bytes q.  Source lane s of group G reads k-row
+// 32 (G/2) + 8r + s/2, columns 16 (G%2) + 8 (s%2) .. +8 of the block, so lane
+// l receives column l%32, k-rows 32 (l/32) + 8r .. +8 in read r: its 32 bytes
+// are k = 32 g .. 32 g + 31 in order, as read_a_f8 delivers A.
+__device__ __forceinline__ i32x8 read_b_f8_n(const char* tb, int i, int wn, int lane) {
+  const int G = lane / 16, s = lane % 16;
+  const int nb = wn * F8Cfg::WTN + i * 32 + 16 * (G & 1);
+  const int kr = 32 * (G >> 1) + (s >> 1);                // h8 is the same for kr + 8r
+  const char* p = tb + kr * 256 + (((nb >> 4) ^ h8(kr)) * 16) + 8 * (s & 1);
+  const i32x2 r0 = read_tr8(p), r1 = read_tr8(p + 8 * 256), r2 = read_tr8(p + 16 * 256),
+              r3 = read_tr8(p + 24 * 256);
+  return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+template <bool BN>
+__device__ __forceinline__ i32x8 read_b_any(const char* tb, int i, int wn, int lane) {
+  if constexpr (BN)
+    return read_b_f8_n(tb, i, wn, lane);
+  else
+    return read_b_f8(tb, i, wn, lane);
+}
+
 template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& b, const i32x8& a, const f32x16& c) {
   // First operand: the B block (format FB); second: the A block (format FA);
@@ -103,7 +184,8 @@ __device__ __forceinline__ u32x4 load_bytes16(const uint8_t* p, int64_t k, int64
 }
 
 // K-contiguous FP8 A and B; formats FA / FB; fp32 partials when PARTIAL.
-template <int FA, int FB, bool PARTIAL>
+// BN: B N-contiguous (B [K, N] row-major) instead of K-contiguous.
+template <int FA, int FB, bool PARTIAL, bool BN = false>
 __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
   using CF = F8Cfg;
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
@@ -136,9 +218,12 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
 
   // Byte-pair views for the DMA: strides and K offsets halve.
   ASourceS<CF::DMA_A> sa;
-  BSourceS<CF::DMA_B, true> sb;
+  std::conditional_t<BN, BSourceN8<CF::DMA_B>, BSourceS<CF::DMA_B, true>> sb;
   sa.init(a.A, a.lda_m / 2, 1, a.M, m0, kb / 2, wave, lane);
-  sb.init(a.B, a.ldb_n / 2, 1, a.N, n0, kb / 2, wave, lane);
+  if constexpr (BN)
+    sb.init(a.B, a.ldb_k, a.N, n0, kb, wave, lane);
+  else
+    sb.init(a.B, a.ldb_n / 2, 1, a.N, n0, kb / 2, wave, lane);
 
   f32x16 acc[CF::FN][CF::FM];
 #pragma unroll
@@ -178,8 +263,8 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     sb.issue_batch(lds_b(2), nfull2 > 2 ? 2 : nfull2 - 1);
     wait_vmcnt<CF::DMA_A + CF::DMA_B>();   // A(0), B(0) and B(1) landed
     wg_barrier();
-    f.fa_[0] = read_b_f8(stage_b(0), 0, wn, lane);
-    f.fa_[1] = read_b_f8(stage_b(0), 1, wn, lane);
+    f.fa_[0] = read_b_any<BN>(stage_b(0), 0, wn, lane);
+    f.fa_[1] = read_b_any<BN>(stage_b(0), 1, wn, lane);
     if (g1) wg_barrier();
 
     // Slot indices rotate in 32-bit registers, as in the fp16 kernel.
@@ -197,8 +282,8 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       // M(t)
       f.fb_[0] = read_a_f8(sl_a(iu), H, 0, wm, lane);
       f.fb_[1] = read_a_f8(sl_a(iu), H, 1, wm, lane);
-      f.fa_[2] = read_b_f8(st_b(t), 2, wn, lane);
-      f.fa_[3] = read_b_f8(st_b(t), 3, wn, lane);
+      f.fa_[2] = read_b_any<BN>(st_b(t), 2, wn, lane);
+      f.fa_[3] = read_b_any<BN>(st_b(t), 3, wn, lane);
       sa.template issue_half_at<H>(la0 + i2 * CF::A_SLOT + (CF::DMA_A / 2) * H * 1024, pa);
       sb.issue_batch_at(lb0 + ((t + 3) & (CF::B_STAGES - 1)) * CF::B_STAGE, pb);
       if (t + 4 < nf2) pb += sb.step;
@@ -220,7 +305,7 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
 #pragma unroll
         for (int j = 0; j < CF::FM; ++j) {
           if (!EDGE || (i < fnv && j < fmv)) acc[i][j] = mfma_f8<FA, FB>(f.fa_[i], f.fb_[j], acc[i][j]);
-          if (j == 0) f.fa_[i - 2] = read_b_f8(nb, i - 2, wn, lane);
+          if (j == 0) f.fa_[i - 2] = read_b_any<BN>(nb, i - 2, wn, lane);
           __builtin_amdgcn_sched_barrier(0);
         }
       wait_vmcnt<CF::DMA_PER_STEP>();
@@ -252,7 +337,7 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     // nfull2 (and nfull2 + 1), all free after the last barrier; rows past M
     // or N read the last valid row.
     const uint8_t* A8 = reinterpret_cast<const uint8_t*>(a.A);
-    const uint8_t* B8 = reinterpret_cast<const uint8_t*>(a.B);
+    [[maybe_unused]] const uint8_t* B8 = reinterpret_cast<const uint8_t*>(a.B);
     const int64_t k0 = kb + 128 * nsup;
     char* sl = slot_a(nsup);
     for (int cell = tid; cell < CF::BM * 8; cell += CF::NT) {
@@ -264,18 +349,22 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     }
     for (int s = 0; s < (rem > 64 ? 2 : 1); ++s) {
       char* st = stage_b(nfull2 + s);
-      for (int cell = tid; cell < CF::BN * 4; cell += CF::NT) {
-        const int r = cell / 4, c = cell % 4;
-        int64_t rr = n0 + r;
-        if (rr > a.N - 1) rr = a.N - 1;
-        *reinterpret_cast<u32x4*>(st + r * 64 + ((c ^ fa(r)) * 16)) =
-            load_bytes16(B8 + rr * a.ldb_n, k0 + 64 * s + 16 * c, ke);
+      if constexpr (BN) {
+        sb.fill_masked(st, wave, lane, nfull2 + s, kb, ke);
+      } else {
+        for (int cell = tid; cell < CF::BN * 4; cell += CF::NT) {
+          const int r = cell / 4, c = cell % 4;
+          int64_t rr = n0 + r;
+          if (rr > a.N - 1) rr = a.N - 1;
+          *reinterpret_cast<u32x4*>(st + r * 64 + ((c ^ fa(r)) * 16)) =
+              load_bytes16(B8 + rr * a.ldb_n, k0 + 64 * s + 16 * c, ke);
+        }
       }
     }
     __syncthreads();
     for (int s = 0; s < (rem > 64 ? 2 : 1); ++s) {
 #pragma unroll
-      for (int i = 0; i < CF::FN; ++i) f.fa_[i] = read_b_f8(stage_b(nfull2 + s), i, wn, lane);
+      for (int i = 0; i < CF::FN; ++i) f.fa_[i] = read_b_any<BN>(stage_b(nfull2 + s), i, wn, lane);
 #pragma unroll
       for (int j = 0; j < CF::FM; ++j) f.fb_[j] = read_a_f8(slot_a(nsup), s, j, wm, lane);
       mma_f8<FA, FB, true>(f, acc, 0, CF::FN, fnv, fmv);

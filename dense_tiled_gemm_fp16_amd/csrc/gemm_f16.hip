@@ -220,10 +220,14 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   // tile, in the main, split-K and stream-K families only.
   const bool f8 = c.dt >= DT_F8;
   if (f8) {
-    // Row strides up to 2^24 bytes: the DMA's 32-bit lane offsets span 255 rows.
-    if (c.lda_k != 1 || c.lda_m % 16 != 0 || ((uintptr_t)c.A & 15u) || c.ldb_k != 1 ||
-        c.ldb_n % 16 != 0 || ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) ||
-        c.ldb_n > (INT64_C(1) << 24))
+    // A K-contiguous; B K-contiguous ([N, K] rows) or N-contiguous ([K, N]
+    // rows, N a multiple of 16); 16-byte aligned rows at most 2^24 bytes
+    // apart (the DMA's 32-bit lane offsets span 255 rows).
+    const bool b_k = c.ldb_k == 1, b_n = !b_k && c.ldb_n == 1;
+    const int64_t ldb = b_k ? c.ldb_n : c.ldb_k;
+    if (c.lda_k != 1 || c.lda_m % 16 != 0 || ((uintptr_t)c.A & 15u) || !(b_k || b_n) ||
+        ldb % 16 != 0 || ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) ||
+        ldb > (INT64_C(1) << 24) || (b_n && c.N % 16 != 0))
       return GEMM_ERR_LAYOUT;
     if (variant == GEMM_VARIANT_SKINNY || variant == GEMM_VARIANT_TILE64X32 ||
         (want_tile && want_tile != TILE_F8))
@@ -253,7 +257,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   if (p.variant == GEMM_VARIANT_SKINNY && c.M > 64) return GEMM_ERR_OPTS;
 
   p.a_path = f8 ? PATH_KVEC : classify(c.A, c.lda_m, c.lda_k);
-  p.b_path = f8 ? PATH_KVEC : classify(c.B, c.ldb_n, c.ldb_k);
+  p.b_path = f8 ? (c.ldb_k == 1 ? PATH_KVEC : PATH_RVEC) : classify(c.B, c.ldb_n, c.ldb_k);
 
   // Tile.
   switch (p.variant) {

@@ -138,12 +138,15 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   return t;
 }
 
-// The FP8 tile: K-contiguous A and B (B given as [N, K] rows), the four
-// format pairs; it takes no other layout and no 16-bit format.
+// The FP8 tile: K-contiguous A; B K-contiguous ([N, K] rows) or
+// N-contiguous ([K, N] rows); the four format pairs; no other layout and no
+// 16-bit format.
 template <int FA, int FB>
 void fill_f8(TileInfo& t) {
   t.final_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_KVEC] = gemm_f8_kernel<FA, FB, false>;
   t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_KVEC] = gemm_f8_kernel<FA, FB, true>;
+  t.final_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, false, true>;
+  t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, true, true>;
 }
 
 inline TileInfo make_f8_info(int id) {

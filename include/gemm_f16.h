@@ -191,10 +191,11 @@ size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16
  * byte per element; strides are in elements as for the 16-bit calls; C is
  * binary16 with row stride ldc.
  *
- * Layout: A must be K-contiguous (lda_k == 1) and B must be K-contiguous
- * (ldb_k == 1: the [N, K] weight layout, seen as a transposed view), with
- * lda_m and ldb_n multiples of 16 and at most 2^24, and A and B 16-byte
- * aligned; any other
+ * Layout: A must be K-contiguous (lda_k == 1).  B is either K-contiguous
+ * (ldb_k == 1: the [N, K] weight layout, seen as a transposed view) or
+ * N-contiguous (ldb_n == 1: B [K, N] row-major, with N a multiple of 16).
+ * Row strides (lda_m, and ldb_n or ldb_k) are multiples of 16 and at most
+ * 2^24, and A and B are 16-byte aligned; any other
  * layout returns GEMM_ERR_LAYOUT before anything is enqueued.  M, N and K are
  * masked as in the 16-bit calls (zero fill on K).  Variants: AUTO, MAIN,
  * SPLITK and STREAMK (SKINNY and TILE64X32 return GEMM_ERR_OPTS); the tile

@@ -191,7 +191,11 @@ def f8call(A=PA, lda_m=64, lda_k=1, B=PB, ldb_k=1, ldb_n=64, C=PC, ldc=32, M=16,
 def test_f8_rejected_before_any_device_work():
     # Layout: K-contiguous A and B with 16-byte aligned rows only.
     assert f8call(lda_m=1, lda_k=64) == -9              # A not K-contiguous
-    assert f8call(ldb_k=32, ldb_n=1) == -9              # B N-contiguous
+    assert f8call(ldb_k=32, ldb_n=1) != -9              # B N-contiguous, N % 16 == 0: taken
+    assert f8call(ldb_k=40, ldb_n=1) == -9              # its k-rows not 16-byte aligned
+    assert f8call(ldb_k=32, ldb_n=1, N=24, ldc=24) == -9   # N not a multiple of 16
+    assert f8call(ldb_k=32, ldb_n=2) == -9              # B contiguous along neither axis
+    assert f8call(ldb_k=(1 << 24) + 16, ldb_n=1) == -9  # k-rows over 2^24 bytes apart
     assert f8call(lda_m=72) == -9                       # A rows not 16-byte aligned
     assert f8call(ldb_n=40) == -9
     assert f8call(A=PA + 8) == -9

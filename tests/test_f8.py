@@ -1,6 +1,7 @@
 """GPU parity of the FP8 entry points (gemm_f8*, TileLang tutorial ch. 14,
 section 5): OCP E4M3 / E5M2 operands, fp32 accumulation, binary16 output,
-against the oracle's FP8 product on the same seeded inputs.  Acceptance as
+against the oracle's FP8 product on the same seeded inputs; B given as
+[N, K] rows (K-contiguous) and as [K, N] rows (N-contiguous).  Acceptance as
 for fp16: bit-exact on integer inputs (exact in both FP8 formats, sums exact
 in fp32), the elementwise tolerance 1e-2 + 2e-3 |C| on U(-1, 1) inputs
 rounded to FP8.  Operand rows are padded with the NaN byte 0x7F (NaN in both
@@ -126,3 +127,91 @@ def test_f8_stride_limit():
     b = f8_rows(Bt, "e4m3").t()
     got = run(a, b, Out(M, N), variant="main")
     assert_bits_equal(got, ref, "f8 lda_m = 2^24")
+
+
+# ---------------------------------------------------------------- N-contiguous B
+
+def f8_krows(bits, fmt, pad=None):
+    """uint8 B [K, N] -> FP8 device view [K, N] whose k-rows are padded to a
+    multiple of 16 bytes (at least 16 more) with 0x7F (NaN)."""
+    K, N = bits.shape
+    pad = (-N) % 16 + 16 if pad is None else pad
+    buf = np.full((K, N + pad), 0x7F, dtype=np.uint8)
+    buf[:, :N] = bits
+    return torch.from_numpy(buf).to(DEV).view(TORCH_F8[fmt])[:, :N]
+
+
+def inputs_bn(M, N, K, seed, mode, fa, fb):
+    A = synth.matrix(M, K, seed, 0, mode, fmt=fa)
+    B = synth.matrix(K, N, seed, 1, mode, fmt=fb)        # [K, N] row-major
+    return A, B
+
+
+def reference_bn(A, B, fa, fb, rows=None):
+    K, N = B.shape
+    if rows is not None:
+        A = np.ascontiguousarray(A[rows])
+    return oracle.gemm(A, (K, 1), B, (N, 1), A.shape[0], N, K, dtype="f8", fmt_a=fa, fmt_b=fb,
+                       nthreads=ORACLE_THREADS)
+
+
+@pytest.mark.parametrize("mode", ["int", "uniform"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_f8_bn_parity_ragged(fa, fb, mode):
+    M, N, K = 600, 528, 700
+    A, B = inputs_bn(M, N, K, 14500, mode, fa, fb)
+    ref = reference_bn(A, B, fa, fb)
+    a, b = f8_rows(A, fa), f8_krows(B, fb)
+    assert b.stride(1) == 1
+    for kw in (dict(variant="main"), dict(variant="splitk", split_k=3),
+               dict(variant="streamk", split_k=2)):
+        p = g.plan(a, b, **kw)
+        assert p["b_path"] == "rvec" and p["tile_id"] == 15, p
+        got = run(a, b, Out(M, N), **kw)
+        what = f"f8 B [K, N] {fa}x{fb} {mode} {kw}"
+        if mode == "int":
+            assert_bits_equal(got, ref, what)
+        else:
+            assert_close(got, ref, what)
+
+
+@pytest.mark.parametrize("K", [1, 7, 64, 100, 128, 192, 255, 384])
+def test_f8_bn_k_tails(K):
+    # Whole 128-k super-steps, an odd 64-k step and ragged tails (k-rows
+    # past K are zero in the stage), byte by byte.
+    M, N = 300, 272
+    A, B = inputs_bn(M, N, K, 14600 + K, "int", "e4m3", "e5m2")
+    ref = reference_bn(A, B, "e4m3", "e5m2")
+    got = run(f8_rows(A, "e4m3"), f8_krows(B, "e5m2"), Out(M, N), variant="main")
+    assert_bits_equal(got, ref, f"f8 B [K, N] K={K}")
+
+
+def test_f8_bn_edge_blocks():
+    # Last tile column with 1..7 live 32-wide blocks and half blocks (N a
+    # multiple of 16), last tile row with every count of live 32-row blocks.
+    K = 192
+    for M in (257, 321, 449):
+        for N in (16, 272, 304, 352, 432, 496):
+            A, B = inputs_bn(M, N, K, 14700 + M + N, "int", "e4m3", "e4m3")
+            ref = reference_bn(A, B, "e4m3", "e4m3")
+            got = run(f8_rows(A, "e4m3"), f8_krows(B, "e4m3", pad=16 + 16 * (N % 32 == 0)),
+                      Out(M, N), variant="main")
+            assert_bits_equal(got, ref, f"f8 B [K, N] edge blocks {M}x{N}")
+
+
+def test_f8_bn_moe_shape_sampled():
+    # The 131072 x 2048 x 7168 product with E4M3 operands and B [K, N]
+    # row-major, as the fp16 workload lays it out.
+    M, N, K = 131072, 2048, 7168
+    say("f8 B [K, N] MoE: generating inputs")
+    A, B = inputs_bn(M, N, K, 14800, "uniform", "e4m3", "e4m3")
+    a = torch.from_numpy(A).to(DEV).view(torch.float8_e4m3fn)
+    b = torch.from_numpy(B).to(DEV).view(torch.float8_e4m3fn)
+    p = g.plan(a, b)
+    assert p["tile_id"] == 15 and p["b_path"] == "rvec", p
+    c = g.gemm(a, b)
+    torch.cuda.synchronize()
+    got = to_host(c)
+    rng = np.random.default_rng(14800)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
+    assert_close(got[rows], reference_bn(A, B, "e4m3", "e4m3", rows), "f8 B [K, N] MoE sampled rows")
