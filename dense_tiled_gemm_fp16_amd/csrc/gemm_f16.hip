@@ -100,6 +100,7 @@ struct Plan {
   int red_lanes;  // lanes per output quad in the split reduction
   int64_t GM, GN, grid, grid2, k_split;
   int64_t sk_tiles;  // STREAMK: tiles split over K after the whole waves
+  bool pack;         // B is packed into the workspace first (see make_plan)
   size_t ws;
 };
 
@@ -202,9 +203,75 @@ bool tile_takes(const TileInfo& t, const Call& c, const Plan& p) {
 
 bool dma_tile_takes(const Call& c, const Plan& p) { return tile_takes(tile_info(TILE_DMA256A128), c, p); }
 
-int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
+constexpr int64_t kPackMinRows = 16384;   // automatic plans pack a K-contiguous B from this M on
+constexpr int32_t kBPathPacked = 3;       // b_path reported for a packing plan
+
+// Pre-packed B: ceil(N/256) panels of ceil(K/32) blocks of 16 KiB (see
+// pack_b_kernel).  0 for shapes out of range or too large to count.
+size_t packed_b_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0 || K > (INT64_C(1) << 40) || N > (INT64_C(1) << 40)) return 0;
+  int64_t blocks, bytes;
+  if (__builtin_mul_overflow(cdiv(N, 256), cdiv(K, 32), &blocks) ||
+      __builtin_mul_overflow(blocks, (int64_t)16384, &bytes))
+    return 0;
+  return (size_t)bytes;
+}
+
+// The packing launch: B [K, N] through its strides into Bp.
+int launch_pack_b(const uint16_t* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int64_t N, uint16_t* Bp,
+                  hipStream_t stream) {
+  int64_t S = cdiv(K, 32);
+  int64_t slots = (int64_t)(packed_b_bytes(K, N) / 16);
+  int kvec = (ldb_k == 1 && ((uintptr_t)B & 15u) == 0 && ldb_n % 8 == 0) ? 1 : 0;
+  void* args[] = {&B, &ldb_k, &ldb_n, &K, &N, &S, &slots, &Bp, &kvec};
+  if (hipLaunchKernel((const void*)pack_b_kernel, dim3((unsigned)cdiv(slots, 256)), dim3(256), args, 0,
+                      stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+// The product launch on a packed B (main variant of the 256 x 256 tile, no
+// split): A K-contiguous with 16-byte aligned rows at most max_ld apart.
+int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* Bp, void* C,
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, int panel, hipStream_t stream) {
+  const TileInfo& ti = tile_info(TILE_DMA256A128);
+  KArgs a;
+  a.A = (const uint16_t*)A;
+  a.lda_m = lda_m;
+  a.lda_k = lda_k;
+  a.B = (const uint16_t*)Bp;
+  a.ldb_k = 1;
+  a.ldb_n = cdiv(K, 32) * 8192;   // elements per 256-column panel
+  a.C = (uint16_t*)C;
+  a.ldc = ldc;
+  a.W = nullptr;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.k_split = K;
+  a.GM = cdiv(M, ti.bm);
+  a.GN = cdiv(N, ti.bn);
+  a.panel = panel;
+  a.c_vec = (((uintptr_t)C & 7u) == 0 && (ldc & 3) == 0) ? 1 : 0;
+  a.g_off = nullptr;
+  a.g_tiles = nullptr;
+  a.ldb_g = 0;
+  a.G = 0;
+  a.sk_first = 0;
+  a.sk_tiles = 0;
+  int64_t grid;
+  if (__builtin_mul_overflow(a.GM, a.GN, &grid) || grid > INT32_MAX) return GEMM_ERR_SHAPE;
+  void* args[] = {&a};
+  if (hipLaunchKernel((const void*)ti.packed_fn[dt], dim3((unsigned)grid), dim3(ti.nt), args, 0,
+                      stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = true) {
   int rc = check_opts(o);
   if (rc) return rc;
+  p.pack = false;
   const int variant = o ? o->variant : GEMM_VARIANT_AUTO;
   const int want_split = o ? o->split_k : 0;
   const int want_panel = o ? o->panel : 0;
@@ -410,7 +477,24 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p) {
   if (__builtin_mul_overflow(T, (int64_t)p.split, &grid) || grid > (INT64_C(1) << 32) / ti.nt - 1)
     return GEMM_ERR_SHAPE;
   p.grid = grid;
-  return plan_partials(c, p);
+  if ((rc = plan_partials(c, p))) return rc;
+
+  // K-contiguous B under the 256 x 256 tile: its K-major stages take half a
+  // cache line per B row per DMA, about 5% slower than an N-contiguous B.
+  // With many row tiles over each B panel, one packing pass over B (the
+  // pre-packed layout, whole lines per DMA) costs less than that, so an
+  // automatic plan packs B into the workspace and runs the packed-B kernel.
+  if (allow_pack && variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN &&
+      p.tile_id == TILE_DMA256A128 && p.split == 1 && p.b_path == PATH_KVEC && !f8 &&
+      c.M >= kPackMinRows && c.K <= ti.max_k && ti.packed_fn[c.dt]) {
+    const size_t bytes = packed_b_bytes(c.K, c.N);
+    if (bytes > 0) {
+      p.pack = true;
+      p.ws = bytes;
+      p.grid2 = cdiv((int64_t)(bytes / 16), 256);   // the packing launch
+    }
+  }
+  return GEMM_OK;
 }
 
 void fill_info(const Plan& p, gemm_f16_plan_info* info) {
@@ -422,7 +506,7 @@ void fill_info(const Plan& p, gemm_f16_plan_info* info) {
   info->split_k = p.split;
   info->panel = p.panel;
   info->a_path = p.a_path;
-  info->b_path = p.b_path;
+  info->b_path = p.pack ? kBPathPacked : p.b_path;
   info->tile_id = p.tile_id;
   info->grid = p.grid;
   info->grid2 = p.grid2;
@@ -504,6 +588,12 @@ int launch_streamk(const Call& c, const Plan& p, KArgs a, kfn_t final_fn, kfn_t 
 
 int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   if (p.gemv_mt) return launch_gemv(c, p, ws, stream);
+  if (p.pack) {
+    int rc = launch_pack_b((const uint16_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream);
+    if (rc) return rc;
+    return launch_packed_product(c.dt, c.A, c.lda_m, c.lda_k, ws, (void*)c.C, c.ldc, c.M, c.N, c.K, p.panel,
+                                 stream);
+  }
   const TileInfo& ti = tile_info(p.tile_id);
   KArgs a;
   a.A = (const uint16_t*)c.A;
@@ -561,6 +651,10 @@ int ex_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, 
   if ((rc = spans(c))) return rc;
   Plan p;
   if ((rc = make_plan(c, opts, p))) return rc;
+  // A packing plan runs only where the room is there: the library's own
+  // allocation, or a caller workspace that holds the packed B.
+  if (p.pack && workspace && workspace_bytes < p.ws && (rc = make_plan(c, opts, p, false)))
+    return rc;
   hipStream_t s = (hipStream_t)stream;
   if (p.ws == 0) return launch(c, p, nullptr, s);
   if (workspace) {
@@ -786,19 +880,7 @@ size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16
 }
 
 // ---- pre-packed B
-static int64_t packed_blocks(int64_t K, int64_t N, int64_t* S) {
-  *S = cdiv(K, 32);
-  return cdiv(N, 256) * *S;
-}
-
-size_t gemm_f16_packed_b_bytes(int64_t K, int64_t N) {
-  if (K <= 0 || N <= 0 || K > (INT64_C(1) << 40) || N > (INT64_C(1) << 40)) return 0;
-  int64_t S;
-  const int64_t blocks = packed_blocks(K, N, &S);
-  int64_t bytes;
-  if (__builtin_mul_overflow(blocks, (int64_t)16384, &bytes)) return 0;
-  return (size_t)bytes;
-}
+size_t gemm_f16_packed_b_bytes(int64_t K, int64_t N) { return packed_b_bytes(K, N); }
 
 int gemm_f16_pack_b(const void* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int64_t N, void* Bp,
                     void* stream) {
@@ -807,21 +889,12 @@ int gemm_f16_pack_b(const void* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int6
   if (ldb_k <= 0 || ldb_n <= 0) return GEMM_ERR_STRIDE;
   int64_t spanB;
   if (!view_span(K, N, ldb_k, ldb_n, &spanB)) return GEMM_ERR_SHAPE;
-  const size_t bytes = gemm_f16_packed_b_bytes(K, N);
+  const size_t bytes = packed_b_bytes(K, N);
   if (bytes == 0 || K > tile_info(TILE_DMA256A128).max_k) return GEMM_ERR_SHAPE;
   if (((uintptr_t)Bp & 255u) != 0) return GEMM_ERR_WORKSPACE;
   const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(spanB + 1);
   if (ranges_overlap(b0, b1, (uintptr_t)Bp, (uintptr_t)Bp + bytes)) return GEMM_ERR_ALIAS;
-  int64_t S;
-  packed_blocks(K, N, &S);
-  int64_t slots = (int64_t)(bytes / 16);
-  const uint16_t* src = (const uint16_t*)B;
-  uint16_t* dst = (uint16_t*)Bp;
-  void* args[] = {&src, &ldb_k, &ldb_n, &K, &N, &S, &slots, &dst};
-  if (hipLaunchKernel((const void*)pack_b_kernel, dim3((unsigned)cdiv(slots, 256)), dim3(256), args, 0,
-                      (hipStream_t)stream) != hipSuccess)
-    return GEMM_ERR_HIP;
-  return GEMM_OK;
+  return launch_pack_b((const uint16_t*)B, ldb_k, ldb_n, K, N, (uint16_t*)Bp, (hipStream_t)stream);
 }
 
 int gemm_f16_packed(const void* A, int64_t lda_m, int64_t lda_k, const void* Bp, void* C, int64_t ldc,
@@ -832,7 +905,7 @@ int gemm_f16_packed(const void* A, int64_t lda_m, int64_t lda_k, const void* Bp,
   if (ldc < N) return GEMM_ERR_LDC;
   int64_t spanA, spanC;
   if (!view_span(M, K, lda_m, lda_k, &spanA) || !view_span(M, N, ldc, 1, &spanC)) return GEMM_ERR_SHAPE;
-  const size_t bytes = gemm_f16_packed_b_bytes(K, N);
+  const size_t bytes = packed_b_bytes(K, N);
   if (bytes == 0 || K > tile_info(TILE_DMA256A128).max_k) return GEMM_ERR_SHAPE;
   // The full-line-A tile's A path: K-contiguous, 16-byte aligned rows.
   if (classify(A, lda_m, lda_k) != PATH_KVEC || ((uintptr_t)Bp & 255u) != 0 ||
@@ -842,38 +915,7 @@ int gemm_f16_packed(const void* A, int64_t lda_m, int64_t lda_k, const void* Bp,
   const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(spanC + 1);
   const uintptr_t p0 = (uintptr_t)Bp, p1 = p0 + bytes;
   if (ranges_overlap(c0, c1, a0, a1) || ranges_overlap(c0, c1, p0, p1)) return GEMM_ERR_ALIAS;
-  const TileInfo& ti = tile_info(TILE_DMA256A128);
-  KArgs a;
-  a.A = (const uint16_t*)A;
-  a.lda_m = lda_m;
-  a.lda_k = lda_k;
-  a.B = (const uint16_t*)Bp;
-  a.ldb_k = 1;
-  a.ldb_n = cdiv(K, 32) * 8192;   // elements per 256-column panel
-  a.C = (uint16_t*)C;
-  a.ldc = ldc;
-  a.W = nullptr;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.k_split = K;
-  a.GM = cdiv(M, ti.bm);
-  a.GN = cdiv(N, ti.bn);
-  a.panel = 4;
-  a.c_vec = (((uintptr_t)C & 7u) == 0 && (ldc & 3) == 0) ? 1 : 0;
-  a.g_off = nullptr;
-  a.g_tiles = nullptr;
-  a.ldb_g = 0;
-  a.G = 0;
-  a.sk_first = 0;
-  a.sk_tiles = 0;
-  int64_t grid;
-  if (__builtin_mul_overflow(a.GM, a.GN, &grid) || grid > INT32_MAX) return GEMM_ERR_SHAPE;
-  void* args[] = {&a};
-  if (hipLaunchKernel((const void*)ti.packed_fn, dim3((unsigned)grid), dim3(ti.nt), args, 0,
-                      (hipStream_t)stream) != hipSuccess)
-    return GEMM_ERR_HIP;
-  return GEMM_OK;
+  return launch_packed_product(DT_F16, A, lda_m, lda_k, Bp, C, ldc, M, N, K, 4, (hipStream_t)stream);
 }
 
 static int f8_dt(int32_t fmt_a, int32_t fmt_b) {

@@ -12,16 +12,22 @@ namespace gemmf16 {
 // (p, s) holds, for row r = o / 64 (n = 256 p + r) and 16-byte slot
 // q = (o % 64) / 16, the 8 elements k = 32 s + 8 (q ^ fa(r)) + e, e = 0..7
 // (zero past N or K): the bytes a DMA of a K-major B stage writes to LDS.
-// One thread per 16-byte slot; B is read through its element strides.
+// One thread per 16-byte slot; B is read through its element strides, or,
+// with kvec (K-contiguous B whose rows start on 16-byte boundaries), with
+// one 16-byte load where all 8 elements lie inside K.
 __global__ __launch_bounds__(256) void pack_b_kernel(const uint16_t* B, int64_t ldb_k, int64_t ldb_n,
                                                      int64_t K, int64_t N, int64_t S, int64_t slots,
-                                                     uint16_t* Bp) {
+                                                     uint16_t* Bp, int kvec) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= slots) return;
   const int64_t blk = q / 1024, o = (q % 1024) * 16;
   const int64_t pnl = blk / S, s = blk - pnl * S;
   const int r = (int)(o / 64), c = (int)((o % 64) / 16) ^ fa(r);
   const int64_t n = 256 * pnl + r, k0 = 32 * s + 8 * c;
+  if (kvec && n < N && k0 + 8 <= K) {
+    *reinterpret_cast<u32x4*>(Bp + q * 8) = *reinterpret_cast<const u32x4*>(B + k0 + n * ldb_n);
+    return;
+  }
   uint32_t h[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)

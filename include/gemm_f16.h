@@ -105,7 +105,8 @@ typedef struct gemm_f16_plan_info {
   int32_t split_k;          /* K ranges (1 = none)                               */
   int32_t panel;            /* raster group height in tiles (-1 = plain order)   */
   int32_t a_path, b_path;   /* operand load path: 0 gather, 1 vector along K,    */
-                            /* 2 vector along M (A) or N (B) with a transpose    */
+                            /* 2 vector along M (A) or N (B) with a transpose;   */
+                            /* b_path 3: B packed into the workspace first      */
   int32_t tile_id;          /* the tile configuration chosen                     */
   int64_t grid;             /* workgroups in the first launch                    */
   int64_t grid2;            /* workgroups in the reduction launch (0 = none)     */
@@ -130,6 +131,15 @@ int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
  * otherwise it must hold at least gemm_f16_workspace_bytes(...) bytes, be
  * 256-byte aligned, and not overlap A, B or C.  The workspace needs no
  * initialisation and its contents are garbage afterwards.  opts may be NULL.
+ *
+ * Packing plan (AUTO only): with K-contiguous B (ldb_k == 1), M >= 16384 and
+ * the MAIN family on the 256x256 LDS-DMA tile, the call first packs B into
+ * the workspace in the layout of gemm_f16_pack_b (one pass over B) and then
+ * runs the packed-B product: the direct K-major B stages take half a cache
+ * line per B row per DMA.  The plan reports b_path 3 and workspace_bytes =
+ * gemm_f16_packed_b_bytes(K, N).  It runs when workspace is NULL or holds
+ * that many bytes; a smaller caller workspace gets the direct plan instead.
+ * Both give the same bits.
  */
 int gemm_f16_ex(const void* A, int64_t lda_m, int64_t lda_k,
                 const void* B, int64_t ldb_k, int64_t ldb_n,

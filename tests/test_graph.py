@@ -94,3 +94,24 @@ def test_graph_replay_grouped():
         g.gemm_grouped(a, b, offsets, out=out, workspace=ws, stream=stream)
 
     _replay_matches(call, out, ws, f"grouped G={G}")
+
+
+def test_graph_replay_packing_plan():
+    # K-contiguous B at M >= 16384: the automatic plan packs B into the
+    # caller's workspace, then runs the packed-B product (two launches).
+    M, N, K = 16384, 264, 296          # rows of 296 and 304 halves: 16-byte multiples
+    A = synth.matrix(M, K, 17200, 0)
+    B = synth.matrix(K, N, 17201, 1)
+    a = to_dev(A)
+    bt = torch.empty((N, K + 8), dtype=torch.float16, device=DEV)
+    bt[:, :K].copy_(to_dev(np.ascontiguousarray(B.T)))
+    b = bt[:, :K].t()
+    out = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    p = g.plan(a, b, out=out)
+    assert p["b_path"] == "packed" and p["workspace_bytes"] > 0, p
+    ws = torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=DEV)
+
+    def call(stream):
+        g.gemm(a, b, out=out, workspace=ws, stream=stream)
+
+    _replay_matches(call, out, ws, f"packing plan {p}")

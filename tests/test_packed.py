@@ -3,6 +3,8 @@ gemm_f16_packed; the C500 log's weight packing done once, outside the timed
 region) against the oracle, and against the general-stride path on integer
 inputs.  B is packed from several layouts; padding of A rows is NaN.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -71,3 +73,103 @@ def test_packed_moe_shape_sampled():
     rng = np.random.default_rng(15100)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
     assert_close(got[rows], reference(A, B, rows), "packed MoE sampled rows")
+
+
+# ---- automatic packing plan: K-contiguous B at large M (gemm_f16_ex, AUTO)
+
+def _kcontig_case(M, N, K, seed, fmt="f16"):
+    A = synth.matrix(M, K, seed, 0, "int", fmt=fmt)
+    B = synth.matrix(K, N, seed, 1, "int", fmt=fmt)
+    a = place(A, "row", (1, (-K) % 8 + 8))
+    b = place(B, "col", (1, (-K) % 8 + 8))     # transposed view: K-contiguous, aligned rows
+    if fmt == "bf16":
+        a, b = a.view(torch.bfloat16), b.view(torch.bfloat16)
+    return A, B, a, b
+
+
+def _out(M, N, fmt):
+    out = Out(M, N)
+    if fmt == "bf16":
+        out.view = out.view.view(torch.bfloat16)
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_auto_packs_kcontig_b(fmt):
+    # M past the packing threshold with ragged M, N and K (K tail 700 % 64 = 60).
+    M, N, K = 16384 + 37, 300, 700
+    A, B, a, b = _kcontig_case(M, N, K, 15200, fmt)
+    p = g.plan(a, b)
+    assert p["b_path"] == "packed" and p["tile_id"] == 14 and p["split_k"] == 1, p
+    assert p["workspace_bytes"] == g.lib.gemm_f16_packed_b_bytes(K, N), p
+    ref = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, nthreads=ORACLE_THREADS,
+                      dtype="bf16" if fmt == "bf16" else "f16")
+    say(f"auto packing plan {fmt} {M}x{N}x{K} B stride {b.stride()}")
+    out = _out(M, N, fmt)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.result(), ref, f"packing plan {fmt}")
+    say(f"forced direct plan {fmt} {M}x{N}x{K}")
+    pd = g.plan(a, b, variant="main", tile=14)
+    assert pd["b_path"] == "kvec" and pd["workspace_bytes"] == 0, pd
+    out2 = _out(M, N, fmt)
+    g.gemm(a, b, out=out2.view, variant="main", tile=14)
+    torch.cuda.synchronize()
+    assert_bits_equal(out2.result(), ref, f"direct K-major plan {fmt}")
+
+
+def test_auto_pack_caller_workspace():
+    M, N, K = 16384, 264, 512
+    A, B, a, b = _kcontig_case(M, N, K, 15300)
+    ref = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, nthreads=ORACLE_THREADS)
+    need = int(g.lib.gemm_f16_packed_b_bytes(K, N))
+    assert g.plan(a, b)["b_path"] == "packed"
+    # Big enough: the packing plan runs in the caller's workspace.
+    ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    say(f"packing plan in a caller workspace of {need} bytes")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view, workspace=ws)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.result(), ref, "caller workspace")
+    assert not torch.isnan(ws[: need // 4]).all()      # the packed B went there
+    # Too small: the direct plan runs, same bits, the workspace untouched.
+    small = torch.full((1024,), float("nan"), dtype=torch.float32, device=DEV)
+    say("packing plan with a too-small caller workspace -> direct plan")
+    out2 = Out(M, N)
+    g.gemm(a, b, out=out2.view, workspace=small)
+    torch.cuda.synchronize()
+    assert_bits_equal(out2.result(), ref, "small workspace")
+    assert torch.isnan(small).all()
+
+
+def test_auto_pack_workspace_overlapping_b_rejected():
+    M, N, K = 16384, 264, 512
+    _, _, a, b = _kcontig_case(M, N, K, 15400)
+    need = int(g.lib.gemm_f16_packed_b_bytes(K, N))
+    assert g.plan(a, b)["b_path"] == "packed"
+    # A workspace that starts inside B's storage: rejected before any launch.
+    base = b.data_ptr() - (b.data_ptr() % 256) + 256
+    c = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    opts = g.make_opts("auto", 0, 0, 0)
+    rc = g.lib.gemm_f16_ex(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
+                           b.stride(1), c.data_ptr(), N, M, N, K, 0, base, need,
+                           ctypes.byref(opts))
+    assert rc == -5, rc
+
+
+def test_auto_pack_moe_shape_sampled():
+    M, N, K = 131072, 2048, 7168
+    say("K-contiguous B MoE: generating inputs")
+    A = synth.matrix(M, K, 15500, 0)
+    B = synth.matrix(K, N, 15501, 1)
+    a = to_dev(A)
+    b = to_dev(np.ascontiguousarray(B.T)).t()        # B as [N, K] weights
+    p = g.plan(a, b)
+    assert p["b_path"] == "packed", p
+    say(f"K-contiguous B MoE plan {p}")
+    c = g.gemm(a, b)
+    torch.cuda.synchronize()
+    got = to_host(c)
+    rng = np.random.default_rng(15500)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
+    assert_close(got[rows], reference(A, B, rows), "K-contiguous B MoE sampled rows")
