@@ -469,33 +469,48 @@ def main():
     bf = torch.from_numpy(synth.matrix(K, N, 4001, synth.TENSOR_B, fmt="e4m3", order="col")).to(
         dev).view(torch.float8_e4m3fn).t()
 
-    def step_f():
-        g.gemm(af, bf, out=c, stream=stream)
+    pf = g.plan(af, bf, c)
+    wsf = (torch.empty(pf["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+           if pf["workspace_bytes"] else None)
 
-    df, _ = timed_launches(step_f, stream, max(5, args.steps // 5), 2)
-    msf = sum(df) / len(df)
+    def step_f():
+        g.gemm(af, bf, out=c, workspace=wsf, stream=stream)
+
+    def step_fd():
+        g.gemm(af, bf, out=c, variant="main", stream=stream)
+
+    # The automatic plan packs B ([N, K] rows) first; timed with the packing
+    # launch, in alternation with the direct plan.
+    df, dfd = timed_pair(step_f, step_fd, stream, max(10, args.steps // 2), 4)
+    msf, msfd = sum(df) / len(df), sum(dfd) / len(dfd)
     f8 = {"workload": f"{M}x{N}x{K}, E4M3 inputs (B as [N, K] weights), fp32 accumulation, fp16 out",
-          "plan": {k: g.plan(af, bf, c)[k] for k in ("variant", "tile_id", "split_k")},
+          "plan": {k: pf[k] for k in ("variant", "tile_id", "split_k", "b_path", "workspace_bytes")},
           "ms": msf, "TFLOPS": flops / (msf * 1e-3) / 1e12,
           "frac": flops / (msf * 1e-3) / 1e12 / PEAK_F8_TFLOPS, "peak": PEAK_F8_TFLOPS,
-          "timing": "HIP events around each call"}
-    del bf
+          "direct_TFLOPS_same_loop": flops / (msfd * 1e-3) / 1e12,
+          "timing": "HIP events around each call (packing and product launches), "
+                    "alternating with the direct plan's call"}
 
     # ---- FP8 with B [K, N] row-major, the fp16 workload's own layout
     bfn = torch.from_numpy(synth.matrix(K, N, 4001, synth.TENSOR_B, fmt="e4m3")).to(dev).view(
         torch.float8_e4m3fn)
 
+    pfn = g.plan(af, bfn, c)
+
     def step_fn():
         g.gemm(af, bfn, out=c, stream=stream)
 
-    dfn, _ = timed_launches(step_fn, stream, max(5, args.steps // 5), 2)
-    msfn = sum(dfn) / len(dfn)
+    # In alternation with the [N, K]-weights call above (its packing plan),
+    # so the two B layouts are compared under the same clocks.
+    dfn, dfk = timed_pair(step_fn, step_f, stream, max(10, args.steps // 2), 4)
+    msfn, msfk = sum(dfn) / len(dfn), sum(dfk) / len(dfk)
     f8_bn = {"workload": f"{M}x{N}x{K}, E4M3 inputs, B [K, N] row-major, fp32 accumulation, fp16 out",
-             "plan": {k: g.plan(af, bfn, c)[k] for k in ("variant", "tile_id", "split_k", "b_path")},
+             "plan": {k: pfn[k] for k in ("variant", "tile_id", "split_k", "b_path", "workspace_bytes")},
              "ms": msfn, "TFLOPS": flops / (msfn * 1e-3) / 1e12,
              "frac": flops / (msfn * 1e-3) / 1e12 / PEAK_F8_TFLOPS, "peak": PEAK_F8_TFLOPS,
-             "timing": "HIP events around each call"}
-    del af, bfn
+             "nk_weights_TFLOPS_same_loop": flops / (msfk * 1e-3) / 1e12,
+             "timing": "HIP events around each call, alternating with the [N, K]-weights call"}
+    del af, bf, wsf, bfn
 
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,

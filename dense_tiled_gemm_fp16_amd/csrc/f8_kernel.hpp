@@ -185,9 +185,13 @@ __device__ __forceinline__ u32x4 load_bytes16(const uint8_t* p, int64_t k, int64
 
 // K-contiguous FP8 A and B; formats FA / FB; fp32 partials when PARTIAL.
 // BN: B N-contiguous (B [K, N] row-major) instead of K-contiguous.
-template <int FA, int FB, bool PARTIAL, bool BN = false>
+// BPACK: B pre-packed by the 16-bit packing pass over its byte pairs (the
+// 16 KiB blocks are then the LDS images of this kernel's K-major 64-k B
+// stages; ldb_n is the panel stride in byte pairs).
+template <int FA, int FB, bool PARTIAL, bool BN = false, bool BPACK = false>
 __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
   using CF = F8Cfg;
+  static_assert(!(BN && BPACK), "packed B stages are K-major");
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,10 +222,13 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
 
   // Byte-pair views for the DMA: strides and K offsets halve.
   ASourceS<CF::DMA_A> sa;
-  std::conditional_t<BN, BSourceN8<CF::DMA_B>, BSourceS<CF::DMA_B, true>> sb;
+  std::conditional_t<BPACK, PackedBSource<CF::DMA_B>,
+                     std::conditional_t<BN, BSourceN8<CF::DMA_B>, BSourceS<CF::DMA_B, true>>> sb;
   sa.init(a.A, a.lda_m / 2, 1, a.M, m0, kb / 2, wave, lane);
   if constexpr (BN)
     sb.init(a.B, a.ldb_k, a.N, n0, kb, wave, lane);
+  else if constexpr (BPACK)
+    sb.init(a.B, a.ldb_n, 1, a.N, n0, kb / 2, wave, lane);
   else
     sb.init(a.B, a.ldb_n / 2, 1, a.N, n0, kb / 2, wave, lane);
 
@@ -351,6 +358,8 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       char* st = stage_b(nfull2 + s);
       if constexpr (BN) {
         sb.fill_masked(st, wave, lane, nfull2 + s, kb, ke);
+      } else if constexpr (BPACK) {
+        sb.fill_masked(st, wave, lane, nfull2 + s, kb, ke, 0);   // zero past K already
       } else {
         for (int cell = tid; cell < CF::BN * 4; cell += CF::NT) {
           const int r = cell / 4, c = cell % 4;

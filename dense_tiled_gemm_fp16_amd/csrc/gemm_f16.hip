@@ -230,6 +230,18 @@ int launch_pack_b(const uint16_t* B, int64_t ldb_k, int64_t ldb_n, int64_t K, in
   return GEMM_OK;
 }
 
+// The FP8 packing launch: B [K, N] bytes through their strides into Bp.
+int launch_pack_b8(const uint8_t* B, int64_t ldb_k, int64_t ldb_n, int64_t K, int64_t N, uint8_t* Bp,
+                   hipStream_t stream) {
+  int64_t S = cdiv(K, 64);
+  int64_t slots = (int64_t)(packed_b_bytes(cdiv(K, 2), N) / 16);
+  void* args[] = {&B, &ldb_k, &ldb_n, &K, &N, &S, &slots, &Bp};
+  if (hipLaunchKernel((const void*)pack_b8_kernel, dim3((unsigned)cdiv(slots, 256)), dim3(256), args, 0,
+                      stream) != hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
 // The product launch on a packed B (main variant of the 256 x 256 tile, no
 // split): A K-contiguous with 16-byte aligned rows at most max_ld apart.
 int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* Bp, void* C,
@@ -479,15 +491,19 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   p.grid = grid;
   if ((rc = plan_partials(c, p))) return rc;
 
-  // K-contiguous B under the 256 x 256 tile: its K-major stages take half a
-  // cache line per B row per DMA, about 5% slower than an N-contiguous B.
+  // K-contiguous B under the 256 x 256 tiles: their K-major stages take half
+  // a cache line per B row per DMA, about 5% slower than an N-contiguous B.
   // With many row tiles over each B panel, one packing pass over B (the
   // pre-packed layout, whole lines per DMA) costs less than that, so an
   // automatic plan packs B into the workspace and runs the packed-B kernel.
-  if (allow_pack && variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN &&
-      p.tile_id == TILE_DMA256A128 && p.split == 1 && p.b_path == PATH_KVEC && !f8 &&
-      c.M >= kPackMinRows && c.K <= ti.max_k && ti.packed_fn[c.dt]) {
-    const size_t bytes = packed_b_bytes(c.K, c.N);
+  // The FP8 kernel's K-major 64-k stages have the same half-line DMA; a
+  // K-contiguous FP8 B packs as 16-bit byte pairs (K even) or byte by byte.
+  // (Its N-contiguous B, read with the transposing LDS read, is as fast
+  // as the packed stages, so the packing pass would only add time.)
+  if (allow_pack && variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN && p.split == 1 &&
+      p.b_path == PATH_KVEC && c.M >= kPackMinRows && ti.packed_fn[c.dt] &&
+      (f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k))) {
+    const size_t bytes = packed_b_bytes(f8 ? cdiv(c.K, 2) : c.K, c.N);
     if (bytes > 0) {
       p.pack = true;
       p.ws = bytes;
@@ -588,11 +604,14 @@ int launch_streamk(const Call& c, const Plan& p, KArgs a, kfn_t final_fn, kfn_t 
 
 int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   if (p.gemv_mt) return launch_gemv(c, p, ws, stream);
+  // Packing plan: B into the workspace (K16: K in 16-bit units).
+  const int64_t K16 = c.dt >= DT_F8 ? cdiv(c.K, 2) : c.K;
   if (p.pack) {
-    int rc = launch_pack_b((const uint16_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream);
+    const int rc = c.dt < DT_F8 ? launch_pack_b((const uint16_t*)c.B, 1, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream)
+                   : c.K % 2 == 0
+                       ? launch_pack_b((const uint16_t*)c.B, 1, c.ldb_n / 2, K16, c.N, (uint16_t*)ws, stream)
+                       : launch_pack_b8((const uint8_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint8_t*)ws, stream);
     if (rc) return rc;
-    return launch_packed_product(c.dt, c.A, c.lda_m, c.lda_k, ws, (void*)c.C, c.ldc, c.M, c.N, c.K, p.panel,
-                                 stream);
   }
   const TileInfo& ti = tile_info(p.tile_id);
   KArgs a;
@@ -623,6 +642,13 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   if (p.variant == GEMM_VARIANT_STREAMK) return launch_streamk(c, p, a, ti.final_fn[c.dt][sel],
                                                                ti.partial_fn[c.dt][sel], ws, stream);
   kfn_t fn = (p.split > 1) ? ti.partial_fn[c.dt][sel] : ti.final_fn[c.dt][sel];
+  if (p.pack) {
+    a.B = (const uint16_t*)ws;
+    a.ldb_k = 1;
+    a.ldb_n = cdiv(K16, 32) * 8192;   // 16-bit units per 256-column panel
+    a.W = nullptr;
+    fn = ti.packed_fn[c.dt];
+  }
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
@@ -685,7 +711,7 @@ size_t ws_impl(int dt, int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opt
                               (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
   if (spans(c)) return 0;
   Plan p;
-  if (make_plan(c, opts, p)) return 0;
+  if (make_plan(c, opts, p, false)) return 0;   // split workspaces only (see the packing plan)
   return p.ws;
 }
 

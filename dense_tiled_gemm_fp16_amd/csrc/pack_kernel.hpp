@@ -36,4 +36,29 @@ __global__ __launch_bounds__(256) void pack_b_kernel(const uint16_t* B, int64_t 
       u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
+// FP8 B [K, N] (bytes, any strides) into the same 16 KiB blocks, one per
+// 64 k: byte o of block (p, s) holds, for row r = o / 64 (n = 256 p + r) and
+// 16-byte slot q = (o % 64) / 16, the bytes k = 64 s + 16 (q ^ fa(r)) + e,
+// e = 0..15 (zero past N or K): the LDS image of the FP8 kernel's K-major
+// B stage.  Thread w of a block takes row w % 256 and k chunk w / 256, so
+// the 64 lanes of a wave read 64 consecutive columns of one k-row when B is
+// N-contiguous.
+__global__ __launch_bounds__(256) void pack_b8_kernel(const uint8_t* B, int64_t ldb_k, int64_t ldb_n,
+                                                      int64_t K, int64_t N, int64_t S, int64_t slots,
+                                                      uint8_t* Bp) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= slots) return;
+  const int64_t blk = q / 1024;
+  const int w = (int)(q % 1024), r = w % 256, c = w / 256;
+  const int64_t pnl = blk / S, s = blk - pnl * S;
+  const int64_t n = 256 * pnl + r, k0 = 64 * s + 16 * c;
+  uint32_t h[4] = {0u, 0u, 0u, 0u};
+  if (n < N) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (k0 + e < K) h[e / 4] |= (uint32_t)B[(k0 + e) * ldb_k + n * ldb_n] << (8 * (e % 4));
+  }
+  *reinterpret_cast<u32x4*>(Bp + blk * 16384 + r * 64 + ((c ^ fa(r)) * 16)) = u32x4{h[0], h[1], h[2], h[3]};
+}
+
 }  // namespace gemmf16

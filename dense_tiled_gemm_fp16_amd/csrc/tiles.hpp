@@ -40,7 +40,7 @@ struct TileInfo {
   kfn_t final_fn[NDT][9];  // [format][a_path * 3 + b_path]; nullptr = not supported
   kfn_t partial_fn[NDT][9];
   kfn_t grouped_fn[9];     // grouped launches, fp16 (nullptr: not instantiated)
-  kfn_t packed_fn[2];      // pre-packed B, K-contiguous A, [fp16, bfloat16] (nullptr: none)
+  kfn_t packed_fn[NDT];    // pre-packed B, K-contiguous A, per format (nullptr: none)
   int fallback;         // tile used for layouts this one does not support
   int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
   int64_t max_k;        // largest K the tile's 32-bit step counters cover (0 = any)
@@ -66,7 +66,7 @@ inline void clear_fns(TileInfo& t) {
   for (int d = 0; d < NDT; ++d)
     for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
   for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
-  t.packed_fn[0] = t.packed_fn[1] = nullptr;
+  for (int d = 0; d < NDT; ++d) t.packed_fn[d] = nullptr;
 }
 
 // Register-path tiles: fp16 always; bfloat16 and grouped launches where asked.
@@ -148,6 +148,7 @@ void fill_f8(TileInfo& t) {
   t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_KVEC] = gemm_f8_kernel<FA, FB, true>;
   t.final_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, false, true>;
   t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, true, true>;
+  t.packed_fn[DT_F8 + 2 * FA + FB] = gemm_f8_kernel<FA, FB, false, false, true>;
 }
 
 inline TileInfo make_f8_info(int id) {

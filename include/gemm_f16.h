@@ -139,7 +139,11 @@ int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
  * line per B row per DMA.  The plan reports b_path 3 and workspace_bytes =
  * gemm_f16_packed_b_bytes(K, N).  It runs when workspace is NULL or holds
  * that many bytes; a smaller caller workspace gets the direct plan instead.
- * Both give the same bits.
+ * Both give the same bits.  The *_workspace_bytes functions report split
+ * workspaces only.  gemm_bf16_ex does the same; gemm_f8_ex too, for an FP8
+ * B with K-contiguous rows, packed into 16 KiB blocks of 64 k (workspace
+ * gemm_f16_packed_b_bytes((K + 1) / 2, N)); an N-contiguous FP8 B is never
+ * packed.
  */
 int gemm_f16_ex(const void* A, int64_t lda_m, int64_t lda_k,
                 const void* B, int64_t ldb_k, int64_t ldb_n,

@@ -102,7 +102,7 @@ def test_f8_moe_shape_sampled():
     a = torch.from_numpy(A).to(DEV).view(torch.float8_e4m3fn)
     b = torch.from_numpy(Bt).to(DEV).view(torch.float8_e4m3fn).t()
     p = g.plan(a, b)
-    assert p["tile_id"] == 15
+    assert p["tile_id"] == 15 and p["b_path"] == "packed", p     # the packing plan
     say(f"f8 MoE: launch {p}")
     c = g.gemm(a, b)
     torch.cuda.synchronize()
@@ -110,6 +110,34 @@ def test_f8_moe_shape_sampled():
     rng = np.random.default_rng(14300)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
     assert_close(got[rows], reference(A, Bt, "e4m3", "e4m3", rows), "f8 MoE sampled rows")
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3")])
+def test_f8_auto_packs_kcontig_b(fa, fb):
+    # M past the packing threshold, ragged M, N and K (700 = 5 x 128 + 60):
+    # B packed as byte pairs, then the packed-B FP8 kernel; same bits as the
+    # oracle and as the direct plan.
+    M, N, K = 16384 + 37, 300, 700
+    A, Bt = inputs(M, N, K, 14400, "int", fa, fb)
+    ref = reference(A, Bt, fa, fb)
+    a, b = f8_rows(A, fa), f8_rows(Bt, fb).t()
+    p = g.plan(a, b)
+    assert p["b_path"] == "packed" and p["tile_id"] == 15, p
+    assert p["workspace_bytes"] == g.lib.gemm_f16_packed_b_bytes(K // 2, N), p
+    assert_bits_equal(run(a, b, Out(M, N)), ref, f"f8 packing plan {fa}x{fb}")
+    assert g.plan(a, b, variant="main")["b_path"] == "kvec"
+    assert_bits_equal(run(a, b, Out(M, N), variant="main"), ref, f"f8 direct plan {fa}x{fb}")
+
+
+def test_f8_odd_k_packed_bytewise():
+    # K odd: the byte-pair packing cannot zero the byte past K, so B packs
+    # byte by byte; 701 = 5 x 128 + 61.
+    M, N, K = 16384, 264, 701
+    A, Bt = inputs(M, N, K, 14500, "int", "e4m3", "e4m3")
+    a, b = f8_rows(A, "e4m3"), f8_rows(Bt, "e4m3").t()
+    p = g.plan(a, b)
+    assert p["b_path"] == "packed" and p["workspace_bytes"] == g.lib.gemm_f16_packed_b_bytes(351, N), p
+    assert_bits_equal(run(a, b, Out(M, N)), reference(A, Bt, "e4m3", "e4m3"), "f8 odd K")
 
 
 def test_f8_stride_limit():
@@ -173,6 +201,18 @@ def test_f8_bn_parity_ragged(fa, fb, mode):
             assert_bits_equal(got, ref, what)
         else:
             assert_close(got, ref, what)
+
+
+@pytest.mark.parametrize("fa,fb,K", [("e4m3", "e5m2", 700), ("e5m2", "e5m2", 333)])
+def test_f8_bn_large_m_direct(fa, fb, K):
+    # B [K, N] row-major past the packing threshold stays on the direct
+    # N-major path (as fast as packed stages); ragged M, N and K.
+    M, N = 16384 + 37, 304
+    A, B = inputs_bn(M, N, K, 14800 + K, "int", fa, fb)
+    a, b = f8_rows(A, fa), f8_krows(B, fb)
+    p = g.plan(a, b)
+    assert p["b_path"] == "rvec" and p["tile_id"] == 15 and p["workspace_bytes"] == 0, p
+    assert_bits_equal(run(a, b, Out(M, N)), reference_bn(A, B, fa, fb), f"f8 B [K, N] {fa}x{fb} K={K}")
 
 
 @pytest.mark.parametrize("K", [1, 7, 64, 100, 128, 192, 255, 384])
