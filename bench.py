@@ -200,7 +200,7 @@ CONFIGS = [
     ("skinny_m1", 1, 2048, 7168, "row"), ("skinny_m16", 16, 2048, 7168, "row"),
     ("skinny_m64", 64, 2048, 7168, "row"), ("splitk_512x512x65536", 512, 512, 65536, "row"),
     ("moe_131072x2048x7168", 131072, 2048, 7168, "row"),
-    ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col", ("main",)),
+    ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col", ("main", "streamk")),
     # not a task workload: 17 x 16 tiles, a final wave of 16 tiles on 256 CUs
     ("tail_4352x4096x8192", 4352, 4096, 8192, "row", ("main",)),
 ]
@@ -270,7 +270,7 @@ def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant):
     print(json.dumps({"config": name, "M": m, "N": n, "K": k, "b_layout": bl,
                       "forced": variant,
                       "plan": {q: p[q] for q in ("variant", "tile_id", "split_k", "grid",
-                                                 "sk_tiles")},
+                                                 "sk_tiles", "b_path")},
                       "us_per_call": ms * 1e3, "TFLOPS": tf, "GBps": gbs, "AI": ai,
                       "bound": bound,
                       "frac": tf / PEAK_F16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS,

@@ -100,7 +100,8 @@ struct Plan {
   int red_lanes;  // lanes per output quad in the split reduction
   int64_t GM, GN, grid, grid2, k_split;
   int64_t sk_tiles;  // STREAMK: tiles split over K after the whole waves
-  bool pack;         // B is packed into the workspace first (see make_plan)
+  bool pack;         // B is packed into the workspace first (see maybe_pack)
+  size_t pack_bytes; // its size; stream-K partials follow it
   size_t ws;
 };
 
@@ -280,10 +281,36 @@ int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, c
   return GEMM_OK;
 }
 
+// K-contiguous B under the 256 x 256 tiles: their K-major stages take half
+// a cache line per B row per DMA, about 5% slower than an N-contiguous B.
+// With many row tiles over each B panel, one packing pass over B (the
+// pre-packed layout, whole lines per DMA) costs less than that, so an
+// automatic MAIN or STREAMK plan packs B into the front of the workspace
+// (stream-K partials follow it) and runs the packed-B kernels.  The FP8
+// kernel's K-major 64-k stages have the same half-line DMA; a K-contiguous
+// FP8 B packs as 16-bit byte pairs (K even) or byte by byte.  (Its
+// N-contiguous B, read with the transposing LDS read, is as fast as the
+// packed stages, so the packing pass would only add time.)
+void maybe_pack(const Call& c, int variant, bool allow_pack, Plan& p) {
+  const TileInfo& ti = tile_info(p.tile_id);
+  const bool f8 = c.dt >= DT_F8;
+  const bool sk = p.variant == GEMM_VARIANT_STREAMK;
+  if (!allow_pack || variant != GEMM_VARIANT_AUTO || !(sk || (p.variant == GEMM_VARIANT_MAIN && p.split == 1)) ||
+      p.b_path != PATH_KVEC || c.M < kPackMinRows || !ti.packed_fn[c.dt] || !ti.packed_partial_fn[c.dt] ||
+      !(f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k)))
+    return;
+  const size_t bytes = packed_b_bytes(f8 ? cdiv(c.K, 2) : c.K, c.N);
+  if (bytes == 0 || p.ws > SIZE_MAX - bytes) return;
+  p.pack = true;
+  p.pack_bytes = bytes;
+  p.ws += bytes;
+}
+
 int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = true) {
   int rc = check_opts(o);
   if (rc) return rc;
   p.pack = false;
+  p.pack_bytes = 0;
   const int variant = o ? o->variant : GEMM_VARIANT_AUTO;
   const int want_split = o ? o->split_k : 0;
   const int want_panel = o ? o->panel : 0;
@@ -450,6 +477,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     if (__builtin_mul_overflow(L * p.split, (int64_t)ti.bm * ti.bn * 4, &bytes) || bytes > INT64_MAX - 256)
       return GEMM_ERR_SHAPE;
     p.ws = (size_t)((bytes + 255) / 256 * 256);
+    maybe_pack(c, variant, allow_pack, p);
     return GEMM_OK;
   }
 
@@ -491,25 +519,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   p.grid = grid;
   if ((rc = plan_partials(c, p))) return rc;
 
-  // K-contiguous B under the 256 x 256 tiles: their K-major stages take half
-  // a cache line per B row per DMA, about 5% slower than an N-contiguous B.
-  // With many row tiles over each B panel, one packing pass over B (the
-  // pre-packed layout, whole lines per DMA) costs less than that, so an
-  // automatic plan packs B into the workspace and runs the packed-B kernel.
-  // The FP8 kernel's K-major 64-k stages have the same half-line DMA; a
-  // K-contiguous FP8 B packs as 16-bit byte pairs (K even) or byte by byte.
-  // (Its N-contiguous B, read with the transposing LDS read, is as fast
-  // as the packed stages, so the packing pass would only add time.)
-  if (allow_pack && variant == GEMM_VARIANT_AUTO && p.variant == GEMM_VARIANT_MAIN && p.split == 1 &&
-      p.b_path == PATH_KVEC && c.M >= kPackMinRows && ti.packed_fn[c.dt] &&
-      (f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k))) {
-    const size_t bytes = packed_b_bytes(f8 ? cdiv(c.K, 2) : c.K, c.N);
-    if (bytes > 0) {
-      p.pack = true;
-      p.ws = bytes;
-      p.grid2 = cdiv((int64_t)(bytes / 16), 256);   // the packing launch
-    }
-  }
+  maybe_pack(c, variant, allow_pack, p);
   return GEMM_OK;
 }
 
@@ -639,16 +649,18 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   a.sk_first = 0;
   a.sk_tiles = 0;
   const int sel = p.a_path * 3 + p.b_path;
-  if (p.variant == GEMM_VARIANT_STREAMK) return launch_streamk(c, p, a, ti.final_fn[c.dt][sel],
-                                                               ti.partial_fn[c.dt][sel], ws, stream);
-  kfn_t fn = (p.split > 1) ? ti.partial_fn[c.dt][sel] : ti.final_fn[c.dt][sel];
-  if (p.pack) {
+  kfn_t final_fn = ti.final_fn[c.dt][sel], partial_fn = ti.partial_fn[c.dt][sel];
+  if (p.pack) {   // the packed B at the front of the workspace, partials after it
     a.B = (const uint16_t*)ws;
     a.ldb_k = 1;
     a.ldb_n = cdiv(K16, 32) * 8192;   // 16-bit units per 256-column panel
-    a.W = nullptr;
-    fn = ti.packed_fn[c.dt];
+    final_fn = ti.packed_fn[c.dt];
+    partial_fn = ti.packed_partial_fn[c.dt];
+    ws = (char*)ws + p.pack_bytes;
+    a.W = (float*)ws;
   }
+  if (p.variant == GEMM_VARIANT_STREAMK) return launch_streamk(c, p, a, final_fn, partial_fn, ws, stream);
+  kfn_t fn = (p.split > 1) ? partial_fn : final_fn;
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;

@@ -41,6 +41,7 @@ struct TileInfo {
   kfn_t partial_fn[NDT][9];
   kfn_t grouped_fn[9];     // grouped launches, fp16 (nullptr: not instantiated)
   kfn_t packed_fn[NDT];    // pre-packed B, K-contiguous A, per format (nullptr: none)
+  kfn_t packed_partial_fn[NDT];  // the same writing fp32 partials (stream-K tails)
   int fallback;         // tile used for layouts this one does not support
   int n_mult;           // N-contiguous B needs N to be a multiple of this (0 = any)
   int64_t max_k;        // largest K the tile's 32-bit step counters cover (0 = any)
@@ -66,7 +67,7 @@ inline void clear_fns(TileInfo& t) {
   for (int d = 0; d < NDT; ++d)
     for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
   for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
-  for (int d = 0; d < NDT; ++d) t.packed_fn[d] = nullptr;
+  for (int d = 0; d < NDT; ++d) t.packed_fn[d] = t.packed_partial_fn[d] = nullptr;
 }
 
 // Register-path tiles: fp16 always; bfloat16 and grouped launches where asked.
@@ -132,6 +133,8 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   t.grouped_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, true>;
   t.packed_fn[DT_F16] = gemm_dma_a128_kernel<CF, true, false, false, DT_F16, true>;
   t.packed_fn[DT_BF16] = gemm_dma_a128_kernel<CF, true, false, false, DT_BF16, true>;
+  t.packed_partial_fn[DT_F16] = gemm_dma_a128_kernel<CF, true, true, false, DT_F16, true>;
+  t.packed_partial_fn[DT_BF16] = gemm_dma_a128_kernel<CF, true, true, false, DT_BF16, true>;
   t.fallback = fallback;
   t.n_mult = 8;
   t.max_k = INT64_C(1) << 36;   // 64-k super-steps counted in int
@@ -149,6 +152,7 @@ void fill_f8(TileInfo& t) {
   t.final_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, false, true>;
   t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, true, true>;
   t.packed_fn[DT_F8 + 2 * FA + FB] = gemm_f8_kernel<FA, FB, false, false, true>;
+  t.packed_partial_fn[DT_F8 + 2 * FA + FB] = gemm_f8_kernel<FA, FB, true, false, true>;
 }
 
 inline TileInfo make_f8_info(int id) {

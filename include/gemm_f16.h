@@ -133,12 +133,13 @@ int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
  * initialisation and its contents are garbage afterwards.  opts may be NULL.
  *
  * Packing plan (AUTO only): with K-contiguous B (ldb_k == 1), M >= 16384 and
- * the MAIN family on the 256x256 LDS-DMA tile, the call first packs B into
- * the workspace in the layout of gemm_f16_pack_b (one pass over B) and then
- * runs the packed-B product: the direct K-major B stages take half a cache
- * line per B row per DMA.  The plan reports b_path 3 and workspace_bytes =
- * gemm_f16_packed_b_bytes(K, N).  It runs when workspace is NULL or holds
- * that many bytes; a smaller caller workspace gets the direct plan instead.
+ * the MAIN (unsplit) or STREAMK family on the 256x256 LDS-DMA tile, the call
+ * first packs B into the front of the workspace in the layout of
+ * gemm_f16_pack_b (one pass over B) and then runs the packed-B kernels: the
+ * direct K-major B stages take half a cache line per B row per DMA.  The
+ * plan reports b_path 3 and workspace_bytes = gemm_f16_packed_b_bytes(K, N)
+ * plus the stream-K partials.  It runs when workspace is NULL or holds that
+ * many bytes; a smaller caller workspace gets the direct plan instead.
  * Both give the same bits.  The *_workspace_bytes functions report split
  * workspaces only.  gemm_bf16_ex does the same; gemm_f8_ex too, for an FP8
  * B with K-contiguous rows, packed into 16 KiB blocks of 64 k (workspace

@@ -129,6 +129,24 @@ def test_f8_auto_packs_kcontig_b(fa, fb):
     assert_bits_equal(run(a, b, Out(M, N), variant="main"), ref, f"f8 direct plan {fa}x{fb}")
 
 
+def test_f8_auto_pack_streamk():
+    # 325 tiles: a stream-K tail of 69; the packed FP8 B in front of the
+    # partials, against the same split forced without packing.
+    M, N, K = 16384 + 37, 1061, 2100
+    A, Bt = inputs(M, N, K, 14900, "int", "e4m3", "e4m3")
+    a, b = f8_rows(A, "e4m3"), f8_rows(Bt, "e4m3").t()
+    p = g.plan(a, b)
+    if p["variant"] != "streamk":
+        pytest.skip(f"this device's compute-unit count gives no stream-K tail here: {p}")
+    assert p["b_path"] == "packed", p
+    got = run(a, b, Out(M, N))
+    direct = run(a, b, Out(M, N), variant="streamk", split_k=p["split_k"])
+    assert_bits_equal(got, direct, "f8 stream-K packed vs direct")
+    rng = np.random.default_rng(14900)
+    rows = np.unique(np.concatenate([[0, 255, 16383, 16384, M - 1], rng.integers(0, M, 8)]))
+    assert_bits_equal(got[rows], reference(A, Bt, "e4m3", "e4m3", rows), "f8 stream-K sampled rows")
+
+
 def test_f8_odd_k_packed_bytewise():
     # K odd: the byte-pair packing cannot zero the byte past K, so B packs
     # byte by byte; 701 = 5 x 128 + 61.

@@ -173,3 +173,31 @@ def test_auto_pack_moe_shape_sampled():
     rng = np.random.default_rng(15500)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
     assert_close(got[rows], reference(A, B, rows), "K-contiguous B MoE sampled rows")
+
+
+def test_auto_pack_streamk():
+    # 65 x 5 = 325 tiles on 256 compute units: a final wave of 69 tiles, so
+    # the automatic plan is stream-K, here with the packed B in front of the
+    # partials.  Same split forced without packing must give the same bits.
+    M, N, K = 16384 + 37, 1061, 2100
+    A, B, a, b = _kcontig_case(M, N, K, 15600)
+    p = g.plan(a, b)
+    if p["variant"] != "streamk":
+        pytest.skip(f"this device's compute-unit count gives no stream-K tail here: {p}")
+    assert p["b_path"] == "packed", p
+    assert p["workspace_bytes"] > g.lib.gemm_f16_packed_b_bytes(K, N), p
+    say(f"stream-K packing plan {p}")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    pd = g.plan(a, b, variant="streamk", split_k=p["split_k"])
+    assert pd["b_path"] == "kvec" and pd["sk_tiles"] == p["sk_tiles"], pd
+    say(f"stream-K direct plan {pd}")
+    out2 = Out(M, N)
+    g.gemm(a, b, out=out2.view, variant="streamk", split_k=p["split_k"])
+    torch.cuda.synchronize()
+    assert_bits_equal(got, out2.result(), "stream-K packed vs direct")
+    rng = np.random.default_rng(15600)
+    rows = np.unique(np.concatenate([[0, 255, 16383, 16384, M - 1], rng.integers(0, M, 8)]))
+    assert_bits_equal(got[rows], reference(A, B, rows), "stream-K packing plan sampled rows")
