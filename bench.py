@@ -77,7 +77,7 @@ MAIN_KERNEL = "void gemmf16::gemm_dma_a128_kernel<gemmf16::DmaA128Cfg<4, 2>, fal
 
 
 def summarize_pmc(fetch_csv, write_csv):
-    """Per-launch HBM bytes of this build's kernels from FETCH_SIZE / WRITE_SIZE.
+    """Per-launch HBM bytes of the library's kernels from FETCH_SIZE / WRITE_SIZE.
 
     Each counter is scaled by bytes-moved / counter-reading of the 1 GiB
     device copy (the largest dispatches of the runtime's copy kernel in the
@@ -191,8 +191,9 @@ def cpu_baseline(budget_s=15.0):
                       f"full K), {dt:.1f} s"}
 
 
-# The five workload families of the task, as (name, M, N, K, B layout); the
-# configurations sweep times each one (not the headline line).
+# The workload families (the pages' shapes and the MoE product), as (name,
+# M, N, K, B layout[, forced variants]); the configurations sweep times each
+# one (not the headline line).
 CONFIGS = [
     ("edge_130x70x65", 130, 70, 65, "row"), ("edge_130x70x65_bt", 130, 70, 65, "col"),
     ("square_256", 256, 256, 256, "row"), ("square_1024", 1024, 1024, 1024, "row"),
@@ -201,7 +202,7 @@ CONFIGS = [
     ("skinny_m64", 64, 2048, 7168, "row"), ("splitk_512x512x65536", 512, 512, 65536, "row"),
     ("moe_131072x2048x7168", 131072, 2048, 7168, "row"),
     ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col", ("main", "streamk")),
-    # not a task workload: 17 x 16 tiles, a final wave of 16 tiles on 256 CUs
+    # not one of the pages' workloads: 17 x 16 tiles, a final wave of 16 tiles on 256 CUs
     ("tail_4352x4096x8192", 4352, 4096, 8192, "row", ("main",)),
 ]
 
