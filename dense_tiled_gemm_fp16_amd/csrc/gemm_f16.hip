@@ -205,6 +205,7 @@ bool tile_takes(const TileInfo& t, const Call& c, const Plan& p) {
 bool dma_tile_takes(const Call& c, const Plan& p) { return tile_takes(tile_info(TILE_DMA256A128), c, p); }
 
 constexpr int64_t kPackMinRows = 16384;   // automatic plans pack a K-contiguous B from this M on
+constexpr int64_t kPackMinRowsGather = 4096;   // and a B the DMA tile cannot read from this M on
 constexpr int32_t kBPathPacked = 3;       // b_path reported for a packing plan
 
 // Pre-packed B: ceil(N/256) panels of ceil(K/32) blocks of 16 KiB (see
@@ -291,12 +292,13 @@ int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, c
 // FP8 B packs as 16-bit byte pairs (K even) or byte by byte.  (Its
 // N-contiguous B, read with the transposing LDS read, is as fast as the
 // packed stages, so the packing pass would only add time.)
-void maybe_pack(const Call& c, int variant, bool allow_pack, Plan& p) {
+void maybe_pack(const Call& c, int variant, bool allow_pack, Plan& p, bool any_b) {
   const TileInfo& ti = tile_info(p.tile_id);
   const bool f8 = c.dt >= DT_F8;
   const bool sk = p.variant == GEMM_VARIANT_STREAMK;
   if (!allow_pack || variant != GEMM_VARIANT_AUTO || !(sk || (p.variant == GEMM_VARIANT_MAIN && p.split == 1)) ||
-      p.b_path != PATH_KVEC || c.M < kPackMinRows || !ti.packed_fn[c.dt] || !ti.packed_partial_fn[c.dt] ||
+      p.b_path != PATH_KVEC || c.M < (any_b ? kPackMinRowsGather : kPackMinRows) || !ti.packed_fn[c.dt] ||
+      !ti.packed_partial_fn[c.dt] ||
       !(f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k)))
     return;
   const size_t bytes = packed_b_bytes(f8 ? cdiv(c.K, 2) : c.K, c.N);
@@ -364,6 +366,16 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
 
   p.a_path = f8 ? PATH_KVEC : classify(c.A, c.lda_m, c.lda_k);
   p.b_path = f8 ? (c.ldb_k == 1 ? PATH_KVEC : PATH_RVEC) : classify(c.B, c.ldb_n, c.ldb_k);
+  // A B that the LDS-DMA tile cannot read directly (rows not 16-byte
+  // aligned, or neither dimension contiguous) would take the element-wise
+  // path on the 128x128 tile, at less than half the rate.  An automatic plan
+  // with enough rows packs it instead (the packing pass reads any strides)
+  // and is planned as for a K-contiguous B; if no packing plan comes of it,
+  // the call is planned again with B's own path.
+  const bool pack_any = allow_pack && variant == GEMM_VARIANT_AUTO && !f8 && p.variant == GEMM_VARIANT_MAIN &&
+                        c.M >= kPackMinRowsGather && p.a_path == PATH_KVEC &&
+                        (p.b_path == PATH_GATHER || (p.b_path == PATH_RVEC && c.N % 8 != 0));
+  if (pack_any) p.b_path = PATH_KVEC;
 
   // Tile.
   switch (p.variant) {
@@ -477,7 +489,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     if (__builtin_mul_overflow(L * p.split, (int64_t)ti.bm * ti.bn * 4, &bytes) || bytes > INT64_MAX - 256)
       return GEMM_ERR_SHAPE;
     p.ws = (size_t)((bytes + 255) / 256 * 256);
-    maybe_pack(c, variant, allow_pack, p);
+    maybe_pack(c, variant, allow_pack, p, pack_any);
+    if (pack_any && !p.pack) return make_plan(c, o, p, false);
     return GEMM_OK;
   }
 
@@ -519,7 +532,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   p.grid = grid;
   if ((rc = plan_partials(c, p))) return rc;
 
-  maybe_pack(c, variant, allow_pack, p);
+  maybe_pack(c, variant, allow_pack, p, pack_any);
+  if (pack_any && !p.pack) return make_plan(c, o, p, false);
   return GEMM_OK;
 }
 
@@ -617,7 +631,7 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   // Packing plan: B into the workspace (K16: K in 16-bit units).
   const int64_t K16 = c.dt >= DT_F8 ? cdiv(c.K, 2) : c.K;
   if (p.pack) {
-    const int rc = c.dt < DT_F8 ? launch_pack_b((const uint16_t*)c.B, 1, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream)
+    const int rc = c.dt < DT_F8 ? launch_pack_b((const uint16_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream)
                    : c.K % 2 == 0
                        ? launch_pack_b((const uint16_t*)c.B, 1, c.ldb_n / 2, K16, c.N, (uint16_t*)ws, stream)
                        : launch_pack_b8((const uint8_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint8_t*)ws, stream);

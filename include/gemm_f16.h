@@ -140,6 +140,10 @@ int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
  * plan reports b_path 3 and workspace_bytes = gemm_f16_packed_b_bytes(K, N)
  * plus the stream-K partials.  It runs when workspace is NULL or holds that
  * many bytes; a smaller caller workspace gets the direct plan instead.
+ * The same holds from M >= 4096 for a 16-bit B that the LDS-DMA tile cannot
+ * read directly (rows not 16-byte aligned, or neither dimension contiguous),
+ * which would otherwise take the element-wise path of the 128x128 tile: the
+ * packing pass reads B through its strides.
  * Both give the same bits.  The *_workspace_bytes functions report split
  * workspaces only.  gemm_bf16_ex does the same; gemm_f8_ex too, for an FP8
  * B with K-contiguous rows, packed into 16 KiB blocks of 64 k (workspace

@@ -201,3 +201,39 @@ def test_auto_pack_streamk():
     rng = np.random.default_rng(15600)
     rows = np.unique(np.concatenate([[0, 255, 16383, 16384, M - 1], rng.integers(0, M, 8)]))
     assert_bits_equal(got[rows], reference(A, B, rows), "stream-K packing plan sampled rows")
+
+
+def _gather_b_case(M, N, K, seed, layout):
+    A = synth.matrix(M, K, seed, 0, "int")
+    B = synth.matrix(K, N, seed, 1, "int")
+    a = place(A, "row", (1, (-K) % 8 + 8))
+    if layout == "row_unaligned":            # rows of N halves, N odd: not 16-byte aligned
+        b = to_dev(B)
+    else:                                    # every other column of a wider buffer
+        wide = np.zeros((K, 2 * N), dtype=np.uint16)
+        wide[:, ::2] = B
+        b = to_dev(wide)[:, ::2]
+    return A, B, a, b
+
+
+@pytest.mark.parametrize("layout", ["row_unaligned", "strided"])
+def test_auto_packs_b_the_dma_tile_cannot_read(layout):
+    # Enough 256 x 256 tiles for half a wave, so the plan takes that tile.
+    M, N, K = (8192 + 37, 1061, 700) if layout == "row_unaligned" else (16384 + 37, 300, 700)
+    A, B, a, b = _gather_b_case(M, N, K, 15700, layout)
+    assert g.plan(a, b, variant="main")["b_path"] == "gather"
+    p = g.plan(a, b)
+    assert p["b_path"] == "packed" and p["tile_id"] == 14, p
+    ref = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, nthreads=ORACLE_THREADS)
+    say(f"packing plan for a {layout} B {M}x{N}x{K} stride {b.stride()}")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    assert_bits_equal(out.result(), ref, f"packing plan, {layout} B")
+    # No room in the caller's workspace: the element-wise plan, same bits.
+    small = torch.empty(1024, dtype=torch.float32, device=DEV)
+    say(f"{layout} B with a too-small workspace")
+    out2 = Out(M, N)
+    g.gemm(a, b, out=out2.view, workspace=small)
+    torch.cuda.synchronize()
+    assert_bits_equal(out2.result(), ref, f"element-wise plan, {layout} B")
