@@ -1,0 +1,80 @@
+"""Seeded randomized parity at large M, where the automatic plans pack B
+(K-contiguous B from M = 16384, a B the LDS-DMA tile cannot read from
+M = 4096) and take the stream-K tail; each B layout is drawn three times.  Integer inputs in [-4, 4] keep every
+fp32 sum exact, so the automatic plan, the forced main plan (never packed)
+and the oracle's sampled rows must agree bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_gemm_fp16_amd as g
+import oracle
+import synth
+from gpu_util import DEV, ORACLE_THREADS, Out, assert_bits_equal, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _b_view(B, layout, fmt):
+    K, N = B.shape
+    if layout == "row":
+        v = to_dev(B)
+    elif layout == "col":                      # [N, K] rows, K padded to 8
+        ld = K + (-K) % 8
+        buf = np.zeros((N, ld), dtype=np.uint16)
+        buf[:, :K] = B.T
+        v = to_dev(buf)[:, :K].t()
+    elif layout == "unaligned":                # rows of N + 1 halves (odd pitch when N is even)
+        ld = N + 1 if N % 2 == 0 else N + 2
+        buf = np.zeros((K, ld), dtype=np.uint16)
+        buf[:, :N] = B
+        v = to_dev(buf)[:, :N]
+    else:                                      # every other column of a wider buffer
+        wide = np.zeros((K, 2 * N), dtype=np.uint16)
+        wide[:, ::2] = B
+        v = to_dev(wide)[:, ::2]
+    return v.view(torch.bfloat16) if fmt == "bf16" else v
+
+
+def _case(seed):
+    rng = np.random.default_rng(seed)
+    layout = ["row", "col", "unaligned", "strided"][seed % 4]
+    M = int(rng.integers(16384 if layout == "col" else 4096, 32769))   # col: past the packing threshold
+    N = int(rng.integers(1, 2201))
+    K = int(rng.integers(1, 3001))
+    fmt = "bf16" if rng.random() < 0.3 else "f16"
+    return M, N, K, layout, fmt
+
+
+@pytest.mark.parametrize("seed", range(19000, 19012))
+def test_random_large_case(seed):
+    M, N, K, layout, fmt = _case(seed)
+    A = synth.matrix(M, K, seed, 0, "int", fmt=fmt)
+    B = synth.matrix(K, N, seed, 1, "int", fmt=fmt)
+    ld = K + (-K) % 8
+    abuf = np.zeros((M, ld), dtype=np.uint16)
+    abuf[:, :K] = A
+    a = to_dev(abuf)[:, :K]
+    if fmt == "bf16":
+        a = a.view(torch.bfloat16)
+    b = _b_view(B, layout, fmt)
+    p = g.plan(a, b)
+    say(f"large fuzz seed={seed} {fmt} {M}x{N}x{K} B={layout} stride={b.stride()} -> {p}")
+    out = Out(M, N)
+    if fmt == "bf16":
+        out.view = out.view.view(torch.bfloat16)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    out2 = Out(M, N)
+    if fmt == "bf16":
+        out2.view = out2.view.view(torch.bfloat16)
+    g.gemm(a, b, out=out2.view, variant="main")
+    torch.cuda.synchronize()
+    assert_bits_equal(got, out2.result(), f"seed {seed}: automatic plan {p} vs forced main")
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 14)]))
+    ref = oracle.gemm(np.ascontiguousarray(A[rows]), (K, 1), B, (N, 1), len(rows), N, K,
+                      nthreads=ORACLE_THREADS, dtype="bf16" if fmt == "bf16" else "f16")
+    assert_bits_equal(got[rows], ref, f"seed {seed}: sampled rows against the oracle")
