@@ -748,6 +748,7 @@ constexpr int32_t kMaxGroups = 1 << 20;
 size_t grouped_ws_bytes(int32_t G) { return (size_t)((16 * ((int64_t)G + 1) + 255) / 256 * 256); }
 
 struct GroupCall {
+  int dt;  // DT_F16 or DT_BF16
   const void *A, *B, *C;
   const int64_t* off;
   int64_t lda_m, lda_k, ldb_g, ldb_k, ldb_n, ldc, M, N, K;
@@ -787,7 +788,7 @@ int grouped_plan(const GroupCall& c, int* tile_id, kfn_t* fn, int64_t* grid) {
   const bool ldb_g_ok = c.ldb_g % 8 == 0;   // every group's B keeps the 16-byte alignment
   int id = TILE_T128;
   const TileInfo& d = tile_info(TILE_DMA256A128);
-  if (ldb_g_ok && c.M >= (int64_t)256 * c.G && d.grouped_fn[a_path * 3 + b_path] &&
+  if (ldb_g_ok && c.M >= (int64_t)256 * c.G && d.grouped_fn[c.dt][a_path * 3 + b_path] &&
       !(b_path == PATH_RVEC && (c.N % d.n_mult != 0 || c.N < d.n_mult)) && !(c.K > d.max_k) &&
       !(std::max(std::max(c.lda_m, c.lda_k), std::max(c.ldb_k, c.ldb_n)) > d.max_ld))
     id = TILE_DMA256A128;
@@ -795,7 +796,7 @@ int grouped_plan(const GroupCall& c, int* tile_id, kfn_t* fn, int64_t* grid) {
   // Layout classes were taken on group 0's B; other groups share them only if
   // ldb_g keeps the alignment, else take the element-wise path for B.
   const int bp = ldb_g_ok ? b_path : PATH_GATHER;
-  *fn = ti.grouped_fn[a_path * 3 + bp];
+  *fn = ti.grouped_fn[c.dt][a_path * 3 + bp];
   if (!*fn) return GEMM_ERR_OPTS;
   const int64_t GN = cdiv(c.N, ti.bn), rows = cdiv(c.M, ti.bm) + c.G;
   if (__builtin_mul_overflow(rows, GN, grid) || *grid > (INT64_C(1) << 31) - 1) return GEMM_ERR_SHAPE;
@@ -845,15 +846,11 @@ int launch_grouped(const GroupCall& c, int tile_id, kfn_t fn, int64_t grid, void
   return GEMM_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_f16_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_g,
-                     int64_t ldb_k, int64_t ldb_n, void* C, int64_t ldc, const int64_t* offsets,
-                     int32_t G, int64_t M_total, int64_t N, int64_t K, void* stream,
-                     void* workspace, size_t workspace_bytes) {
-  GroupCall c{A, B, C, offsets, lda_m, lda_k, ldb_g, ldb_k, ldb_n, ldc, M_total, N, K, G, 0, 0, 0};
+int grouped_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_g,
+                 int64_t ldb_k, int64_t ldb_n, void* C, int64_t ldc, const int64_t* offsets, int32_t G,
+                 int64_t M_total, int64_t N, int64_t K, void* stream, void* workspace,
+                 size_t workspace_bytes) {
+  GroupCall c{dt, A, B, C, offsets, lda_m, lda_k, ldb_g, ldb_k, ldb_n, ldc, M_total, N, K, G, 0, 0, 0};
   int rc = validate_grouped(c);
   if (rc) return rc;
   int tile_id = 0;
@@ -878,6 +875,26 @@ int gemm_f16_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B,
   rc = launch_grouped(c, tile_id, fn, grid, ws, s);
   if (hipFreeAsync(ws, s) != hipSuccess && rc == GEMM_OK) rc = GEMM_ERR_HIP;
   return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_g,
+                     int64_t ldb_k, int64_t ldb_n, void* C, int64_t ldc, const int64_t* offsets,
+                     int32_t G, int64_t M_total, int64_t N, int64_t K, void* stream,
+                     void* workspace, size_t workspace_bytes) {
+  return grouped_impl(DT_F16, A, lda_m, lda_k, B, ldb_g, ldb_k, ldb_n, C, ldc, offsets, G, M_total, N, K,
+                      stream, workspace, workspace_bytes);
+}
+
+int gemm_bf16_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_g,
+                      int64_t ldb_k, int64_t ldb_n, void* C, int64_t ldc, const int64_t* offsets,
+                      int32_t G, int64_t M_total, int64_t N, int64_t K, void* stream,
+                      void* workspace, size_t workspace_bytes) {
+  return grouped_impl(DT_BF16, A, lda_m, lda_k, B, ldb_g, ldb_k, ldb_n, C, ldc, offsets, G, M_total, N, K,
+                      stream, workspace, workspace_bytes);
 }
 
 size_t gemm_f16_grouped_workspace_bytes(int32_t G) {

@@ -39,7 +39,7 @@ struct TileInfo {
   int id, bm, bn, bk, nt;
   kfn_t final_fn[NDT][9];  // [format][a_path * 3 + b_path]; nullptr = not supported
   kfn_t partial_fn[NDT][9];
-  kfn_t grouped_fn[9];     // grouped launches, fp16 (nullptr: not instantiated)
+  kfn_t grouped_fn[2][9];  // grouped launches, [fp16, bfloat16] (nullptr: not instantiated)
   kfn_t packed_fn[NDT];    // pre-packed B, K-contiguous A, per format (nullptr: none)
   kfn_t packed_partial_fn[NDT];  // the same writing fp32 partials (stream-K tails)
   int fallback;         // tile used for layouts this one does not support
@@ -66,7 +66,7 @@ inline void clear_fns(TileInfo& t) {
   t.max_ld = 0;
   for (int d = 0; d < NDT; ++d)
     for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
-  for (int i = 0; i < 9; ++i) t.grouped_fn[i] = nullptr;
+  for (int i = 0; i < 9; ++i) t.grouped_fn[DT_F16][i] = t.grouped_fn[DT_BF16][i] = nullptr;
   for (int d = 0; d < NDT; ++d) t.packed_fn[d] = t.packed_partial_fn[d] = nullptr;
 }
 
@@ -86,7 +86,10 @@ TileInfo make_info(int id) {
     fill_fns<CF, false, false, DT_BF16>(t.final_fn[DT_BF16]);
     fill_fns<CF, true, false, DT_BF16>(t.partial_fn[DT_BF16]);
   }
-  if constexpr (WITH_GROUPED) fill_fns<CF, false, true>(t.grouped_fn);
+  if constexpr (WITH_GROUPED) {
+    fill_fns<CF, false, true>(t.grouped_fn[DT_F16]);
+    if constexpr (WITH_BF16) fill_fns<CF, false, true, DT_BF16>(t.grouped_fn[DT_BF16]);
+  }
   t.fallback = 0;
   t.n_mult = 0;
   return t;
@@ -129,8 +132,10 @@ TileInfo make_dma_a128_info(int id, int fallback) {
   t.final_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, false, DT_BF16>;
   t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, true, false, DT_BF16>;
   t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, true, false, DT_BF16>;
-  t.grouped_fn[PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false, true>;
-  t.grouped_fn[PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, true>;
+  t.grouped_fn[DT_F16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false, true>;
+  t.grouped_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, true>;
+  t.grouped_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_a128_kernel<CF, true, false, true, DT_BF16>;
+  t.grouped_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_a128_kernel<CF, false, false, true, DT_BF16>;
   t.packed_fn[DT_F16] = gemm_dma_a128_kernel<CF, true, false, false, DT_F16, true>;
   t.packed_fn[DT_BF16] = gemm_dma_a128_kernel<CF, true, false, false, DT_BF16, true>;
   t.packed_partial_fn[DT_F16] = gemm_dma_a128_kernel<CF, true, true, false, DT_F16, true>;

@@ -291,7 +291,20 @@ int gemm_f16_grouped(const void* A, int64_t lda_m, int64_t lda_k,
                      int64_t M_total, int64_t N, int64_t K, void* stream,
                      void* workspace, size_t workspace_bytes);
 
-/* Workspace bytes gemm_f16_grouped needs for G groups (0 if G is invalid). */
+/*
+ * The grouped product with bfloat16 A, B and C (fp32 accumulation, output
+ * rounded to nearest-even bfloat16): the same arguments, validation, return
+ * codes and workspace as gemm_f16_grouped.
+ */
+int gemm_bf16_grouped(const void* A, int64_t lda_m, int64_t lda_k,
+                      const void* B, int64_t ldb_g, int64_t ldb_k, int64_t ldb_n,
+                      void* C, int64_t ldc,
+                      const int64_t* offsets, int32_t G,
+                      int64_t M_total, int64_t N, int64_t K, void* stream,
+                      void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes gemm_f16_grouped and gemm_bf16_grouped need for G groups
+ * (0 if G is invalid). */
 size_t gemm_f16_grouped_workspace_bytes(int32_t G);
 
 /* Static, NUL-terminated description of a return code. */

@@ -14,7 +14,8 @@ import torch
 import dense_tiled_gemm_fp16_amd as g
 import oracle
 import synth
-from gpu_util import (DEV, NAN16, ORACLE_THREADS, Out, assert_bits_equal, assert_close, place,
+from gpu_util import (DEV, NAN16, ORACLE_THREADS, Out, assert_bits_equal, assert_close,
+                      assert_close_bf16, place,
                       say, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -123,3 +124,34 @@ def test_grouped_moe_shape_sampled():
         A_rows = synth.rows_of(rows, K, 4001, 0)
         ref = oracle.gemm(A_rows, (K, 1), Bs[e], (N, 1), len(rows), N, K, nthreads=ORACLE_THREADS)
         assert_close(got[rows], ref, f"MoE group {e} rows {rows.tolist()}")
+
+
+@pytest.mark.parametrize("mode", ["int", "uniform"])
+@pytest.mark.parametrize("case", ["small_groups", "large_groups"])
+def test_grouped_bf16_parity(mode, case):
+    # gemm_bf16_grouped: the same launches with bfloat16 A, B and C.
+    if case == "small_groups":
+        sizes, K, N = np.array([0, 37, 130, 0, 1, 64, 255, 3]), 100, 70
+    else:
+        sizes, K, N = np.array([300, 0, 700, 517]), 160, 264
+    offsets = np.concatenate([[3], 3 + np.cumsum(sizes)]).astype(np.int64)
+    M = int(offsets[-1]) + 5
+    G = len(sizes)
+    A = synth.matrix(M, K, 12500 + K, 0, mode, fmt="bf16")
+    Bs = np.stack([synth.matrix(K, N, 12600 + K, 16 + e, mode, fmt="bf16") for e in range(G)])
+    ref = oracle.gemm_grouped(A, Bs, offsets, N, K, C=np.full((M, N), NAN16, dtype=np.uint16),
+                              nthreads=ORACLE_THREADS, dtype="bf16")
+    a = place(A, "row", (1, (-K) % 8 + 8)).view(torch.bfloat16)
+    b = to_dev(Bs).view(torch.bfloat16)
+    off = torch.from_numpy(offsets).to(DEV)
+    out = Out(M, N)
+    out.view = out.view.view(torch.bfloat16)
+    got = run_grouped(a, b, off, out)
+    inside = np.zeros(M, dtype=bool)
+    for e in range(G):
+        inside[offsets[e]:offsets[e + 1]] = True
+    assert np.all(got[~inside] == NAN16), "a row outside every group was written"
+    if mode == "int":
+        assert_bits_equal(got[inside], ref[inside], f"bf16 grouped {case}")
+    else:
+        assert_close_bf16(got[inside], ref[inside], f"bf16 grouped {case}")
