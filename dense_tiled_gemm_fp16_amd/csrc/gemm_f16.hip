@@ -295,12 +295,11 @@ int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, c
 void maybe_pack(const Call& c, int variant, bool allow_pack, Plan& p, bool any_b) {
   const TileInfo& ti = tile_info(p.tile_id);
   const bool f8 = c.dt >= DT_F8;
-  const bool sk = p.variant == GEMM_VARIANT_STREAMK;
-  if (!allow_pack || variant != GEMM_VARIANT_AUTO || !(sk || (p.variant == GEMM_VARIANT_MAIN && p.split == 1)) ||
-      p.b_path != PATH_KVEC || c.M < (any_b ? kPackMinRowsGather : kPackMinRows) || !ti.packed_fn[c.dt] ||
-      !ti.packed_partial_fn[c.dt] ||
-      !(f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k)))
-    return;
+  if (!allow_pack || variant != GEMM_VARIANT_AUTO || p.b_path != PATH_KVEC) return;
+  const bool family = p.variant == GEMM_VARIANT_STREAMK || (p.variant == GEMM_VARIANT_MAIN && p.split == 1);
+  const bool kernels = ti.packed_fn[c.dt] && ti.packed_partial_fn[c.dt];
+  const bool tile = f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k);
+  if (!family || !kernels || !tile || c.M < (any_b ? kPackMinRowsGather : kPackMinRows)) return;
   const size_t bytes = packed_b_bytes(f8 ? cdiv(c.K, 2) : c.K, c.N);
   if (bytes == 0 || p.ws > SIZE_MAX - bytes) return;
   p.pack = true;
@@ -631,10 +630,13 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   // Packing plan: B into the workspace (K16: K in 16-bit units).
   const int64_t K16 = c.dt >= DT_F8 ? cdiv(c.K, 2) : c.K;
   if (p.pack) {
-    const int rc = c.dt < DT_F8 ? launch_pack_b((const uint16_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream)
-                   : c.K % 2 == 0
-                       ? launch_pack_b((const uint16_t*)c.B, 1, c.ldb_n / 2, K16, c.N, (uint16_t*)ws, stream)
-                       : launch_pack_b8((const uint8_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint8_t*)ws, stream);
+    int rc;
+    if (c.dt < DT_F8)        // 16-bit B through its strides
+      rc = launch_pack_b((const uint16_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint16_t*)ws, stream);
+    else if (c.K % 2 == 0)   // K-contiguous FP8 rows as byte pairs
+      rc = launch_pack_b((const uint16_t*)c.B, 1, c.ldb_n / 2, K16, c.N, (uint16_t*)ws, stream);
+    else                     // odd K: byte by byte, zero past K
+      rc = launch_pack_b8((const uint8_t*)c.B, c.ldb_k, c.ldb_n, c.K, c.N, (uint8_t*)ws, stream);
     if (rc) return rc;
   }
   const TileInfo& ti = tile_info(p.tile_id);
