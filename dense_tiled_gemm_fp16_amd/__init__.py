@@ -109,33 +109,42 @@ def gemm_grouped(a, b, offsets, out=None, workspace=None, stream=None):
     """Grouped product: for each g, C[offsets[g]:offsets[g+1]] = a[same rows] @ b[g].
 
     a [M_total, K] and b [G, K, N] on one GPU, both float16 or both bfloat16
-    (out in the same format), offsets a device int64 tensor of G + 1 row
-    offsets (read by the kernels, never by the host).  Rows of out outside
-    every group are left as they were."""
+    (out in the same format) or both FP8 (float8_e4m3fn / float8_e5m2, out
+    float16), offsets a device int64 tensor of G + 1 row offsets (read by
+    the kernels, never by the host).  Rows of out outside every group are
+    left as they were."""
     if a.ndim != 2 or b.ndim != 3:
         raise ValueError("expected a [M, K] matrix and a [G, K, N] stack")
     if not (a.is_cuda and b.is_cuda and offsets.is_cuda) or len({a.device, b.device, offsets.device}) != 1:
         raise ValueError("inputs must share one GPU device")
-    if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype or offsets.dtype != torch.int64:
-        raise TypeError("a and b must be both float16 or both bfloat16, offsets int64")
+    f8 = a.dtype in F8_FORMATS and b.dtype in F8_FORMATS
+    if not (f8 or (a.dtype in (torch.float16, torch.bfloat16) and b.dtype == a.dtype)) or \
+            offsets.dtype != torch.int64:
+        raise TypeError("a and b must be both float16, both bfloat16 or both FP8, offsets int64")
+    c_dtype = torch.float16 if f8 else a.dtype
     m, k = a.shape
     g, kb, n = b.shape
     if kb != k or min(m, n, k, g) <= 0 or offsets.shape != (g + 1,) or offsets.stride(0) != 1:
         raise ValueError("incompatible or empty shape, or offsets not a contiguous [G + 1] vector")
     if out is None:
-        out = torch.empty((m, n), device=a.device, dtype=a.dtype)
-    elif out.dtype != a.dtype or out.device != a.device or out.shape != (m, n) or out.stride(1) != 1:
-        raise ValueError("out must be a row-major [M, N] tensor of the inputs' format and device")
+        out = torch.empty((m, n), device=a.device, dtype=c_dtype)
+    elif out.dtype != c_dtype or out.device != a.device or out.shape != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be a row-major [M, N] tensor of the output format (float16 for FP8 "
+                         "inputs) on the inputs' device")
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(a.device):
-        fn = lib.gemm_f16_grouped if a.dtype == torch.float16 else lib.gemm_bf16_grouped
-        rc = fn(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
-                b.stride(1), b.stride(2), out.data_ptr(), out.stride(0),
-                offsets.data_ptr(), g, m, n, k, stream.cuda_stream, ws_ptr, ws_bytes)
+        args = (a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0), b.stride(1),
+                b.stride(2), out.data_ptr(), out.stride(0), offsets.data_ptr(), g, m, n, k)
+        if f8:
+            rc = lib.gemm_f8_grouped(*args, F8_FORMATS[a.dtype], F8_FORMATS[b.dtype],
+                                     stream.cuda_stream, ws_ptr, ws_bytes)
+        else:
+            fn = lib.gemm_f16_grouped if a.dtype == torch.float16 else lib.gemm_bf16_grouped
+            rc = fn(*args, stream.cuda_stream, ws_ptr, ws_bytes)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return out

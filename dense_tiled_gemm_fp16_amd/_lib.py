@@ -23,7 +23,7 @@ EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes
            "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_plan", "gemm_bf16_workspace_bytes",
            "gemm_f8", "gemm_f8_ex", "gemm_f8_plan", "gemm_f8_workspace_bytes",
            "gemm_f16_packed_b_bytes", "gemm_f16_pack_b", "gemm_f16_packed",
-           "gemm_f16_grouped", "gemm_bf16_grouped", "gemm_f16_grouped_workspace_bytes",
+           "gemm_f16_grouped", "gemm_bf16_grouped", "gemm_f8_grouped", "gemm_f16_grouped_workspace_bytes",
            "gemm_f16_status_string", "gemm_f16_version"]
 
 
@@ -85,6 +85,9 @@ def _load():
     lib.gemm_f16_grouped.restype = ctypes.c_int
     lib.gemm_bf16_grouped.argtypes = lib.gemm_f16_grouped.argtypes
     lib.gemm_bf16_grouped.restype = ctypes.c_int
+    lib.gemm_f8_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, i64, vp, i32, i64, i64, i64,
+                                    i32, i32, vp, vp, sz]
+    lib.gemm_f8_grouped.restype = ctypes.c_int
     lib.gemm_f16_grouped_workspace_bytes.argtypes = [i32]
     lib.gemm_f16_grouped_workspace_bytes.restype = sz
     lib.gemm_f16_status_string.argtypes = [ctypes.c_int]

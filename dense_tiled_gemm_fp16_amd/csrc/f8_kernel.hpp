@@ -188,10 +188,12 @@ __device__ __forceinline__ u32x4 load_bytes16(const uint8_t* p, int64_t k, int64
 // BPACK: B pre-packed by the 16-bit packing pass over its byte pairs (the
 // 16 KiB blocks are then the LDS images of this kernel's K-major 64-k B
 // stages; ldb_n is the panel stride in byte pairs).
-template <int FA, int FB, bool PARTIAL, bool BN = false, bool BPACK = false>
+// GROUPED: one launch over the groups of a grouped product (group_tile).
+template <int FA, int FB, bool PARTIAL, bool BN = false, bool BPACK = false, bool GROUPED = false>
 __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
   using CF = F8Cfg;
   static_assert(!(BN && BPACK), "packed B stages are K-major");
+  static_assert(!(GROUPED && (PARTIAL || BPACK)), "grouped launches are never split or packed");
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -211,7 +213,11 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     }
   }
   int64_t pm, pn;
-  raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  if constexpr (GROUPED) {
+    if (!group_tile<1>(a, w, pm, pn)) return;   // uniform per workgroup, before any barrier
+  } else {
+    raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
+  }
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
   const int64_t kb = split * a.k_split;   // bytes; a multiple of 128
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;

@@ -770,11 +770,22 @@ int validate_grouped(GroupCall& c) {
       __builtin_mul_overflow((int64_t)(c.G - 1), c.ldb_g, &g_off) ||
       __builtin_add_overflow(sb, g_off, &c.spanB) || c.spanB > INT64_MAX / 2 - 1)
     return GEMM_ERR_SHAPE;
-  const uintptr_t a0 = (uintptr_t)c.A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
-  const uintptr_t b0 = (uintptr_t)c.B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+  const uintptr_t eb = c.dt >= DT_F8 ? 1 : 2;   // bytes per A and B element
+  const uintptr_t a0 = (uintptr_t)c.A, a1 = a0 + eb * (uintptr_t)(c.spanA + 1);
+  const uintptr_t b0 = (uintptr_t)c.B, b1 = b0 + eb * (uintptr_t)(c.spanB + 1);
   const uintptr_t c0 = (uintptr_t)c.C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
   if (a1 < a0 || b1 < b0 || c1 < c0) return GEMM_ERR_SHAPE;
   if (ranges_overlap(c0, c1, a0, a1) || ranges_overlap(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
+  if (c.dt >= DT_F8) {
+    // The FP8 tile's layouts (as for gemm_f8_ex), and every group's B on a
+    // 16-byte boundary.
+    const bool b_k = c.ldb_k == 1, b_n = !b_k && c.ldb_n == 1;
+    const int64_t ldb = b_k ? c.ldb_n : c.ldb_k;
+    if (c.lda_k != 1 || c.lda_m % 16 != 0 || ((uintptr_t)c.A & 15u) || !(b_k || b_n) || ldb % 16 != 0 ||
+        ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) || ldb > (INT64_C(1) << 24) ||
+        (b_n && c.N % 16 != 0) || c.ldb_g % 16 != 0)
+      return GEMM_ERR_LAYOUT;
+  }
   return GEMM_OK;
 }
 
@@ -782,6 +793,15 @@ int validate_grouped(GroupCall& c) {
 // the groups average at least one of its 256-row tiles and the layouts suit
 // it, the 128 x 128 register-path tile otherwise.
 int grouped_plan(const GroupCall& c, int* tile_id, kfn_t* fn, int64_t* grid) {
+  if (c.dt >= DT_F8) {   // the FP8 tile, whatever the group sizes
+    const TileInfo& ti = tile_info(TILE_F8);
+    *fn = ti.grouped_fn[c.dt][PATH_KVEC * 3 + (c.ldb_k == 1 ? PATH_KVEC : PATH_RVEC)];
+    if (!*fn) return GEMM_ERR_OPTS;
+    const int64_t GN = cdiv(c.N, ti.bn), rows = cdiv(c.M, ti.bm) + c.G;
+    if (__builtin_mul_overflow(rows, GN, grid) || *grid > (INT64_C(1) << 31) - 1) return GEMM_ERR_SHAPE;
+    *tile_id = TILE_F8;
+    return GEMM_OK;
+  }
   // Groups start at arbitrary rows, so an M-contiguous A (vectors along m)
   // would lose its alignment: it takes the element-wise path.
   int a_path = classify(c.A, c.lda_m, c.lda_k);
@@ -863,9 +883,10 @@ int grouped_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void
   hipStream_t s = (hipStream_t)stream;
   if (workspace) {
     if (workspace_bytes < need || ((uintptr_t)workspace & 255u)) return GEMM_ERR_WORKSPACE;
+    const uintptr_t eb = dt >= DT_F8 ? 1 : 2;
     const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
-    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + 2 * (uintptr_t)(c.spanA + 1);
-    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + 2 * (uintptr_t)(c.spanB + 1);
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + eb * (uintptr_t)(c.spanA + 1);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + eb * (uintptr_t)(c.spanB + 1);
     const uintptr_t c0 = (uintptr_t)C, c1 = c0 + 2 * (uintptr_t)(c.spanC + 1);
     if (ranges_overlap(w0, w1, a0, a1) || ranges_overlap(w0, w1, b0, b1) ||
         ranges_overlap(w0, w1, c0, c1))
@@ -896,6 +917,18 @@ int gemm_bf16_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B
                       int32_t G, int64_t M_total, int64_t N, int64_t K, void* stream,
                       void* workspace, size_t workspace_bytes) {
   return grouped_impl(DT_BF16, A, lda_m, lda_k, B, ldb_g, ldb_k, ldb_n, C, ldc, offsets, G, M_total, N, K,
+                      stream, workspace, workspace_bytes);
+}
+
+static int f8_dt(int32_t fmt_a, int32_t fmt_b);
+
+int gemm_f8_grouped(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_g,
+                    int64_t ldb_k, int64_t ldb_n, void* C, int64_t ldc, const int64_t* offsets,
+                    int32_t G, int64_t M_total, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b,
+                    void* stream, void* workspace, size_t workspace_bytes) {
+  const int dt = f8_dt(fmt_a, fmt_b);
+  if (dt < 0) return GEMM_ERR_OPTS;
+  return grouped_impl(dt, A, lda_m, lda_k, B, ldb_g, ldb_k, ldb_n, C, ldc, offsets, G, M_total, N, K,
                       stream, workspace, workspace_bytes);
 }
 

@@ -87,7 +87,9 @@ struct KArgs {
 // run per XCD kept about eight groups' B live and ran 4-7% slower on the
 // 32-expert MoE workload.  Row tiles past the last multiple of 8 keep plain
 // order.  The group is the last g with tiles[g] <= t (binary search), and A,
-// C, B and M are rebased on it.
+// C, B and M are rebased on it.  ESZ: bytes per A and B element (2; 1 for
+// FP8, whose strides count bytes).
+template <int ESZ = 2>
 __device__ __forceinline__ bool group_tile(KArgs& a, int64_t w, int64_t& pm, int64_t& pn) {
   const int64_t L = a.g_tiles[a.G] * a.GN;
   if (w >= L) return false;
@@ -108,9 +110,9 @@ __device__ __forceinline__ bool group_tile(KArgs& a, int64_t w, int64_t& pm, int
   }
   const int64_t r0 = a.g_off[lo], r1 = a.g_off[lo + 1];
   pm = t - a.g_tiles[lo];
-  a.A += r0 * a.lda_m;
+  a.A = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.A) + r0 * a.lda_m * ESZ);
   a.C += r0 * a.ldc;
-  a.B += (int64_t)lo * a.ldb_g;
+  a.B = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.B) + (int64_t)lo * a.ldb_g * ESZ);
   a.M = r1 - r0;
   return true;
 }

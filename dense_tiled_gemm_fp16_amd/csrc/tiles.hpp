@@ -39,7 +39,7 @@ struct TileInfo {
   int id, bm, bn, bk, nt;
   kfn_t final_fn[NDT][9];  // [format][a_path * 3 + b_path]; nullptr = not supported
   kfn_t partial_fn[NDT][9];
-  kfn_t grouped_fn[2][9];  // grouped launches, [fp16, bfloat16] (nullptr: not instantiated)
+  kfn_t grouped_fn[NDT][9];  // grouped launches, per format (nullptr: not instantiated)
   kfn_t packed_fn[NDT];    // pre-packed B, K-contiguous A, per format (nullptr: none)
   kfn_t packed_partial_fn[NDT];  // the same writing fp32 partials (stream-K tails)
   int fallback;         // tile used for layouts this one does not support
@@ -66,7 +66,8 @@ inline void clear_fns(TileInfo& t) {
   t.max_ld = 0;
   for (int d = 0; d < NDT; ++d)
     for (int i = 0; i < 9; ++i) t.final_fn[d][i] = t.partial_fn[d][i] = nullptr;
-  for (int i = 0; i < 9; ++i) t.grouped_fn[DT_F16][i] = t.grouped_fn[DT_BF16][i] = nullptr;
+  for (int d = 0; d < NDT; ++d)
+    for (int i = 0; i < 9; ++i) t.grouped_fn[d][i] = nullptr;
   for (int d = 0; d < NDT; ++d) t.packed_fn[d] = t.packed_partial_fn[d] = nullptr;
 }
 
@@ -158,6 +159,8 @@ void fill_f8(TileInfo& t) {
   t.partial_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, true, true>;
   t.packed_fn[DT_F8 + 2 * FA + FB] = gemm_f8_kernel<FA, FB, false, false, true>;
   t.packed_partial_fn[DT_F8 + 2 * FA + FB] = gemm_f8_kernel<FA, FB, true, false, true>;
+  t.grouped_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_KVEC] = gemm_f8_kernel<FA, FB, false, false, false, true>;
+  t.grouped_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, false, true, false, true>;
 }
 
 inline TileInfo make_f8_info(int id) {

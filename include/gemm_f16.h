@@ -303,8 +303,24 @@ int gemm_bf16_grouped(const void* A, int64_t lda_m, int64_t lda_k,
                       int64_t M_total, int64_t N, int64_t K, void* stream,
                       void* workspace, size_t workspace_bytes);
 
-/* Workspace bytes gemm_f16_grouped and gemm_bf16_grouped need for G groups
- * (0 if G is invalid). */
+/*
+ * The grouped product with FP8 A and B (formats fmt_a, fmt_b: 0 E4M3, 1 E5M2,
+ * as for gemm_f8_ex), fp32 accumulation and binary16 C.  Strides of A and B
+ * (and ldb_g) count bytes.  The layouts of gemm_f8_ex: A K-contiguous; every
+ * B_g K-contiguous ([N, K] rows) or N-contiguous ([K, N] rows, N a multiple
+ * of 16); 16-byte aligned bases and rows at most 2^24 bytes apart; ldb_g a
+ * multiple of 16 (GEMM_ERR_LAYOUT otherwise).  Other arguments, return
+ * codes and the workspace as for gemm_f16_grouped.
+ */
+int gemm_f8_grouped(const void* A, int64_t lda_m, int64_t lda_k,
+                    const void* B, int64_t ldb_g, int64_t ldb_k, int64_t ldb_n,
+                    void* C, int64_t ldc,
+                    const int64_t* offsets, int32_t G,
+                    int64_t M_total, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b,
+                    void* stream, void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes gemm_f16_grouped, gemm_bf16_grouped and gemm_f8_grouped
+ * need for G groups (0 if G is invalid). */
 size_t gemm_f16_grouped_workspace_bytes(int32_t G);
 
 /* Static, NUL-terminated description of a return code. */

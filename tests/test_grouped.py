@@ -155,3 +155,46 @@ def test_grouped_bf16_parity(mode, case):
         assert_bits_equal(got[inside], ref[inside], f"bf16 grouped {case}")
     else:
         assert_close_bf16(got[inside], ref[inside], f"bf16 grouped {case}")
+
+
+F8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+@pytest.mark.parametrize("b_layout", ["kcontig", "ncontig"])
+@pytest.mark.parametrize("mode", ["int", "uniform"])
+@pytest.mark.parametrize("case", ["small_groups", "large_groups"])
+def test_grouped_f8_parity(case, mode, b_layout):
+    # gemm_f8_grouped: E4M3 A, E5M2 experts, fp16 C; rows padded with the
+    # FP8 NaN byte 0x7F, which must never be read.
+    fa, fb = "e4m3", "e5m2"
+    if case == "small_groups":
+        sizes, K, N = np.array([0, 37, 130, 0, 1, 64, 255, 3]), 100, 80
+    else:
+        sizes, K, N = np.array([300, 0, 700, 517]), 160, 272
+    offsets = np.concatenate([[3], 3 + np.cumsum(sizes)]).astype(np.int64)
+    M = int(offsets[-1]) + 5
+    G = len(sizes)
+    A = synth.matrix(M, K, 12700 + K, 0, mode, fmt=fa)
+    Bs = np.stack([synth.matrix(K, N, 12800 + K, 16 + e, mode, fmt=fb) for e in range(G)])
+    lda = K + (-K) % 16 + 16
+    abuf = np.full((M, lda), 0x7F, dtype=np.uint8)
+    abuf[:, :K] = A
+    a = torch.from_numpy(abuf).to(DEV).view(F8_TORCH[fa])[:, :K]
+    if b_layout == "kcontig":                   # each B_g stored [N, K]
+        ld = K + (-K) % 16 + 16
+        bbuf = np.full((G, N, ld), 0x7F, dtype=np.uint8)
+        bbuf[:, :, :K] = Bs.transpose(0, 2, 1)
+        b = torch.from_numpy(bbuf).to(DEV).view(F8_TORCH[fb])[:, :, :K].transpose(1, 2)
+    else:                                       # each B_g stored [K, N]
+        bbuf = np.full((G, K, N + 16), 0x7F, dtype=np.uint8)
+        bbuf[:, :, :N] = Bs
+        b = torch.from_numpy(bbuf).to(DEV).view(F8_TORCH[fb])[:, :, :N]
+    ref = np.full((M, N), NAN16, dtype=np.uint16)
+    for e in range(G):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            ref[r0:r1] = oracle.gemm(np.ascontiguousarray(A[r0:r1]), (K, 1), Bs[e], (N, 1), r1 - r0, N,
+                                     K, dtype="f8", fmt_a=fa, fmt_b=fb, nthreads=ORACLE_THREADS)
+    off = torch.from_numpy(offsets).to(DEV)
+    got = run_grouped(a, b, off, Out(M, N))
+    check_groups(got, ref, offsets, mode, f"f8 grouped {case} {mode} B={b_layout}")
