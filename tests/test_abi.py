@@ -242,3 +242,28 @@ def test_packed_b_rejected_before_any_device_work():
     assert run(PA, (1 << 23) + 8, 1, PW, PC, 300, 50, 300, 100, 0) == -9   # rows over 2^23 apart
     assert run(PA, 112, 1, PW, PC, 299, 50, 300, 100, 0) == -4
     assert run(PA, 112, 1, PW, PW + 1024, 300, 50, 300, 100, 0) == -5   # C overlaps Bp
+
+
+def f8gcall(A=PA, lda_m=64, lda_k=1, B=PB, ldb_g=32 * 64, ldb_k=1, ldb_n=64, C=PC, ldc=32,
+            off=PO, G=4, M=16, N=32, K=64, fa=0, fb=1, ws=PW, ws_bytes=255):
+    """gemm_f8_grouped with byte strides; by default B_g K-contiguous ([N, K]
+    rows of 64 bytes) and a workspace one byte short, so a call whose
+    layout is accepted stops at the workspace check (-6), before any launch."""
+    return g.lib.gemm_f8_grouped(A, lda_m, lda_k, B, ldb_g, ldb_k, ldb_n, C, ldc, off, G, M, N, K,
+                                 fa, fb, 0, ws, ws_bytes)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), -6),                                    # layout accepted
+    (dict(ldb_k=64, ldb_n=1, N=32), -6),             # N-contiguous B, N a multiple of 16
+    (dict(fa=2), -7), (dict(fb=-1), -7),             # not an FP8 format
+    (dict(lda_k=2, lda_m=128), -9),                  # A not K-contiguous
+    (dict(lda_m=72), -9),                            # A rows not 16-byte multiples
+    (dict(A=PA + 8), -9), (dict(B=PB + 8), -9),      # unaligned bases
+    (dict(ldb_g=32 * 64 + 8), -9),                   # a group's B off the 16-byte grid
+    (dict(ldb_k=48, ldb_n=1, N=40, ldc=40), -9),     # N-contiguous B, N % 16 != 0
+    (dict(ldb_k=2, ldb_n=64), -9),                   # B contiguous along neither axis
+    (dict(lda_m=(1 << 24) + 16, M=2), -9),           # row stride past 2^24 bytes
+])
+def test_f8_grouped_layouts_checked_before_any_device_work(kw, code):
+    assert f8gcall(**kw) == code
