@@ -2,7 +2,11 @@
 a GPU).  Each csrc/*.hip translation unit is compiled in parallel, then all
 are linked into one shared library.
 
-    python dense_tiled_gemm_fp16_amd/build.py
+    python dense_tiled_gemm_fp16_amd/build.py [-v] [--incremental]
+
+--incremental recompiles only the units older than their source or any
+header under csrc/ or include/ (build() from the entry point always
+compiles everything).
 """
 import concurrent.futures
 import glob
@@ -26,8 +30,21 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
+def _obj(src):
+    return os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+
+
+def _stale(src):
+    obj = _obj(src)
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + glob.glob(os.path.join(HERE, "csrc", "*.hpp")) + \
+        glob.glob(os.path.join(HERE, "..", "include", "*.h"))
+    return max(os.path.getmtime(d) for d in deps) > os.path.getmtime(obj)
+
+
 def _compile(src, verbose):
-    obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+    obj = _obj(src)
     cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -35,15 +52,16 @@ def _compile(src, verbose):
     return obj, res
 
 
-def build(verbose=False, jobs=None):
+def build(verbose=False, jobs=None, incremental=False):
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = jobs or max(1, min(16, len(os.sched_getaffinity(0))))
-    objs, failed = [], []
+    objs = [_obj(s) for s in sources()]
+    todo = [s for s in sources() if not incremental or _stale(s)]
+    failed = []
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        for obj, res in ex.map(lambda s: _compile(s, verbose), sources()):
+        for obj, res in ex.map(lambda s: _compile(s, verbose), todo):
             if res.returncode != 0:
                 failed.append(res.stdout + res.stderr)
-            objs.append(obj)
     if failed:
         sys.stderr.write("\n".join(failed))
         raise RuntimeError("hipcc failed to compile libgemmf16")
@@ -60,4 +78,4 @@ def build(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

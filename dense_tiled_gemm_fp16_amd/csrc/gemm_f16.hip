@@ -43,11 +43,12 @@ typedef void (*kfn_gemv)(GemvArgs);
 typedef void (*kfn_reduce)(const float*, int, int64_t, int64_t, uint16_t*, int64_t, int);
 
 const TileInfo& tile_info(int id) {
+  // Unused ids (0, 7 to 12) hold an empty entry: no kernels, nt == 0.
   static const TileInfo table[TILE_MAX + 1] = {
-      TileInfo{},           tile_info_t128(),     tile_info_t64x32(), tile_info_s16(),
-      tile_info_s32(),      tile_info_s64(),      tile_info_t256(),   tile_info_t256x128(),
-      tile_info_t128x256(),   tile_info_t256w8a(), tile_info_t256w8b(), tile_info_dma256(),
-      tile_info_dma256w8a(), tile_info_dma256w8b(), tile_info_dma256a128(), tile_info_f8()};
+      TileInfo{},        tile_info_t128(), tile_info_t64x32(),    tile_info_s16(),
+      tile_info_s32(),   tile_info_s64(),  tile_info_t256(),      TileInfo{},
+      TileInfo{},        TileInfo{},       TileInfo{},            TileInfo{},
+      TileInfo{},        tile_info_dma256w8b(), tile_info_dma256a128(), tile_info_f8()};
   return table[id];
 }
 
@@ -141,7 +142,7 @@ int check_opts(const gemm_f16_opts* o) {
   if (o->variant < GEMM_VARIANT_AUTO || o->variant > GEMM_VARIANT_STREAMK) return GEMM_ERR_OPTS;
   if (o->split_k < 0 || o->split_k > 256) return GEMM_ERR_OPTS;
   if (!(o->panel == -1 || (o->panel >= 0 && o->panel <= 4096))) return GEMM_ERR_OPTS;
-  if (o->tile < 0 || o->tile > TILE_MAX) return GEMM_ERR_OPTS;
+  if (o->tile < 0 || o->tile > TILE_MAX || (o->tile && tile_info(o->tile).nt == 0)) return GEMM_ERR_OPTS;
   return GEMM_OK;
 }
 
@@ -341,6 +342,10 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       return GEMM_ERR_OPTS;
   }
 
+  // A forced tile must have kernels for this format (checked before any
+  // device query).
+  if (want_tile && !has_format(tile_info(want_tile), c.dt)) return GEMM_ERR_OPTS;
+
   p.sk_tiles = 0;
   p.variant = variant;
   if (p.variant == GEMM_VARIANT_AUTO) {
@@ -358,9 +363,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   // query.  bfloat16 is built for the 128x128, skinny and full-line-A tiles.
   if ((p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_TILE64X32) && want_split > 1)
     return GEMM_ERR_OPTS;
-  if (c.dt != DT_F16 && (p.variant == GEMM_VARIANT_TILE64X32 ||
-                         (want_tile && !has_format(tile_info(want_tile), c.dt))))
-    return GEMM_ERR_OPTS;
+  if (c.dt != DT_F16 && p.variant == GEMM_VARIANT_TILE64X32) return GEMM_ERR_OPTS;
   if (p.variant == GEMM_VARIANT_SKINNY && c.M > 64) return GEMM_ERR_OPTS;
 
   p.a_path = f8 ? PATH_KVEC : classify(c.A, c.lda_m, c.lda_k);
@@ -446,8 +449,12 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     const TileInfo& t = tile_info(p.tile_id);
     if (tile_takes(t, c, p)) break;
     // fp16 tiles hand over along their fallback chain; bfloat16 goes straight
-    // to the 128x128 tile, which covers every layout in both formats.
-    p.tile_id = c.dt == DT_F16 ? t.fallback : TILE_T128;
+    // to the 128x128 tile, which covers every layout in both formats.  A
+    // chain that ends without a taker (a tile without this format) is an
+    // option error, never a loop.
+    const int next = c.dt == DT_F16 ? t.fallback : TILE_T128;
+    if (next <= 0 || next > TILE_MAX || next == p.tile_id) return GEMM_ERR_OPTS;
+    p.tile_id = next;
   }
   const TileInfo& ti = tile_info(p.tile_id);
   p.GM = cdiv(c.M, ti.bm);

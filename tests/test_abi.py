@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -79,6 +80,29 @@ def test_option_errors():
     assert call(opts=_lib.Opts(6, 0, 0, 0)) == -7
     assert call(opts=_lib.Opts(5, 0, 0, 1)) == -7
     assert call(lda_m=1, lda_k=64, opts=_lib.Opts(5, 0, 0, 0)) == -7   # A not K-contiguous
+
+
+def test_forced_tile_without_16_bit_kernels_is_an_option_error():
+    # Tile 15 holds FP8 kernels only and ids 7-12 are unused: a 16-bit call
+    # that forces one returns at once with GEMM_ERR_OPTS under every variant.
+    # It runs in a child process with a time limit, so a planning loop fails
+    # the test instead of hanging the suite.
+    code = (
+        "import ctypes, itertools, dense_tiled_gemm_fp16_amd as g\n"
+        "from dense_tiled_gemm_fp16_amd import _lib\n"
+        "info = _lib.PlanInfo()\n"
+        "for v, t in itertools.product((0, 1, 2, 3, 5), (7, 8, 9, 10, 11, 12, 15)):\n"
+        "    o = _lib.Opts(v, 0, 0, t)\n"
+        "    for f in (g.lib.gemm_f16_plan, g.lib.gemm_bf16_plan):\n"
+        f"        print(v, t, f({PA}, 64, 1, {PB}, 32, 1, {PC}, 32, 16, 32, 64, ctypes.byref(o), ctypes.byref(info)))\n"
+        f"    print(v, t, g.gemm_raw({PA}, 64, 1, {PB}, 32, 1, {PC}, 32, 16, 32, 64, 0, 0, 0, o))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         cwd=ROOT)
+    assert out.returncode == 0, out.stderr
+    lines = out.stdout.split("\n")[:-1]
+    assert len(lines) == 5 * 7 * 3
+    for line in lines:
+        assert line.split()[2] == "-7", line
 
 
 def test_workspace_errors():

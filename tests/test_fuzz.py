@@ -19,8 +19,8 @@ from gpu_util import ORACLE_THREADS, Out, assert_bits_equal, place, say
 pytestmark = pytest.mark.gpu
 
 PLANS = [dict(variant="auto"), dict(variant="main"), dict(variant="main", tile=14),
-         dict(variant="main", tile=13), dict(variant="main", tile=1), dict(variant="main", tile=7),
-         dict(variant="main", tile=8), dict(variant="tile64x32"), dict(variant="splitk"),
+         dict(variant="main", tile=13), dict(variant="main", tile=1), dict(variant="main", tile=6),
+         dict(variant="tile64x32"), dict(variant="splitk"),
          dict(variant="splitk", tile=14, split_k=3), dict(variant="splitk", tile=1, split_k=5),
          dict(variant="streamk"), dict(variant="streamk", split_k=2), dict(variant="skinny"),
          dict(variant="skinny", split_k=3), dict(variant="main", panel=-1),
