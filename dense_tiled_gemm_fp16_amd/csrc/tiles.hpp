@@ -157,23 +157,6 @@ void fill_f8(TileInfo& t) {
   t.grouped_fn[DT_F8 + 2 * FA + FB][PATH_KVEC * 3 + PATH_RVEC] = gemm_f8_kernel<FA, FB, false, true, false, true>;
 }
 
-inline TileInfo make_f8_info(int id) {
-  TileInfo t;
-  t.id = id;
-  t.bm = F8Cfg::BM;
-  t.bn = F8Cfg::BN;
-  t.bk = F8Cfg::BK;
-  t.nt = F8Cfg::NT;
-  clear_fns(t);
-  fill_f8<F8_E4M3, F8_E4M3>(t);
-  fill_f8<F8_E4M3, F8_E5M2>(t);
-  fill_f8<F8_E5M2, F8_E4M3>(t);
-  fill_f8<F8_E5M2, F8_E5M2>(t);
-  t.fallback = id;
-  t.n_mult = 0;
-  return t;
-}
-
 // Defined in tile_<id>.hip.
 TileInfo tile_info_t128();
 TileInfo tile_info_t64x32();

@@ -141,3 +141,53 @@ class Out:
             "write outside the output buffer"
         assert np.all(inner[:, self.N:] == CANARY), "write into the ldc padding"
         return np.ascontiguousarray(inner[:, :self.N])
+
+
+def band_rows(M, tile=256):
+    """One row per 256-row band of C, at an offset inside the band that
+    varies from band to band, plus the first and last rows."""
+    bands = np.arange((M + tile - 1) // tile, dtype=np.int64)
+    rows = np.minimum(bands * tile + (bands * 37 + 11) % tile, M - 1)
+    return np.unique(np.concatenate([rows, [0, M - 1]]))
+
+
+def full_size_check(a, b, A, Bh, ldb, M, N, K, seed, what, points=100_000, dtype="f16",
+                    fmt_a="e4m3", fmt_b="e4m3", band=256, **opts):
+    """The automatic plan at full size, with every output checked for a
+    writer and a sample checked against the oracle:
+      - C starts as NaN and no element of the M x N output may still be NaN
+        (counted on the device): every output has been written;
+      - one oracle row per `band`-row band, at varying offsets in the band;
+      - `points` outputs drawn uniformly over the whole of C, each computed
+        by the oracle on its own.
+    Both samples must meet 1e-2 + 2e-3 |C_oracle|; the distance in units in
+    the last place is reported, and at least 95% of the points must agree
+    bit for bit (an fp32 sum in another order rounds to the same fp16 value
+    except near a rounding boundary).  Bh/ldb give the oracle B[k, j] =
+    Bh.flat[k ldb[0] + j ldb[1]]; dtype "f8" takes FP8 bytes of formats
+    fmt_a / fmt_b (fp16 output).  `opts` are passed to the call (the
+    automatic plan by default)."""
+    import dense_tiled_gemm_fp16_amd as g
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    p = g.plan(a, b, out=out, **opts)
+    say(f"full size {what}: M={M} N={N} K={K} plan {p}")
+    g.gemm(a, b, out=out, **opts)
+    torch.cuda.synchronize()
+    unwritten = int(torch.isnan(out).sum().item())
+    assert unwritten == 0, f"{what}: {unwritten} outputs never written (still NaN)"
+    rows = band_rows(M, band)
+    gpu_rows = to_host(out[torch.from_numpy(rows).to(DEV)])
+    ref_rows = oracle.gemm(np.ascontiguousarray(A[rows]), (K, 1), Bh, ldb, rows.size, N, K,
+                           nthreads=ORACLE_THREADS, dtype=dtype, fmt_a=fmt_a, fmt_b=fmt_b)
+    assert_close(gpu_rows, ref_rows, f"{what}: band rows")
+    rng = np.random.default_rng(seed)
+    pr = rng.integers(0, M, points)
+    pc = rng.integers(0, N, points)
+    gpu_pts = to_host(out[torch.from_numpy(pr).to(DEV), torch.from_numpy(pc).to(DEV)])
+    ref_pts = oracle.gemm_points(A, (K, 1), Bh, ldb, K, pr, pc, nthreads=ORACLE_THREADS,
+                                 dtype=dtype, fmt_a=fmt_a, fmt_b=fmt_b)
+    assert_close(gpu_pts, ref_pts, f"{what}: random points")
+    hist = ulp_histogram(gpu_pts, ref_pts)
+    say(f"{what}: ulp distance of {points} points {hist}")
+    assert hist.get(0, 0) >= 0.95 * points, f"{what}: ulp histogram {hist}"
+    return p

@@ -1,8 +1,10 @@
 """Seeded randomized parity at large M, where the automatic plans pack B
 (K-contiguous B from M = 16384, a B the LDS-DMA tile cannot read from
-M = 4096) and take the stream-K tail; each B layout is drawn three times.  Integer inputs in [-4, 4] keep every
-fp32 sum exact, so the automatic plan, the forced main plan (never packed)
-and the oracle's sampled rows must agree bit for bit.
+M = 4096) and take the stream-K tail; each B layout is drawn three times.  Integer
+inputs in [-4, 4] keep every fp32 sum exact.  The automatic plan's output
+must have every element written, and agree bit for bit with the oracle on
+one row per 256-row band and on 20000 points drawn over the whole output,
+and with the forced main plan (never packed) everywhere.
 """
 import numpy as np
 import pytest
@@ -11,7 +13,7 @@ import torch
 import dense_tiled_gemm_fp16_amd as g
 import oracle
 import synth
-from gpu_util import DEV, ORACLE_THREADS, Out, assert_bits_equal, say, to_dev
+from gpu_util import DEV, NAN16, ORACLE_THREADS, Out, assert_bits_equal, band_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -67,14 +69,19 @@ def test_random_large_case(seed):
     g.gemm(a, b, out=out.view)
     torch.cuda.synchronize()
     got = out.result()
+    assert np.all(got != NAN16), f"seed {seed}: outputs never written"
     out2 = Out(M, N)
     if fmt == "bf16":
         out2.view = out2.view.view(torch.bfloat16)
     g.gemm(a, b, out=out2.view, variant="main")
     torch.cuda.synchronize()
     assert_bits_equal(got, out2.result(), f"seed {seed}: automatic plan {p} vs forced main")
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 14)]))
+    dt = "bf16" if fmt == "bf16" else "f16"
+    rows = band_rows(M)
     ref = oracle.gemm(np.ascontiguousarray(A[rows]), (K, 1), B, (N, 1), len(rows), N, K,
-                      nthreads=ORACLE_THREADS, dtype="bf16" if fmt == "bf16" else "f16")
-    assert_bits_equal(got[rows], ref, f"seed {seed}: sampled rows against the oracle")
+                      nthreads=ORACLE_THREADS, dtype=dt)
+    assert_bits_equal(got[rows], ref, f"seed {seed}: band rows against the oracle")
+    rng = np.random.default_rng(seed + 1)
+    pr, pc = rng.integers(0, M, 20000), rng.integers(0, N, 20000)
+    ref = oracle.gemm_points(A, (K, 1), B, (N, 1), K, pr, pc, nthreads=ORACLE_THREADS, dtype=dt)
+    assert_bits_equal(got[pr, pc], ref, f"seed {seed}: points against the oracle")

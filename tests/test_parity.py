@@ -17,7 +17,7 @@ import dense_tiled_gemm_fp16_amd as g
 import oracle
 import synth
 from gpu_util import (CANARY, DEV, NAN16, ORACLE_THREADS, Out, assert_bits_equal, assert_close,
-                      dev_nan, place, say, to_dev, to_host, val)
+                      band_rows, dev_nan, full_size_check, place, say, to_dev, to_host, val)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"
             dict(variant="splitk", split_k=2), dict(variant="splitk", split_k=3),
             dict(variant="splitk", split_k=7), dict(variant="main", panel=-1),
             dict(variant="main", panel=1), dict(variant="main", tile=3),
-            dict(variant="main", tile=11), dict(variant="splitk", tile=11, split_k=3),
+            dict(variant="main", tile=6), dict(variant="splitk", tile=6, split_k=3),
             dict(variant="main", tile=13), dict(variant="splitk", tile=13, split_k=2),
             dict(variant="main", tile=14), dict(variant="splitk", tile=14, split_k=3)]
 
@@ -148,14 +148,10 @@ def test_square_full(n):
 
 
 @pytest.mark.parametrize("n", [4096, 8192])
-def test_square_sampled(n):
+def test_square_full_coverage(n):
     A = synth.matrix(n, n, 2000 + n, 0)
     B = synth.matrix(n, n, 2000 + n, 1)
-    rng = np.random.default_rng(n)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, n - 1], rng.integers(0, n, 20)]))
-    ref = reference(A, B, rows)
-    gpu = run(to_dev(A), to_dev(B))
-    check(gpu[rows], ref, "uniform", f"square {n}")
+    full_size_check(to_dev(A), to_dev(B), A, B, (n, 1), n, n, n, 2000 + n, f"square {n}")
 
 
 # ------------------------------------------------------------------ LDS-DMA tiles, K remainders
@@ -231,15 +227,14 @@ def test_split_k_512x512x65536():
     K = 65536
     A = synth.matrix(M, K, 3004, 0)
     B = synth.matrix(K, N, 3004, 1)
-    rows = np.array([0, 1, 127, 128, 300, 511])
-    ref = reference(A, B, rows)
     a, b = to_dev(A), to_dev(B)
-    p = g.plan(a, b)
+    p = full_size_check(a, b, A, B, (N, 1), M, N, K, 3004, "split-K 512x512x65536", points=20000,
+                        band=64)
     assert p["variant"] == "splitk" and p["split_k"] > 1
     first = run(a, b)
-    check(first[rows], ref, "uniform", "split-K auto")
-    again = run(a, b)
-    assert_bits_equal(again, first, "split-K rerun")
+    assert_bits_equal(run(a, b), first, "split-K rerun")
+    rows = band_rows(M, 64)
+    ref = reference(A, B, rows)
     for kw in (dict(variant="splitk", split_k=16), dict(variant="splitk", split_k=7),
                dict(variant="main")):
         check(run(a, b, **kw)[rows], ref, "uniform", f"split-K {kw}")
@@ -247,37 +242,25 @@ def test_split_k_512x512x65536():
 
 # ------------------------------------------------------------------ full-size configurations
 
-def test_moe_131072x2048x7168_sampled():
+def test_moe_131072x2048x7168_full_coverage():
     M, N, K = 131072, 2048, 7168
     A = synth.matrix(M, K, 4001, 0)
     B = synth.matrix(K, N, 4001, 1)
-    rng = np.random.default_rng(4001)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, M - 129, M - 128, M - 1],
-                                     rng.integers(0, M, 24)]))
-    ref = reference(A, B, rows)
     a, b = to_dev(A), to_dev(B)
-    del A
-    p = g.plan(a, b)
+    p = full_size_check(a, b, A, B, (N, 1), M, N, K, 4001, "MoE 131072x2048x7168")
     assert p["variant"] == "main"
-    gpu = run(a, b)
-    check(gpu[rows], ref, "uniform", "MoE 131072x2048x7168")
 
 
-def test_int64_stride_262181x1061x8192_sampled():
+def test_int64_stride_262181x1061x8192_full_coverage():
     M, N, K = 262181, 1061, 8192
     A = synth.matrix(M, K, 5001, 0)
     Bt = synth.matrix(K, N, 5001, 1, order="col")     # stored [N][K]
-    rng = np.random.default_rng(5001)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 131071, 131072, 262143, 262144, 262145,
-                                      M - 38, M - 37, M - 1], rng.integers(0, M, 16)]))
-    B = np.ascontiguousarray(Bt.T)
-    ref = reference(A, B, rows)
     a = to_dev(A)
-    del A
     b = to_dev(Bt).t()                                  # [K, N] view, strides (1, K)
     assert b.stride() == (1, K)
-    gpu = run(a, b)
-    check(gpu[rows], ref, "uniform", "262181x1061x8192")
+    rows = band_rows(M)
+    assert rows.max() >= 262144 and (rows >= 131072).sum() > 500   # offsets past 2^31 elements
+    full_size_check(a, b, A, Bt, (1, K), M, N, K, 5001, "262181x1061x8192")
 
 
 def test_int64_stride_integer_slice_exact():
