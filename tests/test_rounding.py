@@ -168,7 +168,8 @@ def dev8(vals, fmt, layout="k"):
 def run(a, b, M, N, what, **kw):
     say(f"rounding {what} M={M} N={N} K={a.shape[1]} a.stride={a.stride()} b.stride={b.stride()} {kw}")
     out = Out(M, N, ldc=N + 4)
-    g.gemm(a, b, out=out.view, **kw)
+    view = out.view.view(torch.bfloat16) if a.dtype == torch.bfloat16 else out.view
+    g.gemm(a, b, out=view, **kw)
     torch.cuda.synchronize()
     return out.result()
 
