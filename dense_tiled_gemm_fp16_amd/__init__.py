@@ -10,6 +10,8 @@ device memory and the current stream.
     pack_b(b) / gemm_packed(a, p)  -> a static fp16 B packed once, then C = a @ B
     plan(a, b, out=None, ...)      -> dict describing the kernel that would run
     workspace_bytes(M, N, K, ...)  -> bytes of split-K workspace needed
+    gemm_noalloc(a, b, out)        -> C = a @ b (float16) with no device allocation by the
+                                      library (its workspace in a fixed per-GPU array)
 """
 import ctypes
 
@@ -18,7 +20,7 @@ import torch
 from ._lib import (GEMM_OK, LIB_PATH, PATHS, STATUS, VARIANTS, Opts, PlanInfo, lib, make_opts,
                    status_string)
 
-__all__ = ["gemm", "gemm_raw", "gemm_grouped", "pack_b", "gemm_packed", "PackedB", "plan",
+__all__ = ["gemm", "gemm_raw", "gemm_noalloc", "gemm_grouped", "pack_b", "gemm_packed", "PackedB", "plan",
            "workspace_bytes", "GemmError", "LIB_PATH",
            "VARIANTS"]
 
@@ -100,6 +102,24 @@ def gemm(a, b, out=None, workspace=None, variant="auto", split_k=0, panel=0, til
         rc = _fn(a, "gemm_f16_ex", b)(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
                                    b.stride(0), b.stride(1), out.data_ptr(), out.stride(0), m, n,
                                    k, stream.cuda_stream, ws_ptr, ws_bytes, ctypes.byref(opts))
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return out
+
+
+def gemm_noalloc(a, b, out, stream=None):
+    """C = a @ b for float16 a and b into the caller's float16 `out`, through
+    gemm_f16_noalloc: the library allocates nothing (see that entry point for
+    the size limit and for calls that overlap on one GPU)."""
+    if a.dtype != torch.float16 or b.dtype != torch.float16 or out is None:
+        raise TypeError("gemm_noalloc takes float16 a, b and a float16 out")
+    m, n, k, out = _check(a, b, out)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        rc = lib.gemm_f16_noalloc(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(), b.stride(0),
+                                  b.stride(1), out.data_ptr(), out.stride(0), m, n, k,
+                                  stream.cuda_stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return out

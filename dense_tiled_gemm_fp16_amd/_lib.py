@@ -13,7 +13,8 @@ i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_siz
 GEMM_OK = 0
 STATUS = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_SHAPE", -3: "GEMM_ERR_STRIDE",
           -4: "GEMM_ERR_LDC", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_WORKSPACE",
-          -7: "GEMM_ERR_OPTS", -8: "GEMM_ERR_HIP", -9: "GEMM_ERR_LAYOUT"}
+          -7: "GEMM_ERR_OPTS", -8: "GEMM_ERR_HIP", -9: "GEMM_ERR_LAYOUT", -10: "GEMM_ERR_SCRATCH"}
+SCRATCH_BYTES = 32 << 20   # GEMM_F16_SCRATCH_BYTES
 VARIANT_AUTO, VARIANT_MAIN, VARIANT_SKINNY, VARIANT_SPLITK, VARIANT_TILE64X32, VARIANT_STREAMK = \
     0, 1, 2, 3, 4, 5
 VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4, "streamk": 5}
@@ -24,7 +25,7 @@ EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes
            "gemm_f8", "gemm_f8_ex", "gemm_f8_plan", "gemm_f8_workspace_bytes",
            "gemm_f16_packed_b_bytes", "gemm_f16_pack_b", "gemm_f16_packed",
            "gemm_f16_grouped", "gemm_bf16_grouped", "gemm_f8_grouped", "gemm_f16_grouped_workspace_bytes",
-           "gemm_f16_status_string", "gemm_f16_version"]
+           "gemm_f16_noalloc", "gemm_f16_status_string", "gemm_f16_version"]
 
 
 class Opts(ctypes.Structure):
@@ -48,6 +49,8 @@ def _load():
     args12 = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, vp]
     lib.gemm_f16.argtypes = args12
     lib.gemm_f16.restype = ctypes.c_int
+    lib.gemm_f16_noalloc.argtypes = args12
+    lib.gemm_f16_noalloc.restype = ctypes.c_int
     lib.gemm_f16_ex.argtypes = args12 + [vp, sz, ctypes.POINTER(Opts)]
     lib.gemm_f16_ex.restype = ctypes.c_int
     lib.gemm_f16_plan.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64,

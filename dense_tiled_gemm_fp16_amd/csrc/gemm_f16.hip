@@ -21,6 +21,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gemm_f16.h"
 #include "gemv_kernel.hpp"
@@ -30,6 +31,13 @@
 #include "tiles.hpp"
 
 using namespace gemmf16;
+
+// Workspace of gemm_f16_noalloc: one fixed array per GPU, loaded with the
+// code object.  In host code `scratch` names a host-side stand-in, not device
+// memory; its device address is taken once per device with
+// hipGetSymbolAddress (with that device current, see scratch_address) and
+// only that address is ever passed to kernels or used by host calls.
+static __device__ __align__(256) unsigned char scratch[GEMM_F16_SCRATCH_BYTES];
 
 namespace {
 
@@ -53,6 +61,22 @@ const TileInfo& tile_info(int id) {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Device address of `scratch` on the current device, taken once per device.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GEMM_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return GEMM_OK;
+}
 
 // Compute units of the current device, cached per device.
 int device_cus(int* cus) {
@@ -736,6 +760,23 @@ int ex_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, 
   return rc;
 }
 
+// The automatic fp16 plan without a packing pass, its workspace in scratch.
+int noalloc_impl(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                 int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  Call c{DT_F16, A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
+  int rc = validate(c);
+  if (rc) return rc;
+  if ((rc = spans(c))) return rc;
+  Plan p;
+  if ((rc = make_plan(c, nullptr, p, false))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.ws == 0) return launch(c, p, nullptr, s);
+  if (p.ws > GEMM_F16_SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return launch(c, p, ws, s);
+}
+
 size_t ws_impl(int dt, int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts) {
   // Shape-only plan on non-overlapping, aligned stand-in addresses.
   if (M <= 0 || N <= 0 || K <= 0) return 0;
@@ -967,6 +1008,12 @@ size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_
   return ws_impl(DT_F16, M, N, K, opts);
 }
 
+int gemm_f16_noalloc(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                     int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                     void* stream) {
+  return noalloc_impl(A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, stream);
+}
+
 int gemm_bf16_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
                    int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                    const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
@@ -1075,6 +1122,7 @@ const char* gemm_f16_status_string(int status) {
     case GEMM_ERR_OPTS: return "invalid options (variant, split, panel or tile)";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_LAYOUT: return "operand layout not taken for this format (FP8: K-contiguous A and B, 16-byte aligned rows)";
+    case GEMM_ERR_SCRATCH: return "the plan's workspace exceeds the fixed no-allocation scratch (GEMM_F16_SCRATCH_BYTES, 32 MiB)";
     default: return "unknown status";
   }
 }

@@ -60,7 +60,9 @@ enum gemm_status {
   GEMM_ERR_WORKSPACE = -6, /* the workspace given is smaller than required       */
   GEMM_ERR_OPTS = -7,      /* invalid forced variant, split, panel or tile       */
   GEMM_ERR_HIP = -8,       /* a HIP runtime call failed (no device, launch, ...) */
-  GEMM_ERR_LAYOUT = -9     /* operand layout not taken for the format (FP8 below) */
+  GEMM_ERR_LAYOUT = -9,    /* operand layout not taken for the format (FP8 below) */
+  GEMM_ERR_SCRATCH = -10   /* gemm_f16_noalloc: the plan needs more than the     */
+                           /* library's fixed scratch (GEMM_F16_SCRATCH_BYTES)   */
 };
 
 /* Kernel families (gemm_f16_opts.variant / gemm_f16_plan_info.variant).
@@ -322,6 +324,27 @@ int gemm_f8_grouped(const void* A, int64_t lda_m, int64_t lda_k,
 /* Workspace bytes gemm_f16_grouped, gemm_bf16_grouped and gemm_f8_grouped
  * need for G groups (0 if G is invalid). */
 size_t gemm_f16_grouped_workspace_bytes(int32_t G);
+
+/*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): C := A.B as
+ * gemm_f16, with the same arguments, validation and return codes, but the
+ * library allocates nothing.  The call never runs a packing plan, and a
+ * plan's workspace (split-K, stream-K or decode partials) lives in a fixed
+ * device array of GEMM_F16_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends.  A plan that needs more returns
+ * GEMM_ERR_SCRATCH before anything is enqueued (gemm_f16_plan with opts
+ * NULL reports the workspace a shape needs, packing aside).  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (on different streams, or from several threads without ordering) race and
+ * may give wrong results; calls ordered on one stream do not.  No kernel
+ * reads scratch it has not written in the same call, so it needs no clearing.
+ */
+#define GEMM_F16_SCRATCH_BYTES ((size_t)32 << 20)
+int gemm_f16_noalloc(const void* A, int64_t lda_m, int64_t lda_k,
+                     const void* B, int64_t ldb_k, int64_t ldb_n,
+                     void* C, int64_t ldc,
+                     int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Static, NUL-terminated description of a return code. */
 const char* gemm_f16_status_string(int status);
