@@ -1,0 +1,221 @@
+// Decode-shaped product (M <= 64) with N-contiguous B (gfx950).
+//
+// With a few rows of A the whole of B is streamed once to serve them, so the
+// product is bound by HBM bandwidth, not by matrix throughput (the tiling
+// tutorial, section 04: at M = 1 the weight reads dominate; the TileLang
+// tutorial ch. 14, pitfall 1: pipelining a memory-bound GEMM only takes
+// on-chip space).  Everything here serves the B stream: every 16-byte load of
+// a wave covers whole 128-byte lines, each wave issues all the loads of its
+// share before any arithmetic, and there is no LDS staging of B.
+//
+// Work split: workgroup (nb, s) owns the 128 columns [128 nb, 128 nb + 128)
+// and the K range [s KR, (s+1) KR), cut into units of 32 k.  Its 4 waves
+// take the units round-robin.  In a unit, lane (g, c) (g = lane / 16,
+// c = lane % 16) loads the 8 rows 8g .. 8g+7 of the 8 columns 8c .. 8c+7
+// (one 16-byte vector per row; one load instruction of the wave covers 4
+// rows x 256 bytes), then transposes the 8 x 8 halves in registers into 8
+// k-octets, one per column 8c + f.  Those are exactly the B operands of
+// v_mfma_f32_16x16x32_f16 in which lane (g, c) supplies "column" c and
+// k-octet g: MFMA f multiplies the rows of A by the 16 columns {8c + f}.
+// The A operand is one 16-byte load of 8 consecutive k per lane (row
+// 16 fa + c of A); rows past M are zero, so M = 1 costs the same as M = 16
+// (the matrix cores are idle here anyway).  Lane (g, c) ends with outputs
+// (16 fa + 4g + r, 8c + f), r < 4, f < 8: 8 consecutive columns per row.
+//
+// The 4 waves' sums are added through LDS in ascending wave order; with one
+// K range the workgroup writes C (round to nearest even), with several it
+// writes fp32 partials P[s][m][n] that splitk_reduce sums in ascending s in
+// a second launch.  There is no in-kernel "last workgroup sums" step: it
+// needs a device-scope release per workgroup, an L2 writeback on gfx950,
+// which costs more than the second launch.  K is masked per row with zero
+// fill (never wrapped); N is masked per column; addresses are int64.
+#pragma once
+
+#include "tile_kernel.hpp"
+
+namespace gemmf16 {
+
+struct DecArgs {
+  const uint16_t* A;
+  int64_t lda_m, lda_k;
+  const uint16_t* B;
+  int64_t ldb_k;       // B is N-contiguous (ldb_n == 1), 16-byte aligned, ldb_k % 8 == 0
+  uint16_t* C;
+  int64_t ldc;
+  float* P;            // partials [S][M][N] (S > 1 only)
+  int64_t M, N, K;
+  int64_t kr;          // rows per K range, a multiple of 32
+  int32_t GN, S;
+  int32_t a_vec;       // A K-contiguous with 16-byte aligned rows: vector A loads
+  int32_t c_vec;       // C 16-byte aligned with ldc % 8 == 0: vector C stores
+};
+
+constexpr int kDecCols = 128;  // columns per workgroup
+constexpr int kDecUnit = 32;   // k per unit (one MFMA k-step)
+constexpr int kDecWaves = 4;
+// Units per wave whose loads are in flight together (fewer with 64 rows of
+// A, whose accumulators take a quarter of the registers).
+template <int MT>
+constexpr int dec_upw() { return MT >= 64 ? 2 : 4; }
+
+// 8 consecutive k of A row m from k0, zero past M or at/after ke.
+__device__ __forceinline__ u32x4 dec_load_a(const DecArgs& a, int64_t m, int64_t k0, int64_t ke) {
+  if (m >= a.M || k0 >= ke) return zero4();
+  const uint16_t* p = a.A + m * a.lda_m + k0 * a.lda_k;
+  const int nk = (ke - k0 >= 8) ? 8 : (int)(ke - k0);
+  if (a.a_vec && nk == 8) return *reinterpret_cast<const u32x4*>(p);
+  return load_partial8(p, a.lda_k, nk);
+}
+
+// The k loop of one wave over its units (u = w, w + 4, ...) of [kb, ke).
+// FULL: every unit lies inside the range, the 8 columns of every lane are
+// inside N and A rows are 16-byte vectors, so the loads carry no masks and
+// no branches (rows of A past M are read from row 0 and zeroed); otherwise
+// each load is masked on its own.
+template <int MT, int DT, bool FULL>
+__device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16][8], int w, int g, int c,
+                                          int64_t kb, int64_t ke, const uint16_t* bcol, int nvalid) {
+  constexpr int FA = MT / 16;
+  constexpr int UPW = dec_upw<MT>();
+  const int64_t units = (ke - kb + kDecUnit - 1) / kDecUnit;
+  for (int64_t u0 = w; u0 < units; u0 += kDecWaves * UPW) {
+    // All loads of UPW units first (A, then B), arithmetic after.  A unit
+    // past the range end is read from the last unit (cache hits) and its
+    // operands replaced by zeros, so the code has no branch and the waits
+    // before each unit's arithmetic count only the loads issued before it.
+    u32x4 av[UPW][FA], bv[UPW][8];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int64_t u = u0 + (int64_t)kDecWaves * i;
+      const bool live = u < units;
+      const int64_t k0 = kb + (live ? u : units - 1) * kDecUnit + 8 * g;
+#pragma unroll
+      for (int fa = 0; fa < FA; ++fa) {
+        const int64_t m = 16 * fa + c;
+        if constexpr (FULL) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(a.A + (m < a.M ? m : 0) * a.lda_m + k0);
+          av[i][fa] = (live && m < a.M) ? x : zero4();
+        } else {
+          av[i][fa] = live ? dec_load_a(a, m, k0, ke) : zero4();
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int64_t u = u0 + (int64_t)kDecWaves * i;
+      const bool live = u < units;
+      const int64_t k0 = kb + (live ? u : units - 1) * kDecUnit + 8 * g;
+      if constexpr (FULL) {
+        // (a dead unit's A operand is zero, so its B rows need no mask)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[i][j] = *reinterpret_cast<const u32x4*>(bcol + (k0 + j) * a.ldb_k);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          bv[i][j] = (live && nvalid > 0 && k0 + j < ke) ? load_partial8(bcol + (k0 + j) * a.ldb_k, 1, nvalid)
+                                                          : zero4();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      u32x4 bt[8];
+      transpose8x8(bv[i], bt);
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+#pragma unroll
+        for (int fa = 0; fa < FA; ++fa)
+          acc[fa][f] = mfma<16, DT>(__builtin_bit_cast(f16x8, av[i][fa]), __builtin_bit_cast(f16x8, bt[f]),
+                                    acc[fa][f]);
+    }
+  }
+}
+
+template <int MT, int DT>
+__global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
+  static_assert(MT % 16 == 0 && MT <= 64, "16, 32, 48 or 64 rows of A");
+  constexpr int FA = MT / 16;
+  __shared__ __attribute__((aligned(16))) float red[kDecWaves][16][16][8];   // [wave][m][c][f]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t nb = blockIdx.x % a.GN, s = blockIdx.x / a.GN;
+  const int64_t kb = s * a.kr;
+  const int64_t ke = (kb + a.kr < a.K) ? kb + a.kr : a.K;
+  const int64_t n0 = nb * kDecCols + c * 8;
+  const int nvalid = (n0 + 8 <= a.N) ? 8 : (n0 < a.N ? (int)(a.N - n0) : 0);
+  const uint16_t* bcol = a.B + (nvalid > 0 ? n0 : 0);
+
+  f32x4 acc[FA][8];
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[i][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Uniform per workgroup: whole strip inside N, whole units, vector A.
+  const bool full = (nb + 1) * kDecCols <= a.N && (ke - kb) % kDecUnit == 0 && a.a_vec;
+  if (full)
+    dec_units<MT, DT, true>(a, acc, w, g, c, kb, ke, bcol, nvalid);
+  else
+    dec_units<MT, DT, false>(a, acc, w, g, c, kb, ke, bcol, nvalid);
+
+  // Sum the 4 waves in ascending order, 16 rows of A at a time; thread t
+  // then owns row t / 16 and the 8 columns 8 (t % 16) .. + 7 of the block.
+  const int tm = tid >> 4, tc = tid & 15;
+  const int64_t col = nb * kDecCols + tc * 8;
+  const int cvalid = (col + 8 <= a.N) ? 8 : (col < a.N ? (int)(a.N - col) : 0);
+#pragma unroll
+  for (int fa = 0; fa < FA; ++fa) {
+    if (16 * fa >= a.M) break;   // uniform across the workgroup
+    if (fa > 0) __syncthreads();  // red is free
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* dst = &red[w][4 * g + r][c][0];
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[fa][0][r], acc[fa][1][r], acc[fa][2][r], acc[fa][3][r]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[fa][4][r], acc[fa][5][r], acc[fa][6][r], acc[fa][7][r]};
+    }
+    __syncthreads();
+    const int64_t m = 16 * fa + tm;
+    if (m < a.M && cvalid > 0) {
+      float t[8];
+#pragma unroll
+      for (int f = 0; f < 8; ++f) t[f] = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kDecWaves; ++ww) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(&red[ww][tm][tc][0]);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(&red[ww][tm][tc][4]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          t[f] += lo[f];
+          t[f + 4] += hi[f];
+        }
+      }
+      if (a.S == 1) {
+        uint16_t* o = a.C + m * a.ldc + col;
+        if (a.c_vec && cvalid == 8) {
+          uint32_t h[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            h[d] = (uint32_t)cvt_out<DT>(t[2 * d]) | ((uint32_t)cvt_out<DT>(t[2 * d + 1]) << 16);
+          *reinterpret_cast<u32x4*>(o) = u32x4{h[0], h[1], h[2], h[3]};
+        } else {
+#pragma unroll
+          for (int f = 0; f < 8; ++f)
+            if (f < cvalid) o[f] = cvt_out<DT>(t[f]);
+        }
+      } else {
+        float* o = a.P + (s * a.M + m) * a.N + col;
+        if ((a.N & 3) == 0 && cvalid == 8) {
+          *reinterpret_cast<f32x4*>(o) = f32x4{t[0], t[1], t[2], t[3]};
+          *reinterpret_cast<f32x4*>(o + 4) = f32x4{t[4], t[5], t[6], t[7]};
+        } else {
+#pragma unroll
+          for (int f = 0; f < 8; ++f)
+            if (f < cvalid) o[f] = t[f];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace gemmf16

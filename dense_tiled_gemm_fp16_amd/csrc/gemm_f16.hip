@@ -24,7 +24,7 @@
 #include <mutex>
 
 #include "../../include/gemm_f16.h"
-#include "gemv_kernel.hpp"
+#include "decode_kernel.hpp"
 #include "group_kernel.hpp"
 #include "pack_kernel.hpp"
 #include "reduce_kernel.hpp"
@@ -43,11 +43,7 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
-// The decode-shaped VALU kernel: rows of B per thread per pass.
-constexpr int kGemvRpt = 8;
-constexpr int64_t kGemvRowsPerPass = 8 * kGemvRpt;
-
-typedef void (*kfn_gemv)(GemvArgs);
+typedef void (*kfn_dec)(DecArgs);
 typedef void (*kfn_reduce)(const float*, int, int64_t, int64_t, uint16_t*, int64_t, int);
 
 const TileInfo& tile_info(int id) {
@@ -121,8 +117,8 @@ int classify(const void* base, int64_t s_r, int64_t s_k) {
 
 struct Plan {
   int variant, tile_id, split, panel, a_path, b_path, c_vec;
-  int gemv_mt;  // > 0: the decode-shaped VALU kernel with this many A rows
-  int red_lanes;  // lanes per output quad in the split reduction
+  int dec_mt;   // > 0: the decode kernel with this many rows of A (16, 32 or 64)
+  int red_elem;   // split reduction: one thread per output (else per 4 outputs)
   int64_t GM, GN, grid, grid2, k_split;
   int64_t sk_tiles;  // STREAMK: tiles split over K after the whole waves
   bool pack;         // B is packed into the workspace first (see maybe_pack)
@@ -179,22 +175,21 @@ void set_split(Plan& p, int64_t K, int bk, int64_t split) {
 }
 
 // Workspace and reduction launch of a plan with p.split K ranges.  The
-// reduction's lane-group width depends on the output size only, so a forced
-// plan needs no device query: small outputs (decode shapes) spread each
-// output's sum over more lanes to hide the latency of the partials' loads.
+// reduction's shape depends on the output size only, so a forced plan needs
+// no device query: small outputs (decode shapes) take one thread per output,
+// whose loads of all K ranges are in flight together.
 int plan_partials(const Call& c, Plan& p) {
   p.ws = 0;
   p.grid2 = 0;
-  p.red_lanes = 1;
+  p.red_elem = 0;
   if (p.split <= 1) return GEMM_OK;
   int64_t mn, bytes;
   if (__builtin_mul_overflow(c.M, c.N, &mn) || __builtin_mul_overflow(mn, (int64_t)p.split, &bytes) ||
       __builtin_mul_overflow(bytes, (int64_t)4, &bytes) || bytes > INT64_MAX - 256)
     return GEMM_ERR_SHAPE;
   p.ws = (size_t)((bytes + 255) / 256 * 256);
-  const int64_t quads = c.M * cdiv(c.N, 4);
-  p.red_lanes = (quads <= 16384 && p.split >= 16) ? 16 : ((quads <= 65536 && p.split >= 4) ? 4 : 1);
-  int64_t g2 = cdiv(quads * p.red_lanes, 256);
+  p.red_elem = mn <= (INT64_C(1) << 18) ? 1 : 0;
+  int64_t g2 = p.red_elem ? cdiv(mn, 256) : cdiv(c.M * cdiv(c.N, 4), 256);
   if (g2 > 8192) g2 = 8192;
   p.grid2 = g2;
   return GEMM_OK;
@@ -441,23 +436,25 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     default:
       return GEMM_ERR_OPTS;
   }
-  // M <= 4 with N-contiguous B: the decode-shaped VALU kernel (from M = 5 on
-  // the 16-row MFMA skinny tile streams B as fast and spends less VALU time).
-  p.gemv_mt = 0;
-  p.red_lanes = 1;
-  if (p.variant == GEMM_VARIANT_SKINNY && !want_tile && c.M <= 4 && p.b_path == PATH_RVEC) {
-    p.gemv_mt = c.M <= 1 ? 1 : (c.M <= 2 ? 2 : 4);
+  // M <= 64 with N-contiguous B: the decode kernel (128-column strips, one
+  // workgroup per strip and K range, about one workgroup per compute unit,
+  // K ranges of at least 128 k).
+  p.dec_mt = 0;
+  p.red_elem = 0;
+  if (p.variant == GEMM_VARIANT_SKINNY && !want_tile && c.M <= 64 && p.b_path == PATH_RVEC) {
+    p.dec_mt = c.M <= 16 ? 16 : (c.M <= 32 ? 32 : 64);
     p.GM = 1;
-    p.GN = cdiv(c.N, 256);
+    p.GN = cdiv(c.N, kDecCols);
     int64_t s = want_split;
     if (s == 0) {
       if ((rc = need_cus())) return rc;
-      s = cdiv(2 * (int64_t)cus, p.GN);  // about two workgroups per compute unit
+      s = cdiv((int64_t)cus, p.GN);
+      if (s > cdiv(c.K, 4 * kDecUnit)) s = cdiv(c.K, 4 * kDecUnit);
     }
-    p.k_split = cdiv(cdiv(c.K, s), kGemvRowsPerPass) * kGemvRowsPerPass;
+    p.k_split = cdiv(cdiv(c.K, s), kDecUnit) * kDecUnit;
     p.split = (int)cdiv(c.K, p.k_split);
     p.panel = -1;
-    p.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
+    p.c_vec = (((uintptr_t)c.C & 15u) == 0 && (c.ldc & 7) == 0) ? 1 : 0;
     int64_t grid;
     if (__builtin_mul_overflow(p.GN, (int64_t)p.split, &grid) || grid > INT32_MAX)
       return GEMM_ERR_SHAPE;
@@ -514,7 +511,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     p.grid2 = L * (ti.bm * ti.bn / 1024);
     p.panel = want_panel != 0 ? want_panel : 4;
     p.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
-    p.red_lanes = 1;
+    p.red_elem = 0;
     int64_t bytes;
     if (__builtin_mul_overflow(L * p.split, (int64_t)ti.bm * ti.bn * 4, &bytes) || bytes > INT64_MAX - 256)
       return GEMM_ERR_SHAPE;
@@ -570,9 +567,9 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
 void fill_info(const Plan& p, gemm_f16_plan_info* info) {
   const TileInfo& ti = tile_info(p.tile_id);
   info->variant = p.variant;
-  info->tile_m = p.gemv_mt ? p.gemv_mt : ti.bm;
-  info->tile_n = p.gemv_mt ? 256 : ti.bn;
-  info->tile_k = p.gemv_mt ? (int32_t)kGemvRowsPerPass : ti.bk;
+  info->tile_m = p.dec_mt ? p.dec_mt : ti.bm;
+  info->tile_n = p.dec_mt ? kDecCols : ti.bn;
+  info->tile_k = p.dec_mt ? kDecUnit : ti.bk;
   info->split_k = p.split;
   info->panel = p.panel;
   info->a_path = p.a_path;
@@ -593,8 +590,8 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   uint16_t* C = (uint16_t*)c.C;
   int cv = p.c_vec;
   kfn_reduce fn = c.dt != DT_BF16   // binary16 output for the fp16 and FP8 formats
-      ? (p.red_lanes == 16 ? splitk_reduce<16, DT_F16> : (p.red_lanes == 4 ? splitk_reduce<4, DT_F16> : splitk_reduce<1, DT_F16>))
-      : (p.red_lanes == 16 ? splitk_reduce<16, DT_BF16> : (p.red_lanes == 4 ? splitk_reduce<4, DT_BF16> : splitk_reduce<1, DT_BF16>));
+      ? (p.red_elem ? splitk_reduce_elem<DT_F16> : splitk_reduce_quad<DT_F16>)
+      : (p.red_elem ? splitk_reduce_elem<DT_BF16> : splitk_reduce_quad<DT_BF16>);
   void* rargs[] = {&W, &S, &M, &N, &C, &ldc, &cv};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid2), dim3(256), rargs, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
@@ -602,29 +599,37 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
 }
 
 template <int MT>
-kfn_gemv pick_gemv(int dt) { return dt == DT_F16 ? gemv_kernel<MT, kGemvRpt, DT_F16> : gemv_kernel<MT, kGemvRpt, DT_BF16>; }
+kfn_dec pick_dec(int dt) { return dt == DT_F16 ? decode_kernel<MT, DT_F16> : decode_kernel<MT, DT_BF16>; }
 
-int launch_gemv(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
-  GemvArgs g;
-  g.A = (const uint16_t*)c.A;
-  g.lda_m = c.lda_m;
-  g.lda_k = c.lda_k;
-  g.B = (const uint16_t*)c.B;
-  g.ldb_k = c.ldb_k;
-  g.C = (uint16_t*)c.C;
-  g.ldc = c.ldc;
-  g.P = (float*)ws;
-  g.M = c.M;
-  g.N = c.N;
-  g.K = c.K;
-  g.kr = p.k_split;
-  g.GN = (int32_t)p.GN;
-  g.S = p.split;
-  kfn_gemv fn = p.gemv_mt == 1 ? pick_gemv<1>(c.dt) : p.gemv_mt == 2 ? pick_gemv<2>(c.dt) : pick_gemv<4>(c.dt);
-  void* args[] = {&g};
+int launch_decode(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
+  DecArgs d;
+  d.A = (const uint16_t*)c.A;
+  d.lda_m = c.lda_m;
+  d.lda_k = c.lda_k;
+  d.B = (const uint16_t*)c.B;
+  d.ldb_k = c.ldb_k;
+  d.C = (uint16_t*)c.C;
+  d.ldc = c.ldc;
+  d.P = (float*)ws;
+  d.M = c.M;
+  d.N = c.N;
+  d.K = c.K;
+  d.kr = p.k_split;
+  d.GN = (int32_t)p.GN;
+  d.S = p.split;
+  d.a_vec = (c.lda_k == 1 && c.lda_m % 8 == 0 && ((uintptr_t)c.A & 15u) == 0) ? 1 : 0;
+  d.c_vec = p.c_vec;
+  kfn_dec fn = p.dec_mt == 16 ? pick_dec<16>(c.dt) : p.dec_mt == 32 ? pick_dec<32>(c.dt) : pick_dec<64>(c.dt);
+  void* args[] = {&d};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(256), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
-  return launch_reduce(c, p, ws, stream);
+  if (p.split > 1) {
+    // The reduction writes C with 8-byte vectors (its own alignment rule).
+    Plan q = p;
+    q.c_vec = (((uintptr_t)c.C & 7u) == 0 && (c.ldc & 3) == 0) ? 1 : 0;
+    return launch_reduce(c, q, ws, stream);
+  }
+  return GEMM_OK;
 }
 
 // Stream-K plan: whole waves of tiles (raster ids 0 .. grid-1) with the
@@ -657,7 +662,7 @@ int launch_streamk(const Call& c, const Plan& p, KArgs a, kfn_t final_fn, kfn_t 
 }
 
 int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
-  if (p.gemv_mt) return launch_gemv(c, p, ws, stream);
+  if (p.dec_mt) return launch_decode(c, p, ws, stream);
   // Packing plan: B into the workspace (K16: K in 16-bit units).
   const int64_t K16 = c.dt >= DT_F8 ? cdiv(c.K, 2) : c.K;
   if (p.pack) {

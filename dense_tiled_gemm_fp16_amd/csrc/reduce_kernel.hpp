@@ -6,41 +6,33 @@
 
 namespace gemmf16 {
 
-// C[m][n] = rne( sum over s of W[s][m][n] ) in a fixed order (fp16 or
-// bfloat16 output, by DT).
-//
-// A group of L consecutive lanes owns 4 consecutive n of one row (a "quad");
-// lane j of the group sums the contiguous block of K ranges
-// [j * ceil(S/L), (j+1) * ceil(S/L)) in ascending s, and the group then adds
-// the L block sums in ascending j.  For a given (S, L) the order is fixed, so
-// results are bit-reproducible; the host picks L from the output size only.
-// Loads are issued eight at a time before they are added, so that a lane
-// waits for one memory round trip per eight partials rather than per partial
-// (the partials of a small output were written by other XCDs and come from
-// memory, not from this XCD's L2).
-template <int L, int DT>
-__global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int64_t M, int64_t N,
-                                                     uint16_t* C, int64_t ldc, int c_vec) {
-  static_assert(L >= 1 && 64 % L == 0, "a lane group lies inside one wave");
+// C[m][n] = rne( sum over s of W[s][m][n] ), s ascending from +0 (fp16 or
+// bfloat16 output, by DT): the order is fixed, so results are
+// bit-reproducible.  Two shapes of the same sum:
+//   splitk_reduce_quad: a thread owns 4 consecutive n of one row and loads
+//     16-byte vectors, eight K ranges at a time (large outputs);
+//   splitk_reduce_elem: a thread owns one output and issues the loads of up
+//     to 16 K ranges before adding them (small outputs, e.g. decode shapes,
+//     where a second round trip or any cross-lane step would cost more than
+//     the few bytes moved).
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_quad(const float* W, int S, int64_t M, int64_t N,
+                                                          uint16_t* C, int64_t ldc, int c_vec) {
   const int64_t NQ = (N + 3) / 4;
   const int64_t total = M * NQ;
   const int64_t MN = M * N;
-  const int lane = (int)(threadIdx.x % L);
-  const int per = (S + L - 1) / L;
-  const int sb = lane * per < S ? lane * per : S;
-  const int se = sb + per < S ? sb + per : S;
-  const int64_t step = (int64_t)gridDim.x * (blockDim.x / L);
-  for (int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / L; q < total; q += step) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += step) {
     const int64_t m = q / NQ, n = (q - m * NQ) * 4;
     const int nv = (N - n < 4) ? (int)(N - n) : 4;
     const float* p = W + m * N + n;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = sb; s0 < se; s0 += 8) {
+    for (int s0 = 0; s0 < S; s0 += 8) {
       f32x4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float* ps = p + (int64_t)(s0 + j) * MN;
-        if (s0 + j >= se) {
+        if (s0 + j >= S) {
           v[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         } else if ((N & 3) == 0) {
           v[j] = *reinterpret_cast<const f32x4*>(ps);
@@ -50,35 +42,45 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* W, int S, int6
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (s0 + j < se) {
+        if (s0 + j < S) {
           acc[0] += v[j][0];
           acc[1] += v[j][1];
           acc[2] += v[j][2];
           acc[3] += v[j][3];
         }
     }
-    float tot[4] = {acc[0], acc[1], acc[2], acc[3]};
-    if constexpr (L > 1) {
+    uint16_t* c = C + m * ldc + n;
+    const uint16_t h[4] = {cvt_out<DT>(acc[0]), cvt_out<DT>(acc[1]), cvt_out<DT>(acc[2]),
+                           cvt_out<DT>(acc[3])};
+    if (c_vec && nv == 4) {
+      *reinterpret_cast<u32x2*>(c) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float t = 0.0f;
-#pragma unroll
-        for (int j = 0; j < L; ++j) t += __shfl(acc[e], j, L);
-        tot[e] = t;
-      }
+      for (int e = 0; e < 4; ++e)
+        if (e < nv) c[e] = h[e];
     }
-    if (lane == 0) {
-      uint16_t* c = C + m * ldc + n;
-      const uint16_t h[4] = {cvt_out<DT>(tot[0]), cvt_out<DT>(tot[1]), cvt_out<DT>(tot[2]),
-                             cvt_out<DT>(tot[3])};
-      if (c_vec && nv == 4) {
-        *reinterpret_cast<u32x2*>(c) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
-      } else {
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_elem(const float* W, int S, int64_t M, int64_t N,
+                                                          uint16_t* C, int64_t ldc, int c_vec) {
+  (void)c_vec;
+  const int64_t MN = M * N;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += step) {
+    const float* p = W + e;
+    float acc = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float v[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e < nv) c[e] = h[e];
-      }
+      for (int j = 0; j < 16; ++j) v[j] = (s0 + j < S) ? p[(int64_t)(s0 + j) * MN] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (s0 + j < S) acc += v[j];
     }
+    const int64_t m = e / N, n = e - m * N;
+    C[m * ldc + n] = cvt_out<DT>(acc);
   }
 }
 

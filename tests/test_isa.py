@@ -4,8 +4,9 @@ and each kernel's instruction set is checked on the CPU.
 
 - Every dense-contraction kernel keeps its matrix instructions: the
   256x256 LDS-DMA kernels (final, partial, grouped and packed-B forms) the
-  fp16 or bfloat16 32x32x16 MFMA of their format, the register-path tiles an
-  MFMA of their format, and the FP8 kernels the 32x32x64 f8f6f4 MFMA.  An
+  fp16 or bfloat16 32x32x16 MFMA of their format, the register-path tiles and
+  the decode kernels an MFMA of their format, and the FP8 kernels the
+  32x32x64 f8f6f4 MFMA.  An
   optimisation that silently lost the matrix core would fail here (the C500
   log keeps a change only if the matrix instruction is still in the
   generated code: its final-kernel summary and its record template).
@@ -111,6 +112,14 @@ def test_register_tiles_keep_their_mfma(kernels):
         assert mf and all(k.endswith("_bf16" if bf16 else "_f16") for k in mf), (name, mf)
 
 
+def test_decode_kernels_keep_their_mfma(kernels):
+    found = _of(kernels, "decode_kernel")
+    assert len(found) == 6                  # 16, 32 and 64 rows of A, fp16 and bfloat16
+    for name, ops in found.items():
+        want = {"0": "v_mfma_f32_16x16x32_f16", "1": "v_mfma_f32_16x16x32_bf16"}[_targs(name)[-1]]
+        assert ops[want] >= 8, (name, want)
+
+
 def test_f8_kernels_keep_their_mfma(kernels):
     found = _of(kernels, "gemm_f8_kernel")
     assert len(found) >= 32                 # 4 format pairs x 8 forms
@@ -121,14 +130,14 @@ def test_f8_kernels_keep_their_mfma(kernels):
 def test_output_rounding_instructions(kernels):
     for name, ops in kernels.items():
         assert not [k for k in ops if k.startswith("v_cvt_pkrtz")], name
-    writers = ["gemm_dma_a128_kernel", "gemm_tile_kernel", "gemm_f8_kernel", "gemv_kernel",
-               "splitk_reduce", "sk_fixup"]
+    writers = ["gemm_dma_a128_kernel", "gemm_tile_kernel", "gemm_f8_kernel", "decode_kernel",
+               "splitk_reduce_quad", "splitk_reduce_elem", "sk_fixup"]
     for w in writers:
         for name, ops in _of(kernels, w).items():
             args = _targs(name)
             if w == "gemm_dma_a128_kernel" and args[4] == "1":
                 continue                    # bfloat16 output
-            if w in ("gemv_kernel", "splitk_reduce") and args[-1] == "1":
+            if w in ("decode_kernel", "splitk_reduce_quad", "splitk_reduce_elem") and args[-1] == "1":
                 continue
             if w == "sk_fixup" and args[0] == "1":
                 continue

@@ -402,42 +402,43 @@ def test_caller_workspace_is_used_and_needs_no_reset():
     assert e.value.status == -6
 
 
-# ------------------------------------------------------------------ decode-shaped VALU kernel
+# ------------------------------------------------------------------ decode kernel (M <= 64, N-contiguous B)
 
-def _gemv_case(M, N, K, mode, ldb_pad=0, split=0, seed=7000):
+def _decode_case(M, N, K, mode, ldb_pad=0, split=0, seed=7000):
     A = synth.matrix(M, K, seed + M, 0, mode)
     B = synth.matrix(K, N, seed + N, 1, mode)
     ref = reference(A, B)
     a = place(A, "row", (1, 8))
     b = place(B, "row", (0, ldb_pad)) if ldb_pad else to_dev(B)
     p = g.plan(a, b, variant="skinny", split_k=split)
-    assert p["b_path"] == "rvec" and p["tile_n"] == 256 and p["tile_m"] == {1: 1, 2: 2}.get(M, 4), p
+    assert p["b_path"] == "rvec" and p["tile_n"] == 128 and p["tile_m"] == (
+        16 if M <= 16 else 32 if M <= 32 else 64), p
     need = p["workspace_bytes"]
     ws = torch.full((max(need, 4096) // 4 + 64,), float("nan"), dtype=torch.float32, device=DEV)
     outs = []
     for _ in range(2):
         outs.append(run(a, b, Out(M, N), workspace=ws, variant="skinny", split_k=split))
         ws.fill_(-7.0)                       # the workspace needs no initialisation
-    assert_bits_equal(outs[1], outs[0], f"gemv rerun M={M} N={N} K={K}")
-    check(outs[0], ref, mode, f"gemv M={M} N={N} K={K} pad={ldb_pad} split={split}")
+    assert_bits_equal(outs[1], outs[0], f"decode rerun M={M} N={N} K={K}")
+    check(outs[0], ref, mode, f"decode M={M} N={N} K={K} pad={ldb_pad} split={split}")
     return p
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 17, 40, 64])
 def test_decode_kernel_uniform(M):
-    p = _gemv_case(M, 2048, 7168, "uniform")
+    p = _decode_case(M, 2048, 7168, "uniform")
     assert p["split_k"] > 1
-    _gemv_case(M, 1001, 300, "uniform", ldb_pad=7)       # ragged last vector and last split
-    _gemv_case(M, 520, 1024, "uniform", split=1)          # one split: direct store
-    _gemv_case(M, 264, 2500, "uniform", split=2)          # K ranges longer than one A chunk
-    _gemv_case(M, 1001, 7168, "uniform", ldb_pad=7)      # 16-lane reduction, ragged N
+    _decode_case(M, 1001, 300, "uniform", ldb_pad=7)       # ragged last vector and last split
+    _decode_case(M, 520, 1024, "uniform", split=1)          # one split: direct store
+    _decode_case(M, 264, 2500, "uniform", split=2)          # K ranges longer than one A chunk
+    _decode_case(M, 1001, 7168, "uniform", ldb_pad=7)      # 16-lane reduction, ragged N
 
 
-@pytest.mark.parametrize("M", [1, 3, 4])
+@pytest.mark.parametrize("M", [1, 3, 4, 16, 33, 64])
 def test_decode_kernel_integer_exact(M):
     for split in (0, 1, 3):
-        _gemv_case(M, 777, 128, "int", ldb_pad=7, split=split)
-        _gemv_case(M, 2048, 128, "int", split=split)
+        _decode_case(M, 777, 128, "int", ldb_pad=7, split=split)
+        _decode_case(M, 2048, 128, "int", split=split)
 
 
 def test_wrapper_rejects_bad_arguments():

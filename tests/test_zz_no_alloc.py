@@ -61,7 +61,7 @@ def pair(M, N, K, seed, mode):
 def test_noalloc_two_calls_then_smaller(mode):
     K_big = 16384 if mode == "uniform" else 128
     pair(512, 512, K_big if mode == "uniform" else 4096, 33001, mode)   # split-K partials
-    pair(1, 2048, 7168 if mode == "uniform" else 128, 33002, mode)      # decode partials
+    pair(1, 2048, 7168 if mode == "uniform" else 1024, 33002, mode)     # decode partials
 
 
 def test_noalloc_refuses_a_plan_beyond_the_scratch():
