@@ -25,8 +25,22 @@ METRIC = "TFLOPS & %MFMA peak, fp16 GEMM 131072x2048x7168; GB/s at M=1"
 PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_F8_TFLOPS = 5033.2       # MI355X dense FP8 MFMA (twice the fp16 rate)
-PAGES_TFLOPS = 117.250897     # the pages' TileLang kernel on MetaX C500, same workload
+PAGES_TFLOPS = 117.250897     # the pages' TileLang kernel on MetaX C500, same workload (context)
 M, N, K = 131072, 2048, 7168
+
+
+# Single workloads for profilers (bench.py --case NAME): M, N, K, B layout,
+# seed.  Working sets under 1 GiB rotate over copies of A and B.
+CASES = {
+    "main": (131072, 2048, 7168, "row", 4001),
+    "decode_m1": (1, 2048, 7168, "row", 3001),
+    "decode_m16": (16, 2048, 7168, "row", 3016),
+    "decode_m64": (64, 2048, 7168, "row", 3064),
+    "splitk": (512, 512, 65536, "row", 3004),
+    "square_4096": (4096, 4096, 4096, "row", 6096),
+    "square_8192": (8192, 8192, 8192, "row", 10192),
+    "stride": (262181, 1061, 8192, "col", 5001),
+}
 
 
 def parse():
@@ -43,6 +57,12 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
+    ap.add_argument("--summarize-profile", nargs="+", metavar="CSV",
+                    help="markdown summary of one --case run under rocprofv3: a kernel_trace.csv "
+                         "(durations) and counter_collection.csv files of --pmc passes")
+    ap.add_argument("--case", choices=sorted(CASES),
+                    help="run only this workload's calls (--steps of them after --warmup), for "
+                         "profilers; prints one JSON line with its per-call time")
     return ap.parse_args()
 
 
@@ -115,8 +135,8 @@ def summarize_pmc(fetch_csv, write_csv):
                            "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer"},
            "source_hash": kernel_source_hash()}
     alg = {"main_131072x2048x7168": (MAIN_KERNEL, 2.0 * (M * K + K * N), 2.0 * M * N),
-           "skinny_m1_partials": ("void gemmf16::gemv_kernel<1, 8, 0>", 2.0 * (K + K * N), None),
-           "skinny_m1_reduce": ("void gemmf16::splitk_reduce<16, 0>", None, 2.0 * N)}
+           "skinny_m1_partials": ("void gemmf16::decode_kernel<16, 0>", 2.0 * (K + K * N), None),
+           "skinny_m1_reduce": ("void gemmf16::splitk_reduce_elem<0>", None, 2.0 * N)}
     for key, (sub, alg_read, alg_write) in alg.items():
         k = kernel(sub)
         if k is None:
@@ -129,6 +149,87 @@ def summarize_pmc(fetch_csv, write_csv):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+SIMDS = 1024       # 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def summarize_profile(paths):
+    """Markdown summary of a --case run under rocprofv3.
+
+    From the kernel trace: per library kernel, the steady-state median,
+    mean and minimum duration over its launches after the first fifth (the
+    warm-up).  From counter passes: the per-dispatch mean of every counter
+    over the same steady-state dispatches, and derived figures:
+      clock       GRBM_GUI_ACTIVE / XCDs / median duration (GRBM_GUI_ACTIVE is
+                  counted once per XCD);
+      MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles per XCD x 1024 SIMDs);
+      LDS bank conflicts per active LDS cycle;
+      L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS);
+      FETCH/WRITE bytes, scaled by a 1 GiB device copy in the same pass
+                  (--copy-calibration) when one is there."""
+    import csv
+    import statistics
+
+    def steady(vals):
+        return vals[len(vals) // 5:] if len(vals) >= 5 else vals
+
+    dur, ctr = {}, {}
+    for path in paths:
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        if rows and "Start_Timestamp" in rows[0] and "Counter_Name" not in rows[0]:
+            for r in rows:
+                dur.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        else:
+            per = {}
+            for r in rows:
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                per.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(per)), 0.0)
+                per[key][r.get("Dispatch_Id", len(per))] += float(r["Counter_Value"])
+            for (k, c), d in per.items():
+                ctr.setdefault(k, {})[c] = [d[i] for i in sorted(d, key=lambda x: int(x))]
+    scale = {}
+    for c, kib in (("FETCH_SIZE", COPY_KIB), ("WRITE_SIZE", COPY_KIB)):
+        copy = sorted(ctr.get("__amd_rocclr_copyBuffer", {}).get(c, []))[-3:]
+        if copy:
+            scale[c] = kib * 1024.0 / statistics.median(copy)
+    lines = ["| kernel | launches | median (us) | mean (us) | min (us) |", "|---|---|---|---|---|"]
+    for k in sorted(dur, key=lambda k: -sum(dur[k])):
+        if "gemmf16" not in k:
+            continue
+        v = steady(dur[k])
+        lines.append(f"| `{k[:110]}` | {len(v)} | {statistics.median(v):.2f} | "
+                     f"{statistics.mean(v):.2f} | {min(v):.2f} |")
+    lines += ["", "| kernel | counter | per dispatch (steady mean) |", "|---|---|---|"]
+    derived = ["", "| kernel | clock (GHz) | MFMA busy | LDS bank conflict / LDS active | "
+               "L2 hit rate | fetched bytes | written bytes |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(ctr):
+        if "gemmf16" not in k:
+            continue
+        m = {c: statistics.mean(steady(v)) for c, v in ctr[k].items()}
+        for c in sorted(m):
+            lines.append(f"| `{k[:70]}` | {c} | {m[c]:.6g} |")
+        med = statistics.median(steady(dur[k])) if k in dur else None
+        gui = m.get("GRBM_GUI_ACTIVE")
+        cyc = gui / XCDS if gui else None
+        clock = f"{cyc / (med * 1e3):.3f}" if cyc and med else "-"
+        mfma = (f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * SIMDS):.1f}%"
+                if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in m else "-")
+        lds = (f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.4f}"
+               if m.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in m else "-")
+        hit = (f"{m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.3f}"
+               if "TCC_HIT_sum" in m and m.get("TCC_HIT_sum", 0) + m.get("TCC_MISS_sum", 0) > 0 else "-")
+        fb = f"{m['FETCH_SIZE'] * scale['FETCH_SIZE']:.4g}" if "FETCH_SIZE" in m and "FETCH_SIZE" in scale else "-"
+        wb = f"{m['WRITE_SIZE'] * scale['WRITE_SIZE']:.4g}" if "WRITE_SIZE" in m and "WRITE_SIZE" in scale else "-"
+        derived.append(f"| `{k[:70]}` | {clock} | {mfma} | {lds} | {hit} | {fb} | {wb} |")
+    if scale:
+        derived.append("")
+        derived.append("Byte scale factors from the 1 GiB copy: " +
+                       ", ".join(f"{c} x{v / 1024.0:.4f} per KiB" for c, v in scale.items()))
+    print("\n".join(lines + derived))
 
 
 def timed_launches(fn, stream, steps, warmup):
@@ -168,8 +269,20 @@ def timed_pair(fn1, fn2, stream, steps, warmup):
     return [e[0].elapsed_time(e[1]) for e in ev], [e[2].elapsed_time(e[3]) for e in ev]
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s=15.0):
-    """The CPU oracle (as is) on whole output rows of the same product."""
+    """The CPU oracle (as is) on whole output rows of the same product, with
+    the time of the whole product projected from the sample's row rate."""
     import numpy as np
     import oracle
     import synth
@@ -188,7 +301,11 @@ def cpu_baseline(budget_s=15.0):
     return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOPS", "cores": threads,
             "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product ({rows}x{N} outputs, "
-                      f"full K), {dt:.1f} s"}
+                      f"full K), {dt:.1f} s",
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "threads_note": "one oracle thread per core of this process's affinity, at most 16 "
+                            "(the host share of one GPU)",
+            "projected_full_product_s": round(dt * M / rows, 1)}
 
 
 # The workload families (the pages' shapes and the MoE product), as (name,
@@ -280,10 +397,76 @@ def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant):
     torch.cuda.empty_cache()
 
 
+def copy_calibration():
+    """Three device copies of 1 GiB: a known-size reference for the HBM
+    byte counters of a profiling pass."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.float16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def run_case(name, steps, warmup):
+    """--steps calls of one workload's automatic plan after --warmup, on the
+    current stream; one JSON line with the mean time per call (HIP events
+    around the whole loop)."""
+    import numpy as np
+    import torch
+
+    import dense_tiled_gemm_fp16_amd as g
+    import synth
+
+    m, n, k, bl, seed = CASES[name]
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+
+    a0 = to_dev(synth.matrix(m, k, seed, synth.TENSOR_A))
+    bt = synth.matrix(k, n, seed, synth.TENSOR_B, order="col" if bl == "col" else "row")
+    b0 = to_dev(bt).t() if bl == "col" else to_dev(bt)
+    byts = 2.0 * (m * k + k * n + m * n)
+    copies = int(min(64, max(1, -(-(1 << 30) // int(byts)))))
+    As = [a0] + [a0.clone() for _ in range(copies - 1)]
+    Bs = [b0] + [(b0.t().clone().t() if bl == "col" else b0.clone()) for _ in range(copies - 1)]
+    c = torch.empty((m, n), dtype=torch.float16, device=dev)
+    p = g.plan(a0, b0, c)
+    ws = (torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+          if p["workspace_bytes"] else None)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        g.gemm(As[i % copies], Bs[i % copies], out=c, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        g.gemm(As[i % copies], Bs[i % copies], out=c, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"case": name, "M": m, "N": n, "K": k, "b_layout": bl, "copies": copies,
+                      "steps": steps, "warmup": warmup, "us_per_call": us,
+                      "TFLOPS": 2.0 * m * n * k / us / 1e6, "GBps": byts / us / 1e3,
+                      "plan": {q: p[q] for q in ("variant", "tile_id", "tile_m", "tile_n",
+                                                 "split_k", "grid", "grid2", "b_path")}}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
+    if args.case:
+        if args.copy_calibration:
+            copy_calibration()
+        run_case(args.case, args.steps, args.warmup)
         return
     if args.configs:
         configs_sweep()
@@ -306,12 +489,7 @@ def main():
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
 
     if args.copy_calibration:
-        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     # ---- headline workload
     a = to_dev(synth.matrix(M, K, 4001, synth.TENSOR_A))
@@ -517,7 +695,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": round(tflops / PAGES_TFLOPS, 3), "dtype": "f16",
+        "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded U(-1,1) fp16, counter-based generator)",
         "config": {"workload": "MoE-derived dense GEMM 131072x2048x7168 fp16, fp32 accumulate",
                    "M": M, "N": N, "K": K, "a_layout": "row-major", "b_layout": "row-major",
@@ -537,10 +715,14 @@ def main():
         "f8_bn": f8_bn,
         "packed_b": packed_b,
         "b_kmajor": b_kmajor,
-        "vs_baseline_ref": "pages' TileLang kernel on MetaX C500, 117.25 TFLOPS (context only)",
+        "context": {"pages_tilelang_metax_c500_tflops": PAGES_TFLOPS,
+                    "note": "another machine's figure for the same workload; not a target"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+        # the stated baseline is the CPU oracle on this host (vs_baseline stays
+        # null: the pages' figure is another machine's, context only)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(tflops / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 

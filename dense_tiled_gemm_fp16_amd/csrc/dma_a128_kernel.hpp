@@ -340,8 +340,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
       split = w / a.sk_tiles;
       w = a.sk_first + (w - split * a.sk_tiles);
     } else {
-      split = w / T;
-      w -= split * T;
+      split_tile_of(blockIdx.x, T, a.split_xcd, split, w);
     }
   }
   int64_t pm, pn;

@@ -286,10 +286,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
   const int64_t T = a.GM * a.GN;
   int64_t w = blockIdx.x;
   int64_t split = 0;
-  if constexpr (PARTIAL) {
-    split = w / T;
-    w -= split * T;
-  }
+  if constexpr (PARTIAL) split_tile_of(blockIdx.x, T, a.split_xcd, split, w);
   int64_t pm, pn;
   raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;

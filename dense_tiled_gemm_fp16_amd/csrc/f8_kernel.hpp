@@ -208,8 +208,7 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
       split = w / a.sk_tiles;
       w = a.sk_first + (w - split * a.sk_tiles);
     } else {
-      split = w / T;
-      w -= split * T;
+      split_tile_of(blockIdx.x, T, a.split_xcd, split, w);
     }
   }
   int64_t pm, pn;

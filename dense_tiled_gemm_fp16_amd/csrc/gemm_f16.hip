@@ -293,6 +293,7 @@ int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, c
   a.G = 0;
   a.sk_first = 0;
   a.sk_tiles = 0;
+  a.split_xcd = 0;
   int64_t grid;
   if (__builtin_mul_overflow(a.GM, a.GN, &grid) || grid > INT32_MAX) return GEMM_ERR_SHAPE;
   void* args[] = {&a};
@@ -529,11 +530,14 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       // Workgroups per compute unit: two for split-K on 128x128 tiles; one
       // for skinny tiles, where every K range adds S x M x N x 4 bytes of
       // partials against the 2KN bytes of B (M = 32..64 ran fastest at one);
-      // one half for the 256x256 tile, whose partials are 4x larger per
-      // workgroup (512 x 512 x 65536 ran fastest there).
-      const int64_t per_cu2 = p.variant == GEMM_VARIANT_SKINNY ? 2 : (ti.bm >= 256 ? 1 : 4);
-      s = cdiv(per_cu2 * (int64_t)cus, 2 * T);
+      // five eighths for the 256x256 tile, whose partials are 4x larger per
+      // workgroup (512 x 512 x 65536: 51 us at 160 workgroups against 54 at
+      // 128 and 57 at 256).  Split counts of 8 or more are rounded up to a
+      // multiple of 8 so the launch can keep each K range's tiles on one XCD.
+      const int64_t per_cu8 = p.variant == GEMM_VARIANT_SKINNY ? 8 : (ti.bm >= 256 ? 5 : 16);
+      s = cdiv(per_cu8 * (int64_t)cus, 8 * T);
       const int64_t max_by_k = cdiv(c.K, 2 * ti.bk);  // at least two K steps per split
+      if (s >= 8) s = cdiv(s, 8) * 8;
       if (s > max_by_k) s = max_by_k;
       if (s > 64) s = 64;
     }
@@ -700,6 +704,7 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   a.G = 0;
   a.sk_first = 0;
   a.sk_tiles = 0;
+  a.split_xcd = 0;
   const int sel = p.a_path * 3 + p.b_path;
   kfn_t final_fn = ti.final_fn[c.dt][sel], partial_fn = ti.partial_fn[c.dt][sel];
   if (p.pack) {   // the packed B at the front of the workspace, partials after it
@@ -713,6 +718,7 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   }
   if (p.variant == GEMM_VARIANT_STREAMK) return launch_streamk(c, p, a, final_fn, partial_fn, ws, stream);
   kfn_t fn = (p.split > 1) ? partial_fn : final_fn;
+  a.split_xcd = (p.split > 1 && p.split % 8 == 0) ? 1 : 0;
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(ti.nt), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
@@ -915,6 +921,7 @@ int launch_grouped(const GroupCall& c, int tile_id, kfn_t fn, int64_t grid, void
   a.G = c.G;
   a.sk_first = 0;
   a.sk_tiles = 0;
+  a.split_xcd = 0;
   void* args[] = {&a};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(ti.nt), args, 0, s) != hipSuccess)
     return GEMM_ERR_HIP;

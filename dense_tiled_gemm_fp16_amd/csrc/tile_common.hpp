@@ -238,7 +238,10 @@ struct OperandStage {
 // threadblock rasterisation for L2 reuse) and the Triton article (section
 // "neighbouring programs share cache"): consecutive ids walk down a panel of
 // `panel` tile-rows before moving to the next tile-column, so workgroups that
-// run together share A row-panels and B column-panels in cache.
+// run together share A row-panels and B column-panels in cache.  Panels run
+// along the longer side of the tile grid (the direction rule of the TileLang
+// tutorial, sections 1.5 and 6.1): with more tile-columns than tile-rows a
+// panel is `panel` tile-columns wide and consecutive ids walk across it.
 //
 // XCD remap (gfx950-specific): the dispatcher hands consecutive workgroup ids
 // to the 8 XCDs round-robin, and each XCD has its own L2.  Id w is first
@@ -255,14 +258,17 @@ __device__ __forceinline__ void raster_tile(int64_t w, int64_t GM, int64_t GN, i
   }
   const int64_t per = T / 8;
   if (w < per * 8) w = (w % 8) * per + w / 8;
-  const int64_t group_size = (int64_t)panel * GN;
+  const bool by_cols = GN > GM;             // panels of tile-columns
+  const int64_t R = by_cols ? GN : GM, X = by_cols ? GM : GN;
+  const int64_t group_size = (int64_t)panel * X;
   const int64_t group = w / group_size;
-  const int64_t first_m = group * panel;
-  int64_t rows = GM - first_m;
+  const int64_t first = group * panel;
+  int64_t rows = R - first;
   if (rows > panel) rows = panel;
   const int64_t in_group = w - group * group_size;
-  pm = first_m + in_group % rows;
-  pn = in_group / rows;
+  const int64_t r = first + in_group % rows, x = in_group / rows;
+  pm = by_cols ? x : r;
+  pn = by_cols ? r : x;
 }
 
 }  // namespace gemmf16

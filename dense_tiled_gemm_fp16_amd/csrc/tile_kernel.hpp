@@ -72,7 +72,27 @@ struct KArgs {
   // tile densely to W at slot w (BM x BN floats, row-major).
   int64_t sk_first;
   int64_t sk_tiles;
+  // Split-K launches (PARTIAL, sk_tiles == 0): ids that share w mod 8 (one
+  // XCD's share under the dispatcher's round-robin) hold all T tiles of the
+  // same K ranges; needs a split count that is a multiple of 8.
+  int32_t split_xcd;
 };
+
+// Workgroup id of a split-K launch -> (K range, tile index).  With
+// split_xcd the T tiles of one K range read the same A rows and B columns
+// at the same time on one XCD, so that XCD's L2 fetches them once instead of
+// each tile's XCD fetching them again.
+__device__ __forceinline__ void split_tile_of(int64_t w, int64_t T, int split_xcd, int64_t& split,
+                                              int64_t& tile) {
+  if (split_xcd) {
+    const int64_t r = w >> 3;
+    split = (w & 7) + 8 * (r / T);
+    tile = r - (r / T) * T;
+  } else {
+    split = w / T;
+    tile = w - split * T;
+  }
+}
 
 // Grouped product (TileLang tutorial ch. 14, section 4.3: one launch over
 // several GEMMs that share N and K, with per-group row counts; here group g
@@ -266,10 +286,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_tile_kernel(KArgs a) {
   const int64_t T = a.GM * a.GN;
   int64_t w = blockIdx.x;
   int64_t split = 0;
-  if constexpr (PARTIAL) {
-    split = w / T;
-    w -= split * T;
-  }
+  if constexpr (PARTIAL) split_tile_of(blockIdx.x, T, a.split_xcd, split, w);
   int64_t pm, pn;
   if constexpr (GROUPED) {
     if (!group_tile(a, w, pm, pn)) return;   // uniform per workgroup, before any barrier

@@ -59,8 +59,7 @@ def pair(M, N, K, seed, mode):
 
 @pytest.mark.parametrize("mode", ["uniform", "int"])
 def test_noalloc_two_calls_then_smaller(mode):
-    K_big = 16384 if mode == "uniform" else 128
-    pair(512, 512, K_big if mode == "uniform" else 4096, 33001, mode)   # split-K partials
+    pair(384, 384, 16384 if mode == "uniform" else 4096, 33001, mode)   # split-K partials
     pair(1, 2048, 7168 if mode == "uniform" else 1024, 33002, mode)     # decode partials
 
 
