@@ -54,9 +54,10 @@ def parse():
                     help="first run a 1 GiB device copy (a known-size reference for HBM counters)")
     ap.add_argument("--configs", action="store_true",
                     help="time every workload family (one JSON line each) instead of the headline")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
-                         "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="turn rocprofv3 --pmc counter_collection.csv files (pairs of FETCH_SIZE "
+                         "and WRITE_SIZE passes of --copy-calibration runs, e.g. --case main and "
+                         "--case decode_m1) into profiles/traffic.json")
     ap.add_argument("--summarize-profile", nargs="+", metavar="CSV",
                     help="markdown summary of one --case run under rocprofv3: a kernel_trace.csv "
                          "(durations) and counter_collection.csv files of --pmc passes")
@@ -96,7 +97,7 @@ COPY_KIB = float(1 << 20)      # the calibration copy reads and writes 1 GiB
 MAIN_KERNEL = "void gemmf16::gemm_dma_a128_kernel<gemmf16::DmaA128Cfg<4, 2>, false, false, false, 0, false>"
 
 
-def summarize_pmc(fetch_csv, write_csv):
+def summarize_pmc(*paths):
     """Per-launch HBM bytes of the library's kernels from FETCH_SIZE / WRITE_SIZE.
 
     Each counter is scaled by bytes-moved / counter-reading of the 1 GiB
@@ -106,19 +107,28 @@ def summarize_pmc(fetch_csv, write_csv):
     import csv
     import statistics
 
-    def load(path, counter):
-        per = {}
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter:
-                    per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        copy = sorted(per.get("__amd_rocclr_copyBuffer", []))[-3:]
-        if not copy:
-            raise SystemExit(f"{path}: no calibration copy found (run with --copy-calibration)")
-        return per, COPY_KIB / statistics.median(copy)
+    def load(counter):
+        per, scales = {}, []
+        for path in paths:
+            mine = {}
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        mine.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            if not mine:
+                continue
+            copy = sorted(mine.get("__amd_rocclr_copyBuffer", []))[-3:]
+            if not copy:
+                raise SystemExit(f"{path}: no calibration copy found (run with --copy-calibration)")
+            scales.append(COPY_KIB / statistics.median(copy))
+            for k, v in mine.items():
+                per.setdefault(k, []).extend(v)
+        if not scales:
+            raise SystemExit(f"no {counter} pass among the files")
+        return per, statistics.median(scales)
 
-    fetch, f_scale = load(fetch_csv, "FETCH_SIZE")
-    write, w_scale = load(write_csv, "WRITE_SIZE")
+    fetch, f_scale = load("FETCH_SIZE")
+    write, w_scale = load("WRITE_SIZE")
 
     def kernel(prefix):
         # The instantiation itself: the grouped and bfloat16 launches of the
@@ -163,7 +173,7 @@ def summarize_profile(paths):
     warm-up).  From counter passes: the per-dispatch mean of every counter
     over the same steady-state dispatches, and derived figures:
       clock       GRBM_GUI_ACTIVE / XCDs / median duration (GRBM_GUI_ACTIVE is
-                  counted once per XCD);
+                  counted once per XCD), for launches of 100 us or more;
       MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles per XCD x 1024 SIMDs);
       LDS bank conflicts per active LDS cycle;
       L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS);
@@ -215,7 +225,9 @@ def summarize_profile(paths):
         med = statistics.median(steady(dur[k])) if k in dur else None
         gui = m.get("GRBM_GUI_ACTIVE")
         cyc = gui / XCDS if gui else None
-        clock = f"{cyc / (med * 1e3):.3f}" if cyc and med else "-"
+        # (over launches shorter than 100 us the GUI-active window, which
+        # includes the dispatch's own set-up and cache actions, overstates it)
+        clock = f"{cyc / (med * 1e3):.3f}" if cyc and med and med >= 100.0 else "-"
         mfma = (f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * SIMDS):.1f}%"
                 if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in m else "-")
         lds = (f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.4f}"
