@@ -584,13 +584,17 @@ def main():
     def step_g():
         g.gemm_grouped(a, bg, offs, out=c, workspace=wsg, stream=stream)
 
-    dg, _ = timed_launches(step_g, stream, max(5, args.steps // 5), 2)
-    msg = sum(dg) / len(dg)
+    # In alternation with the dense product on the same rows, so both run
+    # under the same clocks.
+    dg, dd = timed_pair(step_g, step, stream, max(10, args.steps // 2), 4)
+    msg, msd = sum(dg) / len(dg), sum(dd) / len(dd)
     grouped = {"workload": f"{M} routed tokens over {G} experts (seeded skewed counts "
                            f"{int(sizes.min())}..{int(sizes.max())}), K={K}, N={N}, one B per expert",
                "ms": msg, "TFLOPS": flops / (msg * 1e-3) / 1e12,
                "frac": flops / (msg * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
-               "timing": "HIP events around each call (set-up and product launches)"}
+               "dense_TFLOPS_same_loop": flops / (msd * 1e-3) / 1e12,
+               "timing": "HIP events around each call (set-up and product launches), alternating "
+                         "with the dense product's call"}
     del bg
 
     # ---- bfloat16: the same product in the other 16-bit format

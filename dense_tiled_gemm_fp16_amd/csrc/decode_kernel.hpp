@@ -106,9 +106,19 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
       const bool live = u < units;
       const int64_t k0 = kb + (live ? u : units - 1) * kDecUnit + 8 * g;
       if constexpr (FULL) {
-        // (a dead unit's A operand is zero, so its B rows need no mask)
+        // (a dead unit's A operand is zero, so its B rows need no mask).
+        // B is read once: non-temporal loads keep it from displacing what
+        // the caches hold (M = 1: 10.6 -> 10.1 us per call); with 64 rows
+        // of A, whose re-reads by every strip come from L2, plain loads
+        // were faster (16.2 against 18.0 us).
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[i][j] = *reinterpret_cast<const u32x4*>(bcol + (k0 + j) * a.ldb_k);
+        for (int j = 0; j < 8; ++j) {
+          const u32x4* q = reinterpret_cast<const u32x4*>(bcol + (k0 + j) * a.ldb_k);
+          if constexpr (MT <= 32)
+            bv[i][j] = __builtin_nontemporal_load(q);
+          else
+            bv[i][j] = *q;
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
