@@ -52,6 +52,10 @@ struct DecArgs {
 
 constexpr int kDecCols = 128;  // columns per workgroup
 constexpr int kDecUnit = 32;   // k per unit (one MFMA k-step)
+// Waves per workgroup (the block is 64 * kDecWaves threads).  Four, with
+// one workgroup per compute unit, ran fastest: 8 waves took 10.3 us per M = 1
+// call against 10.0, and two workgroups per compute unit (K ranges of 224,
+// registers for only one of them at a time) 14.1.
 constexpr int kDecWaves = 4;
 // Units per wave whose loads are in flight together (fewer with 64 rows of
 // A, whose accumulators take a quarter of the registers).
@@ -141,7 +145,7 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
 }
 
 template <int MT, int DT>
-__global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   static_assert(MT % 16 == 0 && MT <= 64, "16, 32, 48 or 64 rows of A");
   constexpr int FA = MT / 16;
   __shared__ __attribute__((aligned(16))) float red[kDecWaves][16][16][8];   // [wave][m][c][f]
@@ -169,9 +173,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   else
     dec_units<MT, DT, false>(a, acc, w, g, c, kb, ke, bcol, nvalid);
 
-  // Sum the 4 waves in ascending order, 16 rows of A at a time; thread t
+  // Sum the waves in ascending order, 16 rows of A at a time; thread t < 256
   // then owns row t / 16 and the 8 columns 8 (t % 16) .. + 7 of the block.
-  const int tm = tid >> 4, tc = tid & 15;
+  const int tm = (tid >> 4) & 15, tc = tid & 15;
+  const bool summer = tid < 256;
   const int64_t col = nb * kDecCols + tc * 8;
   const int cvalid = (col + 8 <= a.N) ? 8 : (col < a.N ? (int)(a.N - col) : 0);
 #pragma unroll
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     }
     __syncthreads();
     const int64_t m = 16 * fa + tm;
-    if (m < a.M && cvalid > 0) {
+    if (summer && m < a.M && cvalid > 0) {
       float t[8];
 #pragma unroll
       for (int f = 0; f < 8; ++f) t[f] = 0.0f;

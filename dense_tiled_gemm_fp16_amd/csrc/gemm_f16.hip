@@ -625,7 +625,7 @@ int launch_decode(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   d.c_vec = p.c_vec;
   kfn_dec fn = p.dec_mt == 16 ? pick_dec<16>(c.dt) : p.dec_mt == 32 ? pick_dec<32>(c.dt) : pick_dec<64>(c.dt);
   void* args[] = {&d};
-  if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(256), args, 0, stream) != hipSuccess)
+  if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(64 * kDecWaves), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;
   if (p.split > 1) {
     // The reduction writes C with 8-byte vectors (its own alignment rule).
