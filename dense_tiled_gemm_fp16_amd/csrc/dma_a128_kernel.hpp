@@ -319,6 +319,66 @@ __device__ __forceinline__ void mma_frags_a128(const DmaFrags<CF>& f, f32x16 (&a
   }
 }
 
+// Exchange of lanes 32..63 of x with lanes 0..31 of y (v_permlane32_swap).
+__device__ __forceinline__ void swap_lane_halves(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack_out2(float lo, float hi) {
+  return (uint32_t)cvt_out<DT>(lo) | ((uint32_t)cvt_out<DT>(hi) << 16);
+}
+
+// Output of a whole tile (every row and column inside C, C 16-byte aligned,
+// ldc % 8 == 0), staged through LDS so that each store instruction writes
+// four whole 256-byte rows of the wave's 64 x 128 block.  The direct form
+// writes 8 bytes into each of 32 rows per instruction: the L1 and L2 take
+// one request per row piece, and on 256 CUs finishing their tiles together
+// that burst cost about 10 us per 256 x 256 tile (5% of the 131072 x 2048 x
+// 7168 product); staged, it costs about half of that.
+//
+// In a 32 x 32 block lane l holds, per group g of 4 registers, columns
+// 8 g + 4 (l / 32) .. + 3 of row l % 32.  Packed to binary16 pairs, one lane
+// swap across the two wave halves gives lane l < 32 columns 16 p .. 16 p + 7
+// of groups 2 p, 2 p + 1 and lane l + 32 columns 16 p + 8 .. 16 p + 15: one
+// 16-byte chunk each.  A wave writes its chunks into its own 16 KiB of LDS
+// (rows of 256 bytes, chunk c of row r at position c ^ (r % 16), so that
+// both the writes of 32 rows and the reads of 4 whole rows fall on distinct
+// banks) and reads them back row by row.  The caller has made the LDS free.
+template <class CF, int DT>
+__device__ __forceinline__ void store_whole_tile(const KArgs& a, const f32x16 (&acc)[CF::FN][CF::FM],
+                                                 char* smem, int64_t m0, int64_t n0, int wave, int wm,
+                                                 int wn, int lane) {
+  static_assert(CF::WTN == 128, "16 chunks of 16 bytes per wave row");
+  static_assert(CF::NW * CF::WTM * CF::WTN * 2 <= CF::LDS, "staging space");
+  const int lr = lane % 32, h = lane >> 5;
+  char* const stage = smem + wave * (CF::WTM * CF::WTN * 2);
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        uint32_t x0 = pack_out2<DT>(acc[i][j][8 * p], acc[i][j][8 * p + 1]);
+        uint32_t x1 = pack_out2<DT>(acc[i][j][8 * p + 2], acc[i][j][8 * p + 3]);
+        uint32_t y0 = pack_out2<DT>(acc[i][j][8 * p + 4], acc[i][j][8 * p + 5]);
+        uint32_t y1 = pack_out2<DT>(acc[i][j][8 * p + 6], acc[i][j][8 * p + 7]);
+        swap_lane_halves(x0, y0);
+        swap_lane_halves(x1, y1);
+        const int r = j * 32 + lr, c = 4 * i + 2 * p + h;
+        *reinterpret_cast<u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4)) = u32x4{x0, x1, y0, y1};
+      }
+  uint16_t* const cw = a.C + (m0 + wm * CF::WTM) * a.ldc + n0 + wn * CF::WTN;
+#pragma unroll
+  for (int it = 0; it < CF::WTM / 4; ++it) {
+    const int r = 4 * it + lane / 16, c = lane % 16;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
+    *reinterpret_cast<u32x4*>(cw + (int64_t)r * a.ldc + c * 8) = v;
+  }
+}
+
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
 // BPACK: B comes pre-packed (PackedBSource; read as a K-major B).
 template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false, int DT = DT_F16,
@@ -507,6 +567,15 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     }
   }
 
+  if constexpr (!PARTIAL) {
+    // (A condition uniform over the workgroup: every wave takes the barrier.)
+    if (m0 + CF::BM <= a.M && n0 + CF::BN <= a.N && ((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0) {
+      wait_lgkmcnt0();   // this wave's last LDS reads have returned,
+      wg_barrier();      // and every other wave's: the LDS is free
+      store_whole_tile<CF, DT>(a, acc, smem, m0, n0, wave, wm, wn, lane);
+      return;
+    }
+  }
   // Epilogue: the same C^T-block layout as the other kernels.
   const int lr = lane % 32;
 #pragma unroll
