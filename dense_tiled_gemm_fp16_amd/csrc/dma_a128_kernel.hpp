@@ -331,9 +331,10 @@ __device__ __forceinline__ uint32_t pack_out2(float lo, float hi) {
   return (uint32_t)cvt_out<DT>(lo) | ((uint32_t)cvt_out<DT>(hi) << 16);
 }
 
-// Output of a whole tile (every row and column inside C, C 16-byte aligned,
-// ldc % 8 == 0), staged through LDS so that each store instruction writes
-// four whole 256-byte rows of the wave's 64 x 128 block.  The direct form
+// Output of a tile staged through LDS (C 16-byte aligned, ldc % 8 == 0, and
+// the tile's columns inside C or N % 8 == 0), so that each store instruction
+// writes four whole 256-byte rows of the wave's 64 x 128 block; rows past M
+// and 8-column chunks past N are not stored.  The direct form
 // writes 8 bytes into each of 32 rows per instruction: the L1 and L2 take
 // one request per row piece, and on 256 CUs finishing their tiles together
 // that burst cost about 10 us per 256 x 256 tile (5% of the 131072 x 2048 x
@@ -348,9 +349,9 @@ __device__ __forceinline__ uint32_t pack_out2(float lo, float hi) {
 // both the writes of 32 rows and the reads of 4 whole rows fall on distinct
 // banks) and reads them back row by row.  The caller has made the LDS free.
 template <class CF, int DT>
-__device__ __forceinline__ void store_whole_tile(const KArgs& a, const f32x16 (&acc)[CF::FN][CF::FM],
-                                                 char* smem, int64_t m0, int64_t n0, int wave, int wm,
-                                                 int wn, int lane) {
+__device__ __forceinline__ void store_tile_staged(const KArgs& a, const f32x16 (&acc)[CF::FN][CF::FM],
+                                                  char* smem, int64_t m0, int64_t n0, int wave, int wm,
+                                                  int wn, int lane) {
   static_assert(CF::WTN == 128, "16 chunks of 16 bytes per wave row");
   static_assert(CF::NW * CF::WTM * CF::WTN * 2 <= CF::LDS, "staging space");
   const int lr = lane % 32, h = lane >> 5;
@@ -371,11 +372,15 @@ __device__ __forceinline__ void store_whole_tile(const KArgs& a, const f32x16 (&
         *reinterpret_cast<u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4)) = u32x4{x0, x1, y0, y1};
       }
   uint16_t* const cw = a.C + (m0 + wm * CF::WTM) * a.ldc + n0 + wn * CF::WTN;
+  // Rows and columns of this wave's block that lie inside C (clamped).
+  const int64_t mr = a.M - (m0 + wm * CF::WTM), nc = a.N - (n0 + wn * CF::WTN);
+  const int rows = mr < 0 ? 0 : (mr > CF::WTM ? CF::WTM : (int)mr);
+  const int cols = nc < 0 ? 0 : (nc > CF::WTN ? CF::WTN : (int)nc);
 #pragma unroll
   for (int it = 0; it < CF::WTM / 4; ++it) {
     const int r = 4 * it + lane / 16, c = lane % 16;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
-    *reinterpret_cast<u32x4*>(cw + (int64_t)r * a.ldc + c * 8) = v;
+    if (r < rows && 8 * c + 8 <= cols) *reinterpret_cast<u32x4*>(cw + (int64_t)r * a.ldc + c * 8) = v;
   }
 }
 
@@ -569,10 +574,10 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
 
   if constexpr (!PARTIAL) {
     // (A condition uniform over the workgroup: every wave takes the barrier.)
-    if (m0 + CF::BM <= a.M && n0 + CF::BN <= a.N && ((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0) {
+    if (((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0 && (n0 + CF::BN <= a.N || (a.N & 7) == 0)) {
       wait_lgkmcnt0();   // this wave's last LDS reads have returned,
       wg_barrier();      // and every other wave's: the LDS is free
-      store_whole_tile<CF, DT>(a, acc, smem, m0, n0, wave, wm, wn, lane);
+      store_tile_staged<CF, DT>(a, acc, smem, m0, n0, wave, wm, wn, lane);
       return;
     }
   }

@@ -385,6 +385,15 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     }
   }
 
+  if constexpr (!PARTIAL) {
+    // Staged through LDS, as in the 16-bit kernel (uniform condition).
+    if (((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0 && (n0 + CF::BN <= a.N || (a.N & 7) == 0)) {
+      wait_lgkmcnt0();
+      wg_barrier();
+      store_tile_staged<CF, DT_F16>(a, acc, smem, m0, n0, wave, wm, wn, lane);
+      return;
+    }
+  }
   // Epilogue: the C^T-block layout of the 16-bit kernels.
   const int lr = lane % 32;
 #pragma unroll
