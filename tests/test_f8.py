@@ -73,6 +73,20 @@ def test_f8_parity_ragged(fa, fb, mode):
             assert_close(got, ref, what)
 
 
+def test_f8_output_store_forms():
+    # As for the 16-bit tile: C staged through LDS in 16-byte chunks (16-byte
+    # aligned C, ldc % 8 == 0, tile columns inside N or N % 8 == 0), element
+    # by element otherwise, and both within one call when N % 8 != 0.
+    K = 256
+    for M, N, ldc, guard in ((300, 520, None, 64), (300, 520, 524, 64), (300, 520, None, 65),
+                             (513, 300, None, 64)):
+        A, Bt = inputs(M, N, K, 14050 + M + N, "int", "e4m3", "e4m3")
+        got = run(f8_rows(A, "e4m3"), f8_rows(Bt, "e4m3").t(), Out(M, N, ldc=ldc, guard=guard),
+                  variant="main")
+        assert_bits_equal(got, reference(A, Bt, "e4m3", "e4m3"),
+                          f"f8 {M}x{N} ldc={ldc or N} guard={guard}")
+
+
 @pytest.mark.parametrize("K", [1, 33, 64, 100, 128, 192, 255, 384])
 def test_f8_k_tails(K):
     # Whole 128-k super-steps, an odd 64-k step and ragged tails, byte by byte.

@@ -194,6 +194,36 @@ def test_main_tile_edge_blocks(b_layout):
                 check(run(a, b, Out(M, N), **kw), ref, "int", f"edge blocks {M}x{N} {kw}")
 
 
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_main_tile_output_store_forms(fmt):
+    # The 256x256 tile writes C through LDS in whole 16-byte chunks when C is
+    # 16-byte aligned with ldc % 8 == 0 and either the tile's columns lie
+    # inside N or N % 8 == 0 (rows past M and chunks past N left out), and
+    # element by element otherwise.  Each form, and their mix within one
+    # call (N % 8 != 0: staged inner tiles, direct last tile column), against
+    # the oracle, with NaN-filled outputs and canaries around them.
+    # (N % 8 != 0 needs a K-contiguous B on this tile.)
+    K = 64
+    cases = [(300, 520, None, 64, "row"),    # staged, row and 8-column chunk edges
+             (300, 520, 524, 64, "row"),     # ldc % 8 == 4: direct
+             (300, 520, None, 65, "row"),    # C 2 bytes past a 16-byte boundary: direct
+             (513, 300, None, 64, "col"),    # N % 8 == 4: staged inner, direct last column
+             (512, 512, 520, 64, "row")]     # whole tiles, padded ldc: staged
+    for M, N, ldc, guard, b_layout in cases:
+        A = synth.matrix(M, K, 8700 + M, 0, "int", fmt=fmt)
+        B = synth.matrix(K, N, 8700 + N, 1, "int", fmt=fmt)
+        ref = oracle.gemm(A, (K, 1), B, (N, 1), M, N, K, nthreads=ORACLE_THREADS,
+                          dtype="bf16" if fmt == "bf16" else "f16")
+        a, b = to_dev(A), place(B, b_layout)
+        out = Out(M, N, ldc=ldc, guard=guard)
+        if fmt == "bf16":
+            a, b = a.view(torch.bfloat16), b.view(torch.bfloat16)
+            out.view = out.view.view(torch.bfloat16)
+        assert g.plan(a, b, out=out.view, variant="main", tile=14)["tile_id"] == 14
+        got = run(a, b, out, variant="main", tile=14)
+        assert_bits_equal(got, ref, f"{fmt} {M}x{N} ldc={ldc or N} guard={guard} B {b_layout}")
+
+
 # ------------------------------------------------------------------ skinny / decode
 
 @pytest.mark.parametrize("M", [1, 7, 16, 33, 64])
