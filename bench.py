@@ -61,6 +61,11 @@ def parse():
     ap.add_argument("--summarize-profile", nargs="+", metavar="CSV",
                     help="markdown summary of one --case run under rocprofv3: a kernel_trace.csv "
                          "(durations) and counter_collection.csv files of --pmc passes")
+    ap.add_argument("--operands", choices=["uniform", "int", "a_half", "b_half", "b_zero"],
+                    default="uniform",
+                    help="with --case: operand values (U(-1,1); integers in [-4,4]; or every "
+                         "element of A or of B set to 0.5, or B to 0), to show how the clock "
+                         "depends on the data the matrix cores multiply")
     ap.add_argument("--case", choices=sorted(CASES),
                     help="run only this workload's calls (--steps of them after --warmup), for "
                          "profilers; prints one JSON line with its per-call time")
@@ -421,7 +426,7 @@ def copy_calibration():
     del src, dst
 
 
-def run_case(name, steps, warmup):
+def run_case(name, steps, warmup, operands="uniform"):
     """--steps calls of one workload's automatic plan after --warmup, on the
     current stream; one JSON line with the mean time per call (HIP events
     around the whole loop)."""
@@ -437,9 +442,16 @@ def run_case(name, steps, warmup):
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
 
-    a0 = to_dev(synth.matrix(m, k, seed, synth.TENSOR_A))
-    bt = synth.matrix(k, n, seed, synth.TENSOR_B, order="col" if bl == "col" else "row")
+    mode = "int" if operands == "int" else "uniform"
+    a0 = to_dev(synth.matrix(m, k, seed, synth.TENSOR_A, mode))
+    bt = synth.matrix(k, n, seed, synth.TENSOR_B, mode, order="col" if bl == "col" else "row")
     b0 = to_dev(bt).t() if bl == "col" else to_dev(bt)
+    if operands == "a_half":
+        a0.fill_(0.5)
+    elif operands == "b_half":
+        b0.fill_(0.5)
+    elif operands == "b_zero":
+        b0.zero_()
     byts = 2.0 * (m * k + k * n + m * n)
     copies = int(min(64, max(1, -(-(1 << 30) // int(byts)))))
     As = [a0] + [a0.clone() for _ in range(copies - 1)]
@@ -459,7 +471,8 @@ def run_case(name, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    print(json.dumps({"case": name, "M": m, "N": n, "K": k, "b_layout": bl, "copies": copies,
+    print(json.dumps({"case": name, "operands": operands, "M": m, "N": n, "K": k, "b_layout": bl,
+                      "copies": copies,
                       "steps": steps, "warmup": warmup, "us_per_call": us,
                       "TFLOPS": 2.0 * m * n * k / us / 1e6, "GBps": byts / us / 1e3,
                       "plan": {q: p[q] for q in ("variant", "tile_id", "tile_m", "tile_n",
@@ -478,7 +491,7 @@ def main():
     if args.case:
         if args.copy_calibration:
             copy_calibration()
-        run_case(args.case, args.steps, args.warmup)
+        run_case(args.case, args.steps, args.warmup, args.operands)
         return
     if args.configs:
         configs_sweep()
