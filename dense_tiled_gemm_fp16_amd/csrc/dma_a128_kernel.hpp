@@ -331,14 +331,38 @@ __device__ __forceinline__ uint32_t pack_out2(float lo, float hi) {
   return (uint32_t)cvt_out<DT>(lo) | ((uint32_t)cvt_out<DT>(hi) << 16);
 }
 
-// Output of a tile staged through LDS (C 16-byte aligned, ldc % 8 == 0, and
-// the tile's columns inside C or N % 8 == 0), so that each store instruction
-// writes four whole 256-byte rows of the wave's 64 x 128 block; rows past M
-// and 8-column chunks past N are not stored.  The direct form
-// writes 8 bytes into each of 32 rows per instruction: the L1 and L2 take
-// one request per row piece, and on 256 CUs finishing their tiles together
-// that burst cost about 10 us per 256 x 256 tile (5% of the 131072 x 2048 x
-// 7168 product); staged, it costs about half of that.
+// Eight consecutive outputs v (binary16 pairs, lowest column first) to dst,
+// with the widest stores dst's alignment allows: one 16-byte store, two of
+// 8, four of 4, or, 2 bytes past a 4-byte boundary, 2 + 3 x 4 + 2 bytes.
+__device__ __forceinline__ void store8_any(uint16_t* dst, u32x4 v) {
+  const uintptr_t ad = (uintptr_t)dst;
+  if ((ad & 15u) == 0) {
+    *reinterpret_cast<u32x4*>(dst) = v;
+  } else if ((ad & 7u) == 0) {
+    reinterpret_cast<u32x2*>(dst)[0] = u32x2{v[0], v[1]};
+    reinterpret_cast<u32x2*>(dst)[1] = u32x2{v[2], v[3]};
+  } else if ((ad & 3u) == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) reinterpret_cast<uint32_t*>(dst)[q] = v[q];
+  } else {
+    dst[0] = (uint16_t)v[0];
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + 1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) d[q] = __builtin_amdgcn_alignbit(v[q + 1], v[q], 16);
+    dst[7] = (uint16_t)(v[3] >> 16);
+  }
+}
+
+// Output of a tile staged through LDS, so that each store instruction
+// writes four whole rows of the wave's 64 x 128 block (256 bytes each) rather
+// than 8 bytes into each of 32 rows.  Stored straight from the accumulators,
+// the L1 and L2 take one request per row piece, and on 256 CUs finishing
+// their tiles together that burst cost about 10 us per 256 x 256 tile (5%
+// of the 131072 x 2048 x 7168 product); staged, it costs about half of that.
+// Rows past M are not stored; nor are the columns past N of an 8-column chunk
+// that crosses N.  With C 16-byte aligned and ldc % 8 == 0 every chunk is one
+// 16-byte store; otherwise each chunk takes the widest stores its address
+// allows (the 16 lanes of one row share that choice).
 //
 // In a 32 x 32 block lane l holds, per group g of 4 registers, columns
 // 8 g + 4 (l / 32) .. + 3 of row l % 32.  Packed to binary16 pairs, one lane
@@ -376,11 +400,27 @@ __device__ __forceinline__ void store_tile_staged(const KArgs& a, const f32x16 (
   const int64_t mr = a.M - (m0 + wm * CF::WTM), nc = a.N - (n0 + wn * CF::WTN);
   const int rows = mr < 0 ? 0 : (mr > CF::WTM ? CF::WTM : (int)mr);
   const int cols = nc < 0 ? 0 : (nc > CF::WTN ? CF::WTN : (int)nc);
+  if (((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0) {
 #pragma unroll
-  for (int it = 0; it < CF::WTM / 4; ++it) {
-    const int r = 4 * it + lane / 16, c = lane % 16;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
-    if (r < rows && 8 * c + 8 <= cols) *reinterpret_cast<u32x4*>(cw + (int64_t)r * a.ldc + c * 8) = v;
+    for (int it = 0; it < CF::WTM / 4; ++it) {
+      const int r = 4 * it + lane / 16, c = lane % 16;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
+      if (r < rows && 8 * c + 8 <= cols) *reinterpret_cast<u32x4*>(cw + (int64_t)r * a.ldc + c * 8) = v;
+    }
+  } else {
+    for (int it = 0; it < CF::WTM / 4; ++it) {
+      const int r = 4 * it + lane / 16, c = lane % 16;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
+      const int nv = cols - 8 * c;
+      uint16_t* const dst = cw + (int64_t)r * a.ldc + c * 8;
+      if (r < rows && nv >= 8) {
+        store8_any(dst, v);
+      } else if (r < rows && nv > 0) {
+#pragma unroll
+        for (int e = 0; e < 7; ++e)
+          if (e < nv) dst[e] = (uint16_t)(v[e / 2] >> (16 * (e % 2)));
+      }
+    }
   }
 }
 
@@ -573,36 +613,30 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   }
 
   if constexpr (!PARTIAL) {
-    // (A condition uniform over the workgroup: every wave takes the barrier.)
-    if (((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0 && (n0 + CF::BN <= a.N || (a.N & 7) == 0)) {
-      wait_lgkmcnt0();   // this wave's last LDS reads have returned,
-      wg_barrier();      // and every other wave's: the LDS is free
-      store_tile_staged<CF, DT>(a, acc, smem, m0, n0, wave, wm, wn, lane);
-      return;
-    }
-  }
-  // Epilogue: the same C^T-block layout as the other kernels.
-  const int lr = lane % 32;
+    wait_lgkmcnt0();   // this wave's last LDS reads have returned,
+    wg_barrier();      // and every other wave's: the LDS is free
+    store_tile_staged<CF, DT>(a, acc, smem, m0, n0, wave, wm, wn, lane);
+  } else {
+    // fp32 partials in the C^T-block layout of the other kernels.
+    const int lr = lane % 32;
 #pragma unroll
-  for (int i = 0; i < CF::FN; ++i)
+    for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::FM; ++j) {
-      const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
+      for (int j = 0; j < CF::FM; ++j) {
+        const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if constexpr (PARTIAL) {
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if (a.sk_tiles > 0)
             store4_tile<CF::BM, CF::BN>(a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN), m - m0, n - n0,
                                         v0, v1, v2, v3);
           else
             store4_f32(a, split, m, n, v0, v1, v2, v3);
-        } else
-          store4_out<DT>(a, m, n, v0, v1, v2, v3);
+        }
       }
-    }
+  }
 }
 
 }  // namespace gemmf16

@@ -386,37 +386,31 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
   }
 
   if constexpr (!PARTIAL) {
-    // Staged through LDS, as in the 16-bit kernel (uniform condition).
-    if (((uintptr_t)a.C & 15u) == 0 && (a.ldc & 7) == 0 && (n0 + CF::BN <= a.N || (a.N & 7) == 0)) {
-      wait_lgkmcnt0();
-      wg_barrier();
-      store_tile_staged<CF, DT_F16>(a, acc, smem, m0, n0, wave, wm, wn, lane);
-      return;
-    }
-  }
-  // Epilogue: the C^T-block layout of the 16-bit kernels.
-  const int lr = lane % 32;
+    // Staged through LDS, as in the 16-bit kernel.
+    wait_lgkmcnt0();
+    wg_barrier();
+    store_tile_staged<CF, DT_F16>(a, acc, smem, m0, n0, wave, wm, wn, lane);
+  } else {
+    // fp32 partials in the C^T-block layout of the other kernels.
+    const int lr = lane % 32;
 #pragma unroll
-  for (int i = 0; i < CF::FN; ++i)
+    for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::FM; ++j) {
-      const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
+      for (int j = 0; j < CF::FM; ++j) {
+        const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if constexpr (PARTIAL) {
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if (a.sk_tiles > 0)
             store4_tile<CF::BM, CF::BN>(a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN), m - m0, n - n0,
                                         v0, v1, v2, v3);
           else
             store4_f32(a, split, m, n, v0, v1, v2, v3);
-        } else {
-          store4_out<DT_F16>(a, m, n, v0, v1, v2, v3);
         }
       }
-    }
+  }
 }
 
 }  // namespace gemmf16
