@@ -290,9 +290,9 @@ __device__ __forceinline__ void read_frags_a128(DmaFrags<CF>& f, const char* ta,
 // reads one MFMA later the 131072 x 2048 x 7168 product ran 0.3-2.7% faster
 // on three machines and 8192^3 moved -0.6 to +1.6% (same bits).  `nxt` may
 // be the registers of a fragment set consumed earlier in program order.
-// EDGE: a wave of an edge tile skips the MFMAs of 32 x 32 blocks that lie
-// wholly past N (i >= fnv) or past M (j >= fmv); their outputs are never
-// stored.  fnv and fmv are uniform over the wave.
+// EDGE: a wave of an edge tile skips the MFMAs of the 32 x 32 blocks i >= fnv
+// or j >= fmv, whose outputs are never stored (the kernel skips only blocks
+// wholly past M: fnv = FN, see there).  fnv and fmv are uniform over the wave.
 template <class CF, int H, bool BKMAJOR, int DT, bool EDGE>
 __device__ __forceinline__ void mma_and_read(const DmaFrags<CF>& cur, DmaFrags<CF>& nxt,
                                              f32x16 (&acc)[CF::FN][CF::FM], const char* ta,
@@ -457,12 +457,17 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
   const int64_t kb = split * a.k_split;
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
-  // 32-wide blocks of this wave's sub-tile that hold any output (all of
-  // them except in the last tile row or column).
-  const int64_t nrem = a.N - (n0 + wn * CF::WTN), mrem = a.M - (m0 + wm * CF::WTM);
-  const int fnv = nrem <= 0 ? 0 : (nrem >= CF::WTN ? CF::FN : (int)((nrem + 31) / 32));
+  // 32-row blocks of this wave's sub-tile that hold any output (all of them
+  // except in the last tile row).  Blocks past N are computed anyway: a tile
+  // of the last column that skipped them would finish early, the tiles of its
+  // row (which share their A panel in L2 while they run in step) would drift
+  // apart, and A would be fetched again.  Computing them was 6.5% faster on
+  // 262181 x 1061 x 8192 (37 live columns of 256 in the last tile column),
+  // 8.4% on 131072 x 1061 x 7168 and 2.2% on 131072 x 2080 x 7168.
+  const int64_t mrem = a.M - (m0 + wm * CF::WTM);
+  const int fnv = CF::FN;
   const int fmv = mrem <= 0 ? 0 : (mrem >= CF::WTM ? CF::FM : (int)((mrem + 31) / 32));
-  const bool edge = fnv < CF::FN || fmv < CF::FM;
+  const bool edge = fmv < CF::FM;
 
   ASourceS<CF::DMA_A> sa;
   std::conditional_t<BPACK, PackedBSource<CF::DMA_B>, BSourceS<CF::DMA_B, BKMAJOR>> sb;

@@ -220,10 +220,12 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
   const int64_t kb = split * a.k_split;   // bytes; a multiple of 128
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
-  const int64_t nrem = a.N - (n0 + wn * CF::WTN), mrem = a.M - (m0 + wm * CF::WTM);
-  const int fnv = nrem <= 0 ? 0 : (nrem >= CF::WTN ? CF::FN : (int)((nrem + 31) / 32));
+  // Only blocks wholly past M are skipped; blocks past N are computed so the
+  // tiles of one row stay in step (as in the 16-bit kernel).
+  const int64_t mrem = a.M - (m0 + wm * CF::WTM);
+  const int fnv = CF::FN;
   const int fmv = mrem <= 0 ? 0 : (mrem >= CF::WTM ? CF::FM : (int)((mrem + 31) / 32));
-  const bool edge = fnv < CF::FN || fmv < CF::FM;
+  const bool edge = fmv < CF::FM;
 
   // Byte-pair views for the DMA: strides and K offsets halve.
   ASourceS<CF::DMA_A> sa;
