@@ -30,6 +30,11 @@
 // and/or a K tail) is filled by masked register loads with zero fill after
 // the pipelined loop.
 //
+// C leaves through the LDS, free after the last step: rounded to the output
+// format, staged per wave and read back row by row, so that each store
+// instruction writes whole 256-byte rows (store_tile_staged).  Split
+// launches write their fp32 partials straight from the accumulators.
+//
 // Issue economy: a wave's memory phase is short of issue slots, not of
 // bandwidth, so the loop keeps its bookkeeping cheap.  LDS slot indices
 // rotate in 32-bit scalar registers, and the DMA uses the SGPR-base form of
