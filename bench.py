@@ -72,18 +72,21 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dense_tiled_gemm_fp16_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
+def library_hash():
+    """Hash of the built libgemmf16.so, the code the counters describe (the
+    build is reproducible: the same sources give the same bytes, whatever
+    their comments), or None when it is not built."""
+    path = os.path.join(ROOT, "dense_tiled_gemm_fp16_amd", "libgemmf16.so")
+    try:
+        with open(path, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
 
 
 def measured_traffic(kind):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources (else None)."""
+    taken on the library as built now (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -91,7 +94,7 @@ def measured_traffic(kind):
     except (OSError, ValueError):
         return None
     e = t.get(kind)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("library_hash") is None or e.get("library_hash") != library_hash():
         return None
     return e.get("bytes_per_launch")
 
@@ -148,7 +151,7 @@ def summarize_pmc(*paths):
 
     out = {"calibration": {"copy_bytes": COPY_KIB * 1024, "fetch_scale": f_scale,
                            "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer"},
-           "source_hash": kernel_source_hash()}
+           "library_hash": library_hash()}
     alg = {"main_131072x2048x7168": (MAIN_KERNEL, 2.0 * (M * K + K * N), 2.0 * M * N),
            "skinny_m1_partials": ("void gemmf16::decode_kernel<16, 0>", 2.0 * (K + K * N), None),
            "skinny_m1_reduce": ("void gemmf16::splitk_reduce_elem<0>", None, 2.0 * N)}
@@ -159,7 +162,7 @@ def summarize_pmc(*paths):
         name, fb, wb = k
         out[key] = {"kernel": name, "fetch_bytes": fb, "write_bytes": wb,
                     "bytes_per_launch": fb + wb, "algorithmic_read_bytes": alg_read,
-                    "algorithmic_write_bytes": alg_write, "source_hash": out["source_hash"]}
+                    "algorithmic_write_bytes": alg_write, "library_hash": out["library_hash"]}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
