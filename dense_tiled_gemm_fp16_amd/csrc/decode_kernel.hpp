@@ -22,6 +22,12 @@
 // (the matrix cores are idle here anyway).  Lane (g, c) ends with outputs
 // (16 fa + 4g + r, 8c + f), r < 4, f < 8: 8 consecutive columns per row.
 //
+// B stored as [N, K] rows (K-contiguous, BK): lane (g, c) loads, for each
+// group f of 16 columns, the 8 k of octet g of column 16 f + c, one 16-byte
+// vector that is already the B operand of the MFMA (no transpose), and ends
+// with outputs (16 fa + 4g + r, 16 f + c).  One load instruction of the wave
+// covers 16 columns x 64 bytes.
+//
 // The 4 waves' sums are added through LDS in ascending wave order; with one
 // K range the workgroup writes C (round to nearest even), with several it
 // writes fp32 partials P[s][m][n] that splitk_reduce sums in ascending s in
@@ -39,7 +45,8 @@ struct DecArgs {
   const uint16_t* A;
   int64_t lda_m, lda_k;
   const uint16_t* B;
-  int64_t ldb_k;       // B is N-contiguous (ldb_n == 1), 16-byte aligned, ldb_k % 8 == 0
+  int64_t ldb_k;       // N-contiguous B (ldb_n == 1): 16-byte aligned, ldb_k % 8 == 0
+  int64_t ldb_n;       // K-contiguous B (ldb_k == 1, BK kernels): 16-byte aligned, ldb_n % 8 == 0
   uint16_t* C;
   int64_t ldc;
   float* P;            // partials [S][M][N] (S > 1 only)
@@ -76,9 +83,10 @@ __device__ __forceinline__ u32x4 dec_load_a(const DecArgs& a, int64_t m, int64_t
 // inside N and A rows are 16-byte vectors, so the loads carry no masks and
 // no branches (rows of A past M are read from row 0 and zeroed); otherwise
 // each load is masked on its own.
-template <int MT, int DT, bool FULL>
+template <int MT, int DT, bool FULL, bool BK>
 __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16][8], int w, int g, int c,
-                                          int64_t kb, int64_t ke, const uint16_t* bcol, int nvalid) {
+                                          int64_t kb, int64_t ke, const uint16_t* bcol, int nvalid,
+                                          int64_t n0) {
   constexpr int FA = MT / 16;
   constexpr int UPW = dec_upw<MT>();
   const int64_t units = (ke - kb + kDecUnit - 1) / kDecUnit;
@@ -109,7 +117,25 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
       const int64_t u = u0 + (int64_t)kDecWaves * i;
       const bool live = u < units;
       const int64_t k0 = kb + (live ? u : units - 1) * kDecUnit + 8 * g;
-      if constexpr (FULL) {
+      if constexpr (BK) {
+        // Column 16 f + c of the strip, k0 .. k0 + 7; columns past N read
+        // zeros (FULL: the whole strip is inside N).
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          const int64_t n = n0 + 16 * f + c;
+          const uint16_t* q = a.B + n * a.ldb_n + k0;
+          if constexpr (FULL) {
+            if constexpr (MT <= 32)
+              bv[i][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+            else
+              bv[i][f] = *reinterpret_cast<const u32x4*>(q);
+          } else {
+            const int64_t d = ke - k0;
+            const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
+            bv[i][f] = (live && n < a.N && nk > 0) ? load_partial8(q, 1, nk) : zero4();
+          }
+        }
+      } else if constexpr (FULL) {
         // (a dead unit's A operand is zero, so its B rows need no mask).
         // B is read once: non-temporal loads keep it from displacing what
         // the caches hold (M = 1: 10.6 -> 10.1 us per call); with 64 rows
@@ -133,7 +159,12 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       u32x4 bt[8];
-      transpose8x8(bv[i], bt);
+      if constexpr (BK) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f) bt[f] = bv[i][f];
+      } else {
+        transpose8x8(bv[i], bt);
+      }
 #pragma unroll
       for (int f = 0; f < 8; ++f)
 #pragma unroll
@@ -144,7 +175,7 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
   }
 }
 
-template <int MT, int DT>
+template <int MT, int DT, bool BK = false>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   static_assert(MT % 16 == 0 && MT <= 64, "16, 32, 48 or 64 rows of A");
   constexpr int FA = MT / 16;
@@ -156,9 +187,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   const int64_t nb = blockIdx.x % a.GN, s = blockIdx.x / a.GN;
   const int64_t kb = s * a.kr;
   const int64_t ke = (kb + a.kr < a.K) ? kb + a.kr : a.K;
-  const int64_t n0 = nb * kDecCols + c * 8;
+  const int64_t n0 = nb * kDecCols + c * 8;   // N-contiguous B: this lane's 8 columns
   const int nvalid = (n0 + 8 <= a.N) ? 8 : (n0 < a.N ? (int)(a.N - n0) : 0);
   const uint16_t* bcol = a.B + (nvalid > 0 ? n0 : 0);
+  const int64_t sn0 = nb * kDecCols;            // the strip's first column
 
   f32x4 acc[FA][8];
 #pragma unroll
@@ -169,9 +201,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   // Uniform per workgroup: whole strip inside N, whole units, vector A.
   const bool full = (nb + 1) * kDecCols <= a.N && (ke - kb) % kDecUnit == 0 && a.a_vec;
   if (full)
-    dec_units<MT, DT, true>(a, acc, w, g, c, kb, ke, bcol, nvalid);
+    dec_units<MT, DT, true, BK>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
   else
-    dec_units<MT, DT, false>(a, acc, w, g, c, kb, ke, bcol, nvalid);
+    dec_units<MT, DT, false, BK>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
 
   // Sum the waves in ascending order, 16 rows of A at a time; thread t < 256
   // then owns row t / 16 and the 8 columns 8 (t % 16) .. + 7 of the block.
@@ -183,11 +215,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   for (int fa = 0; fa < FA; ++fa) {
     if (16 * fa >= a.M) break;   // uniform across the workgroup
     if (fa > 0) __syncthreads();  // red is free
+    // red[w][m] holds the strip's 128 columns in order (the view [c][f] is
+    // column 8 c + f); K-contiguous B leaves lane c with columns 16 f + c.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float* dst = &red[w][4 * g + r][c][0];
-      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[fa][0][r], acc[fa][1][r], acc[fa][2][r], acc[fa][3][r]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[fa][4][r], acc[fa][5][r], acc[fa][6][r], acc[fa][7][r]};
+      float* dst = &red[w][4 * g + r][0][0];
+      if constexpr (BK) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f) dst[16 * f + c] = acc[fa][f][r];
+      } else {
+        *reinterpret_cast<f32x4*>(dst + 8 * c) = f32x4{acc[fa][0][r], acc[fa][1][r], acc[fa][2][r], acc[fa][3][r]};
+        *reinterpret_cast<f32x4*>(dst + 8 * c + 4) =
+            f32x4{acc[fa][4][r], acc[fa][5][r], acc[fa][6][r], acc[fa][7][r]};
+      }
     }
     __syncthreads();
     const int64_t m = 16 * fa + tm;

@@ -437,19 +437,29 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     default:
       return GEMM_ERR_OPTS;
   }
-  // M <= 64 with N-contiguous B: the decode kernel (128-column strips, one
-  // workgroup per strip and K range, about one workgroup per compute unit,
-  // K ranges of at least 128 k).
+  // M <= 64 with N-contiguous B, or M <= 16 with K-contiguous B (16-byte
+  // vectors): the decode kernel (128-column strips, one workgroup per strip
+  // and K range, about one workgroup per compute unit, K ranges of at least
+  // 128 k).  With K-contiguous B and 17..64 rows the skinny tiles were faster
+  // (M = 32, 48, 64: 15.3, 17.4, 19.3 us per call against 16.6, 19.4, 20.9);
+  // up to 16 rows the decode kernel (M = 1 and 16: 12.3 and 12.9 against
+  // 13.4 and 13.5).
   p.dec_mt = 0;
   p.red_elem = 0;
-  if (p.variant == GEMM_VARIANT_SKINNY && !want_tile && c.M <= 64 && p.b_path == PATH_RVEC) {
+  if (p.variant == GEMM_VARIANT_SKINNY && !want_tile && c.M <= 64 &&
+      (p.b_path == PATH_RVEC || (p.b_path == PATH_KVEC && c.M <= 16))) {
     p.dec_mt = c.M <= 16 ? 16 : (c.M <= 32 ? 32 : 64);
     p.GM = 1;
     p.GN = cdiv(c.N, kDecCols);
     int64_t s = want_split;
     if (s == 0) {
+      // As many K ranges as keep the workgroups within one per compute unit:
+      // a second round for a few of them costs a whole extra pass (N = 7168,
+      // K = 2048: 56 strips x 5 ranges = 280 workgroups took 14.2 us per
+      // M = 1 call, x 4 ranges 10.6 us).
       if ((rc = need_cus())) return rc;
-      s = cdiv((int64_t)cus, p.GN);
+      s = cus / p.GN;
+      if (s < 1) s = 1;
       if (s > cdiv(c.K, 4 * kDecUnit)) s = cdiv(c.K, 4 * kDecUnit);
     }
     p.k_split = cdiv(cdiv(c.K, s), kDecUnit) * kDecUnit;
@@ -604,6 +614,9 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
 
 template <int MT>
 kfn_dec pick_dec(int dt) { return dt == DT_F16 ? decode_kernel<MT, DT_F16> : decode_kernel<MT, DT_BF16>; }
+kfn_dec pick_dec_bk(int dt) {   // B as [N, K] rows, up to 16 rows of A
+  return dt == DT_F16 ? decode_kernel<16, DT_F16, true> : decode_kernel<16, DT_BF16, true>;
+}
 
 int launch_decode(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   DecArgs d;
@@ -612,6 +625,7 @@ int launch_decode(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   d.lda_k = c.lda_k;
   d.B = (const uint16_t*)c.B;
   d.ldb_k = c.ldb_k;
+  d.ldb_n = c.ldb_n;
   d.C = (uint16_t*)c.C;
   d.ldc = c.ldc;
   d.P = (float*)ws;
@@ -623,7 +637,10 @@ int launch_decode(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   d.S = p.split;
   d.a_vec = (c.lda_k == 1 && c.lda_m % 8 == 0 && ((uintptr_t)c.A & 15u) == 0) ? 1 : 0;
   d.c_vec = p.c_vec;
-  kfn_dec fn = p.dec_mt == 16 ? pick_dec<16>(c.dt) : p.dec_mt == 32 ? pick_dec<32>(c.dt) : pick_dec<64>(c.dt);
+  kfn_dec fn = p.b_path == PATH_KVEC ? pick_dec_bk(c.dt)
+               : p.dec_mt == 16       ? pick_dec<16>(c.dt)
+               : p.dec_mt == 32       ? pick_dec<32>(c.dt)
+                                      : pick_dec<64>(c.dt);
   void* args[] = {&d};
   if (hipLaunchKernel((const void*)fn, dim3((unsigned)p.grid), dim3(64 * kDecWaves), args, 0, stream) != hipSuccess)
     return GEMM_ERR_HIP;

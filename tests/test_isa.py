@@ -114,9 +114,10 @@ def test_register_tiles_keep_their_mfma(kernels):
 
 def test_decode_kernels_keep_their_mfma(kernels):
     found = _of(kernels, "decode_kernel")
-    assert len(found) == 6                  # 16, 32 and 64 rows of A, fp16 and bfloat16
+    assert len(found) == 8                  # 16, 32, 64 rows of A with N-contiguous B, 16 with
+                                            # K-contiguous B; fp16 and bfloat16
     for name, ops in found.items():
-        want = {"0": "v_mfma_f32_16x16x32_f16", "1": "v_mfma_f32_16x16x32_bf16"}[_targs(name)[-1]]
+        want = {"0": "v_mfma_f32_16x16x32_f16", "1": "v_mfma_f32_16x16x32_bf16"}[_targs(name)[1]]
         assert ops[want] >= 8, (name, want)
 
 
@@ -137,7 +138,9 @@ def test_output_rounding_instructions(kernels):
             args = _targs(name)
             if w == "gemm_dma_a128_kernel" and args[4] == "1":
                 continue                    # bfloat16 output
-            if w in ("decode_kernel", "splitk_reduce_quad", "splitk_reduce_elem") and args[-1] == "1":
+            if w == "decode_kernel" and args[1] == "1":
+                continue
+            if w in ("splitk_reduce_quad", "splitk_reduce_elem") and args[-1] == "1":
                 continue
             if w == "sk_fixup" and args[0] == "1":
                 continue

@@ -434,41 +434,69 @@ def test_caller_workspace_is_used_and_needs_no_reset():
 
 # ------------------------------------------------------------------ decode kernel (M <= 64, N-contiguous B)
 
-def _decode_case(M, N, K, mode, ldb_pad=0, split=0, seed=7000):
+def _decode_case(M, N, K, mode, ldb_pad=0, split=0, seed=7000, b_layout="row"):
+    # b_layout "row": B [K, N] N-contiguous (rows padded by ldb_pad);
+    # "col": B as [N, K] rows, each padded to a multiple of 8 elements with at
+    # least 8 NaN past K, so a read beyond K turns outputs into NaN.
     A = synth.matrix(M, K, seed + M, 0, mode)
     B = synth.matrix(K, N, seed + N, 1, mode)
     ref = reference(A, B)
     a = place(A, "row", (1, 8))
-    b = place(B, "row", (0, ldb_pad)) if ldb_pad else to_dev(B)
+    if b_layout == "col":
+        b = place(B, "col", (1, (-K) % 8 + 8))
+    else:
+        b = place(B, "row", (0, ldb_pad)) if ldb_pad else to_dev(B)
     p = g.plan(a, b, variant="skinny", split_k=split)
-    assert p["b_path"] == "rvec" and p["tile_n"] == 128 and p["tile_m"] == (
-        16 if M <= 16 else 32 if M <= 32 else 64), p
+    assert p["b_path"] == ("kvec" if b_layout == "col" else "rvec") and p["tile_n"] == 128 and \
+        p["tile_m"] == (16 if M <= 16 else 32 if M <= 32 else 64), p
     need = p["workspace_bytes"]
     ws = torch.full((max(need, 4096) // 4 + 64,), float("nan"), dtype=torch.float32, device=DEV)
     outs = []
     for _ in range(2):
         outs.append(run(a, b, Out(M, N), workspace=ws, variant="skinny", split_k=split))
         ws.fill_(-7.0)                       # the workspace needs no initialisation
-    assert_bits_equal(outs[1], outs[0], f"decode rerun M={M} N={N} K={K}")
-    check(outs[0], ref, mode, f"decode M={M} N={N} K={K} pad={ldb_pad} split={split}")
+    assert_bits_equal(outs[1], outs[0], f"decode rerun M={M} N={N} K={K} B {b_layout}")
+    check(outs[0], ref, mode, f"decode M={M} N={N} K={K} pad={ldb_pad} split={split} B {b_layout}")
     return p
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 17, 40, 64])
-def test_decode_kernel_uniform(M):
-    p = _decode_case(M, 2048, 7168, "uniform")
+DECODE_CASES = [(M, "row") for M in (1, 2, 3, 4, 16, 17, 40, 64)] + [(M, "col") for M in (1, 2, 3, 4, 16)]
+
+
+@pytest.mark.parametrize("M,b_layout", DECODE_CASES)
+def test_decode_kernel_uniform(M, b_layout):
+    p = _decode_case(M, 2048, 7168, "uniform", b_layout=b_layout)
     assert p["split_k"] > 1
-    _decode_case(M, 1001, 300, "uniform", ldb_pad=7)       # ragged last vector and last split
-    _decode_case(M, 520, 1024, "uniform", split=1)          # one split: direct store
-    _decode_case(M, 264, 2500, "uniform", split=2)          # K ranges longer than one A chunk
-    _decode_case(M, 1001, 7168, "uniform", ldb_pad=7)      # 16-lane reduction, ragged N
+    _decode_case(M, 1001, 300, "uniform", ldb_pad=7, b_layout=b_layout)   # ragged last vector and last split
+    _decode_case(M, 520, 1024, "uniform", split=1, b_layout=b_layout)     # one split: direct store
+    _decode_case(M, 264, 2500, "uniform", split=2, b_layout=b_layout)     # K ranges longer than one A chunk
+    _decode_case(M, 1001, 7168, "uniform", ldb_pad=7, b_layout=b_layout)  # 16-lane reduction, ragged N
+    if b_layout == "col":
+        _decode_case(M, 130, 301, "uniform", b_layout=b_layout)         # K tail inside a k-octet
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 16, 33, 64])
-def test_decode_kernel_integer_exact(M):
+@pytest.mark.parametrize("M,b_layout", [(M, "row") for M in (1, 3, 4, 16, 33, 64)] +
+                         [(M, "col") for M in (1, 3, 4, 16)])
+def test_decode_kernel_integer_exact(M, b_layout):
     for split in (0, 1, 3):
-        _decode_case(M, 777, 128, "int", ldb_pad=7, split=split)
-        _decode_case(M, 2048, 128, "int", split=split)
+        _decode_case(M, 777, 128, "int", ldb_pad=7, split=split, b_layout=b_layout)
+        _decode_case(M, 2048, 128, "int", split=split, b_layout=b_layout)
+        if b_layout == "col":
+            _decode_case(M, 300, 133, "int", split=split, b_layout=b_layout)
+
+
+def test_skinny_plans_by_b_layout():
+    # K-contiguous B: the decode kernel (128-column strips) up to 16 rows of
+    # A, the skinny MFMA tiles from 17 to 64 rows; N-contiguous B: the decode
+    # kernel up to 64 rows.
+    K, N = 7168, 2048
+    for M, tile_m, decode in ((1, 16, True), (16, 16, True), (17, 32, False), (64, 64, False)):
+        a = to_dev(synth.matrix(M, K, 1, 0))
+        p = g.plan(a, place(synth.matrix(K, N, 1, 1), "col"))
+        assert (p["variant"], p["b_path"], p["tile_m"]) == ("skinny", "kvec", tile_m), p
+        assert (p["tile_n"] == 128) == decode, p
+        q = g.plan(a, to_dev(synth.matrix(K, N, 1, 1)))
+        assert (q["variant"], q["b_path"], q["tile_n"]) == ("skinny", "rvec", 128), q
 
 
 def test_wrapper_rejects_bad_arguments():

@@ -23,7 +23,7 @@ Paths: the 256x256 LDS-DMA tiles (ids 14 and 13) with N- and K-contiguous
 B, the 256x256 and 128x128 register tiles, the pages' 64x32x32 tile, split-K
 (256x256 and 128x128 partials, the fixed-order reduction at 1, 4 and 16
 lanes per output), stream-K (its fix-up), the skinny MFMA tiles (16, 32 and 64
-rows), the decode kernel (M <= 64, N-contiguous B), the pre-packed B, grouped products,
+rows), the decode kernel (M <= 64 with N-contiguous B, M <= 16 with K-contiguous B), the pre-packed B, grouped products,
 and the same in bfloat16 and FP8 (E4M3 and E5M2 operands, fp16 output).
 """
 import numpy as np
@@ -239,19 +239,22 @@ def test_fp16_rounding_skinny_tiles(M):
                               f"skinny M={M} B={layout} plan {p}")
 
 
+@pytest.mark.parametrize("b_layout", ["row", "col"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-def test_fp16_rounding_decode_kernel(M):
+def test_fp16_rounding_decode_kernel(M, b_layout):
     # Split counts 18, 5 and 3 reach the reduction with 16, 4 and 1 lanes per
     # output; split 1 stores from the decode kernel itself; 0 is automatic.
+    # B N-contiguous, or as [N, K] rows (the kernel's K-contiguous form).
     N, K = 520, 1152
     plant = (0, M - 1 if M > 1 else None, [0, 255, 256, N - 1])
     A, B = int_inputs(M, N, K, 91200 + M, row_scales=(2, 4, 8), plant=plant)
     ref, S = oracle_out(A, B, "f16")
     check_census(ref, S, "f16", plant, f"decode M={M}", min_rounded=50, min_ties=5)
-    a, b = dev16(A, "f16"), dev16(B, "f16")
+    a, b = dev16(A, "f16"), dev16(B, "f16", b_layout)
     for split in (0, 18, 5, 3, 1):
         p = g.plan(a, b, variant="skinny", split_k=split)
-        assert p["tile_m"] == 16 and p["tile_n"] == 128 and p["b_path"] == "rvec", p
+        assert p["tile_m"] == 16 and p["tile_n"] == 128, p
+        assert p["b_path"] == ("kvec" if b_layout == "col" else "rvec"), p
         assert split == 0 or p["split_k"] == split, p
         assert_bits_equal(run(a, b, M, N, f"decode M={M}", variant="skinny", split_k=split), ref,
                           f"decode M={M} split {split} plan {p}")
