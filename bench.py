@@ -153,7 +153,7 @@ def summarize_pmc(*paths):
                            "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer"},
            "library_hash": library_hash()}
     alg = {"main_131072x2048x7168": (MAIN_KERNEL, 2.0 * (M * K + K * N), 2.0 * M * N),
-           "skinny_m1_partials": ("void gemmf16::decode_kernel<16, 0>", 2.0 * (K + K * N), None),
+           "skinny_m1_partials": ("void gemmf16::decode_kernel<16, 0, false>", 2.0 * (K + K * N), None),
            "skinny_m1_reduce": ("void gemmf16::splitk_reduce_elem<0>", None, 2.0 * N)}
     for key, (sub, alg_read, alg_write) in alg.items():
         k = kernel(sub)
@@ -336,7 +336,10 @@ CONFIGS = [
     ("square_256", 256, 256, 256, "row"), ("square_1024", 1024, 1024, 1024, "row"),
     ("square_4096", 4096, 4096, 4096, "row"), ("square_8192", 8192, 8192, 8192, "row"),
     ("skinny_m1", 1, 2048, 7168, "row"), ("skinny_m16", 16, 2048, 7168, "row"),
-    ("skinny_m64", 64, 2048, 7168, "row"), ("splitk_512x512x65536", 512, 512, 65536, "row"),
+    ("skinny_m64", 64, 2048, 7168, "row"),
+    # B as [N, K] rows (the usual storage of weights): not one of the pages' workloads
+    ("skinny_m1_bt", 1, 2048, 7168, "col"), ("skinny_m16_bt", 16, 2048, 7168, "col"),
+    ("splitk_512x512x65536", 512, 512, 65536, "row"),
     ("moe_131072x2048x7168", 131072, 2048, 7168, "row"),
     ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col", ("main", "streamk")),
     # not one of the pages' workloads: 17 x 16 tiles, a final wave of 16 tiles on 256 CUs
@@ -538,54 +541,64 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic("main_131072x2048x7168")
 
-    # ---- decode-shaped M = 1
-    m1 = 1
-    copies = 40                                   # 40 x 28 MiB of B > 1 GiB
-    a1 = to_dev(synth.matrix(m1, K, 3001, synth.TENSOR_A))
-    b1 = to_dev(synth.matrix(K, N, 3001, synth.TENSOR_B))
-    bs = [b1.clone() for _ in range(copies)]
-    c1 = torch.empty((m1, N), dtype=torch.float16, device=dev)
-    p1 = g.plan(a1, b1, c1)
-    ws1 = None
-    if p1["workspace_bytes"]:
-        ws1 = torch.empty(p1["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
-    # One CUDA/HIP graph holds one call per copy of B, so the timing is GPU
-    # time per call (both launches and the gap between them), free of the
-    # Python wrapper's per-call host cost.
-    cap = torch.cuda.Stream(dev)
-    with torch.cuda.stream(cap):
-        g.gemm(a1, bs[0], out=c1, workspace=ws1, stream=cap)
-    torch.cuda.synchronize()
-    eager = c1.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        for i in range(copies):
-            g.gemm(a1, bs[i], out=c1, workspace=ws1, stream=cap)
-    reps = max(1, args.skinny_reps // copies)
-    per_call = []
-    graph_ok = True
-    for r in range(reps + 2):
-        c1.fill_(float("nan"))
+    # ---- decode-shaped M = 1, B N-contiguous (the workload) and as [N, K] rows
+    def decode_line(b_layout):
+        m1 = 1
+        copies = 40                                   # 40 x 28 MiB of B > 1 GiB
+        a1 = to_dev(synth.matrix(m1, K, 3001, synth.TENSOR_A))
+        if b_layout == "col":
+            b1 = to_dev(synth.matrix(K, N, 3001, synth.TENSOR_B, order="col")).t()
+            bs = [b1.t().clone().t() for _ in range(copies)]
+        else:
+            b1 = to_dev(synth.matrix(K, N, 3001, synth.TENSOR_B))
+            bs = [b1.clone() for _ in range(copies)]
+        c1 = torch.empty((m1, N), dtype=torch.float16, device=dev)
+        p1 = g.plan(a1, b1, c1)
+        ws1 = None
+        if p1["workspace_bytes"]:
+            ws1 = torch.empty(p1["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
+        # One CUDA/HIP graph holds one call per copy of B, so the timing is GPU
+        # time per call (both launches and the gap between them), free of the
+        # Python wrapper's per-call host cost.
+        cap = torch.cuda.Stream(dev)
+        with torch.cuda.stream(cap):
+            g.gemm(a1, bs[0], out=c1, workspace=ws1, stream=cap)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        e1.synchronize()
-        graph_ok = graph_ok and torch.equal(c1.view(torch.int16), eager.view(torch.int16))
-        if r >= 2:
-            per_call.append(e0.elapsed_time(e1) / copies)
-    per_call.sort()
-    med1 = per_call[len(per_call) // 2]
-    bytes1 = 2.0 * (m1 * K + K * N + m1 * N)
-    skinny = {"workload": f"M={m1} N={N} K={K}, B rotated over {copies} copies",
-              "plan": {k: p1[k] for k in ("variant", "tile_m", "tile_n", "split_k", "grid",
-                                           "grid2")},
-              "median_us": med1 * 1e3, "GBps": bytes1 / (med1 * 1e-3) / 1e9,
-              "frac_hbm": bytes1 / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
-              "replays_match_eager": graph_ok,
-              "timing": f"HIP events around replays of a graph of {copies} calls "
-                        f"({reps} replays, median per call)"}
+        eager = c1.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(copies):
+                g.gemm(a1, bs[i], out=c1, workspace=ws1, stream=cap)
+        reps = max(1, args.skinny_reps // copies)
+        per_call = []
+        graph_ok = True
+        for r in range(reps + 2):
+            c1.fill_(float("nan"))
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            e1.synchronize()
+            graph_ok = graph_ok and torch.equal(c1.view(torch.int16), eager.view(torch.int16))
+            if r >= 2:
+                per_call.append(e0.elapsed_time(e1) / copies)
+        per_call.sort()
+        med1 = per_call[len(per_call) // 2]
+        bytes1 = 2.0 * (m1 * K + K * N + m1 * N)
+        del graph, bs
+        what = "B [K, N]" if b_layout == "row" else "B as [N, K] rows"
+        return {"workload": f"M={m1} N={N} K={K}, {what}, B rotated over {copies} copies",
+                "plan": {k: p1[k] for k in ("variant", "tile_m", "tile_n", "split_k", "grid",
+                                             "grid2", "b_path")},
+                "median_us": med1 * 1e3, "GBps": bytes1 / (med1 * 1e-3) / 1e9,
+                "frac_hbm": bytes1 / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "replays_match_eager": graph_ok,
+                "timing": f"HIP events around replays of a graph of {copies} calls "
+                          f"({reps} replays, median per call)"}
+
+    skinny = decode_line("row")
+    skinny_nk = decode_line("col")
 
     # ---- grouped product: the same tokens routed to 32 experts
     G = 32
@@ -741,6 +754,7 @@ def main():
                    "median_ms": sorted(durs)[len(durs) // 2], "min_ms": min(durs),
                    "wall_s": wall},
         "skinny_m1": skinny,
+        "skinny_m1_nk": skinny_nk,
         "grouped_moe": grouped,
         "bf16": bf16,
         "f8": f8,
