@@ -429,6 +429,52 @@ __device__ __forceinline__ void store_tile_staged(const KArgs& a, const f32x16 (
   }
 }
 
+// fp32 partials of the wave's 64 x 128 block to base (its element (0, 0); row
+// stride ld floats; rows x cols of it inside the target), staged through
+// LDS in two passes of 32 rows so that each store instruction writes two
+// whole 512-byte rows rather than 32 bytes into each of 32 rows.  In a
+// 32 x 32 block lane l holds, per group g, the 4 floats of columns
+// 8 g + 4 (l / 32) .. + 3 of row l % 32: one 16-byte chunk, chunk
+// 8 i + 2 g + l / 32 of its 512-byte row, placed at c ^ (r % 32) (distinct
+// banks for the 32 rows written and for the rows read back).  With ld % 4 == 0
+// and a 16-byte aligned base every whole chunk is one 16-byte store; other
+// chunks store element by element.  The caller has made the LDS free.
+template <class CF>
+__device__ __forceinline__ void store_partial_staged(float* base, int64_t ld, int rows, int cols,
+                                                     const f32x16 (&acc)[CF::FN][CF::FM], char* smem,
+                                                     int wave, int lane) {
+  static_assert(CF::WTN == 128 && CF::WTM == 64, "32 chunks of 16 bytes per row, two passes");
+  static_assert(CF::NW * 32 * CF::WTN * 4 <= CF::LDS, "staging space");
+  float* const stage = reinterpret_cast<float*>(smem + wave * (32 * CF::WTN * 4));
+  const int lr = lane % 32, h = lane >> 5;
+  const bool vec = (ld & 3) == 0 && ((uintptr_t)base & 15u) == 0;
+#pragma unroll
+  for (int j = 0; j < CF::FM; ++j) {
+#pragma unroll
+    for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 8 * i + 2 * g + h;
+        *reinterpret_cast<f32x4*>(stage + lr * 128 + ((c ^ lr) << 2)) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int r = 2 * it + lane / 32, c = lane % 32;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + r * 128 + ((c ^ r) << 2));
+      const int row = 32 * j + r, nv = cols - 4 * c;
+      float* const dst = base + (int64_t)row * ld + 4 * c;
+      if (row < rows && nv >= 4 && vec) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else if (row < rows && nv > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < nv) dst[e] = v[e];
+      }
+    }
+  }
+}
+
 // K-contiguous A; N-contiguous B, or K-contiguous B with BKMAJOR.
 // BPACK: B comes pre-packed (PackedBSource; read as a K-major B).
 template <class CF, bool BKMAJOR, bool PARTIAL, bool GROUPED = false, int DT = DT_F16,
@@ -627,25 +673,21 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_a128_kernel(KArgs a) {
     wg_barrier();      // and every other wave's: the LDS is free
     store_tile_staged<CF, DT>(a, acc, smem, m0, n0, wave, wm, wn, lane);
   } else {
-    // fp32 partials in the C^T-block layout of the other kernels.
-    const int lr = lane % 32;
-#pragma unroll
-    for (int i = 0; i < CF::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < CF::FM; ++j) {
-        const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (a.sk_tiles > 0)
-            store4_tile<CF::BM, CF::BN>(a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN), m - m0, n - n0,
-                                        v0, v1, v2, v3);
-          else
-            store4_f32(a, split, m, n, v0, v1, v2, v3);
-        }
-      }
+    // fp32 partials, staged through LDS: a stream-K tail tile to its dense
+    // slot (the whole tile, edges included), a split K range to W[split].
+    wait_lgkmcnt0();
+    wg_barrier();
+    if (a.sk_tiles > 0) {
+      float* const slot = a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN);
+      store_partial_staged<CF>(slot + (wm * CF::WTM) * CF::BN + wn * CF::WTN, CF::BN, CF::WTM, CF::WTN,
+                               acc, smem, wave, lane);
+    } else {
+      const int64_t mr = a.M - (m0 + wm * CF::WTM), nc = a.N - (n0 + wn * CF::WTN);
+      const int rows = mr < 0 ? 0 : (mr > CF::WTM ? CF::WTM : (int)mr);
+      const int cols = nc < 0 ? 0 : (nc > CF::WTN ? CF::WTN : (int)nc);
+      store_partial_staged<CF>(a.W + (split * a.M + m0 + wm * CF::WTM) * a.N + n0 + wn * CF::WTN, a.N,
+                               rows, cols, acc, smem, wave, lane);
+    }
   }
 }
 

@@ -393,25 +393,20 @@ __global__ __launch_bounds__(F8Cfg::NT) void gemm_f8_kernel(KArgs a) {
     wg_barrier();
     store_tile_staged<CF, DT_F16>(a, acc, smem, m0, n0, wave, wm, wn, lane);
   } else {
-    // fp32 partials in the C^T-block layout of the other kernels.
-    const int lr = lane % 32;
-#pragma unroll
-    for (int i = 0; i < CF::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < CF::FM; ++j) {
-        const int64_t m = m0 + wm * CF::WTM + j * 32 + lr;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + wn * CF::WTN + i * 32 + 8 * g + 4 * (lane >> 5);
-          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (a.sk_tiles > 0)
-            store4_tile<CF::BM, CF::BN>(a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN), m - m0, n - n0,
-                                        v0, v1, v2, v3);
-          else
-            store4_f32(a, split, m, n, v0, v1, v2, v3);
-        }
-      }
+    // fp32 partials staged through LDS, as in the 16-bit kernel.
+    wait_lgkmcnt0();
+    wg_barrier();
+    if (a.sk_tiles > 0) {
+      float* const slot = a.W + (int64_t)blockIdx.x * (CF::BM * CF::BN);
+      store_partial_staged<CF>(slot + (wm * CF::WTM) * CF::BN + wn * CF::WTN, CF::BN, CF::WTM, CF::WTN,
+                               acc, smem, wave, lane);
+    } else {
+      const int64_t mr = a.M - (m0 + wm * CF::WTM), nc = a.N - (n0 + wn * CF::WTN);
+      const int rows = mr < 0 ? 0 : (mr > CF::WTM ? CF::WTM : (int)mr);
+      const int cols = nc < 0 ? 0 : (nc > CF::WTN ? CF::WTN : (int)nc);
+      store_partial_staged<CF>(a.W + (split * a.M + m0 + wm * CF::WTM) * a.N + n0 + wn * CF::WTN, a.N,
+                               rows, cols, acc, smem, wave, lane);
+    }
   }
 }
 

@@ -191,14 +191,6 @@ __device__ __forceinline__ void store4_f32(const KArgs& a, int64_t split, int64_
   }
 }
 
-// Four consecutive fp32 partials of a dense BM x BN tile slot (row r,
-// columns c .. c+3 of the tile; whole tile written, edges included).
-template <int BM, int BN>
-__device__ __forceinline__ void store4_tile(float* slot, int64_t r, int64_t c, float v0, float v1,
-                                            float v2, float v3) {
-  *reinterpret_cast<f32x4*>(slot + r * BN + c) = f32x4{v0, v1, v2, v3};
-}
-
 // MFMAs of one BK step from one LDS stage.  Operand fragments are double
 // buffered in registers: the reads for k-step ks+1 are issued before the
 // MFMAs of k-step ks so LDS latency hides behind matrix work.
