@@ -6,7 +6,7 @@ integer, and both sides round the same exact sum once to bfloat16);
 |C_gpu - C_oracle| <= 1e-2 + 8e-3 |C_oracle| on U(-1, 1) inputs (one
 bfloat16 ulp is at most 2^-7 |C|).  The kernel families are forced as for
 fp16: main (full-line-A and 128x128 tiles), split-K, skinny MFMA tiles and
-the decode-shaped VALU kernel.
+the decode kernel (B N-contiguous, or as [N, K] rows).
 """
 import numpy as np
 import pytest
@@ -89,21 +89,23 @@ def test_bf16_square(n):
     check(run(a, bt, BOut(n, n)), ref, "uniform", f"bf16 square {n} transposed B")
 
 
+@pytest.mark.parametrize("b_layout", ["row", "col"])
 @pytest.mark.parametrize("M", [1, 2, 4, 16, 64])
-def test_bf16_skinny(M):
+def test_bf16_skinny(M, b_layout):
     N, K = 2048, 7168
     A = synth.matrix(M, K, 3000 + M, 0, fmt="bf16")
     B = synth.matrix(K, N, 3000 + M, 1, fmt="bf16")
     ref = ref_bf16(A, B)
-    a, b = bdev(A), bdev(B)
+    a, b = bdev(A), bplace(B, b_layout)
     p = g.plan(a, b)
     assert p["variant"] == "skinny"
     for kw in (dict(variant="auto"), dict(variant="skinny", split_k=1),
                dict(variant="skinny", split_k=8), dict(variant="skinny", tile=3)):
-        check(run(a, b, BOut(M, N), **kw), ref, "uniform", f"bf16 skinny M={M} {kw}")
+        check(run(a, b, BOut(M, N), **kw), ref, "uniform", f"bf16 skinny M={M} B {b_layout} {kw}")
     Ai = synth.matrix(M, 128, 3100 + M, 0, "int", fmt="bf16")
     Bi = synth.matrix(128, N, 3100 + M, 1, "int", fmt="bf16")
-    check(run(bdev(Ai), bdev(Bi), BOut(M, N)), ref_bf16(Ai, Bi), "int", f"bf16 skinny int M={M}")
+    check(run(bdev(Ai), bplace(Bi, b_layout), BOut(M, N)), ref_bf16(Ai, Bi), "int",
+          f"bf16 skinny int M={M} B {b_layout}")
 
 
 def test_bf16_moe_shape_sampled():
