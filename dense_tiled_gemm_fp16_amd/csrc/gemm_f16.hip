@@ -123,6 +123,9 @@ struct Plan {
   int64_t sk_tiles;  // STREAMK: tiles split over K after the whole waves
   bool pack;         // B is packed into the workspace first (see maybe_pack)
   size_t pack_bytes; // its size; stream-K partials follow it
+  bool pack_a;       // A is realigned into the front of the workspace first
+  size_t pack_a_bytes;   // its size (a multiple of 256); packed B and partials follow
+  int64_t lda_p;     // row stride of the realigned A (K rounded up to 64)
   size_t ws;
 };
 
@@ -225,8 +228,35 @@ bool tile_takes(const TileInfo& t, const Call& c, const Plan& p) {
 bool dma_tile_takes(const Call& c, const Plan& p) { return tile_takes(tile_info(TILE_DMA256A128), c, p); }
 
 constexpr int64_t kPackMinRows = 16384;   // automatic plans pack a K-contiguous B from this M on
-constexpr int64_t kPackMinRowsGather = 4096;   // and a B the DMA tile cannot read from this M on
-constexpr int32_t kBPathPacked = 3;       // b_path reported for a packing plan
+constexpr int64_t kPackMinRowsGather = 1024;   // and a B the DMA tile cannot read from this M on
+constexpr int32_t kBPathPacked = 3;       // a_path / b_path reported for a packed operand
+constexpr int64_t kRealignMinN = 256;     // automatic plans realign an unreadable A from this N on,
+constexpr int64_t kRealignMinWorkMC = INT64_C(1) << 33;   // an M-contiguous one from this M N K on
+constexpr double kPackMinWork = 134217728.0;   // and pack or realign nothing below 2^27 M N K
+
+bool worth_packing(const Call& c) { return (double)c.M * (double)c.N * (double)c.K >= kPackMinWork; }
+
+// Realigned A: M rows of K rounded up to 64 elements (128-byte rows), the
+// whole rounded up to 256 bytes.  0 when the size does not fit.
+size_t realign_a_bytes(int64_t M, int64_t K) {
+  const int64_t ldp = cdiv(K, 64) * 64;
+  int64_t n;
+  if (__builtin_mul_overflow(M, ldp, &n) || n > (INT64_MAX - 255) / 2 || cdiv(M, 64) * cdiv(ldp, 128) > INT32_MAX)
+    return 0;
+  return (size_t)((2 * n + 255) / 256 * 256);
+}
+
+// The realigning launch: A [M, K] through its strides into Ap [M, ldp].
+int launch_realign_a(const uint16_t* A, int64_t lda_m, int64_t lda_k, int64_t M, int64_t K, int64_t ldp,
+                     uint16_t* Ap, hipStream_t stream) {
+  int64_t nbk = cdiv(ldp, 128);
+  const int64_t blocks = cdiv(M, 64) * nbk;
+  void* args[] = {&A, &lda_m, &lda_k, &M, &K, &ldp, &nbk, &Ap};
+  if (hipLaunchKernel((const void*)realign_a_kernel, dim3((unsigned)blocks), dim3(256), args, 0, stream) !=
+      hipSuccess)
+    return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
 
 // Pre-packed B: ceil(N/256) panels of ceil(K/32) blocks of 16 KiB (see
 // pack_b_kernel).  0 for shapes out of range or too large to count.
@@ -328,11 +358,27 @@ void maybe_pack(const Call& c, int variant, bool allow_pack, Plan& p, bool any_b
   p.ws += bytes;
 }
 
-int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = true) {
+// Adds the realigned A in front of the workspace (false if the sizes overflow).
+bool add_realign(const Call& c, Plan& p) {
+  const size_t bytes = realign_a_bytes(c.M, c.K);
+  if (bytes == 0 || p.ws > SIZE_MAX - bytes) return false;
+  p.pack_a = true;
+  p.pack_a_bytes = bytes;
+  p.lda_p = cdiv(c.K, 64) * 64;
+  p.ws += bytes;
+  return true;
+}
+
+// allow_pack: automatic plans may pack B; allow_realign: and realign A.
+int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = true,
+              bool allow_realign = true) {
   int rc = check_opts(o);
   if (rc) return rc;
   p.pack = false;
   p.pack_bytes = 0;
+  p.pack_a = false;
+  p.pack_a_bytes = 0;
+  p.lda_p = 0;
   const int variant = o ? o->variant : GEMM_VARIANT_AUTO;
   const int want_split = o ? o->split_k : 0;
   const int want_panel = o ? o->panel : 0;
@@ -388,6 +434,17 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
 
   p.a_path = f8 ? PATH_KVEC : classify(c.A, c.lda_m, c.lda_k);
   p.b_path = f8 ? (c.ldb_k == 1 ? PATH_KVEC : PATH_RVEC) : classify(c.B, c.ldb_n, c.ldb_k);
+  // An A that the LDS-DMA tile cannot read (rows not on 16-byte boundaries,
+  // or M-contiguous) would keep every plan on the 128x128 tile's element-wise
+  // or transposing loads, at a half to a third of the rate.  An automatic
+  // plan copies it first into K-contiguous 128-byte rows in the workspace
+  // (one pass of 4MK bytes) and is planned as for that A.
+  const bool realign = allow_realign && variant == GEMM_VARIANT_AUTO && !f8 &&
+                       (p.variant == GEMM_VARIANT_MAIN || p.variant == GEMM_VARIANT_SPLITK) &&
+                       p.a_path != PATH_KVEC && c.N >= kRealignMinN && worth_packing(c) &&
+                       realign_a_bytes(c.M, c.K) != 0 &&
+                       (p.a_path == PATH_GATHER || (double)c.M * c.N * c.K >= (double)kRealignMinWorkMC);
+  if (realign) p.a_path = PATH_KVEC;
   // A B that the LDS-DMA tile cannot read directly (rows not 16-byte
   // aligned, or neither dimension contiguous) would take the element-wise
   // path on the 128x128 tile, at less than half the rate.  An automatic plan
@@ -395,7 +452,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   // and is planned as for a K-contiguous B; if no packing plan comes of it,
   // the call is planned again with B's own path.
   const bool pack_any = allow_pack && variant == GEMM_VARIANT_AUTO && !f8 && p.variant == GEMM_VARIANT_MAIN &&
-                        c.M >= kPackMinRowsGather && p.a_path == PATH_KVEC &&
+                        c.M >= kPackMinRowsGather && worth_packing(c) && p.a_path == PATH_KVEC &&
                         (p.b_path == PATH_GATHER || (p.b_path == PATH_RVEC && c.N % 8 != 0));
   if (pack_any) p.b_path = PATH_KVEC;
 
@@ -409,10 +466,20 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       } else {
         // 256x256 tiles once they give at least half a wave of workgroups,
         // or, with a long K, when the stream-K plan below spreads fewer of
-        // them over the compute units (the layout permitting).
+        // them over the compute units (the layout permitting).  From a
+        // quarter wave on the DMA tile still wins where K is not short: a
+        // quarter-full wave of 256x256 tiles beat a full wave of 128x128
+        // ones by 8% at 2048^3 and by 20-24% at 81-100 tiles (2304^3,
+        // 2560^3); at 2048 x 2048 x 1024 the 128x128 plan was 5% ahead,
+        // while from 96 tiles on K = 1024 went to the big tile too.
         if ((rc = need_cus())) return rc;
         const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
-        p.tile_id = (2 * t256 >= cus || (small_grid_streamk(c, t256, cus) && dma_tile_takes(c, p)))
+        // A B to be packed (one the DMA cannot read) takes the big tile once
+        // N fills one: the 128x128 tile would read it element by element.
+        const bool quarter = 4 * t256 >= cus && (c.K >= 2048 || 3 * t256 >= cus);
+        const bool packed_b = pack_any && c.N >= 256;
+        p.tile_id = (2 * t256 >= cus ||
+                     ((quarter || packed_b || small_grid_streamk(c, t256, cus)) && dma_tile_takes(c, p)))
                         ? TILE_DMA256A128 : TILE_T128;
       }
       break;
@@ -528,7 +595,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       return GEMM_ERR_SHAPE;
     p.ws = (size_t)((bytes + 255) / 256 * 256);
     maybe_pack(c, variant, allow_pack, p, pack_any);
-    if (pack_any && !p.pack) return make_plan(c, o, p, false);
+    if (pack_any && !p.pack) return make_plan(c, o, p, false, allow_realign);
+    if (realign && !add_realign(c, p)) return make_plan(c, o, p, allow_pack, false);
     return GEMM_OK;
   }
 
@@ -574,7 +642,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   if ((rc = plan_partials(c, p))) return rc;
 
   maybe_pack(c, variant, allow_pack, p, pack_any);
-  if (pack_any && !p.pack) return make_plan(c, o, p, false);
+  if (pack_any && !p.pack) return make_plan(c, o, p, false, allow_realign);
+  if (realign && !add_realign(c, p)) return make_plan(c, o, p, allow_pack, false);
   return GEMM_OK;
 }
 
@@ -586,7 +655,7 @@ void fill_info(const Plan& p, gemm_f16_plan_info* info) {
   info->tile_k = p.dec_mt ? kDecUnit : ti.bk;
   info->split_k = p.split;
   info->panel = p.panel;
-  info->a_path = p.a_path;
+  info->a_path = p.pack_a ? kBPathPacked : p.a_path;
   info->b_path = p.pack ? kBPathPacked : p.b_path;
   info->tile_id = p.tile_id;
   info->grid = p.grid;
@@ -684,6 +753,14 @@ int launch_streamk(const Call& c, const Plan& p, KArgs a, kfn_t final_fn, kfn_t 
 
 int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   if (p.dec_mt) return launch_decode(c, p, ws, stream);
+  // Realigning plan: A into the front of the workspace.
+  if (p.pack_a) {
+    const int rc = launch_realign_a((const uint16_t*)c.A, c.lda_m, c.lda_k, c.M, c.K, p.lda_p,
+                                    (uint16_t*)ws, stream);
+    if (rc) return rc;
+  }
+  const void* const A = p.pack_a ? ws : c.A;
+  if (p.pack_a) ws = (char*)ws + p.pack_a_bytes;
   // Packing plan: B into the workspace (K16: K in 16-bit units).
   const int64_t K16 = c.dt >= DT_F8 ? cdiv(c.K, 2) : c.K;
   if (p.pack) {
@@ -698,9 +775,9 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
   }
   const TileInfo& ti = tile_info(p.tile_id);
   KArgs a;
-  a.A = (const uint16_t*)c.A;
-  a.lda_m = c.lda_m;
-  a.lda_k = c.lda_k;
+  a.A = (const uint16_t*)A;
+  a.lda_m = p.pack_a ? p.lda_p : c.lda_m;
+  a.lda_k = p.pack_a ? 1 : c.lda_k;
   a.B = (const uint16_t*)c.B;
   a.ldb_k = c.ldb_k;
   a.ldb_n = c.ldb_n;
@@ -765,8 +842,9 @@ int ex_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, 
   Plan p;
   if ((rc = make_plan(c, opts, p))) return rc;
   // A packing plan runs only where the room is there: the library's own
-  // allocation, or a caller workspace that holds the packed B.
-  if (p.pack && workspace && workspace_bytes < p.ws && (rc = make_plan(c, opts, p, false)))
+  // allocation, or a caller workspace that holds the packed operands.
+  if ((p.pack || p.pack_a) && workspace && workspace_bytes < p.ws &&
+      (rc = make_plan(c, opts, p, false, false)))
     return rc;
   hipStream_t s = (hipStream_t)stream;
   if (p.ws == 0) return launch(c, p, nullptr, s);
@@ -796,7 +874,7 @@ int noalloc_impl(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int
   if (rc) return rc;
   if ((rc = spans(c))) return rc;
   Plan p;
-  if ((rc = make_plan(c, nullptr, p, false))) return rc;
+  if ((rc = make_plan(c, nullptr, p, false, false))) return rc;
   hipStream_t s = (hipStream_t)stream;
   if (p.ws == 0) return launch(c, p, nullptr, s);
   if (p.ws > GEMM_F16_SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
@@ -815,7 +893,7 @@ size_t ws_impl(int dt, int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opt
                               (const void*)0x300000000000ull, K, 1, N, 1, N, M, N, K, 0, 0, 0};
   if (spans(c)) return 0;
   Plan p;
-  if (make_plan(c, opts, p, false)) return 0;   // split workspaces only (see the packing plan)
+  if (make_plan(c, opts, p, false, false)) return 0;   // split workspaces only (see the packing plans)
   return p.ws;
 }
 

@@ -61,4 +61,48 @@ __global__ __launch_bounds__(256) void pack_b8_kernel(const uint8_t* B, int64_t 
   *reinterpret_cast<u32x4*>(Bp + blk * 16384 + r * 64 + ((c ^ fa(r)) * 16)) = u32x4{h[0], h[1], h[2], h[3]};
 }
 
+// A [M, K] (16-bit elements, any strides) realigned into Ap [M, ldp], K
+// contiguous, ldp a multiple of 64 (rows on 128-byte boundaries), zero at
+// k in [K, ldp): the layout the LDS-DMA tile's A stages read.  A workgroup
+// moves a 64 x 128 block through LDS: all 32 of a thread's element loads
+// are issued before the first LDS write, with consecutive lanes along k when
+// A is K-contiguous (else along m, so an M-contiguous A is read in whole
+// lines too); then each row leaves as 16-byte stores.  Workgroup ids are
+// dealt so that the ids one XCD receives (the dispatcher sends id b to XCD
+// b % 8) hold neighbouring blocks along k, which share the cache lines that
+// a row not on a 128-byte boundary straddles.  Rows past M are neither read
+// nor written.
+__global__ __launch_bounds__(256) void realign_a_kernel(const uint16_t* A, int64_t lda_m, int64_t lda_k,
+                                                        int64_t M, int64_t K, int64_t ldp, int64_t nbk,
+                                                        uint16_t* Ap) {
+  __shared__ __align__(16) uint16_t t[64][128 + 8];   // 272-byte rows: 16-byte reads stay aligned
+  const int64_t T = (int64_t)gridDim.x, per = T / 8;
+  int64_t b = blockIdx.x;
+  if (b < per * 8) b = (b % 8) * per + b / 8;
+  const int64_t m0 = (b / nbk) * 64, k0 = (b % nbk) * 128;
+  const int tid = threadIdx.x;
+  const bool k_fast = lda_k == 1 || lda_m != 1;
+  uint32_t v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int e = i * 256 + tid;
+    const int r = k_fast ? e >> 7 : e & 63, c = k_fast ? e & 127 : e >> 6;
+    const int64_t m = m0 + r, k = k0 + c;
+    v[i] = (m < M && k < K) ? (uint32_t)A[m * lda_m + k * lda_k] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int e = i * 256 + tid;
+    const int r = k_fast ? e >> 7 : e & 63, c = k_fast ? e & 127 : e >> 6;
+    t[r][c] = (uint16_t)v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = j * 256 + tid, r = q >> 4, c = (q & 15) * 8;
+    if (m0 + r < M && k0 + c < ldp)
+      *reinterpret_cast<u32x4*>(Ap + (m0 + r) * ldp + k0 + c) = *reinterpret_cast<const u32x4*>(&t[r][c]);
+  }
+}
+
 }  // namespace gemmf16

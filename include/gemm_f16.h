@@ -108,7 +108,7 @@ typedef struct gemm_f16_plan_info {
   int32_t panel;            /* raster group height in tiles (-1 = plain order)   */
   int32_t a_path, b_path;   /* operand load path: 0 gather, 1 vector along K,    */
                             /* 2 vector along M (A) or N (B) with a transpose;   */
-                            /* b_path 3: B packed into the workspace first      */
+                            /* 3: packed (B) or realigned (A) into the workspace */
   int32_t tile_id;          /* the tile configuration chosen                     */
   int64_t grid;             /* workgroups in the first launch                    */
   int64_t grid2;            /* workgroups in the reduction launch (0 = none)     */
@@ -142,10 +142,17 @@ int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
  * plan reports b_path 3 and workspace_bytes = gemm_f16_packed_b_bytes(K, N)
  * plus the stream-K partials.  It runs when workspace is NULL or holds that
  * many bytes; a smaller caller workspace gets the direct plan instead.
- * The same holds from M >= 4096 for a 16-bit B that the LDS-DMA tile cannot
+ * The same holds from M >= 1024 for a 16-bit B that the LDS-DMA tile cannot
  * read directly (rows not 16-byte aligned, or neither dimension contiguous),
  * which would otherwise take the element-wise path of the 128x128 tile: the
  * packing pass reads B through its strides.
+ * Realigning plan (AUTO only, MAIN/SPLITK/STREAMK, N >= 256): a 16-bit A
+ * that the LDS-DMA tile cannot read (rows not 16-byte aligned or not
+ * K-contiguous; an M-contiguous A only from M*N*K >= 2^33) is first copied
+ * through its strides into the front of the workspace as M rows of
+ * ceil(K/64)*64 elements (zero past K), 256-byte rounded, and the product
+ * runs on that copy.  The plan reports a_path 3; a packed B and any
+ * partials follow the copy.  Neither pass runs below M*N*K = 2^27.
  * Both give the same bits.  The *_workspace_bytes functions report split
  * workspaces only.  gemm_bf16_ex does the same; gemm_f8_ex too, for an FP8
  * B with K-contiguous rows, packed into 16 KiB blocks of 64 k (workspace

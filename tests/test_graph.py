@@ -115,3 +115,21 @@ def test_graph_replay_packing_plan():
         g.gemm(a, b, out=out, workspace=ws, stream=stream)
 
     _replay_matches(call, out, ws, f"packing plan {p}")
+
+
+def test_graph_replay_realigning_plan():
+    # Rows of K = 2051 halves: the automatic plan copies A into aligned rows
+    # in the caller's workspace, then runs the product on them.
+    M, N, K = 2085, 2056, 2051
+    A = synth.matrix(M, K, 17300, 0)
+    B = synth.matrix(K, N, 17301, 1)
+    a, b = to_dev(A), to_dev(B)
+    out = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    p = g.plan(a, b, out=out)
+    assert p["a_path"] == "packed" and p["workspace_bytes"] > 0, p
+    ws = torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=DEV)
+
+    def call(stream):
+        g.gemm(a, b, out=out, workspace=ws, stream=stream)
+
+    _replay_matches(call, out, ws, f"realigning plan {p}")

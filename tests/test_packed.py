@@ -12,7 +12,8 @@ import torch
 import dense_tiled_gemm_fp16_amd as g
 import oracle
 import synth
-from gpu_util import (DEV, ORACLE_THREADS, Out, assert_bits_equal, assert_close, place, say,
+from gpu_util import (DEV, ORACLE_THREADS, Out, assert_bits_equal, assert_close, band_rows, dev_nan,
+                      place, say,
                       to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -237,3 +238,101 @@ def test_auto_packs_b_the_dma_tile_cannot_read(layout):
     g.gemm(a, b, out=out2.view, workspace=small)
     torch.cuda.synchronize()
     assert_bits_equal(out2.result(), ref, f"element-wise plan, {layout} B")
+
+
+# ---- automatic realigning plan: an A the DMA tile cannot read (gemm_f16_ex, AUTO)
+
+def _a_view(A, layout):
+    """A [M, K] on the GPU inside NaN storage, laid out so that the LDS-DMA
+    tile cannot read it: rows of a length that is not a 16-byte multiple,
+    every other column of a wider buffer, or M-contiguous."""
+    M, K = A.shape
+    if layout == "odd_ld":
+        return place(A, "row", (1, (3 - K) % 8 + 8))          # row stride = 3 (mod 8)
+    if layout == "strided":
+        buf = dev_nan((M + 1) * 2 * K)
+        v = buf[2 * K:].view(M, 2 * K)[:, ::2]
+        v.copy_(to_dev(A))
+        return v
+    if layout == "mcontig":
+        return place(A, "col", (1, 8))
+    raise ValueError(layout)
+
+
+def _without_realign(a, b, M, N, K):
+    """The automatic plan again with a caller workspace too small for the
+    realigned A (the size the split plans need on aligned operands), which
+    must give the plan on A's own layout."""
+    small = torch.full((max(256, g.workspace_bytes(M, N, K)) // 4 + 64,), float("nan"),
+                       dtype=torch.float32, device=DEV)
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view, workspace=small)
+    torch.cuda.synchronize()
+    return out.result()
+
+
+@pytest.mark.parametrize("layout,shape", [("odd_ld", (2085, 2056, 2051)), ("strided", (2085, 2056, 2051)),
+                                          ("mcontig", (2048, 2048, 2048))])
+def test_auto_realigns_a_the_dma_tile_cannot_read(layout, shape):
+    # Integer inputs keep every fp32 sum exact, so the realigned plan, the
+    # plan on A's own layout and the oracle must agree bit for bit.
+    M, N, K = shape
+    seed = 16000 + len(layout)
+    A = synth.matrix(M, K, seed, 0, "int")
+    B = synth.matrix(K, N, seed, 1, "int")
+    a, b = _a_view(A, layout), to_dev(B)
+    p = g.plan(a, b)
+    assert p["a_path"] == "packed" and p["b_path"] == "rvec", p
+    ldp = -(-K // 64) * 64
+    assert p["workspace_bytes"] >= M * ldp * 2, p
+    say(f"realigning plan, A {layout} {M}x{N}x{K} stride {a.stride()}: {p}")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    rows = band_rows(M)
+    assert_bits_equal(got[rows], reference(A, B, rows), f"realigned A {layout}, sampled rows")
+    say(f"A {layout}: plan without the realigned A")
+    assert_bits_equal(got, _without_realign(a, b, M, N, K), f"realigned A {layout} vs A's own layout")
+
+
+def test_auto_realigns_a_and_packs_b():
+    # Neither operand readable by the DMA (rows of 2100 halves): A realigned,
+    # B packed, both in the library's workspace.
+    M, N, K = 2100, 2100, 2100
+    A = synth.matrix(M, K, 16100, 0, "int")
+    B = synth.matrix(K, N, 16101, 1, "int")
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    assert (p["a_path"], p["b_path"], p["tile_id"]) == ("packed", "packed", 14), p
+    say(f"realigned A and packed B {M}x{N}x{K}: {p}")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    rows = band_rows(M)
+    assert_bits_equal(got[rows], reference(A, B, rows), "realigned A, packed B, sampled rows")
+    assert_bits_equal(got, _without_realign(a, b, M, N, K), "realigned A, packed B vs element-wise")
+
+
+@pytest.mark.parametrize("shape,variant", [((512, 512, 65539), "splitk"), ((1536, 1536, 8195), "streamk")])
+def test_auto_realign_split_plans(shape, variant):
+    # Odd K: A's rows are never 16-byte aligned.  The split plans put their
+    # partials after the realigned A; integer sums stay exact in fp32
+    # (|sum| < 2^24), so any K split gives the oracle's bits.
+    M, N, K = shape
+    A = synth.matrix(M, K, 16200 + M, 0, "int")
+    B = synth.matrix(K, N, 16200 + M, 1, "int")
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    if p["variant"] != variant:
+        pytest.skip(f"this device's compute-unit count gives another plan here: {p}")
+    assert p["a_path"] == "packed", p
+    say(f"realigning {variant} plan {M}x{N}x{K}: {p}")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    rows = band_rows(M, 128)
+    assert_bits_equal(got[rows], reference(A, B, rows), f"realigned A {variant}, sampled rows")
+    assert_bits_equal(got, _without_realign(a, b, M, N, K), f"realigned A {variant} vs A's own layout")

@@ -154,6 +154,31 @@ def test_square_full_coverage(n):
     full_size_check(to_dev(A), to_dev(B), A, B, (n, 1), n, n, n, 2000 + n, f"square {n}")
 
 
+@pytest.mark.parametrize("M,N,K,tile", [(1792, 1792, 1792, 1), (2048, 2048, 1024, 1),
+                                        (2048, 2048, 2048, 14), (3072, 2048, 1024, 14),
+                                        (2100, 2304, 2056, 14), (2100, 2300, 2056, 14),
+                                        (1000, 4100, 2048, 1)])
+def test_main_tile_from_a_quarter_wave(M, N, K, tile):
+    # 256 x 256 tiles from a quarter wave (64 of them on 256 compute units)
+    # with K >= 2048, or from 86 at any K; below, the 128 x 128 tile.  A B
+    # whose rows are not 16-byte multiples (N = 2300, 4100) is packed for the
+    # big tile from M = 1024 on; below that it keeps the 128 x 128 tile.
+    # Integer inputs keep every fp32 sum exact, so the automatic plan and the
+    # other tile give the same bits, which sampled rows check against the
+    # oracle (the first and last rows and one in every 256-row band).
+    A = synth.matrix(M, K, 2500 + M, 0, "int")
+    B = synth.matrix(K, N, 2500 + M, 1, "int")
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (p["variant"], p["tile_id"]) == ("main", tile), p
+    got = run(a, b)
+    other = run(a, b, variant="main", tile=1 if p["tile_id"] == 14 else 14)
+    assert_bits_equal(got, other, f"{M}x{N}x{K} tile {p['tile_id']} against the other tile")
+    rows = band_rows(M)
+    assert_bits_equal(got[rows], reference(A, B, rows), f"{M}x{N}x{K} sampled rows")
+
+
 # ------------------------------------------------------------------ LDS-DMA tiles, K remainders
 
 @pytest.mark.parametrize("tile", [13, 14])
