@@ -241,7 +241,8 @@ bool worth_packing(const Call& c) { return (double)c.M * (double)c.N * (double)c
 size_t realign_a_bytes(int64_t M, int64_t K) {
   const int64_t ldp = cdiv(K, 64) * 64;
   int64_t n;
-  if (__builtin_mul_overflow(M, ldp, &n) || n > (INT64_MAX - 255) / 2 || cdiv(M, 64) * cdiv(ldp, 128) > INT32_MAX)
+  if (__builtin_mul_overflow(M, ldp, &n) || n > (INT64_MAX - 255) / 2 || cdiv(M, 64) * cdiv(ldp, 128) > INT32_MAX ||
+      cdiv(M * cdiv(ldp, 1024), 4) > INT32_MAX)
     return 0;
   return (size_t)((2 * n + 255) / 256 * 256);
 }
@@ -249,6 +250,15 @@ size_t realign_a_bytes(int64_t M, int64_t K) {
 // The realigning launch: A [M, K] through its strides into Ap [M, ldp].
 int launch_realign_a(const uint16_t* A, int64_t lda_m, int64_t lda_k, int64_t M, int64_t K, int64_t ldp,
                      uint16_t* Ap, hipStream_t stream) {
+  if (lda_k == 1) {   // rows already K-contiguous: a straight copy into aligned rows
+    int64_t nseg = cdiv(ldp, 1024);
+    const int64_t blocks = cdiv(M * nseg, 4);
+    void* args[] = {&A, &lda_m, &M, &K, &ldp, &nseg, &Ap};
+    if (hipLaunchKernel((const void*)realign_a_rows_kernel, dim3((unsigned)blocks), dim3(256), args, 0,
+                        stream) != hipSuccess)
+      return GEMM_ERR_HIP;
+    return GEMM_OK;
+  }
   int64_t nbk = cdiv(ldp, 128);
   const int64_t blocks = cdiv(M, 64) * nbk;
   void* args[] = {&A, &lda_m, &lda_k, &M, &K, &ldp, &nbk, &Ap};

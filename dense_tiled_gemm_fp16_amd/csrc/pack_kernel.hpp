@@ -105,4 +105,32 @@ __global__ __launch_bounds__(256) void realign_a_kernel(const uint16_t* A, int64
   }
 }
 
+// The same copy for an A with K-contiguous rows (lda_k == 1) that start
+// off 16-byte boundaries: no transpose, so no LDS.  Each wave takes one
+// (row, 1024-element segment) unit: its 16 loads per lane, 128 consecutive
+// bytes per instruction, are all in flight before the 16 stores.  Units of
+// one row sit in neighbouring waves, so the cache lines a misaligned row
+// straddles are fetched once.
+__global__ __launch_bounds__(256) void realign_a_rows_kernel(const uint16_t* A, int64_t lda_m, int64_t M,
+                                                             int64_t K, int64_t ldp, int64_t nseg,
+                                                             uint16_t* Ap) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= M * nseg) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = u / nseg, k0 = (u - m * nseg) * 1024 + lane;
+  const uint16_t* src = A + m * lda_m;
+  uint16_t* dst = Ap + m * ldp;
+  uint32_t v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t k = k0 + 64 * j;
+    v[j] = k < K ? (uint32_t)src[k] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t k = k0 + 64 * j;
+    if (k < ldp) dst[k] = (uint16_t)v[j];
+  }
+}
+
 }  // namespace gemmf16
