@@ -285,6 +285,13 @@ int launch_pack_b(const uint16_t* B, int64_t ldb_k, int64_t ldb_n, int64_t K, in
   int64_t S = cdiv(K, 32);
   int64_t slots = (int64_t)(packed_b_bytes(K, N) / 16);
   int kvec = (ldb_k == 1 && ((uintptr_t)B & 15u) == 0 && ldb_n % 8 == 0) ? 1 : 0;
+  if (ldb_n == 1 && ldb_k != 1) {   // N-contiguous rows: transposed through LDS, one block per workgroup
+    void* rargs[] = {&B, &ldb_k, &K, &N, &S, &Bp};
+    if (hipLaunchKernel((const void*)pack_b_rows_kernel, dim3((unsigned)(slots / 1024)), dim3(256), rargs, 0,
+                        stream) != hipSuccess)
+      return GEMM_ERR_HIP;
+    return GEMM_OK;
+  }
   void* args[] = {&B, &ldb_k, &ldb_n, &K, &N, &S, &slots, &Bp, &kvec};
   if (hipLaunchKernel((const void*)pack_b_kernel, dim3((unsigned)cdiv(slots, 256)), dim3(256), args, 0,
                       stream) != hipSuccess)

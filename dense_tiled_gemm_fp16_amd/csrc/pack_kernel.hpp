@@ -36,6 +36,38 @@ __global__ __launch_bounds__(256) void pack_b_kernel(const uint16_t* B, int64_t 
       u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
+// The same blocks from an N-contiguous B (ldb_n == 1) whose rows start off
+// 16-byte boundaries, through LDS: workgroup b builds block b (panel
+// b / S, k-block b % S).  Its 32 loads per thread (k-row i, column tid) are
+// all in flight before the first LDS write, each instruction reading 128
+// consecutive bytes of one k-row; then each thread gathers four 16-byte
+// slots (8 k of one n) from LDS and stores them, the block's bytes in order.
+__global__ __launch_bounds__(256) void pack_b_rows_kernel(const uint16_t* B, int64_t ldb_k, int64_t K,
+                                                          int64_t N, int64_t S, uint16_t* Bp) {
+  __shared__ uint16_t t[32][256 + 2];   // k-rows of 516 bytes: the column reads spread over the banks
+  const int64_t blk = blockIdx.x;
+  const int64_t pnl = blk / S, s = blk - pnl * S;
+  const int64_t n0 = 256 * pnl, k0 = 32 * s;
+  const int tid = threadIdx.x;
+  const int64_t n = n0 + tid;
+  uint32_t v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = (n < N && k0 + i < K) ? (uint32_t)B[(k0 + i) * ldb_k + n] : 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) t[i][tid] = (uint16_t)v[i];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = j * 256 + tid;                   // 16-byte slot of the block
+    const int r = q / 4, c = (q % 4) ^ fa(r);      // n-row r, k chunk c
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = t[8 * c + e][r];
+    *reinterpret_cast<u32x4*>(Bp + blk * 8192 + q * 8) =
+        u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  }
+}
+
 // FP8 B [K, N] (bytes, any strides) into the same 16 KiB blocks, one per
 // 64 k: byte o of block (p, s) holds, for row r = o / 64 (n = 256 p + r) and
 // 16-byte slot q = (o % 64) / 16, the bytes k = 64 s + 16 (q ^ fa(r)) + e,
