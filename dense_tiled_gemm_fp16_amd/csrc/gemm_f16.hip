@@ -438,7 +438,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     } else {
       const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
       const int64_t mn = c.M > c.N ? c.M : c.N;
-      p.variant = (2 * T <= cus && c.K >= 4 * mn) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
+      p.variant = (2 * T <= cus && c.K >= 2 * mn) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
     }
   }
 
@@ -631,6 +631,11 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       // multiple of 8 so the launch can keep each K range's tiles on one XCD.
       const int64_t per_cu8 = p.variant == GEMM_VARIANT_SKINNY ? 8 : (ti.bm >= 256 ? 5 : 16);
       s = cdiv(per_cu8 * (int64_t)cus, 8 * T);
+      // On the 256x256 tiles, K ranges of at least 512 k: at smaller K more,
+      // shorter ranges cost more in partials and per-workgroup start-up than
+      // the extra compute units give (1024 x 1024 x 4096: 29.0 us with 8
+      // ranges against 33.4 with 16; 1024 x 1024 x 2048: 23.8 with 4).
+      if (p.variant == GEMM_VARIANT_SPLITK && ti.bm >= 256 && s > c.K / 512) s = c.K / 512 > 1 ? c.K / 512 : 1;
       const int64_t max_by_k = cdiv(c.K, 2 * ti.bk);  // at least two K steps per split
       if (s >= 8) s = cdiv(s, 8) * 8;
       if (s > max_by_k) s = max_by_k;

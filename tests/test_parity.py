@@ -154,6 +154,25 @@ def test_square_full_coverage(n):
     full_size_check(to_dev(A), to_dev(B), A, B, (n, 1), n, n, n, 2000 + n, f"square {n}")
 
 
+
+@pytest.mark.parametrize("M,N,K,variant,split", [(1024, 1024, 2048, "splitk", 4), (768, 768, 2048, "splitk", 4),
+                                                 (1024, 1024, 4096, "splitk", 8), (1024, 1024, 1024, "main", 1)])
+def test_auto_split_k_on_small_products(M, N, K, variant, split):
+    # Split-K from K = 2 max(M, N) while the 128 x 128 tiles fill at most
+    # half the compute units, with K ranges of at least 512 k on the
+    # 256 x 256 tile.  Integer inputs keep every sum exact, so the split plan
+    # gives the main plan's bits, and sampled rows the oracle's.
+    A = synth.matrix(M, K, 2700 + M, 0, "int")
+    B = synth.matrix(K, N, 2700 + K, 1, "int")
+    a, b = to_dev(A), to_dev(B)
+    p = g.plan(a, b)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (p["variant"], p["split_k"]) == (variant, split), p
+    got = run(a, b, Out(M, N))
+    assert_bits_equal(got, run(a, b, Out(M, N), variant="main"), f"{M}x{N}x{K} auto {p['variant']} vs main")
+    rows = band_rows(M)
+    assert_bits_equal(got[rows], reference(A, B, rows), f"{M}x{N}x{K} auto, sampled rows")
+
 @pytest.mark.parametrize("M,N,K,tile", [(1792, 1792, 1792, 1), (2048, 2048, 1024, 1),
                                         (2048, 2048, 2048, 14), (3072, 2048, 1024, 14),
                                         (2100, 2304, 2056, 14), (2100, 2300, 2056, 14),
