@@ -336,3 +336,27 @@ def test_auto_realign_split_plans(shape, variant):
     rows = band_rows(M, 128)
     assert_bits_equal(got[rows], reference(A, B, rows), f"realigned A {variant}, sampled rows")
     assert_bits_equal(got, _without_realign(a, b, M, N, K), f"realigned A {variant} vs A's own layout")
+
+
+def test_auto_realigns_a_bf16():
+    # The realigning pass moves 16-bit words, so bfloat16 takes it too.
+    M, N, K = 2085, 2056, 2051
+    A = synth.matrix(M, K, 16300, 0, "int", fmt="bf16")
+    B = synth.matrix(K, N, 16301, 1, "int", fmt="bf16")
+    a = _a_view(A, "odd_ld").view(torch.bfloat16)
+    b = to_dev(B).view(torch.bfloat16)
+    p = g.plan(a, b)
+    assert p["a_path"] == "packed", p
+    say(f"bf16 realigning plan {M}x{N}x{K}: {p}")
+    out = _out(M, N, "bf16")
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    rows = band_rows(M)
+    ref = oracle.gemm(np.ascontiguousarray(A[rows]), (K, 1), B, (N, 1), len(rows), N, K,
+                      nthreads=ORACLE_THREADS, dtype="bf16")
+    assert_bits_equal(got[rows], ref, "bf16 realigned A, sampled rows")
+    out2 = _out(M, N, "bf16")
+    g.gemm(a, b, out=out2.view, variant="main", tile=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(got, out2.result(), "bf16 realigned A vs the 128x128 tile on A's own layout")
