@@ -78,7 +78,9 @@ enum gemm_status {
  * 256x256 LDS-DMA tile (K-contiguous A; N-contiguous B with N % 8 == 0, or
  * K-contiguous B; every stride at most 2^23 elements); forcing it for other
  * layouts returns GEMM_ERR_OPTS.
- * AUTO picks it when the partial wave is at most half full and K >= 2048,
+ * AUTO picks SKINNY for M <= 64; SPLITK when the 128x128 tiles would fill
+ * at most half the compute units and K >= 2 max(M, N); otherwise MAIN, which
+ * becomes STREAMK when the partial wave is at most half full and K >= 2048,
  * and, with every tile in the tail, when all the 256x256 tiles together fill
  * less than half a wave, K >= 3072 and M, N >= 256. */
 enum gemm_variant {
