@@ -359,15 +359,20 @@ int launch_packed_product(int dt, const void* A, int64_t lda_m, int64_t lda_k, c
 // kernel's K-major 64-k stages have the same half-line DMA; a K-contiguous
 // FP8 B packs as 16-bit byte pairs (K even) or byte by byte.  (Its
 // N-contiguous B, read with the transposing LDS read, is as fast as the
-// packed stages, so the packing pass would only add time.)
+// packed stages, so the packing pass would only add time.)  A B the DMA
+// cannot read at all (any_b) is packed for MAIN and STREAMK plans from 1024
+// rows and for SPLITK plans on the 256 x 256 tile from 256 rows, their
+// partials after it.
 void maybe_pack(const Call& c, int variant, bool allow_pack, Plan& p, bool any_b) {
   const TileInfo& ti = tile_info(p.tile_id);
   const bool f8 = c.dt >= DT_F8;
   if (!allow_pack || variant != GEMM_VARIANT_AUTO || p.b_path != PATH_KVEC) return;
-  const bool family = p.variant == GEMM_VARIANT_STREAMK || (p.variant == GEMM_VARIANT_MAIN && p.split == 1);
+  const bool family = p.variant == GEMM_VARIANT_STREAMK || (p.variant == GEMM_VARIANT_MAIN && p.split == 1) ||
+                      (p.variant == GEMM_VARIANT_SPLITK && any_b);
   const bool kernels = ti.packed_fn[c.dt] && ti.packed_partial_fn[c.dt];
   const bool tile = f8 || (p.tile_id == TILE_DMA256A128 && c.K <= ti.max_k);
-  if (!family || !kernels || !tile || c.M < (any_b ? kPackMinRowsGather : kPackMinRows)) return;
+  const int64_t min_rows = !any_b ? kPackMinRows : (p.variant == GEMM_VARIANT_SPLITK ? 256 : kPackMinRowsGather);
+  if (!family || !kernels || !tile || c.M < min_rows) return;
   const size_t bytes = packed_b_bytes(f8 ? cdiv(c.K, 2) : c.K, c.N);
   if (bytes == 0 || p.ws > SIZE_MAX - bytes) return;
   p.pack = true;
@@ -468,8 +473,13 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   // with enough rows packs it instead (the packing pass reads any strides)
   // and is planned as for a K-contiguous B; if no packing plan comes of it,
   // the call is planned again with B's own path.
-  const bool pack_any = allow_pack && variant == GEMM_VARIANT_AUTO && !f8 && p.variant == GEMM_VARIANT_MAIN &&
-                        c.M >= kPackMinRowsGather && worth_packing(c) && p.a_path == PATH_KVEC &&
+  // Split-K plans pack it from the 256x256 tile's M, N >= 256 on: with
+  // K >> M the element-wise B loads cost far more than one pass over B
+  // (512 x 514 x 65536: 215 us on the element-wise plan).
+  const bool pack_any = allow_pack && variant == GEMM_VARIANT_AUTO && !f8 &&
+                        ((p.variant == GEMM_VARIANT_MAIN && c.M >= kPackMinRowsGather) ||
+                         (p.variant == GEMM_VARIANT_SPLITK && c.M >= 256 && c.N >= 256)) &&
+                        worth_packing(c) && p.a_path == PATH_KVEC &&
                         (p.b_path == PATH_GATHER || (p.b_path == PATH_RVEC && c.N % 8 != 0));
   if (pack_any) p.b_path = PATH_KVEC;
 

@@ -147,7 +147,8 @@ int gemm_f16(const void* A, int64_t lda_m, int64_t lda_k,
  * The same holds from M >= 1024 for a 16-bit B that the LDS-DMA tile cannot
  * read directly (rows not 16-byte aligned, or neither dimension contiguous),
  * which would otherwise take the element-wise path of the 128x128 tile: the
- * packing pass reads B through its strides.
+ * packing pass reads B through its strides.  SPLITK plans pack such a B
+ * from M, N >= 256, their partials after it.
  * Realigning plan (AUTO only, MAIN/SPLITK/STREAMK, N >= 256): a 16-bit A
  * that the LDS-DMA tile cannot read (rows not 16-byte aligned or not
  * K-contiguous; an M-contiguous A only from M*N*K >= 2^33) is first copied

@@ -360,3 +360,28 @@ def test_auto_realigns_a_bf16():
     g.gemm(a, b, out=out2.view, variant="main", tile=1)
     torch.cuda.synchronize()
     assert_bits_equal(got, out2.result(), "bf16 realigned A vs the 128x128 tile on A's own layout")
+
+
+@pytest.mark.parametrize("layout", ["row_unaligned", "strided"])
+def test_auto_split_k_packs_b_the_dma_tile_cannot_read(layout):
+    # K >> M, N: the split-K plan packs B for the 256 x 256 tile (its fp32
+    # partials after the packed B) rather than read it element by element.
+    # Integer sums stay exact in fp32 (|sum| < 2^24), so the packed plan, the
+    # element-wise plan and the oracle agree bit for bit.
+    M, N, K = (512, 515, 16384) if layout == "row_unaligned" else (520, 300, 12000)
+    A, B, a, b = _gather_b_case(M, N, K, 16400, layout)
+    p = g.plan(a, b)
+    assert (p["variant"], p["b_path"], p["tile_id"]) == ("splitk", "packed", 14), p
+    say(f"split-K packing plan, {layout} B {M}x{N}x{K}: {p}")
+    out = Out(M, N)
+    g.gemm(a, b, out=out.view)
+    torch.cuda.synchronize()
+    got = out.result()
+    rows = band_rows(M, 128)
+    assert_bits_equal(got[rows], reference(A, B, rows), f"split-K packing plan, {layout} B, sampled rows")
+    small = torch.full((max(256, g.workspace_bytes(M, N, K)) // 4 + 64,), float("nan"),
+                       dtype=torch.float32, device=DEV)
+    out2 = Out(M, N)
+    g.gemm(a, b, out=out2.view, workspace=small)
+    torch.cuda.synchronize()
+    assert_bits_equal(got, out2.result(), f"split-K packing plan vs element-wise plan, {layout} B")
