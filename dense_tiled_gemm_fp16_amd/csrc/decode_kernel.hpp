@@ -79,11 +79,13 @@ __device__ __forceinline__ u32x4 dec_load_a(const DecArgs& a, int64_t m, int64_t
 }
 
 // The k loop of one wave over its units (u = w, w + 4, ...) of [kb, ke).
-// FULL: every unit lies inside the range, the 8 columns of every lane are
-// inside N and A rows are 16-byte vectors, so the loads carry no masks and
-// no branches (rows of A past M are read from row 0 and zeroed); otherwise
-// each load is masked on its own.
-template <int MT, int DT, bool FULL, bool BK>
+// FULL: every unit lies inside the range and the 8 columns of every lane
+// are inside N, so the B loads carry no masks and no branches; otherwise
+// each load is masked on its own.  AVEC (with FULL): A rows are 16-byte
+// vectors, read unmasked (rows past M from row 0, then zeroed); without it
+// A is read element by element (M <= 64 rows, a small share of the bytes),
+// so an A with unaligned rows (K odd, say) keeps B's full-width loads.
+template <int MT, int DT, bool FULL, bool BK, bool AVEC = FULL>
 __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16][8], int w, int g, int c,
                                           int64_t kb, int64_t ke, const uint16_t* bcol, int nvalid,
                                           int64_t n0) {
@@ -104,7 +106,7 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
 #pragma unroll
       for (int fa = 0; fa < FA; ++fa) {
         const int64_t m = 16 * fa + c;
-        if constexpr (FULL) {
+        if constexpr (FULL && AVEC) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(a.A + (m < a.M ? m : 0) * a.lda_m + k0);
           av[i][fa] = (live && m < a.M) ? x : zero4();
         } else {
@@ -132,7 +134,9 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
           } else {
             const int64_t d = ke - k0;
             const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
-            bv[i][f] = (live && n < a.N && nk > 0) ? load_partial8(q, 1, nk) : zero4();
+            bv[i][f] = (live && n < a.N && nk > 0)
+                           ? (nk == 8 ? *reinterpret_cast<const u32x4*>(q) : load_partial8(q, 1, nk))
+                           : zero4();
           }
         }
       } else if constexpr (FULL) {
@@ -150,10 +154,19 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
             bv[i][j] = *q;
         }
       } else {
+        // Whole 8-column chunks load as one vector: the decode plan takes
+        // only 16-byte aligned B rows with ldb_k % 8 == 0 (and [N, K] rows
+        // with ldb_n % 8 == 0), so such a chunk is 16-byte aligned.  A
+        // ragged last K range with element loads ran 4x slower than the other
+        // ranges and held the whole launch (1 x 2048 x 7170: 22 us against
+        // 5.5 for K = 7168).
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          bv[i][j] = (live && nvalid > 0 && k0 + j < ke) ? load_partial8(bcol + (k0 + j) * a.ldb_k, 1, nvalid)
-                                                          : zero4();
+        for (int j = 0; j < 8; ++j) {
+          const uint16_t* q = bcol + (k0 + j) * a.ldb_k;
+          bv[i][j] = (live && nvalid > 0 && k0 + j < ke)
+                         ? (nvalid == 8 ? *reinterpret_cast<const u32x4*>(q) : load_partial8(q, 1, nvalid))
+                         : zero4();
+        }
       }
     }
 #pragma unroll
@@ -198,12 +211,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int f = 0; f < 8; ++f) acc[i][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Uniform per workgroup: whole strip inside N, whole units, vector A.
-  const bool full = (nb + 1) * kDecCols <= a.N && (ke - kb) % kDecUnit == 0 && a.a_vec;
-  if (full)
-    dec_units<MT, DT, true, BK>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
+  // Uniform per workgroup: whole strip inside N and whole units (and, for
+  // A's vector loads, 16-byte A rows).  An A with unaligned rows (1 x 2048
+  // x 7170) took 24.7 us per call with every load masked, against 15.3 for
+  // K = 7168.
+  const bool full = (nb + 1) * kDecCols <= a.N && (ke - kb) % kDecUnit == 0;
+  if (full && a.a_vec)
+    dec_units<MT, DT, true, BK, true>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
+  else if (full)
+    dec_units<MT, DT, true, BK, false>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
   else
-    dec_units<MT, DT, false, BK>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
+    dec_units<MT, DT, false, BK, false>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
 
   // Sum the waves in ascending order, 16 rows of A at a time; thread t < 256
   // then owns row t / 16 and the 8 columns 8 (t % 16) .. + 7 of the block.

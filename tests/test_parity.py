@@ -525,6 +525,7 @@ def test_decode_kernel_integer_exact(M, b_layout):
     for split in (0, 1, 3):
         _decode_case(M, 777, 128, "int", ldb_pad=7, split=split, b_layout=b_layout)
         _decode_case(M, 2048, 128, "int", split=split, b_layout=b_layout)
+        _decode_case(M, 2048, 130, "int", split=split, b_layout=b_layout)   # A rows not 16-byte aligned
         if b_layout == "col":
             _decode_case(M, 300, 133, "int", split=split, b_layout=b_layout)
 
