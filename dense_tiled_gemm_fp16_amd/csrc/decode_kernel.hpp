@@ -158,8 +158,8 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
         // only 16-byte aligned B rows with ldb_k % 8 == 0 (and [N, K] rows
         // with ldb_n % 8 == 0), so such a chunk is 16-byte aligned.  A
         // ragged last K range with element loads ran 4x slower than the other
-        // ranges and held the whole launch (1 x 2048 x 7170: 22 us against
-        // 5.5 for K = 7168).
+        // ranges and held the whole launch (1 x 2048 x 7170: 22.2 us of
+        // kernel time, now 8.0-8.8, against 5.4 for K = 7168).
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint16_t* q = bcol + (k0 + j) * a.ldb_k;
@@ -212,9 +212,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
     for (int f = 0; f < 8; ++f) acc[i][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Uniform per workgroup: whole strip inside N and whole units (and, for
-  // A's vector loads, 16-byte A rows).  An A with unaligned rows (1 x 2048
-  // x 7170) took 24.7 us per call with every load masked, against 15.3 for
-  // K = 7168.
+  // A's vector loads, 16-byte A rows): A rows that are not 16-byte aligned
+  // keep the unmasked B loads (1 x 2048 x 7168 with rows of 7170 halves:
+  // 5.5 us of kernel time, as for aligned rows).
   const bool full = (nb + 1) * kDecCols <= a.N && (ke - kb) % kDecUnit == 0;
   if (full && a.a_vec)
     dec_units<MT, DT, true, BK, true>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
