@@ -20,7 +20,7 @@ VARIANT_AUTO, VARIANT_MAIN, VARIANT_SKINNY, VARIANT_SPLITK, VARIANT_TILE64X32, V
 VARIANTS = {"auto": 0, "main": 1, "skinny": 2, "splitk": 3, "tile64x32": 4, "streamk": 5}
 PATHS = {0: "gather", 1: "kvec", 2: "rvec", 3: "packed"}
 
-EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_workspace_bytes",
+EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_plan_cus", "gemm_f16_workspace_bytes",
            "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_plan", "gemm_bf16_workspace_bytes",
            "gemm_f8", "gemm_f8_ex", "gemm_f8_plan", "gemm_f8_workspace_bytes",
            "gemm_f16_packed_b_bytes", "gemm_f16_pack_b", "gemm_f16_packed",
@@ -56,6 +56,9 @@ def _load():
     lib.gemm_f16_plan.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64,
                                   ctypes.POINTER(Opts), ctypes.POINTER(PlanInfo)]
     lib.gemm_f16_plan.restype = ctypes.c_int
+    lib.gemm_f16_plan_cus.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i32,
+                                      ctypes.POINTER(Opts), ctypes.POINTER(PlanInfo)]
+    lib.gemm_f16_plan_cus.restype = ctypes.c_int
     lib.gemm_f16_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(Opts)]
     lib.gemm_f16_workspace_bytes.restype = sz
     for pre in ("gemm_bf16",):

@@ -392,8 +392,10 @@ bool add_realign(const Call& c, Plan& p) {
 }
 
 // allow_pack: automatic plans may pack B; allow_realign: and realign A.
+// cus_given > 0: plan for that many compute units instead of asking the
+// current device.
 int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = true,
-              bool allow_realign = true) {
+              bool allow_realign = true, int cus_given = 0) {
   int rc = check_opts(o);
   if (rc) return rc;
   p.pack = false;
@@ -406,7 +408,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   const int want_panel = o ? o->panel : 0;
   const int want_tile = o ? o->tile : 0;
 
-  int cus = 0;
+  int cus = cus_given;
   auto need_cus = [&]() -> int {
     if (cus > 0) return GEMM_OK;
     return device_cus(&cus);
@@ -443,7 +445,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     } else {
       const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
       const int64_t mn = c.M > c.N ? c.M : c.N;
-      p.variant = (2 * T <= cus && c.K >= 2 * mn) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
+      // (K >= 1024: two K ranges of at least 512 on the 256x256 tile.)
+      p.variant = (2 * T <= cus && c.K >= 2 * mn && c.K >= 1024) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
     }
   }
 
@@ -622,8 +625,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       return GEMM_ERR_SHAPE;
     p.ws = (size_t)((bytes + 255) / 256 * 256);
     maybe_pack(c, variant, allow_pack, p, pack_any);
-    if (pack_any && !p.pack) return make_plan(c, o, p, false, allow_realign);
-    if (realign && !add_realign(c, p)) return make_plan(c, o, p, allow_pack, false);
+    if (pack_any && !p.pack) return make_plan(c, o, p, false, allow_realign, cus_given);
+    if (realign && !add_realign(c, p)) return make_plan(c, o, p, allow_pack, false, cus_given);
     return GEMM_OK;
   }
 
@@ -674,8 +677,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   if ((rc = plan_partials(c, p))) return rc;
 
   maybe_pack(c, variant, allow_pack, p, pack_any);
-  if (pack_any && !p.pack) return make_plan(c, o, p, false, allow_realign);
-  if (realign && !add_realign(c, p)) return make_plan(c, o, p, allow_pack, false);
+  if (pack_any && !p.pack) return make_plan(c, o, p, false, allow_realign, cus_given);
+  if (realign && !add_realign(c, p)) return make_plan(c, o, p, allow_pack, false, cus_given);
   return GEMM_OK;
 }
 
@@ -853,13 +856,13 @@ int launch(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
 
 int plan_impl(int dt, const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
               int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-              const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
+              const gemm_f16_opts* opts, gemm_f16_plan_info* info, int cus = 0) {
   Call c{dt, A, B, C, lda_m, lda_k, ldb_k, ldb_n, ldc, M, N, K, 0, 0, 0};
   int rc = validate(c);
   if (rc) return rc;
   if ((rc = spans(c))) return rc;
   Plan p;
-  if ((rc = make_plan(c, opts, p))) return rc;
+  if ((rc = make_plan(c, opts, p, true, true, cus))) return rc;
   if (info) fill_info(p, info);
   return GEMM_OK;
 }
@@ -1128,6 +1131,13 @@ int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, in
                   int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                   const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
   return plan_impl(DT_F16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info);
+}
+
+int gemm_f16_plan_cus(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                      int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                      int32_t cus, const gemm_f16_opts* opts, gemm_f16_plan_info* info) {
+  if (cus < 1 || cus > 65536) return GEMM_ERR_OPTS;
+  return plan_impl(DT_F16, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info, cus);
 }
 
 int gemm_f16_ex(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,

@@ -79,7 +79,7 @@ enum gemm_status {
  * K-contiguous B; every stride at most 2^23 elements); forcing it for other
  * layouts returns GEMM_ERR_OPTS.
  * AUTO picks SKINNY for M <= 64; SPLITK when the 128x128 tiles would fill
- * at most half the compute units and K >= 2 max(M, N); otherwise MAIN, which
+ * at most half the compute units, K >= 2 max(M, N) and K >= 1024; otherwise MAIN, which
  * becomes STREAMK when the partial wave is at most half full and K >= 2048,
  * and, with every tile in the tail, when all the 256x256 tiles together fill
  * less than half a wave, K >= 3072 and M, N >= 256. */
@@ -179,6 +179,20 @@ int gemm_f16_plan(const void* A, int64_t lda_m, int64_t lda_k,
                   const void* C, int64_t ldc,
                   int64_t M, int64_t N, int64_t K,
                   const gemm_f16_opts* opts, gemm_f16_plan_info* info);
+
+/*
+ * As gemm_f16_plan, for a device with `cus` compute units (1..65536, else
+ * GEMM_ERR_OPTS), without querying any device: the dispatch rules of
+ * TileLang tutorial ch. 14, sections 4.1-4.2 (split-K, stream-K) and the
+ * tile choice, as a host computation.  For planning ahead and for tests of
+ * the rules on hosts without a GPU.  The pointers are read for their
+ * alignment only.
+ */
+int gemm_f16_plan_cus(const void* A, int64_t lda_m, int64_t lda_k,
+                      const void* B, int64_t ldb_k, int64_t ldb_n,
+                      const void* C, int64_t ldc,
+                      int64_t M, int64_t N, int64_t K, int32_t cus,
+                      const gemm_f16_opts* opts, gemm_f16_plan_info* info);
 
 /* Workspace bytes gemm_f16_ex needs for this shape and these options
  * (0 when the plan has no K split).  Returns 0 for invalid arguments too. */
