@@ -32,7 +32,7 @@
 // lane's LDS slot is fixed by its lane id):
 //   A (and K-contiguous B): [rows][BK] row-major, 64 bytes per row; octet c of
 //     row r sits in slot c ^ fa(r).
-//   N-contiguous B: [BK][BN] row-major, 512 bytes per k-row; the 32-byte
+//   N-contiguous B: [BK][BN] row-major, 2 BN bytes per k-row; the 32-byte
 //     block b of row k sits at block b ^ hb(k).
 //
 // Edges: rows past M (A) or N (B) are loaded from the last valid row and the
@@ -45,9 +45,9 @@
 
 namespace gemmf16 {
 
-template <int STAGES_, int WAVES_M_ = 2, int WAVES_N_ = 2>
+template <int STAGES_, int WAVES_M_ = 2, int WAVES_N_ = 2, int BM_ = 256, int BN_ = 256>
 struct DmaCfg {
-  static constexpr int BM = 256, BN = 256, BK = 32, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
   static constexpr int MI = 32, KI = 16, KS = BK / KI;   // 2 MFMA k-steps per stage
@@ -62,6 +62,7 @@ struct DmaCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(DMA_A * NW * 1024 == A_BYTES && DMA_B * NW * 1024 == B_BYTES, "DMA split");
   static_assert(FN * FM >= 4, "DMA placement");
+  static_assert(BN == 128 || BN == 256, "N-major B k-rows of 256 or 512 bytes");
 };
 
 // octet slot permutation of the 64-byte rows: distinct banks for 8 and for 16
@@ -145,11 +146,13 @@ __device__ __forceinline__ f16x8 read_tr_pair(const char* p0, const char* p1) {
 //   KMAJOR: a K-contiguous operand (A, or B given as a transposed view):
 //     instruction i of wave w covers rows (4w + i) * 16 .. +16 of the tile;
 //     lane l -> row +l/4, slot l%4 -> octet (l%4) ^ fa(row).
-//   else (N-contiguous B): instruction i of wave w covers k-rows
-//     (4w + i) * 2 .. +2; lane l -> k-row +l/32, 16-byte slot l%32 ->
-//     32-byte block (slot/2) ^ hb(k), half slot%2.
-template <int NI, bool KMAJOR>
+//   else (N-contiguous B, k-rows of BN columns): instruction i of wave w
+//     covers the 1024 / (2 BN) k-rows from (NI w + i) * 1024 / (2 BN); lane l
+//     -> k-row + l / SPR, 16-byte slot l % SPR (SPR = BN / 8 slots per
+//     k-row) -> 32-byte block (slot/2) ^ hb(k), half slot%2.
+template <int NI, bool KMAJOR, int BN = 256>
 struct DmaSource {
+  static constexpr int SPR = BN / 8, KPI = 64 / SPR;   // slots per k-row, k-rows per instruction
   const uint16_t* p[NI];
   int64_t step;  // elements per BK step
 
@@ -164,8 +167,8 @@ struct DmaSource {
         if (rr > R_tot - 1) rr = R_tot - 1;
         p[i] = base + rr * s_r + (kb + 8 * c) * s_k;
       } else {
-        const int k = (NI * wave + i) * 2 + lane / 32;
-        const int slot = lane % 32;
+        const int k = (NI * wave + i) * KPI + lane / SPR;
+        const int slot = lane % SPR;
         const int b = (slot / 2) ^ hb(k);
         int64_t n = r0 + b * 16 + (slot % 2) * 8;
         if (n > R_tot - 8) n = R_tot - 8;   // whole chunk past N: any valid chunk
@@ -202,7 +205,7 @@ struct DmaSource {
         const int nk = d < 0 ? 0 : (d < 8 ? (int)d : 8);
         v = load_partial8(q, s_k, nk);
       } else {
-        const int k = (NI * wave + i) * 2 + lane / 32;
+        const int k = (NI * wave + i) * KPI + lane / SPR;
         const bool ok = kb + t * 32 + k < k_end;
         v = ok ? *reinterpret_cast<const u32x4*>(q) : zero4();
       }
@@ -237,13 +240,14 @@ __device__ __forceinline__ void read_frags(DmaFrags<CF>& f, const char* ta, cons
   } else {
     // 16-lane group g: columns +16*(g%2), k-octet g/2; source lane s reads
     // k-row 8*octet + s/4 (+4 for the second half), columns 4*(s%4)..+3.
+    constexpr int ROWB = 2 * CF::BN;   // bytes per k-row
     const int g = lane / 16, s = lane % 16;
     const int kr = ks * 16 + 8 * (g / 2) + s / 4;
 #pragma unroll
     for (int i = 0; i < CF::FN; ++i) {
       const int n = wn * CF::WTN + i * 32 + 16 * (g % 2);
-      const char* p0 = tb + kr * 512 + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
-      f.fa_[i] = read_tr_pair(p0, p0 + 4 * 512);
+      const char* p0 = tb + kr * ROWB + (((n >> 4) ^ hb(kr)) * 32) + 8 * (s % 4);
+      f.fa_[i] = read_tr_pair(p0, p0 + 4 * ROWB);
     }
   }
 }
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
   const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
 
   DmaSource<CF::DMA_A, true> sa;
-  DmaSource<CF::DMA_B, BKMAJOR> sb;
+  DmaSource<CF::DMA_B, BKMAJOR, CF::BN> sb;
   sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, kb, wave, lane);
   sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, kb, wave, lane);
 

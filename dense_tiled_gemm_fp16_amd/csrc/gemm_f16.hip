@@ -47,10 +47,10 @@ typedef void (*kfn_dec)(DecArgs);
 typedef void (*kfn_reduce)(const float*, int, int64_t, int64_t, uint16_t*, int64_t, int);
 
 const TileInfo& tile_info(int id) {
-  // Unused ids (0, 7 to 12) hold an empty entry: no kernels, nt == 0.
+  // Unused ids (0, 8 to 12) hold an empty entry: no kernels, nt == 0.
   static const TileInfo table[TILE_MAX + 1] = {
       TileInfo{},        tile_info_t128(), tile_info_t64x32(),    tile_info_s16(),
-      tile_info_s32(),   tile_info_s64(),  tile_info_t256(),      TileInfo{},
+      tile_info_s32(),   tile_info_s64(),  tile_info_t256(),      tile_info_dma128(),
       TileInfo{},        TileInfo{},       TileInfo{},            TileInfo{},
       TileInfo{},        tile_info_dma256w8b(), tile_info_dma256a128(), tile_info_f8()};
   return table[id];
@@ -494,23 +494,34 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       } else if (want_tile) {
         p.tile_id = want_tile;
       } else {
-        // 256x256 tiles once they give at least half a wave of workgroups,
-        // or, with a long K, when the stream-K plan below spreads fewer of
-        // them over the compute units (the layout permitting).  From a
-        // quarter wave on the DMA tile still wins where K is not short: a
-        // quarter-full wave of 256x256 tiles beat a full wave of 128x128
-        // ones by 8% at 2048^3 and by 20-24% at 81-100 tiles (2304^3,
-        // 2560^3); at 2048 x 2048 x 1024 the 128x128 plan was 5% ahead,
-        // while from 96 tiles on K = 1024 went to the big tile too.
+        // The 128x128 LDS-DMA tile (fp16, K-contiguous A, B either way with
+        // N % 8 == 0) up to 80 tiles of 256x256 (on 256 compute units): 1.3-1.4x
+        // the 128x128 register tile (1536^3: 20.4 against 28.0 us) and ahead of
+        // the 256x256 tile below a wave (2048^3: 28.2 against 38.1 us); from 81
+        // tiles on the 256x256 tile leads (2304^3: 41.9 against 43.8; 3072^3:
+        // 60.7 against 88.7).  A B to be packed (one the DMA cannot read) takes
+        // the 256x256 tile, the one with packed-B kernels.  Few tiles with a
+        // long K (K >= 4096, under three quarters of a wave of 128x128 tiles)
+        // keep the stream-K plan of the 256x256 tile below (1536^2 x 8192:
+        // 64.4 against 79.5 us); with more tiles or a shorter K the 128x128
+        // DMA tile is ahead of it (2048^2 x 4096: 49.0 against 56.1; 1536^2 x
+        // 3072: 34.6 against 38.6).  Without that tile: 256x256 tiles from a
+        // quarter wave on when K is not short, else the 128x128 register tile.
         if ((rc = need_cus())) return rc;
         const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
-        // A B to be packed (one the DMA cannot read) takes the big tile once
-        // N fills one: the 128x128 tile would read it element by element.
+        const bool t14 = dma_tile_takes(c, p);
+        const bool t7 = tile_takes(tile_info(TILE_DMA128), c, p);
+        const bool big = 16 * t256 >= 5 * (int64_t)cus;
+        const bool sk_small = small_grid_streamk(c, t256, cus) && 16 * t256 < 3 * (int64_t)cus && c.K >= 4096;
         const bool quarter = 4 * t256 >= cus && (c.K >= 2048 || 3 * t256 >= cus);
         const bool packed_b = pack_any && c.N >= 256;
-        p.tile_id = (2 * t256 >= cus ||
-                     ((quarter || packed_b || small_grid_streamk(c, t256, cus)) && dma_tile_takes(c, p)))
-                        ? TILE_DMA256A128 : TILE_T128;
+        if (t14 && (packed_b || big || sk_small))
+          p.tile_id = TILE_DMA256A128;
+        else if (t7 && !big)
+          p.tile_id = TILE_DMA128;
+        else
+          p.tile_id = (2 * t256 >= cus || ((quarter || small_grid_streamk(c, t256, cus)) && t14))
+                          ? TILE_DMA256A128 : TILE_T128;
       }
       break;
     case GEMM_VARIANT_SPLITK:

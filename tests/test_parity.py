@@ -51,7 +51,8 @@ VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"
             dict(variant="main", panel=1), dict(variant="main", tile=3),
             dict(variant="main", tile=6), dict(variant="splitk", tile=6, split_k=3),
             dict(variant="main", tile=13), dict(variant="splitk", tile=13, split_k=2),
-            dict(variant="main", tile=14), dict(variant="splitk", tile=14, split_k=3)]
+            dict(variant="main", tile=14), dict(variant="splitk", tile=14, split_k=3),
+            dict(variant="main", tile=7), dict(variant="splitk", tile=7, split_k=2)]
 
 
 # ------------------------------------------------------------------ the edge case
@@ -173,15 +174,16 @@ def test_auto_split_k_on_small_products(M, N, K, variant, split):
     rows = band_rows(M)
     assert_bits_equal(got[rows], reference(A, B, rows), f"{M}x{N}x{K} auto, sampled rows")
 
-@pytest.mark.parametrize("M,N,K,tile", [(1792, 1792, 1792, 1), (2048, 2048, 1024, 1),
-                                        (2048, 2048, 2048, 14), (3072, 2048, 1024, 14),
+@pytest.mark.parametrize("M,N,K,tile", [(1792, 1792, 1792, 7), (2048, 2048, 1024, 7),
+                                        (2048, 2048, 2048, 7), (3072, 2048, 1024, 14),
                                         (2100, 2304, 2056, 14), (2100, 2300, 2056, 14),
-                                        (1000, 4100, 2048, 1)])
-def test_main_tile_from_a_quarter_wave(M, N, K, tile):
-    # 256 x 256 tiles from a quarter wave (64 of them on 256 compute units)
-    # with K >= 2048, or from 86 at any K; below, the 128 x 128 tile.  A B
-    # whose rows are not 16-byte multiples (N = 2300, 4100) is packed for the
-    # big tile from M = 1024 on; below that it keeps the 128 x 128 tile.
+                                        (1000, 4100, 2048, 1), (1000, 2052, 2048, 1)])
+def test_main_tile_rule(M, N, K, tile):
+    # The 128 x 128 LDS-DMA tile below 80 tiles of 256 x 256 (on 256 compute
+    # units), the 256 x 256 tile from there on.  A B whose rows are not
+    # 16-byte multiples (N = 2300, 4100) is packed for the big tile from M =
+    # 1024 on; below that it keeps the 128 x 128 register tile, as does a B
+    # with N % 8 != 0 in 16-byte rows (N = 2052).
     # Integer inputs keep every fp32 sum exact, so the automatic plan and the
     # other tile give the same bits, which sampled rows check against the
     # oracle (the first and last rows and one in every 256-row band).
@@ -192,7 +194,7 @@ def test_main_tile_from_a_quarter_wave(M, N, K, tile):
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert (p["variant"], p["tile_id"]) == ("main", tile), p
     got = run(a, b)
-    other = run(a, b, variant="main", tile=1 if p["tile_id"] == 14 else 14)
+    other = run(a, b, variant="main", tile=1 if p["tile_id"] != 1 else 14)
     assert_bits_equal(got, other, f"{M}x{N}x{K} tile {p['tile_id']} against the other tile")
     rows = band_rows(M)
     assert_bits_equal(got[rows], reference(A, B, rows), f"{M}x{N}x{K} sampled rows")
@@ -200,7 +202,7 @@ def test_main_tile_from_a_quarter_wave(M, N, K, tile):
 
 # ------------------------------------------------------------------ LDS-DMA tiles, K remainders
 
-@pytest.mark.parametrize("tile", [13, 14])
+@pytest.mark.parametrize("tile", [7, 13, 14])
 @pytest.mark.parametrize("K", [32, 64, 96, 100, 160, 241])
 @pytest.mark.parametrize("b_layout", ["row", "col"])
 def test_dma_tiles_k_remainders(tile, K, b_layout):

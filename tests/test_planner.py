@@ -14,7 +14,7 @@ from dense_tiled_gemm_fp16_amd import _lib
 PA, PB, PC = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
 MAIN, SKINNY, SPLITK, STREAMK = 1, 2, 3, 5
 GATHER, KVEC, RVEC, PACKED = 0, 1, 2, 3
-T128, T256_DMA = 1, 14
+T128, T128_DMA, T256_DMA = 1, 7, 14
 
 
 def plan(M, N, K, lda=None, ldb=None, a="row", b="row", cus=256, A=PA, B=PB, opts=None):
@@ -43,19 +43,29 @@ def test_compute_unit_count_is_checked():
                                        ctypes.byref(info)) == -7
 
 
-@pytest.mark.parametrize("M,N,K,tile", [(2048, 2048, 2048, T256_DMA), (2304, 2304, 2304, T256_DMA),
-                                        (3072, 2048, 1024, T256_DMA), (2048, 2048, 1024, T128),
-                                        (1792, 1792, 1792, T128), (1536, 1536, 1536, T128),
-                                        (4096, 4096, 4096, T256_DMA)])
-def test_main_tile_from_a_quarter_wave(M, N, K, tile):
+@pytest.mark.parametrize("M,N,K,tile", [(2048, 2048, 2048, T128_DMA), (2304, 2304, 2304, T256_DMA),
+                                        (3072, 2048, 1024, T256_DMA), (2048, 2048, 1024, T128_DMA),
+                                        (1792, 1792, 1792, T128_DMA), (1536, 1536, 1536, T128_DMA),
+                                        (1024, 1024, 1024, T128_DMA), (4096, 4096, 4096, T256_DMA),
+                                        (2048, 2048, 4096, T128_DMA), (1536, 1536, 3072, T128_DMA)])
+def test_main_tile_rule(M, N, K, tile):
+    # The 128x128 LDS-DMA tile below 80 tiles of 256x256, the 256x256 tile
+    # from there on (256 compute units).
     p = plan(M, N, K)
     assert (p.variant, p.tile_id, p.split_k) == (MAIN, tile, 1)
 
 
 def test_tile_rule_scales_with_the_compute_units():
-    # 64 tiles of 256 x 256 are half a wave on 128 compute units.
-    assert plan(2048, 2048, 1024, cus=256).tile_id == T128
+    # 64 tiles of 256 x 256: under 80 on 256 compute units, past 40 on 128.
+    assert plan(2048, 2048, 1024, cus=256).tile_id == T128_DMA
     assert plan(2048, 2048, 1024, cus=128).tile_id == T256_DMA
+
+
+def test_layouts_the_128x128_dma_tile_does_not_take():
+    # An N-contiguous B needs N % 8 == 0 on the DMA tiles: the register tile
+    # takes it (16-byte rows of 2056 halves holding N = 2052).
+    p = plan(1000, 2052, 2048, ldb=2056)
+    assert (p.tile_id, p.b_path) == (T128, RVEC)
 
 
 @pytest.mark.parametrize("M,N,K,variant,split", [(1024, 1024, 2048, SPLITK, 4), (768, 768, 2048, SPLITK, 4),
