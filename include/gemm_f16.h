@@ -103,6 +103,23 @@ typedef struct gemm_f16_opts {
   int32_t tile;    /* main-kernel tile id (0 = choose; see gemm_f16_plan_info)   */
 } gemm_f16_opts;
 
+/* Tile ids (gemm_f16_opts.tile, gemm_f16_plan_info.tile_id):
+ *   1  128x128x64 register path (every layout; fp16 and bfloat16)
+ *   2  64x32x32, the pages' Triton geometry (forced only; fp16)
+ *   3, 4, 5  skinny 16, 32 and 64-row tiles (SKINNY; 3 is also reported
+ *      for the decode kernel)
+ *   6  256x256 register path (fp16; where tile 13 cannot read the layout)
+ *   7  128x128 LDS-DMA, 4-stage ring (fp16; K-contiguous A, B either way
+ *      with N % 8 == 0 when B is N-contiguous)
+ *   13 256x256 LDS-DMA, 4-stage ring (fp16; the same layouts, any stride)
+ *   14 256x256 LDS-DMA with 128-byte A rows (fp16, bfloat16; the same
+ *      layouts, strides up to 2^23 elements)
+ *   15 256x256 FP8 (the FP8 entry points only)
+ * A tile that does not take the operand layout hands over to the next one
+ * that does: fp16 along 7 -> 1 and 14 -> 13 -> 6, bfloat16 straight to 1.
+ * Forcing an id without kernels for the call's format returns
+ * GEMM_ERR_OPTS. */
+
 typedef struct gemm_f16_plan_info {
   int32_t variant;          /* the family that runs (never AUTO)                 */
   int32_t tile_m, tile_n, tile_k; /* workgroup tile                              */
