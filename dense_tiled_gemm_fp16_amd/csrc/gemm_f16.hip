@@ -227,6 +227,15 @@ bool tile_takes(const TileInfo& t, const Call& c, const Plan& p) {
 
 bool dma_tile_takes(const Call& c, const Plan& p) { return tile_takes(tile_info(TILE_DMA256A128), c, p); }
 
+// Whether the 128x128 LDS-DMA tile reads the operands as they lie (fp16,
+// K-contiguous A, B either way with N % 8 == 0 when N-contiguous).
+bool dma128_reads(const Call& c) {
+  Plan q{};
+  q.a_path = classify(c.A, c.lda_m, c.lda_k);
+  q.b_path = classify(c.B, c.ldb_n, c.ldb_k);
+  return tile_takes(tile_info(TILE_DMA128), c, q);
+}
+
 constexpr int64_t kPackMinRows = 16384;   // automatic plans pack a K-contiguous B from this M on
 constexpr int64_t kPackMinRowsGather = 1024;   // and a B the DMA tile cannot read from this M on
 constexpr int32_t kBPathPacked = 3;       // a_path / b_path reported for a packed operand
@@ -445,8 +454,16 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     } else {
       const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
       const int64_t mn = c.M > c.N ? c.M : c.N;
-      // (K >= 1024: two K ranges of at least 512 on the 256x256 tile.)
-      p.variant = (2 * T <= cus && c.K >= 2 * mn && c.K >= 1024) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
+      // Split-K when the 128x128 tiles fill at most half the compute units.
+      // On the 128x128 LDS-DMA tile from K >= 2048: below it the main plan
+      // was ahead (1024^3: 13.6 us against 16.8 with 2 ranges; 768^2 x 1024
+      // 13.4 against 15.3), from it on the split was (1024^2 x 2048: 18.5
+      // against 23.7; 128 x 2048 x 2048 15.4 against 20.8; 96 x 8192 x 8192
+      // 31.1 against 72.0; 1024 x 2048 x 2048 level).  For operands that
+      // tile does not read, from K >= 2 max(M, N) and K >= 1024 (two K
+      // ranges of at least 512 on the 256x256 tile).
+      const bool split = dma128_reads(c) ? c.K >= 2048 : (c.K >= 2 * mn && c.K >= 1024);
+      p.variant = (2 * T <= cus && split) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
     }
   }
 
@@ -503,16 +520,18 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         // the 256x256 tile, the one with packed-B kernels.  Few tiles with a
         // long K (K >= 4096, under three quarters of a wave of 128x128 tiles)
         // keep the stream-K plan of the 256x256 tile below (1536^2 x 8192:
-        // 64.4 against 79.5 us); with more tiles or a shorter K the 128x128
-        // DMA tile is ahead of it (2048^2 x 4096: 49.0 against 56.1; 1536^2 x
-        // 3072: 34.6 against 38.6).  Without that tile: 256x256 tiles from a
+        // 64.4 against 79.5 us), and so does any grid under half a wave with
+        // K >= 8192 (2048^2 x 8192: 86.5 against 89.9; x 16384: 140.8 against
+        // 166.4; 1792^2 x 8192: 74.1 against 86.2); with a shorter K the
+        // 128x128 DMA tile is ahead of it (2048^2 x 4096: 49.0 against 56.1;
+        // 2048^2 x 6144: 70.9 against 73.3; 1536^2 x 3072: 34.6 against 38.6).  Without that tile: 256x256 tiles from a
         // quarter wave on when K is not short, else the 128x128 register tile.
         if ((rc = need_cus())) return rc;
         const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
         const bool t14 = dma_tile_takes(c, p);
         const bool t7 = tile_takes(tile_info(TILE_DMA128), c, p);
         const bool big = 16 * t256 >= 5 * (int64_t)cus;
-        const bool sk_small = small_grid_streamk(c, t256, cus) && 16 * t256 < 3 * (int64_t)cus && c.K >= 4096;
+        const bool sk_small = small_grid_streamk(c, t256, cus) && (16 * t256 < 3 * (int64_t)cus ? c.K >= 4096 : c.K >= 8192);
         const bool quarter = 4 * t256 >= cus && (c.K >= 2048 || 3 * t256 >= cus);
         const bool packed_b = pack_any && c.N >= 256;
         if (t14 && (packed_b || big || sk_small))
@@ -524,12 +543,35 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
                           ? TILE_DMA256A128 : TILE_T128;
       }
       break;
-    case GEMM_VARIANT_SPLITK:
-      // The 256x256 full-line-A tile once the output holds a whole one (it
+    case GEMM_VARIANT_SPLITK: {
+      // The 128x128 LDS-DMA tile where it reads the operands (a realigned A
+      // included; a B to be packed needs the 256x256 tile's packed-B
+      // kernels) and its K ranges, one workgroup per compute unit, come to
+      // at most 2048 k: 1024^2 x 4096 in 24.1 us against 30.5 on the 256x256
+      // tile, 256^2 x 16384 16.5 against 22.9, 1024^2 x 8192 36.1 against
+      // 40.7, and 128 x 4096 x 8192 23.7 against 31.0 on the 128x128
+      // register tile.  Longer ranges repay the 256x256 tile's larger
+      // partials (512^2 x 65536: 52.9 against 61.0; 768^2 x 32768: 58.9
+      // against 70.4; 1024 x 2048 x 8192: 54.5 against 65.0).  Otherwise
+      // the 256x256 full-line-A tile once the output holds a whole one (it
       // falls back to 128x128 for layouts it does not take).
-      p.tile_id = f8 ? TILE_F8
-                     : (want_tile ? want_tile : ((c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128));
+      bool dma128 = false;
+      if (!f8 && !want_tile && !pack_any && tile_takes(tile_info(TILE_DMA128), c, p)) {
+        if ((rc = need_cus())) return rc;
+        const int64_t t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
+        const int64_t s7 = std::min<int64_t>((int64_t)cus / t128, c.K / 512);
+        dma128 = c.M < 256 || c.N < 256 || (s7 >= 1 && c.K <= 2048 * s7);
+      }
+      if (f8)
+        p.tile_id = TILE_F8;
+      else if (want_tile)
+        p.tile_id = want_tile;
+      else if (dma128)
+        p.tile_id = TILE_DMA128;
+      else
+        p.tile_id = (c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128;
       break;
+    }
     case GEMM_VARIANT_STREAMK:
       if (!f8 && want_tile && want_tile != TILE_DMA256A128) return GEMM_ERR_OPTS;
       p.tile_id = f8 ? TILE_F8 : TILE_DMA256A128;
@@ -653,15 +695,28 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       // workgroup (512 x 512 x 65536: 51 us at 160 workgroups against 54 at
       // 128 and 57 at 256).  Split counts of 8 or more are rounded up to a
       // multiple of 8 so the launch can keep each K range's tiles on one XCD.
+      // The 128x128 LDS-DMA tile: one workgroup per compute unit, rounded
+      // down (1024^2 x 2048: 18.5 us with 4 ranges against 27.5 with 8;
+      // 256 x 1024 x 4096: 16.3 with 8 against 19.4 with 16).
+      const bool dma128 = p.tile_id == TILE_DMA128 && p.variant == GEMM_VARIANT_SPLITK;
       const int64_t per_cu8 = p.variant == GEMM_VARIANT_SKINNY ? 8 : (ti.bm >= 256 ? 5 : 16);
-      s = cdiv(per_cu8 * (int64_t)cus, 8 * T);
-      // On the 256x256 tiles, K ranges of at least 512 k: at smaller K more,
+      s = dma128 ? cus / T : cdiv(per_cu8 * (int64_t)cus, 8 * T);
+      // Two per compute unit while the K ranges stay at least 2048 k long
+      // (M or N under 256): its 64 KiB ring lets two workgroups share a
+      // compute unit, and over a long range the second hides the first
+      // one's waits (1024^2 x 16384: 51.9 us with 8 ranges against 62.7
+      // with 4; 1024^2 x 8192: 35.4 with 8, 36.1 with 4).
+      if (dma128 && s >= 1 && c.K / s >= 4096) s *= 2;
+      // On the LDS-DMA tiles, K ranges of at least 512 k: at smaller K more,
       // shorter ranges cost more in partials and per-workgroup start-up than
       // the extra compute units give (1024 x 1024 x 4096: 29.0 us with 8
-      // ranges against 33.4 with 16; 1024 x 1024 x 2048: 23.8 with 4).
-      if (p.variant == GEMM_VARIANT_SPLITK && ti.bm >= 256 && s > c.K / 512) s = c.K / 512 > 1 ? c.K / 512 : 1;
+      // ranges against 33.4 with 16 on the 256x256 tile; 1024 x 1024 x 2048:
+      // 23.8 with 4).
+      if (p.variant == GEMM_VARIANT_SPLITK && (ti.bm >= 256 || dma128) && s > c.K / 512)
+        s = c.K / 512 > 1 ? c.K / 512 : 1;
+      if (s < 1) s = 1;
       const int64_t max_by_k = cdiv(c.K, 2 * ti.bk);  // at least two K steps per split
-      if (s >= 8) s = cdiv(s, 8) * 8;
+      if (s >= 8) s = dma128 ? s / 8 * 8 : cdiv(s, 8) * 8;
       if (s > max_by_k) s = max_by_k;
       if (s > 64) s = 64;
     }

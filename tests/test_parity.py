@@ -157,12 +157,15 @@ def test_square_full_coverage(n):
 
 
 @pytest.mark.parametrize("M,N,K,variant,split", [(1024, 1024, 2048, "splitk", 4), (768, 768, 2048, "splitk", 4),
-                                                 (1024, 1024, 4096, "splitk", 8), (1024, 1024, 1024, "main", 1)])
+                                                 (1024, 1024, 4096, "splitk", 4), (1024, 1024, 1024, "main", 1),
+                                                 (96, 8192, 8192, "splitk", 4), (200, 2048, 8192, "splitk", 8),
+                                                 (256, 256, 16384, "splitk", 32), (128, 128, 65536, "splitk", 64)])
 def test_auto_split_k_on_small_products(M, N, K, variant, split):
-    # Split-K from K = 2 max(M, N) while the 128 x 128 tiles fill at most
-    # half the compute units, with K ranges of at least 512 k on the
-    # 256 x 256 tile.  Integer inputs keep every sum exact, so the split plan
-    # gives the main plan's bits, and sampled rows the oracle's.
+    # Split-K on the 128 x 128 LDS-DMA tile from K = 2048 while the 128 x
+    # 128 tiles fill at most half the compute units: one workgroup per
+    # compute unit, K ranges of at least 512 k.  Integer inputs keep every
+    # sum exact, so the split plan gives the main plan's bits, and sampled
+    # rows the oracle's.
     A = synth.matrix(M, K, 2700 + M, 0, "int")
     B = synth.matrix(K, N, 2700 + K, 1, "int")
     a, b = to_dev(A), to_dev(B)

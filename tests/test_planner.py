@@ -68,18 +68,44 @@ def test_layouts_the_128x128_dma_tile_does_not_take():
     assert (p.tile_id, p.b_path) == (T128, RVEC)
 
 
-@pytest.mark.parametrize("M,N,K,variant,split", [(1024, 1024, 2048, SPLITK, 4), (768, 768, 2048, SPLITK, 4),
-                                                 (1024, 1024, 4096, SPLITK, 8), (512, 512, 65536, SPLITK, 40),
-                                                 (512, 512, 2048, SPLITK, 4), (1024, 1024, 1024, MAIN, 1),
-                                                 (1024, 1024, 1536, MAIN, 1), (300, 256, 1001, MAIN, 1),
-                                                 (256, 256, 768, MAIN, 1)])
-def test_split_k_rule(M, N, K, variant, split):
+@pytest.mark.parametrize("M,N,K,variant,split,tile", [
+    (1024, 1024, 2048, SPLITK, 4, T128_DMA), (768, 768, 2048, SPLITK, 4, T128_DMA),
+    (1024, 1024, 4096, SPLITK, 4, T128_DMA), (512, 512, 2048, SPLITK, 4, T128_DMA),
+    (1024, 2048, 2048, SPLITK, 2, T128_DMA), (1024, 1024, 8192, SPLITK, 4, T128_DMA),
+    (96, 8192, 8192, SPLITK, 4, T128_DMA), (128, 4096, 8192, SPLITK, 8, T128_DMA),
+    (128, 128, 65536, SPLITK, 64, T128_DMA), (256, 256, 16384, SPLITK, 32, T128_DMA),
+    (200, 4096, 32768, SPLITK, 8, T128_DMA),      # M < 256, ranges of 8192 k: two per compute unit
+    (512, 512, 65536, SPLITK, 40, T256_DMA),      # ranges of 4096 k and more: the 256x256 tile
+    (1024, 1024, 16384, SPLITK, 16, T256_DMA), (1024, 2048, 8192, SPLITK, 5, T256_DMA),
+    (1024, 1024, 1024, MAIN, 1, T128_DMA), (1024, 1024, 1536, MAIN, 1, T128_DMA),
+    (512, 512, 1024, MAIN, 1, T128_DMA), (256, 256, 768, MAIN, 1, T128_DMA),
+    (2048, 1024, 1024, MAIN, 1, T128_DMA)])
+def test_split_k_rule(M, N, K, variant, split, tile):
+    # Operands the 128x128 LDS-DMA tile reads: split-K from K >= 2048 while
+    # the 128x128 tiles fill at most half the compute units.  On that tile
+    # while its K ranges, one workgroup per compute unit, stay within 2048 k
+    # (always with M or N under 256, then two per compute unit once the
+    # ranges reach 4096 k); K ranges of at least 512 k.  Longer ranges run
+    # on the 256x256 tile, five eighths of a workgroup per compute unit.
     p = plan(M, N, K)
-    assert (p.variant, p.split_k) == (variant, split)
+    assert (p.variant, p.split_k, p.tile_id) == (variant, split, tile)
     if variant == SPLITK:
-        assert p.tile_id == T256_DMA and p.workspace_bytes == split * M * N * 4
+        assert p.workspace_bytes == split * M * N * 4 and p.grid <= 512
         # split counts of 8 or more keep each K range's tiles on one XCD
         assert split < 8 or split % 8 == 0
+
+
+def test_split_k_rule_for_operands_the_dma_tiles_do_not_read():
+    # A with unaligned rows (and N < 256: no realigning copy): split-K from
+    # K >= 2 max(M, N), two workgroups per compute unit on the register tile.
+    p = plan(512, 200, 2048, lda=2049)
+    assert (p.variant, p.tile_id, p.split_k, p.a_path) == (SPLITK, T128, 16, GATHER)
+    p = plan(512, 200, 1000, lda=1001)
+    assert (p.variant, p.tile_id) == (MAIN, T128)
+    # With N >= 256 the same A is realigned, and the split runs on the
+    # 128x128 LDS-DMA tile.
+    p = plan(1024, 1024, 2048, lda=2049)
+    assert (p.variant, p.tile_id, p.split_k, p.a_path) == (SPLITK, T128_DMA, 4, PACKED)
 
 
 def test_split_k_512x512x65536_grid():
@@ -96,6 +122,10 @@ def test_stream_k_rules():
     assert (p.variant, p.sk_tiles) == (MAIN, 0)
     p = plan(1536, 1536, 8192)                  # 36 tiles under half a wave, long K: all tiles
     assert (p.variant, p.sk_tiles, p.grid) == (STREAMK, 36, 0)
+    p = plan(2048, 2048, 8192)                  # 64 tiles: all in the tail from K = 8192
+    assert (p.variant, p.sk_tiles, p.grid) == (STREAMK, 64, 0)
+    p = plan(2048, 2048, 6144)                  # below: the 128x128 LDS-DMA tile
+    assert (p.variant, p.tile_id) == (MAIN, T128_DMA)
     p = plan(131072, 2048, 7168)                # 16 whole waves
     assert (p.variant, p.tile_id, p.sk_tiles) == (MAIN, T256_DMA, 0)
 

@@ -179,11 +179,13 @@ def run(a, b, M, N, what, **kw):
 MAIN_PLANS = [
     ("dma256 tile 14", dict(variant="main", tile=14)),
     ("dma256 tile 13", dict(variant="main", tile=13)),
+    ("dma128 tile 7", dict(variant="main", tile=7)),
     ("register 256", dict(variant="main", tile=6)),
     ("register 128", dict(variant="main", tile=1)),
     ("64x32x32", dict(variant="tile64x32")),
     ("split-K 256 x3", dict(variant="splitk", tile=14, split_k=3)),
     ("split-K 128 x5", dict(variant="splitk", tile=1, split_k=5)),
+    ("split-K dma128 x3", dict(variant="splitk", tile=7, split_k=3)),
     ("stream-K x3", dict(variant="streamk", split_k=3)),
     ("auto", dict(variant="auto")),
 ]

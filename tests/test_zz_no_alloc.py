@@ -64,8 +64,8 @@ def test_noalloc_two_calls_then_smaller(mode):
 
 
 def test_noalloc_refuses_a_plan_beyond_the_scratch():
-    M = N = 768
-    K = 65536
+    M = N = 2048                 # stream-K, all 64 tiles in 4 K ranges: 64 MiB of partials
+    K = 8192
     a = torch.zeros((M, K), dtype=torch.float16, device="cuda:0")
     b = torch.zeros((K, N), dtype=torch.float16, device="cuda:0")
     p = g.plan(a, b)
