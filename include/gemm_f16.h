@@ -79,10 +79,14 @@ enum gemm_status {
  * K-contiguous B; every stride at most 2^23 elements); forcing it for other
  * layouts returns GEMM_ERR_OPTS.
  * AUTO picks SKINNY for M <= 64; SPLITK when the 128x128 tiles would fill
- * at most half the compute units, K >= 2 max(M, N) and K >= 1024; otherwise MAIN, which
- * becomes STREAMK when the partial wave is at most half full and K >= 2048,
- * and, with every tile in the tail, when all the 256x256 tiles together fill
- * less than half a wave, K >= 3072 and M, N >= 256. */
+ * at most half the compute units and K >= 2048 (fp16 operands the 128x128
+ * LDS-DMA tile reads as they lie), or K >= 2 max(M, N) and K >= 1024 (any
+ * other operands); otherwise MAIN, which becomes STREAMK when the partial
+ * wave is at most half full and K >= 2048, and, with every tile in the
+ * tail, when all the 256x256 tiles together fill less than half a wave with
+ * M, N >= 256 and K long enough: K >= 4096 under 3/16 of a wave, K >= 8192
+ * from 3/16 to 5/16, K >= 3072 from 5/16 on or where the 128x128 LDS-DMA
+ * tile does not take the call. */
 enum gemm_variant {
   GEMM_VARIANT_AUTO = 0,    /* choose from the shape (the default)                */
   GEMM_VARIANT_MAIN = 1,    /* one workgroup per output tile, whole K            */
