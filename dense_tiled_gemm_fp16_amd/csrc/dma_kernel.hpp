@@ -50,6 +50,9 @@ struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
+  // Waves per SIMD the register budget must allow: two for the 4-wave
+  // 128x128 tile, so that two workgroups share a compute unit.
+  static constexpr int WPE = (NW == 4 && BM == 128) ? 2 : 1;
   static constexpr int MI = 32, KI = 16, KS = BK / KI;   // 2 MFMA k-steps per stage
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -255,7 +258,7 @@ __device__ __forceinline__ void read_frags(DmaFrags<CF>& f, const char* ta, cons
 // The MFMAs of one k-step with this wave's DMA batches of the step
 // STAGES-1 ahead placed a quarter and three quarters of the way through, so
 // their address and m0 setup issue in the shadow of matrix work.
-template <class CF, class SA, class SB>
+template <class CF, int DT, class SA, class SB>
 __device__ __forceinline__ void mma_frags_dma(const DmaFrags<CF>& f, f32x16 (&acc)[CF::FN][CF::FM],
                                               SA& sa, SB& sb, uint32_t la, uint32_t lb,
                                               int64_t t) {
@@ -264,7 +267,7 @@ __device__ __forceinline__ void mma_frags_dma(const DmaFrags<CF>& f, f32x16 (&ac
   for (int i = 0; i < CF::FN; ++i)
 #pragma unroll
     for (int j = 0; j < CF::FM; ++j) {
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.fa_[i], f.fb_[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
       const int q = i * CF::FM + j;
       if (q == NQ / 4 - 1) sa.issue_batch(la, t);
       if (q == 3 * NQ / 4 - 1) sb.issue_batch(lb, t);
@@ -279,8 +282,9 @@ __device__ __forceinline__ void mma_frags(const DmaFrags<CF>& f, f32x16 (&acc)[C
     for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
 }
 
-template <class CF, bool BKMAJOR, bool PARTIAL>
-__global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
+// DT: DT_F16 or DT_BF16 operands and output.
+template <class CF, bool BKMAJOR, bool PARTIAL, int DT = DT_F16>
+__global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE))) void gemm_dma_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -342,13 +346,13 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
           __builtin_amdgcn_readfirstlane(lds_addr(stage_b(ahead)) + CF::DMA_B * wave * 1024);
       read_frags<CF, BKMAJOR>(f1, stage_a(t), stage_b(t), 1, wm, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mma_frags_dma<CF>(f0, acc, sa, sb, la, lb, tt);
+      mma_frags_dma<CF, DT>(f0, acc, sa, sb, la, lb, tt);
       __builtin_amdgcn_sched_barrier(0);
       // First fragments of step t+1 (complete since the last barrier).  On
       // the last step this reads a stale stage and the values go unused.
       read_frags<CF, BKMAJOR>(f0, stage_a(t + 1), stage_b(t + 1), 0, wm, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mma_frags<CF>(f1, acc);
+      mma_frags<CF, DT>(f1, acc);
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<CF::DMA_PER_STAGE * (CF::STAGES - 3)>();   // step t+2 landed
       wg_barrier();
@@ -363,8 +367,8 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
     __syncthreads();
     read_frags<CF, BKMAJOR>(f0, stage_a(nfull), stage_b(nfull), 0, wm, wn, lane);
     read_frags<CF, BKMAJOR>(f1, stage_a(nfull), stage_b(nfull), 1, wm, wn, lane);
-    mma_frags<CF>(f0, acc);
-    mma_frags<CF>(f1, acc);
+    mma_frags<CF, DT>(f0, acc);
+    mma_frags<CF, DT>(f1, acc);
   }
 
   // Epilogue: the same C^T-block layout as the register-staged kernel.
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
         if constexpr (PARTIAL)
           store4_f32(a, split, m, n, v0, v1, v2, v3);
         else
-          store4_out<DT_F16>(a, m, n, v0, v1, v2, v3);
+          store4_out<DT>(a, m, n, v0, v1, v2, v3);
       }
     }
 }

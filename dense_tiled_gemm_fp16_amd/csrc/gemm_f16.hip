@@ -1046,7 +1046,10 @@ int validate_grouped(GroupCall& c) {
 
 // The tile and kernel of a grouped launch: the full-line-A LDS-DMA tile when
 // the groups average at least one of its 256-row tiles and the layouts suit
-// it, the 128 x 128 register-path tile otherwise.
+// it, the 128 x 128 register-path tile otherwise.  (The 128 x 128 LDS-DMA
+// tile, ahead below a wave of tiles, fell behind it over the many waves of
+// a grouped launch: G = 128 groups of 128 rows, N = 2048, K = 7168 in 948 us
+// against 809.)
 int grouped_plan(const GroupCall& c, int* tile_id, kfn_t* fn, int64_t* grid) {
   if (c.dt >= DT_F8) {   // the FP8 tile, whatever the group sizes
     const TileInfo& ti = tile_info(TILE_F8);

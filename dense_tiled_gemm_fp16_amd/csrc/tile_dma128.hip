@@ -2,5 +2,5 @@
 #include "tiles.hpp"
 
 namespace gemmf16 {
-TileInfo tile_info_dma128() { return make_dma_info<CfgDma128>(TILE_DMA128, TILE_T128); }
+TileInfo tile_info_dma128() { return make_dma_info<CfgDma128, true>(TILE_DMA128, TILE_T128); }
 }  // namespace gemmf16

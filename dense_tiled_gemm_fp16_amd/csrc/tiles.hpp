@@ -91,8 +91,9 @@ TileInfo make_info(int id) {
   return t;
 }
 
-// The LDS-DMA kernel takes K-contiguous A with K- or N-contiguous B only.
-template <class CF>
+// The LDS-DMA kernel takes K-contiguous A with K- or N-contiguous B only;
+// bfloat16 where asked.
+template <class CF, bool WITH_BF16 = false>
 TileInfo make_dma_info(int id, int fallback) {
   TileInfo t;
   t.id = id;
@@ -105,6 +106,12 @@ TileInfo make_dma_info(int id, int fallback) {
   t.final_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false>;
   t.partial_fn[DT_F16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true>;
   t.partial_fn[DT_F16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, true>;
+  if constexpr (WITH_BF16) {
+    t.final_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, false, DT_BF16>;
+    t.final_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false, DT_BF16>;
+    t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true, DT_BF16>;
+    t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, true, DT_BF16>;
+  }
   t.fallback = fallback;
   t.n_mult = 8;
   return t;

@@ -52,11 +52,14 @@ def check_groups(got, ref, offsets, mode, what):
 
 @pytest.mark.parametrize("mode", ["int", "uniform"])
 @pytest.mark.parametrize("b_layout", ["row", "col"])
-@pytest.mark.parametrize("case", ["small_groups", "large_groups"])
+@pytest.mark.parametrize("case", ["small_groups", "mid_groups", "large_groups"])
 def test_grouped_parity(mode, b_layout, case):
     if case == "small_groups":      # 128 x 128 register-path tile
         sizes = np.array([0, 37, 130, 0, 1, 64, 255, 3])
         K, N = 100, 70
+    elif case == "mid_groups":      # the same tile, with whole 16-byte B rows (N = 264)
+        sizes = np.array([0, 37, 130, 0, 1, 64, 255, 3, 200])
+        K, N = 160, 264
     else:                           # 256 x 256 LDS-DMA tile (groups average >= 256 rows)
         sizes = np.array([300, 0, 700, 517])
         K, N = 160, 264
@@ -127,11 +130,13 @@ def test_grouped_moe_shape_sampled():
 
 
 @pytest.mark.parametrize("mode", ["int", "uniform"])
-@pytest.mark.parametrize("case", ["small_groups", "large_groups"])
+@pytest.mark.parametrize("case", ["small_groups", "mid_groups", "large_groups"])
 def test_grouped_bf16_parity(mode, case):
     # gemm_bf16_grouped: the same launches with bfloat16 A, B and C.
     if case == "small_groups":
         sizes, K, N = np.array([0, 37, 130, 0, 1, 64, 255, 3]), 100, 70
+    elif case == "mid_groups":
+        sizes, K, N = np.array([0, 37, 130, 0, 1, 64, 255, 3, 200]), 160, 264
     else:
         sizes, K, N = np.array([300, 0, 700, 517]), 160, 264
     offsets = np.concatenate([[3], 3 + np.cumsum(sizes)]).astype(np.int64)

@@ -102,7 +102,9 @@ def test_dma_tiles_keep_their_mfma(kernels):
         want = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_32x32x16_bf16"}[dt]
         assert ops[want] >= 16, (name, want, ops[want])
     for name, ops in _of(kernels, "gemm_dma_kernel").items():
-        assert ops["v_mfma_f32_32x32x16_f16"] >= 16, name
+        dt = int(_targs(name)[3])           # <Cfg<..>, kmajor, partial, format>
+        want = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_32x32x16_bf16"}[dt]
+        assert ops[want] >= 16, (name, want, ops[want])
 
 
 def test_register_tiles_keep_their_mfma(kernels):

@@ -304,6 +304,7 @@ def test_fp16_rounding_grouped():
 
 @pytest.mark.parametrize("M,N,K,plans", [
     (600, 520, 384, [dict(variant="main", tile=14), dict(variant="main", tile=1),
+                     dict(variant="main", tile=7), dict(variant="splitk", tile=7, split_k=3),
                      dict(variant="splitk", tile=14, split_k=3), dict(variant="splitk", split_k=5),
                      dict(variant="auto")]),
     (40, 520, 1152, [dict(variant="skinny"), dict(variant="skinny", split_k=5)]),
