@@ -86,7 +86,7 @@ enum gemm_status {
  * tail, when all the 256x256 tiles together fill less than half a wave with
  * M, N >= 256 and K long enough: K >= 4096 under 3/16 of a wave, K >= 8192
  * from 3/16 to 5/16, K >= 3072 from 5/16 on or where the 128x128 LDS-DMA
- * tile does not take the call. */
+ * tile does not take the call (fp16 and bfloat16 alike). */
 enum gemm_variant {
   GEMM_VARIANT_AUTO = 0,    /* choose from the shape (the default)                */
   GEMM_VARIANT_MAIN = 1,    /* one workgroup per output tile, whole K            */
@@ -113,8 +113,8 @@ typedef struct gemm_f16_opts {
  *   3, 4, 5  skinny 16, 32 and 64-row tiles (SKINNY; 3 is also reported
  *      for the decode kernel)
  *   6  256x256 register path (fp16; where tile 13 cannot read the layout)
- *   7  128x128 LDS-DMA, 4-stage ring (fp16; K-contiguous A, B either way
- *      with N % 8 == 0 when B is N-contiguous)
+ *   7  128x128 LDS-DMA, 4-stage ring (fp16, bfloat16; K-contiguous A, B
+ *      either way with N % 8 == 0 when B is N-contiguous)
  *   13 256x256 LDS-DMA, 4-stage ring (fp16; the same layouts, any stride)
  *   14 256x256 LDS-DMA with 128-byte A rows (fp16, bfloat16; the same
  *      layouts, strides up to 2^23 elements)
