@@ -50,9 +50,6 @@ struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
-  // Waves per SIMD the register budget must allow: two for the 4-wave
-  // 128x128 tile, so that two workgroups share a compute unit.
-  static constexpr int WPE = (NW == 4 && BM == 128) ? 2 : 1;
   static constexpr int MI = 32, KI = 16, KS = BK / KI;   // 2 MFMA k-steps per stage
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -284,7 +281,7 @@ __device__ __forceinline__ void mma_frags(const DmaFrags<CF>& f, f32x16 (&acc)[C
 
 // DT: DT_F16 or DT_BF16 operands and output.
 template <class CF, bool BKMAJOR, bool PARTIAL, int DT = DT_F16>
-__global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE))) void gemm_dma_kernel(KArgs a) {
+__global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;

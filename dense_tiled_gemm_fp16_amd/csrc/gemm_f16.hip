@@ -47,11 +47,11 @@ typedef void (*kfn_dec)(DecArgs);
 typedef void (*kfn_reduce)(const float*, int, int64_t, int64_t, uint16_t*, int64_t, int);
 
 const TileInfo& tile_info(int id) {
-  // Unused ids (0, 8 to 12) hold an empty entry: no kernels, nt == 0.
+  // Unused ids (0, 9 to 12) hold an empty entry: no kernels, nt == 0.
   static const TileInfo table[TILE_MAX + 1] = {
       TileInfo{},        tile_info_t128(), tile_info_t64x32(),    tile_info_s16(),
       tile_info_s32(),   tile_info_s64(),  tile_info_t256(),      tile_info_dma128(),
-      TileInfo{},        TileInfo{},       TileInfo{},            TileInfo{},
+      tile_info_dma64x128(), TileInfo{},   TileInfo{},            TileInfo{},
       TileInfo{},        tile_info_dma256w8b(), tile_info_dma256a128(), tile_info_f8()};
   return table[id];
 }
@@ -534,10 +534,15 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         const bool sk_small = small_grid_streamk(c, t256, cus) && (16 * t256 < 3 * (int64_t)cus ? c.K >= 4096 : c.K >= 8192);
         const bool quarter = 4 * t256 >= cus && (c.K >= 2048 || 3 * t256 >= cus);
         const bool packed_b = pack_any && c.N >= 256;
+        // Up to a quarter wave of 128x128 tiles, the 64x128 LDS-DMA tile
+        // (same layouts), with twice the workgroups: 1024^3 in 12.5 us against
+        // 13.5, 512^3 8.2 against 8.9, 256^3 6.3 against 7.0; from 1536^3 (144
+        // tiles) on it falls behind (22.3 against 20.0).
+        const int64_t t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
         if (t14 && (packed_b || big || sk_small))
           p.tile_id = TILE_DMA256A128;
         else if (t7 && !big)
-          p.tile_id = TILE_DMA128;
+          p.tile_id = 4 * t128 <= (int64_t)cus ? TILE_DMA64X128 : TILE_DMA128;
         else
           p.tile_id = (2 * t256 >= cus || ((quarter || small_grid_streamk(c, t256, cus)) && t14))
                           ? TILE_DMA256A128 : TILE_T128;

@@ -19,13 +19,14 @@ typedef TileCfg<64, 256, 64, 1, 4, 32> CfgS64;      // skinny, M <= 64
 typedef TileCfg<256, 256, 64, 2, 2, 32> CfgT256;    // register path for layouts the DMA tiles skip
 typedef DmaCfg<4, 4, 2> CfgDma256W8B;               // 256x256x32, 4-stage LDS-DMA ring, 8 waves of 64x128
 typedef DmaCfg<4, 2, 2, 128, 128> CfgDma128;        // 128x128x32, 4-stage LDS-DMA ring, 4 waves of 64x64
+typedef DmaCfg<4, 1, 2, 64, 128> CfgDma64x128;      // 64x128x32, the same ring, 2 waves of 64x64
 typedef DmaA128Cfg<4, 2> CfgDmaA128;                // same tile, A staged in 128-byte rows
 
-// Ids 8 to 12 belonged to superseded 256-wide tiles that no plan chose; they
+// Ids 9 to 12 belonged to superseded 256-wide tiles that no plan chose; they
 // stay unused so that the other ids keep their meaning.
 enum TileId {
   TILE_T128 = 1, TILE_T64X32 = 2, TILE_S16 = 3, TILE_S32 = 4, TILE_S64 = 5,
-  TILE_T256 = 6, TILE_DMA128 = 7, TILE_DMA256W8B = 13, TILE_DMA256A128 = 14, TILE_F8 = 15, TILE_MAX = 15
+  TILE_T256 = 6, TILE_DMA128 = 7, TILE_DMA64X128 = 8, TILE_DMA256W8B = 13, TILE_DMA256A128 = 14, TILE_F8 = 15, TILE_MAX = 15
 };
 
 typedef void (*kfn_t)(KArgs);
@@ -174,6 +175,7 @@ TileInfo tile_info_s64();
 TileInfo tile_info_t256();
 TileInfo tile_info_dma256w8b();
 TileInfo tile_info_dma128();
+TileInfo tile_info_dma64x128();
 TileInfo tile_info_dma256a128();
 TileInfo tile_info_f8();
 

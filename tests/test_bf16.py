@@ -62,7 +62,7 @@ def check(got, ref, mode, what):
 VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="main", tile=14),
             dict(variant="main", tile=1), dict(variant="splitk", split_k=3),
             dict(variant="splitk", tile=14, split_k=2), dict(variant="main", tile=7),
-            dict(variant="splitk", tile=7, split_k=2)]
+            dict(variant="splitk", tile=7, split_k=2), dict(variant="main", tile=8)]
 
 
 @pytest.mark.parametrize("mode", ["int", "uniform"])

@@ -52,7 +52,8 @@ VARIANTS = [dict(variant="auto"), dict(variant="main"), dict(variant="tile64x32"
             dict(variant="main", tile=6), dict(variant="splitk", tile=6, split_k=3),
             dict(variant="main", tile=13), dict(variant="splitk", tile=13, split_k=2),
             dict(variant="main", tile=14), dict(variant="splitk", tile=14, split_k=3),
-            dict(variant="main", tile=7), dict(variant="splitk", tile=7, split_k=2)]
+            dict(variant="main", tile=7), dict(variant="splitk", tile=7, split_k=2),
+            dict(variant="main", tile=8), dict(variant="splitk", tile=8, split_k=3)]
 
 
 # ------------------------------------------------------------------ the edge case
@@ -177,12 +178,14 @@ def test_auto_split_k_on_small_products(M, N, K, variant, split):
     rows = band_rows(M)
     assert_bits_equal(got[rows], reference(A, B, rows), f"{M}x{N}x{K} auto, sampled rows")
 
-@pytest.mark.parametrize("M,N,K,tile", [(1792, 1792, 1792, 7), (2048, 2048, 1024, 7),
+@pytest.mark.parametrize("M,N,K,tile", [(1024, 1024, 1024, 8), (768, 768, 768, 8),
+                                        (1792, 1792, 1792, 7), (2048, 2048, 1024, 7),
                                         (2048, 2048, 2048, 7), (3072, 2048, 1024, 14),
                                         (2100, 2304, 2056, 14), (2100, 2300, 2056, 14),
                                         (1000, 4100, 2048, 1), (1000, 2052, 2048, 1)])
 def test_main_tile_rule(M, N, K, tile):
-    # The 128 x 128 LDS-DMA tile below 80 tiles of 256 x 256 (on 256 compute
+    # The 64 x 128 LDS-DMA tile up to a quarter wave of 128 x 128 tiles, the
+    # 128 x 128 LDS-DMA tile below 80 tiles of 256 x 256 (on 256 compute
     # units), the 256 x 256 tile from there on.  A B whose rows are not
     # 16-byte multiples (N = 2300, 4100) is packed for the big tile from M =
     # 1024 on; below that it keeps the 128 x 128 register tile, as does a B
@@ -205,7 +208,7 @@ def test_main_tile_rule(M, N, K, tile):
 
 # ------------------------------------------------------------------ LDS-DMA tiles, K remainders
 
-@pytest.mark.parametrize("tile", [7, 13, 14])
+@pytest.mark.parametrize("tile", [7, 8, 13, 14])
 @pytest.mark.parametrize("K", [32, 64, 96, 100, 160, 241])
 @pytest.mark.parametrize("b_layout", ["row", "col"])
 def test_dma_tiles_k_remainders(tile, K, b_layout):

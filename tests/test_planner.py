@@ -14,7 +14,7 @@ from dense_tiled_gemm_fp16_amd import _lib
 PA, PB, PC = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
 MAIN, SKINNY, SPLITK, STREAMK = 1, 2, 3, 5
 GATHER, KVEC, RVEC, PACKED = 0, 1, 2, 3
-T128, T128_DMA, T256_DMA = 1, 7, 14
+T128, T128_DMA, T64_DMA, T256_DMA = 1, 7, 8, 14
 
 
 def plan(M, N, K, lda=None, ldb=None, a="row", b="row", cus=256, A=PA, B=PB, opts=None):
@@ -46,11 +46,14 @@ def test_compute_unit_count_is_checked():
 @pytest.mark.parametrize("M,N,K,tile", [(2048, 2048, 2048, T128_DMA), (2304, 2304, 2304, T256_DMA),
                                         (3072, 2048, 1024, T256_DMA), (2048, 2048, 1024, T128_DMA),
                                         (1792, 1792, 1792, T128_DMA), (1536, 1536, 1536, T128_DMA),
-                                        (1024, 1024, 1024, T128_DMA), (4096, 4096, 4096, T256_DMA),
-                                        (2048, 2048, 4096, T128_DMA), (1536, 1536, 3072, T128_DMA)])
+                                        (1024, 1024, 1024, T64_DMA), (4096, 4096, 4096, T256_DMA),
+                                        (2048, 2048, 4096, T128_DMA), (1536, 1536, 3072, T128_DMA),
+                                        (256, 256, 256, T64_DMA), (512, 2048, 1024, T64_DMA),
+                                        (2048, 1024, 1024, T128_DMA)])
 def test_main_tile_rule(M, N, K, tile):
-    # The 128x128 LDS-DMA tile below 80 tiles of 256x256, the 256x256 tile
-    # from there on (256 compute units).
+    # The 64x128 LDS-DMA tile up to a quarter wave of 128x128 tiles, the
+    # 128x128 LDS-DMA tile below 80 tiles of 256x256, the 256x256 tile from
+    # there on (256 compute units).
     p = plan(M, N, K)
     assert (p.variant, p.tile_id, p.split_k) == (MAIN, tile, 1)
 
@@ -59,6 +62,9 @@ def test_tile_rule_scales_with_the_compute_units():
     # 64 tiles of 256 x 256: under 80 on 256 compute units, past 40 on 128.
     assert plan(2048, 2048, 1024, cus=256).tile_id == T128_DMA
     assert plan(2048, 2048, 1024, cus=128).tile_id == T256_DMA
+    # 64 tiles of 128 x 128: a quarter wave on 256 compute units, more on 128.
+    assert plan(1024, 1024, 1024, cus=256).tile_id == T64_DMA
+    assert plan(1024, 1024, 1024, cus=128).tile_id == T128_DMA
 
 
 def test_layouts_the_128x128_dma_tile_does_not_take():
@@ -77,8 +83,8 @@ def test_layouts_the_128x128_dma_tile_does_not_take():
     (200, 4096, 32768, SPLITK, 8, T128_DMA),      # M < 256, ranges of 8192 k: two per compute unit
     (512, 512, 65536, SPLITK, 40, T256_DMA),      # ranges of 4096 k and more: the 256x256 tile
     (1024, 1024, 16384, SPLITK, 16, T256_DMA), (1024, 2048, 8192, SPLITK, 5, T256_DMA),
-    (1024, 1024, 1024, MAIN, 1, T128_DMA), (1024, 1024, 1536, MAIN, 1, T128_DMA),
-    (512, 512, 1024, MAIN, 1, T128_DMA), (256, 256, 768, MAIN, 1, T128_DMA),
+    (1024, 1024, 1024, MAIN, 1, T64_DMA), (1024, 1024, 1536, MAIN, 1, T64_DMA),
+    (512, 512, 1024, MAIN, 1, T64_DMA), (256, 256, 768, MAIN, 1, T64_DMA),
     (2048, 1024, 1024, MAIN, 1, T128_DMA)])
 def test_split_k_rule(M, N, K, variant, split, tile):
     # Operands the 128x128 LDS-DMA tile reads: split-K from K >= 2048 while

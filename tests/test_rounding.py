@@ -180,6 +180,7 @@ MAIN_PLANS = [
     ("dma256 tile 14", dict(variant="main", tile=14)),
     ("dma256 tile 13", dict(variant="main", tile=13)),
     ("dma128 tile 7", dict(variant="main", tile=7)),
+    ("dma64x128 tile 8", dict(variant="main", tile=8)),
     ("register 256", dict(variant="main", tile=6)),
     ("register 128", dict(variant="main", tile=1)),
     ("64x32x32", dict(variant="tile64x32")),
@@ -305,6 +306,7 @@ def test_fp16_rounding_grouped():
 @pytest.mark.parametrize("M,N,K,plans", [
     (600, 520, 384, [dict(variant="main", tile=14), dict(variant="main", tile=1),
                      dict(variant="main", tile=7), dict(variant="splitk", tile=7, split_k=3),
+                     dict(variant="main", tile=8),
                      dict(variant="splitk", tile=14, split_k=3), dict(variant="splitk", split_k=5),
                      dict(variant="auto")]),
     (40, 520, 1152, [dict(variant="skinny"), dict(variant="skinny", split_k=5)]),
