@@ -115,12 +115,14 @@ typedef struct gemm_f16_opts {
  *   6  256x256 register path (fp16; where tile 13 cannot read the layout)
  *   7  128x128 LDS-DMA, 4-stage ring (fp16, bfloat16; K-contiguous A, B
  *      either way with N % 8 == 0 when B is N-contiguous)
+ *   8  64x128 LDS-DMA, the same ring with two waves (as tile 7)
  *   13 256x256 LDS-DMA, 4-stage ring (fp16; the same layouts, any stride)
  *   14 256x256 LDS-DMA with 128-byte A rows (fp16, bfloat16; the same
  *      layouts, strides up to 2^23 elements)
  *   15 256x256 FP8 (the FP8 entry points only)
  * A tile that does not take the operand layout hands over to the next one
- * that does: fp16 along 7 -> 1 and 14 -> 13 -> 6, bfloat16 straight to 1.
+ * that does: fp16 along 7 -> 1, 8 -> 1 and 14 -> 13 -> 6, bfloat16 straight
+ * to 1.
  * Forcing an id without kernels for the call's format returns
  * GEMM_ERR_OPTS. */
 
