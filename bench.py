@@ -329,11 +329,12 @@ def cpu_baseline(budget_s=15.0):
 
 
 # The workload families (the pages' shapes and the MoE product), as (name,
-# M, N, K, B layout[, forced variants]); the configurations sweep times each
-# one (not the headline line).
+# M, N, K, B layout[, forced plans: a variant name or a dict of options]);
+# the configurations sweep times each one (not the headline line).
 CONFIGS = [
     ("edge_130x70x65", 130, 70, 65, "row"), ("edge_130x70x65_bt", 130, 70, 65, "col"),
-    ("square_256", 256, 256, 256, "row"), ("square_1024", 1024, 1024, 1024, "row"),
+    ("square_256", 256, 256, 256, "row"),
+    ("square_1024", 1024, 1024, 1024, "row", ({"variant": "main", "tile": 1},)),
     ("square_4096", 4096, 4096, 4096, "row"), ("square_8192", 8192, 8192, 8192, "row"),
     ("skinny_m1", 1, 2048, 7168, "row"), ("skinny_m16", 16, 2048, 7168, "row"),
     ("skinny_m64", 64, 2048, 7168, "row"),
@@ -344,6 +345,9 @@ CONFIGS = [
     ("stride_262181x1061x8192_bt", 262181, 1061, 8192, "col", ("main", "streamk")),
     # not one of the pages' workloads: 17 x 16 tiles, a final wave of 16 tiles on 256 CUs
     ("tail_4352x4096x8192", 4352, 4096, 8192, "row", ("main",)),
+    # not one of the pages' workloads: mid-size products under a wave of 256 x 256 tiles
+    ("mid_2048", 2048, 2048, 2048, "row", ({"variant": "main", "tile": 1}, {"variant": "main", "tile": 14})),
+    ("splitk_1024x1024x4096", 1024, 1024, 4096, "row", ({"variant": "splitk", "tile": 14},)),
 ]
 
 
@@ -366,13 +370,15 @@ def configs_sweep():
 
     for i, cfg in enumerate(CONFIGS):
         name, m, n, k, bl = cfg[:5]
-        for variant in ("auto",) + (cfg[5] if len(cfg) > 5 else ()):
-            sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant)
+        for forced in ("auto",) + (cfg[5] if len(cfg) > 5 else ()):
+            sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, forced)
 
 
-def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant):
+def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, forced):
     """Time one configuration under one plan (see configs_sweep)."""
     import torch
+    opts = {"variant": forced} if isinstance(forced, str) else dict(forced)
+    label = forced if isinstance(forced, str) else " ".join(f"{q}={v}" for q, v in forced.items())
     a0 = to_dev(synth.matrix(m, k, 7000 + i, synth.TENSOR_A))
     bt = synth.matrix(k, n, 7000 + i, synth.TENSOR_B, order="col" if bl == "col" else "row")
     b0 = to_dev(bt).t() if bl == "col" else to_dev(bt)
@@ -381,19 +387,18 @@ def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant):
     As = [a0] + [a0.clone() for _ in range(copies - 1)]
     Bs = [b0] + [(b0.t().clone().t() if bl == "col" else b0.clone()) for _ in range(copies - 1)]
     c = torch.empty((m, n), dtype=torch.float16, device=dev)
-    p = g.plan(a0, b0, c, variant=variant)
+    p = g.plan(a0, b0, c, **opts)
     ws = (torch.empty(p["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
           if p["workspace_bytes"] else None)
     cap = torch.cuda.Stream(dev)
     with torch.cuda.stream(cap):
-        g.gemm(a0, b0, out=c, workspace=ws, stream=cap, variant=variant)
+        g.gemm(a0, b0, out=c, workspace=ws, stream=cap, **opts)
     torch.cuda.synchronize()
     reps = copies if byts * copies >= (1 << 28) else max(copies, 64)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
         for r in range(reps):
-            g.gemm(As[r % copies], Bs[r % copies], out=c, workspace=ws, stream=cap,
-                   variant=variant)
+            g.gemm(As[r % copies], Bs[r % copies], out=c, workspace=ws, stream=cap, **opts)
     times = []
     for r in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -409,7 +414,7 @@ def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, variant):
     tf, gbs = flops / (ms * 1e-3) / 1e12, byts / (ms * 1e-3) / 1e9
     bound = "mfma" if ai >= PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     print(json.dumps({"config": name, "M": m, "N": n, "K": k, "b_layout": bl,
-                      "forced": variant,
+                      "forced": label,
                       "plan": {q: p[q] for q in ("variant", "tile_id", "split_k", "grid",
                                                  "sk_tiles", "b_path")},
                       "us_per_call": ms * 1e3, "TFLOPS": tf, "GBps": gbs, "AI": ai,
