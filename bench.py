@@ -394,7 +394,9 @@ def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, forced):
     with torch.cuda.stream(cap):
         g.gemm(a0, b0, out=c, workspace=ws, stream=cap, **opts)
     torch.cuda.synchronize()
-    reps = copies if byts * copies >= (1 << 28) else max(copies, 64)
+    # At least 4 calls per replay, so a large product is timed back to back
+    # (a replay of a single call measures a launch after an idle gap).
+    reps = max(copies, 4) if byts * copies >= (1 << 28) else max(copies, 64)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
         for r in range(reps):
