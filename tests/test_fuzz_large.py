@@ -6,7 +6,10 @@ layout, where the automatic plans also realign A and split K.  Integer
 inputs in [-4, 4] keep every fp32 sum exact.  The automatic plan's output
 must have every element written, and agree bit for bit with the oracle on
 one row per 256-row band and on 20000 points drawn over the whole output,
-and with the forced main plan (never packed) everywhere.
+and with the forced main plan (never packed) everywhere; the mid-size sets
+compare with the 128 x 128 register-path tile, another kernel, instead.  A
+third set draws small and mid-size outputs with long K, where the plans
+split K on the LDS-DMA tiles.
 """
 import numpy as np
 import pytest
@@ -117,7 +120,8 @@ def _a_view(A, layout, fmt):
 def test_random_mid_case(seed):
     # Integer inputs keep every sum exact, so the automatic plan (realigned
     # A, packed B, split K or stream-K as the shape and layouts decide) must
-    # equal the forced main plan on the operands' own layouts everywhere.
+    # equal the main plan of the 128 x 128 register-path tile, another
+    # kernel, on the operands' own layouts everywhere.
     rng = np.random.default_rng(seed)
     a_layout = ["row", "odd", "mcontig", "strided"][seed % 4]
     b_layout = ["row", "col", "unaligned", "strided"][(seed // 4) % 4]
@@ -140,11 +144,49 @@ def test_random_mid_case(seed):
     out2 = Out(M, N)
     if fmt == "bf16":
         out2.view = out2.view.view(torch.bfloat16)
-    g.gemm(a, b, out=out2.view, variant="main")
+    g.gemm(a, b, out=out2.view, variant="main", tile=1)
     torch.cuda.synchronize()
-    assert_bits_equal(got, out2.result(), f"seed {seed}: automatic plan {p} vs forced main")
+    assert_bits_equal(got, out2.result(), f"seed {seed}: automatic plan {p} vs the register tile")
     dt = "bf16" if fmt == "bf16" else "f16"
     rows = band_rows(M)
     ref = oracle.gemm(np.ascontiguousarray(A[rows]), (K, 1), B, (N, 1), len(rows), N, K,
                       nthreads=ORACLE_THREADS, dtype=dt)
     assert_bits_equal(got[rows], ref, f"seed {seed}: band rows against the oracle")
+
+
+@pytest.mark.parametrize("seed", range(19200, 19216))
+def test_random_small_long_k_case(seed):
+    # Small and mid-size outputs with long K: the 64 x 128 and 128 x 128
+    # LDS-DMA tiles, split-K on them or on the 256 x 256 tile, and stream-K
+    # over every tile, as the planner decides.  Integer inputs keep every sum
+    # exact: the automatic plan must equal the register tile's main plan
+    # everywhere, and sampled rows the oracle.
+    rng = np.random.default_rng(seed)
+    a_layout = ["row", "row", "odd", "strided"][seed % 4]
+    b_layout = ["row", "col", "row", "unaligned"][(seed // 4) % 4]
+    M = int(rng.integers(65, 1281))
+    N = int(rng.integers(64, 1281))
+    if b_layout == "row" and rng.random() < 0.7:
+        N = N // 8 * 8 or 8                    # whole 16-byte B rows: the DMA tiles take it
+    K = int(rng.integers(1024, 10001))
+    fmt = "bf16" if rng.random() < 0.25 else "f16"
+    A = synth.matrix(M, K, seed, 0, "int", fmt=fmt)
+    B = synth.matrix(K, N, seed, 1, "int", fmt=fmt)
+    a, b = _a_view(A, a_layout, fmt), _b_view(B, b_layout, fmt)
+    p = g.plan(a, b)
+    say(f"small long-K fuzz seed={seed} {fmt} {M}x{N}x{K} A={a_layout} B={b_layout} -> {p}")
+    outs = []
+    for kw in ({}, dict(variant="main", tile=1)):
+        out = Out(M, N)
+        if fmt == "bf16":
+            out.view = out.view.view(torch.bfloat16)
+        g.gemm(a, b, out=out.view, **kw)
+        torch.cuda.synchronize()
+        outs.append(out.result())
+    assert np.all(outs[0] != NAN16), f"seed {seed}: outputs never written"
+    assert_bits_equal(outs[0], outs[1], f"seed {seed}: automatic plan {p} vs the register tile")
+    dt = "bf16" if fmt == "bf16" else "f16"
+    rows = band_rows(M)
+    ref = oracle.gemm(np.ascontiguousarray(A[rows]), (K, 1), B, (N, 1), len(rows), N, K,
+                      nthreads=ORACLE_THREADS, dtype=dt)
+    assert_bits_equal(outs[0][rows], ref, f"seed {seed}: band rows against the oracle")
