@@ -71,6 +71,48 @@ constexpr int kDecWaves = 4;
 template <int MT>
 constexpr int dec_upw() { return 4; }
 
+// FP8 operands (F8 = 2 fmt_a + fmt_b, 0 E4M3 and 1 E5M2 per operand): the
+// bytes are widened to binary16, which holds every E4M3 and E5M2 value
+// exactly, and the same fp16 MFMAs run on them (a product of two binary16
+// values is exact in fp32, so the sums are those of FP8 products).  The
+// packed convert of gfx950 takes a byte pair of a word's low or high half;
+// it is written out here because the builtin's vector result lost its second
+// element (the compiler copied the first into it).  All 256 codes of both
+// formats, NaNs included, convert to the binary16 values of the OCP formats.
+template <int FMT>
+__device__ __forceinline__ uint32_t f8pair_to_f16(uint32_t w, bool hi) {
+  uint32_t r;
+  if constexpr (FMT == 0) {
+    if (hi)
+      asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+    else
+      asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  } else {
+    if (hi)
+      asm("v_cvt_scalef32_pk_f16_bf8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+    else
+      asm("v_cvt_scalef32_pk_f16_bf8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  }
+  return r;
+}
+
+// 8 FP8 bytes (two words, byte j = element j) as 8 binary16 values.
+template <int FMT>
+__device__ __forceinline__ u32x4 f8x8_to_f16(uint32_t lo, uint32_t hi) {
+  return u32x4{f8pair_to_f16<FMT>(lo, false), f8pair_to_f16<FMT>(lo, true), f8pair_to_f16<FMT>(hi, false),
+               f8pair_to_f16<FMT>(hi, true)};
+}
+
+// 8 FP8 bytes from p with element stride s (bytes), the first n of them
+// (zero past), packed as two words.
+__device__ __forceinline__ void load_partial8_b(const uint8_t* p, int64_t s, int n, uint32_t& lo, uint32_t& hi) {
+  uint32_t b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = e < n ? (uint32_t)p[e * s] : 0u;
+  lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+}
+
 // 8 consecutive k of A row m from k0, zero past M or at/after ke.
 __device__ __forceinline__ u32x4 dec_load_a(const DecArgs& a, int64_t m, int64_t k0, int64_t ke) {
   if (m >= a.M || k0 >= ke) return zero4();
@@ -80,6 +122,23 @@ __device__ __forceinline__ u32x4 dec_load_a(const DecArgs& a, int64_t m, int64_t
   return load_partial8(p, a.lda_k, nk);
 }
 
+// The same for FP8 A of format FMT (strides in bytes), widened to binary16.
+template <int FMT>
+__device__ __forceinline__ u32x4 dec_load_a8(const DecArgs& a, int64_t m, int64_t k0, int64_t ke) {
+  if (m >= a.M || k0 >= ke) return zero4();
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(a.A) + m * a.lda_m + k0 * a.lda_k;
+  const int nk = (ke - k0 >= 8) ? 8 : (int)(ke - k0);
+  uint32_t lo, hi;
+  if (a.a_vec && nk == 8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    lo = v.x;
+    hi = v.y;
+  } else {
+    load_partial8_b(p, a.lda_k, nk, lo, hi);
+  }
+  return f8x8_to_f16<FMT>(lo, hi);
+}
+
 // The k loop of one wave over its units (u = w, w + 4, ...) of [kb, ke).
 // FULL: every unit lies inside the range and the 8 columns of every lane
 // are inside N, so the B loads carry no masks and no branches; otherwise
@@ -87,11 +146,17 @@ __device__ __forceinline__ u32x4 dec_load_a(const DecArgs& a, int64_t m, int64_t
 // vectors, read unmasked (rows past M from row 0, then zeroed); without it
 // A is read element by element (M <= 64 rows, a small share of the bytes),
 // so an A with unaligned rows (K odd, say) keeps B's full-width loads.
-template <int MT, int DT, bool FULL, bool BK, bool AVEC = FULL>
+// F8 >= 0: FP8 A and N-contiguous B (formats F8 / 2 and F8 % 2), loaded as
+// 8-byte vectors (a wave's load instruction still covers 4 rows x 128
+// bytes, whole lines) and widened to binary16; bcol then points at bytes.
+template <int MT, int DT, bool FULL, bool BK, bool AVEC = FULL, int F8 = -1>
 __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16][8], int w, int g, int c,
                                           int64_t kb, int64_t ke, const uint16_t* bcol, int nvalid,
                                           int64_t n0) {
+  static_assert(F8 < 0 || !BK, "FP8 B is read N-contiguous");
   constexpr int FA = MT / 16;
+  constexpr int FMA_ = F8 < 0 ? 0 : F8 / 2, FMB = F8 < 0 ? 0 : F8 % 2;
+  const uint8_t* bcol8 = reinterpret_cast<const uint8_t*>(bcol);
   constexpr int UPW = dec_upw<MT>();
   const int64_t units = (ke - kb + kDecUnit - 1) / kDecUnit;
   for (int64_t u0 = w; u0 < units; u0 += kDecWaves * UPW) {
@@ -108,7 +173,15 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
 #pragma unroll
       for (int fa = 0; fa < FA; ++fa) {
         const int64_t m = 16 * fa + c;
-        if constexpr (FULL && AVEC) {
+        if constexpr (F8 >= 0) {
+          if constexpr (FULL && AVEC) {
+            const u32x2 x = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.A) +
+                                                            (m < a.M ? m : 0) * a.lda_m + k0);
+            av[i][fa] = (live && m < a.M) ? f8x8_to_f16<FMA_>(x[0], x[1]) : zero4();
+          } else {
+            av[i][fa] = live ? dec_load_a8<FMA_>(a, m, k0, ke) : zero4();
+          }
+        } else if constexpr (FULL && AVEC) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(a.A + (m < a.M ? m : 0) * a.lda_m + k0);
           av[i][fa] = (live && m < a.M) ? x : zero4();
         } else {
@@ -139,6 +212,29 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
             bv[i][f] = (live && n < a.N && nk > 0)
                            ? (nk == 8 ? *reinterpret_cast<const u32x4*>(q) : load_partial8(q, 1, nk))
                            : zero4();
+          }
+        }
+      } else if constexpr (F8 >= 0) {
+        // FP8 rows: 8 bytes per lane and k-row, masked as the 16-bit rows
+        // below (N % 16 == 0, so a lane's 8 columns are all inside N or all
+        // past it).
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2* q = reinterpret_cast<const u32x2*>(bcol8 + (k0 + j) * a.ldb_k);
+          u32x2 x;
+          if constexpr (FULL) {
+            if constexpr (MT <= 32)
+              x = __builtin_nontemporal_load(q);
+            else
+              x = *q;
+            bv[i][j] = f8x8_to_f16<FMB>(x[0], x[1]);
+          } else {
+            if (live && nvalid == 8 && k0 + j < ke) {
+              x = *q;
+              bv[i][j] = f8x8_to_f16<FMB>(x[0], x[1]);
+            } else {
+              bv[i][j] = zero4();
+            }
           }
         }
       } else if constexpr (FULL) {
@@ -190,9 +286,12 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
   }
 }
 
-template <int MT, int DT, bool BK = false>
+// F8 >= 0: FP8 A and N-contiguous B of formats (F8 / 2, F8 % 2), binary16 out
+// (DT = DT_F16); the B strip is then 128 bytes wide per k-row.
+template <int MT, int DT, bool BK = false, int F8 = -1>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   static_assert(MT % 16 == 0 && MT <= 64, "16, 32, 48 or 64 rows of A");
+  static_assert(F8 < 0 || (DT == DT_F16 && !BK), "FP8: N-contiguous B, binary16 out");
   constexpr int FA = MT / 16;
   __shared__ __attribute__((aligned(16))) float red[kDecWaves][16][16][8];   // [wave][m][c][f]
   const int tid = threadIdx.x;
@@ -204,7 +303,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   const int64_t ke = (kb + a.kr < a.K) ? kb + a.kr : a.K;
   const int64_t n0 = nb * kDecCols + c * 8;   // N-contiguous B: this lane's 8 columns
   const int nvalid = (n0 + 8 <= a.N) ? 8 : (n0 < a.N ? (int)(a.N - n0) : 0);
-  const uint16_t* bcol = a.B + (nvalid > 0 ? n0 : 0);
+  const uint16_t* bcol = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.B) +
+                                                          (nvalid > 0 ? n0 : 0) * (F8 >= 0 ? 1 : 2));
   const int64_t sn0 = nb * kDecCols;            // the strip's first column
 
   f32x4 acc[FA][8];
@@ -219,11 +319,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   // 5.5 us of kernel time, as for aligned rows).
   const bool full = (nb + 1) * kDecCols <= a.N && (ke - kb) % kDecUnit == 0;
   if (full && a.a_vec)
-    dec_units<MT, DT, true, BK, true>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
+    dec_units<MT, DT, true, BK, true, F8>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
   else if (full)
-    dec_units<MT, DT, true, BK, false>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
+    dec_units<MT, DT, true, BK, false, F8>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
   else
-    dec_units<MT, DT, false, BK, false>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
+    dec_units<MT, DT, false, BK, false, F8>(a, acc, w, g, c, kb, ke, bcol, nvalid, sn0);
 
   // Sum the waves in ascending order, 16 rows of A at a time; thread t < 256
   // then owns row t / 16 and the 8 columns 8 (t % 16) .. + 7 of the block.

@@ -424,7 +424,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   };
 
   // FP8 operands: K-contiguous A and B with 16-byte aligned rows, on the FP8
-  // tile, in the main, split-K and stream-K families only.
+  // tile, in the main, split-K and stream-K families; with N-contiguous B
+  // also the skinny family (the decode kernel).
   const bool f8 = c.dt >= DT_F8;
   if (f8) {
     // A K-contiguous; B K-contiguous ([N, K] rows) or N-contiguous ([K, N]
@@ -436,7 +437,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         ldb % 16 != 0 || ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) ||
         ldb > (INT64_C(1) << 24) || (b_n && c.N % 16 != 0))
       return GEMM_ERR_LAYOUT;
-    if (variant == GEMM_VARIANT_SKINNY || variant == GEMM_VARIANT_TILE64X32 ||
+    if ((variant == GEMM_VARIANT_SKINNY && (!b_n || want_tile)) || variant == GEMM_VARIANT_TILE64X32 ||
         (want_tile && want_tile != TILE_F8))
       return GEMM_ERR_OPTS;
   }
@@ -449,7 +450,12 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   p.variant = variant;
   if (p.variant == GEMM_VARIANT_AUTO) {
     if ((rc = need_cus())) return rc;
-    if (c.M <= 64 && !f8) {
+    // FP8 with N-contiguous B streams through the decode kernel too, up to
+    // 32 rows (N = 2048, K = 7168, per call in graphs of calls: M = 1, 16,
+    // 32 in 8.9, 10.4, 12.7 us against 14.2, 14.8, 14.9 on the 256 x 256 FP8
+    // tile split over K; M = 33 level, M = 48 and 64 behind: 16.3 and 19.1
+    // against 15.5 and 15.8).
+    if (c.M <= 64 && (!f8 || (c.ldb_n == 1 && c.M <= 32))) {
       p.variant = GEMM_VARIANT_SKINNY;
     } else {
       const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
@@ -788,7 +794,16 @@ int launch_reduce(const Call& c, const Plan& p, void* ws, hipStream_t stream) {
 }
 
 template <int MT>
-kfn_dec pick_dec(int dt) { return dt == DT_F16 ? decode_kernel<MT, DT_F16> : decode_kernel<MT, DT_BF16>; }
+kfn_dec pick_dec(int dt) {
+  switch (dt) {
+    case DT_F16: return decode_kernel<MT, DT_F16>;
+    case DT_BF16: return decode_kernel<MT, DT_BF16>;
+    case DT_F8 + 0: return decode_kernel<MT, DT_F16, false, 0>;
+    case DT_F8 + 1: return decode_kernel<MT, DT_F16, false, 1>;
+    case DT_F8 + 2: return decode_kernel<MT, DT_F16, false, 2>;
+    default: return decode_kernel<MT, DT_F16, false, 3>;
+  }
+}
 kfn_dec pick_dec_bk(int dt) {   // B as [N, K] rows, up to 16 rows of A
   return dt == DT_F16 ? decode_kernel<16, DT_F16, true> : decode_kernel<16, DT_BF16, true>;
 }

@@ -276,3 +276,50 @@ def test_f8_bn_moe_shape_full_coverage():
     b = torch.from_numpy(B).to(DEV).view(torch.float8_e4m3fn)
     p = full_size_check(a, b, A, B, (N, 1), M, N, K, 14800, "f8 B [K, N] MoE", dtype="f8")
     assert p["tile_id"] == 15 and p["b_path"] == "rvec", p
+
+
+F8_DECODE_CASES = [(1, 2048, 7168, {}), (16, 1040, 1000, {}), (17, 272, 130, {}),
+                   (64, 528, 96, dict(variant="skinny")),
+                   (3, 2048, 7168, dict(variant="skinny", split_k=1)),
+                   (40, 1040, 2500, dict(variant="skinny", split_k=5))]
+
+
+@pytest.mark.parametrize("mode", ["int", "uniform"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_f8_decode(fa, fb, mode):
+    # Up to 32 rows of A with B as [K, N] rows (64 when forced): the decode kernel, the FP8
+    # bytes widened to binary16 (exact for both formats), fp32 sums over K
+    # ranges and the fixed-order reduction.  The cases cover a ragged last
+    # column strip (N = 1040: 16 columns past the eighth strip), ragged last
+    # K ranges, 16, 32 and 64-row kernels, one K range (C written directly)
+    # and a forced split; rows padded with NaN bytes past K and N.
+    for M, N, K, kw in F8_DECODE_CASES:
+        A, Bt = inputs(M, N, K, 14400 + M + K, mode, fa, fb)
+        ref = reference(A, Bt, fa, fb)
+        a = f8_rows(A, fa)
+        b = f8_rows(np.ascontiguousarray(Bt.T), fb)          # [K, N] rows
+        p = g.plan(a, b, **kw)
+        assert p["variant"] == "skinny" and p["tile_n"] == 128, p
+        if "split_k" in kw:
+            assert p["split_k"] == kw["split_k"], p
+        got = run(a, b, Out(M, N), **kw)
+        what = f"f8 decode {fa}x{fb} {mode} {M}x{N}x{K} {kw} plan {p}"
+        if mode == "int":
+            assert_bits_equal(got, ref, what)
+        else:
+            assert_close(got, ref, what)
+
+
+def test_f8_decode_plan_bounds():
+    # B as [N, K] rows at decode shapes stays on the FP8 tile (split over K),
+    # and so does B as [K, N] rows from 33 rows of A on.
+    for M, nk in ((16, True), (33, False)):
+        N, K = 512, 4096
+        A, Bt = inputs(M, N, K, 14480 + M, "int", "e4m3", "e4m3")
+        a = f8_rows(A, "e4m3")
+        b = f8_rows(Bt, "e4m3").t() if nk else f8_rows(np.ascontiguousarray(Bt.T), "e4m3")
+        p = g.plan(a, b)
+        assert p["variant"] != "skinny" and p["tile_id"] == 15, p
+        assert_bits_equal(run(a, b, Out(M, N)), reference(A, Bt, "e4m3", "e4m3"), f"f8 M = {M}, nk {nk}")
+    A, Bt = inputs(32, 512, 4096, 14532, "int", "e4m3", "e4m3")
+    assert g.plan(f8_rows(A, "e4m3"), f8_rows(np.ascontiguousarray(Bt.T), "e4m3"))["variant"] == "skinny"
