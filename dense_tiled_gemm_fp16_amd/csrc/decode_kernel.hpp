@@ -146,14 +146,15 @@ __device__ __forceinline__ u32x4 dec_load_a8(const DecArgs& a, int64_t m, int64_
 // vectors, read unmasked (rows past M from row 0, then zeroed); without it
 // A is read element by element (M <= 64 rows, a small share of the bytes),
 // so an A with unaligned rows (K odd, say) keeps B's full-width loads.
-// F8 >= 0: FP8 A and N-contiguous B (formats F8 / 2 and F8 % 2), loaded as
-// 8-byte vectors (a wave's load instruction still covers 4 rows x 128
-// bytes, whole lines) and widened to binary16; bcol then points at bytes.
+// F8 >= 0: FP8 A and B (formats F8 / 2 and F8 % 2), loaded as 8-byte
+// vectors and widened to binary16: N-contiguous B as 8 columns of a k-row
+// per lane (a wave's load instruction still covers 4 rows x 128 bytes,
+// whole lines; bcol then points at bytes), K-contiguous B as 8 k of one
+// column (16 columns x 32 bytes per instruction).
 template <int MT, int DT, bool FULL, bool BK, bool AVEC = FULL, int F8 = -1>
 __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16][8], int w, int g, int c,
                                           int64_t kb, int64_t ke, const uint16_t* bcol, int nvalid,
                                           int64_t n0) {
-  static_assert(F8 < 0 || !BK, "FP8 B is read N-contiguous");
   constexpr int FA = MT / 16;
   constexpr int FMA_ = F8 < 0 ? 0 : F8 / 2, FMB = F8 < 0 ? 0 : F8 % 2;
   const uint8_t* bcol8 = reinterpret_cast<const uint8_t*>(bcol);
@@ -194,7 +195,31 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
       const int64_t u = u0 + (int64_t)kDecWaves * i;
       const bool live = u < units;
       const int64_t k0 = kb + (live ? u : units - 1) * kDecUnit + 8 * g;
-      if constexpr (BK) {
+      if constexpr (BK && F8 >= 0) {
+        // FP8 [N, K] rows: 8 bytes of column 16 f + c, k0 .. k0 + 7.
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          const int64_t n = n0 + 16 * f + c;
+          const uint8_t* q = reinterpret_cast<const uint8_t*>(a.B) + n * a.ldb_n + k0;
+          uint32_t lo, hi;
+          if constexpr (FULL) {
+            const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q));
+            lo = x[0];
+            hi = x[1];
+          } else {
+            const int64_t d = ke - k0;
+            const int nk = (live && n < a.N) ? (d < 0 ? 0 : (d < 8 ? (int)d : 8)) : 0;
+            if (nk == 8) {
+              const u32x2 x = *reinterpret_cast<const u32x2*>(q);
+              lo = x[0];
+              hi = x[1];
+            } else {
+              load_partial8_b(q, 1, nk, lo, hi);
+            }
+          }
+          bv[i][f] = f8x8_to_f16<FMB>(lo, hi);
+        }
+      } else if constexpr (BK) {
         // Column 16 f + c of the strip, k0 .. k0 + 7; columns past N read
         // zeros (FULL: the whole strip is inside N).
 #pragma unroll
@@ -286,12 +311,12 @@ __device__ __forceinline__ void dec_units(const DecArgs& a, f32x4 (&acc)[MT / 16
   }
 }
 
-// F8 >= 0: FP8 A and N-contiguous B of formats (F8 / 2, F8 % 2), binary16 out
-// (DT = DT_F16); the B strip is then 128 bytes wide per k-row.
+// F8 >= 0: FP8 A and B of formats (F8 / 2, F8 % 2), binary16 out (DT =
+// DT_F16); an N-contiguous B strip is then 128 bytes wide per k-row.
 template <int MT, int DT, bool BK = false, int F8 = -1>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(DecArgs a) {
   static_assert(MT % 16 == 0 && MT <= 64, "16, 32, 48 or 64 rows of A");
-  static_assert(F8 < 0 || (DT == DT_F16 && !BK), "FP8: N-contiguous B, binary16 out");
+  static_assert(F8 < 0 || DT == DT_F16, "FP8: binary16 out");
   constexpr int FA = MT / 16;
   __shared__ __attribute__((aligned(16))) float red[kDecWaves][16][16][8];   // [wave][m][c][f]
   const int tid = threadIdx.x;

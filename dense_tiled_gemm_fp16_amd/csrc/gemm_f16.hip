@@ -437,7 +437,8 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         ldb % 16 != 0 || ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) ||
         ldb > (INT64_C(1) << 24) || (b_n && c.N % 16 != 0))
       return GEMM_ERR_LAYOUT;
-    if ((variant == GEMM_VARIANT_SKINNY && (!b_n || want_tile)) || variant == GEMM_VARIANT_TILE64X32 ||
+    if ((variant == GEMM_VARIANT_SKINNY && (!(b_n || (b_k && c.M <= 16)) || want_tile)) ||
+        variant == GEMM_VARIANT_TILE64X32 ||
         (want_tile && want_tile != TILE_F8))
       return GEMM_ERR_OPTS;
   }
@@ -454,8 +455,10 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     // 32 rows (N = 2048, K = 7168, per call in graphs of calls: M = 1, 16,
     // 32 in 8.9, 10.4, 12.7 us against 14.2, 14.8, 14.9 on the 256 x 256 FP8
     // tile split over K; M = 33 level, M = 48 and 64 behind: 16.3 and 19.1
-    // against 15.5 and 15.8).
-    if (c.M <= 64 && (!f8 || (c.ldb_n == 1 && c.M <= 32))) {
+    // against 15.5 and 15.8), and with B as [N, K] rows up to 16 rows (M = 1
+    // and 16: 11.4 and 12.5 us against 14.8 and 15.2; N = 7168: 28.9 and
+    // 32.6 against 64.0 and 64.3).
+    if (c.M <= 64 && (!f8 || (c.ldb_n == 1 && c.M <= 32) || (c.ldb_k == 1 && c.M <= 16))) {
       p.variant = GEMM_VARIANT_SKINNY;
     } else {
       const int64_t T = cdiv(c.M, CfgT128::BM) * cdiv(c.N, CfgT128::BN);
@@ -805,7 +808,14 @@ kfn_dec pick_dec(int dt) {
   }
 }
 kfn_dec pick_dec_bk(int dt) {   // B as [N, K] rows, up to 16 rows of A
-  return dt == DT_F16 ? decode_kernel<16, DT_F16, true> : decode_kernel<16, DT_BF16, true>;
+  switch (dt) {
+    case DT_F16: return decode_kernel<16, DT_F16, true>;
+    case DT_BF16: return decode_kernel<16, DT_BF16, true>;
+    case DT_F8 + 0: return decode_kernel<16, DT_F16, true, 0>;
+    case DT_F8 + 1: return decode_kernel<16, DT_F16, true, 1>;
+    case DT_F8 + 2: return decode_kernel<16, DT_F16, true, 2>;
+    default: return decode_kernel<16, DT_F16, true, 3>;
+  }
 }
 
 int launch_decode(const Call& c, const Plan& p, void* ws, hipStream_t stream) {

@@ -266,12 +266,12 @@ size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16
  * 2^24, and A and B are 16-byte aligned; any other
  * layout returns GEMM_ERR_LAYOUT before anything is enqueued.  M, N and K are
  * masked as in the 16-bit calls (zero fill on K).  Variants: AUTO, MAIN,
- * SPLITK and STREAMK on the 256 x 256 x 64 FP8 tile, and SKINNY (M <= 64)
- * with N-contiguous B: the decode kernel, which widens the bytes to
- * binary16 (exact for both formats) and runs the 16-bit decode path; AUTO
- * takes it up to 32 rows.  SKINNY with K-contiguous B, a forced tile with
- * SKINNY, and TILE64X32 return GEMM_ERR_OPTS.  Workspace contract and other
- * return codes as above.
+ * SPLITK and STREAMK on the 256 x 256 x 64 FP8 tile, and SKINNY (M <= 64
+ * with N-contiguous B, M <= 16 with K-contiguous B): the decode kernel,
+ * which widens the bytes to binary16 (exact for both formats) and runs the
+ * 16-bit decode path; AUTO takes it up to 32 and 16 rows.  SKINNY outside
+ * those bounds or with a forced tile, and TILE64X32, return GEMM_ERR_OPTS.
+ * Workspace contract and other return codes as above.
  */
 int gemm_f8(const void* A, int64_t lda_m, int64_t lda_k,
             const void* B, int64_t ldb_k, int64_t ldb_n,

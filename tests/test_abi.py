@@ -226,7 +226,11 @@ def test_f8_rejected_before_any_device_work():
     assert f8call(lda_m=(1 << 24) + 16) == -9           # rows over 2^24 bytes apart
     assert f8call(ldb_n=(1 << 24) + 16) == -9
     assert f8call(fa=2) == -7 and f8call(fb=-1) == -7   # formats 0 (E4M3) and 1 (E5M2)
-    assert f8call(opts=_lib.Opts(2, 0, 0, 0)) == -7     # no skinny FP8 path
+    # skinny FP8 (the decode kernel): up to 16 rows with B as [N, K] rows, 64
+    # with [K, N] rows, no forced tile
+    assert f8call(M=17, opts=_lib.Opts(2, 0, 0, 0)) == -7
+    assert f8call(M=65, ldb_k=32, ldb_n=1, opts=_lib.Opts(2, 0, 0, 0)) == -7
+    assert f8call(opts=_lib.Opts(2, 0, 0, 15)) == -7
     assert f8call(opts=_lib.Opts(4, 0, 0, 0)) == -7
     assert f8call(opts=_lib.Opts(1, 0, 0, 14)) == -7    # the FP8 tile only
     assert f8call(M=0) == -2 and f8call(ldc=31) == -4 and f8call(A=0) == -1

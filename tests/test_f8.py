@@ -284,20 +284,31 @@ F8_DECODE_CASES = [(1, 2048, 7168, {}), (16, 1040, 1000, {}), (17, 272, 130, {})
                    (40, 1040, 2500, dict(variant="skinny", split_k=5))]
 
 
+F8_DECODE_NK_CASES = [(1, 2048, 7168, {}), (16, 1030, 1000, {}), (5, 272, 130, {}),
+                      (3, 2048, 7168, dict(variant="skinny", split_k=1)),
+                      (9, 1040, 2500, dict(variant="skinny", split_k=5))]
+
+
 @pytest.mark.parametrize("mode", ["int", "uniform"])
 @pytest.mark.parametrize("fa,fb", PAIRS)
-def test_f8_decode(fa, fb, mode):
-    # Up to 32 rows of A with B as [K, N] rows (64 when forced): the decode kernel, the FP8
-    # bytes widened to binary16 (exact for both formats), fp32 sums over K
-    # ranges and the fixed-order reduction.  The cases cover a ragged last
-    # column strip (N = 1040: 16 columns past the eighth strip), ragged last
-    # K ranges, 16, 32 and 64-row kernels, one K range (C written directly)
-    # and a forced split; rows padded with NaN bytes past K and N.
-    for M, N, K, kw in F8_DECODE_CASES:
+@pytest.mark.parametrize("b_layout", ["kn", "nk"])
+def test_f8_decode(fa, fb, mode, b_layout):
+    # Up to 32 rows of A with B as [K, N] rows (64 when forced), up to 16
+    # with B as [N, K] rows: the decode kernel, the FP8 bytes widened to
+    # binary16 (exact for both formats), fp32 sums over K ranges and the
+    # fixed-order reduction.  The cases cover ragged last column strips (N =
+    # 1040: 16 columns past the eighth strip; N = 1030 with [N, K] rows),
+    # ragged last K ranges, 16, 32 and 64-row kernels, one K range (C
+    # written directly) and forced splits; rows padded with NaN bytes past K
+    # and N.
+    for M, N, K, kw in (F8_DECODE_CASES if b_layout == "kn" else F8_DECODE_NK_CASES):
         A, Bt = inputs(M, N, K, 14400 + M + K, mode, fa, fb)
         ref = reference(A, Bt, fa, fb)
         a = f8_rows(A, fa)
-        b = f8_rows(np.ascontiguousarray(Bt.T), fb)          # [K, N] rows
+        if b_layout == "kn":
+            b = f8_rows(np.ascontiguousarray(Bt.T), fb)      # [K, N] rows
+        else:
+            b = f8_rows(Bt, fb).t()                          # [N, K] rows
         p = g.plan(a, b, **kw)
         assert p["variant"] == "skinny" and p["tile_n"] == 128, p
         if "split_k" in kw:
@@ -311,9 +322,9 @@ def test_f8_decode(fa, fb, mode):
 
 
 def test_f8_decode_plan_bounds():
-    # B as [N, K] rows at decode shapes stays on the FP8 tile (split over K),
-    # and so does B as [K, N] rows from 33 rows of A on.
-    for M, nk in ((16, True), (33, False)):
+    # The FP8 tile (split over K) from 17 rows of A with B as [N, K] rows and
+    # from 33 rows with B as [K, N] rows.
+    for M, nk in ((17, True), (33, False)):
         N, K = 512, 4096
         A, Bt = inputs(M, N, K, 14480 + M, "int", "e4m3", "e4m3")
         a = f8_rows(A, "e4m3")
@@ -323,3 +334,5 @@ def test_f8_decode_plan_bounds():
         assert_bits_equal(run(a, b, Out(M, N)), reference(A, Bt, "e4m3", "e4m3"), f"f8 M = {M}, nk {nk}")
     A, Bt = inputs(32, 512, 4096, 14532, "int", "e4m3", "e4m3")
     assert g.plan(f8_rows(A, "e4m3"), f8_rows(np.ascontiguousarray(Bt.T), "e4m3"))["variant"] == "skinny"
+    A, Bt = inputs(16, 512, 4096, 14548, "int", "e4m3", "e4m3")
+    assert g.plan(f8_rows(A, "e4m3"), f8_rows(Bt, "e4m3").t())["variant"] == "skinny"

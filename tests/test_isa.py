@@ -116,9 +116,9 @@ def test_register_tiles_keep_their_mfma(kernels):
 
 def test_decode_kernels_keep_their_mfma(kernels):
     found = _of(kernels, "decode_kernel")
-    assert len(found) == 20                 # 16, 32, 64 rows of A with N-contiguous B, 16 with
-                                            # K-contiguous B; fp16 and bfloat16; and the four
-                                            # FP8 format pairs with N-contiguous B
+    assert len(found) == 24                 # 16, 32, 64 rows of A with N-contiguous B, 16 with
+                                            # K-contiguous B; fp16, bfloat16 and the four FP8
+                                            # format pairs
     for name, ops in found.items():
         want = {"0": "v_mfma_f32_16x16x32_f16", "1": "v_mfma_f32_16x16x32_bf16"}[_targs(name)[1]]
         assert ops[want] >= 8, (name, want)
