@@ -279,9 +279,45 @@ __device__ __forceinline__ void mma_frags(const DmaFrags<CF>& f, f32x16 (&acc)[C
     for (int j = 0; j < CF::FM; ++j) acc[i][j] = mfma<32, DT>(f.fa_[i], f.fb_[j], acc[i][j]);
 }
 
-// DT: DT_F16 or DT_BF16 operands and output.
-template <class CF, bool BKMAJOR, bool PARTIAL, int DT = DT_F16>
+// FP8 operands (F8 = 2 fmt_a + fmt_b, 0 E4M3 and 1 E5M2): a stage of the
+// 16-bit layout then holds 64 k of bytes, and the fragments of its two
+// k-substeps (chunks lo and 2 + lo of a row for lane half lo) together are
+// the 32 bytes one v_mfma_f32_32x32x64_f8f6f4 takes per lane.  That
+// instruction pairs byte b of one operand with byte b of the other, so a k
+// order that A and B share gives the step's whole product.  The DMA batches
+// of the step STAGES-1 ahead sit after the first and the third MFMA.
+__device__ __forceinline__ i32x8 cat16(const f16x8& x, const f16x8& y) {
+  const u32x4 a = __builtin_bit_cast(u32x4, x), b = __builtin_bit_cast(u32x4, y);
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+template <class CF, int F8, bool WITH_DMA, class SA, class SB>
+__device__ __forceinline__ void mma_frags_f8(const DmaFrags<CF>& f0, const DmaFrags<CF>& f1,
+                                             f32x16 (&acc)[CF::FN][CF::FM], SA& sa, SB& sb, uint32_t la,
+                                             uint32_t lb, int64_t t) {
+  constexpr int NQ = CF::FN * CF::FM;
+#pragma unroll
+  for (int i = 0; i < CF::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FM; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat16(f0.fa_[i], f1.fa_[i]),
+                                                                  cat16(f0.fb_[j], f1.fb_[j]), acc[i][j],
+                                                                  F8 % 2, F8 / 2, 0, 0, 0, 0);
+      if constexpr (WITH_DMA) {
+        const int q = i * CF::FM + j;
+        if (q == NQ / 4 - 1) sa.issue_batch(la, t);
+        if (q == 3 * NQ / 4 - 1) sb.issue_batch(lb, t);
+      }
+    }
+}
+
+// DT: DT_F16 or DT_BF16 operands and output.  F8 >= 0: FP8 A and
+// K-contiguous B (formats F8 / 2, F8 % 2; strides and K in bytes, K even,
+// row strides even), binary16 out: the operands are read as byte pairs, so a
+// stage holds 64 k.
+template <class CF, bool BKMAJOR, bool PARTIAL, int DT = DT_F16, int F8 = -1>
 __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
+  static_assert(F8 < 0 || (BKMAJOR && DT == DT_F16), "FP8: K-contiguous B, binary16 out");
   __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -295,13 +331,16 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
   int64_t pm, pn;
   raster_tile(w, a.GM, a.GN, a.panel, pm, pn);
   const int64_t m0 = pm * CF::BM, n0 = pn * CF::BN;
-  const int64_t kb = split * a.k_split;
-  const int64_t ke = (kb + a.k_split < a.K) ? kb + a.k_split : a.K;
+  // FP8: byte offsets and strides halved into 16-bit pair units.
+  constexpr int SH = F8 >= 0 ? 1 : 0;
+  const int64_t kb8 = split * a.k_split;
+  const int64_t kb = kb8 >> SH;
+  const int64_t ke = ((kb8 + a.k_split < a.K) ? kb8 + a.k_split : a.K) >> SH;
 
   DmaSource<CF::DMA_A, true> sa;
   DmaSource<CF::DMA_B, BKMAJOR, CF::BN> sb;
-  sa.init(a.A, a.lda_m, a.lda_k, a.M, m0, kb, wave, lane);
-  sb.init(a.B, a.ldb_n, a.ldb_k, a.N, n0, kb, wave, lane);
+  sa.init(a.A, a.lda_m >> SH, a.lda_k, a.M, m0, kb, wave, lane);
+  sb.init(a.B, a.ldb_n >> SH, a.ldb_k, a.N, n0, kb, wave, lane);
 
   f32x16 acc[CF::FN][CF::FM];
 #pragma unroll
@@ -343,14 +382,21 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
           __builtin_amdgcn_readfirstlane(lds_addr(stage_b(ahead)) + CF::DMA_B * wave * 1024);
       read_frags<CF, BKMAJOR>(f1, stage_a(t), stage_b(t), 1, wm, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mma_frags_dma<CF, DT>(f0, acc, sa, sb, la, lb, tt);
-      __builtin_amdgcn_sched_barrier(0);
-      // First fragments of step t+1 (complete since the last barrier).  On
-      // the last step this reads a stale stage and the values go unused.
-      read_frags<CF, BKMAJOR>(f0, stage_a(t + 1), stage_b(t + 1), 0, wm, wn, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_frags<CF, DT>(f1, acc);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (F8 >= 0) {
+        mma_frags_f8<CF, F8, true>(f0, f1, acc, sa, sb, la, lb, tt);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags<CF, BKMAJOR>(f0, stage_a(t + 1), stage_b(t + 1), 0, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        mma_frags_dma<CF, DT>(f0, acc, sa, sb, la, lb, tt);
+        __builtin_amdgcn_sched_barrier(0);
+        // First fragments of step t+1 (complete since the last barrier).  On
+        // the last step this reads a stale stage and the values go unused.
+        read_frags<CF, BKMAJOR>(f0, stage_a(t + 1), stage_b(t + 1), 0, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags<CF, DT>(f1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       wait_vmcnt<CF::DMA_PER_STAGE * (CF::STAGES - 3)>();   // step t+2 landed
       wg_barrier();
     }
@@ -364,8 +410,12 @@ __global__ __launch_bounds__(CF::NT) void gemm_dma_kernel(KArgs a) {
     __syncthreads();
     read_frags<CF, BKMAJOR>(f0, stage_a(nfull), stage_b(nfull), 0, wm, wn, lane);
     read_frags<CF, BKMAJOR>(f1, stage_a(nfull), stage_b(nfull), 1, wm, wn, lane);
-    mma_frags<CF, DT>(f0, acc);
-    mma_frags<CF, DT>(f1, acc);
+    if constexpr (F8 >= 0) {
+      mma_frags_f8<CF, F8, false>(f0, f1, acc, sa, sb, 0, 0, 0);
+    } else {
+      mma_frags<CF, DT>(f0, acc);
+      mma_frags<CF, DT>(f1, acc);
+    }
   }
 
   // Epilogue: the same C^T-block layout as the register-staged kernel.

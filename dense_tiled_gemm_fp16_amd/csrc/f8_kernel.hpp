@@ -30,7 +30,6 @@
 
 namespace gemmf16 {
 
-typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 enum F8Format { F8_E4M3 = 0, F8_E5M2 = 1 };
 

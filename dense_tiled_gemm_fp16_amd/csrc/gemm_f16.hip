@@ -220,7 +220,9 @@ int64_t max_stride(const Call& c) {
 // Whether a tile's kernels take this call's format and layout (needs
 // p.a_path and p.b_path).
 bool tile_takes(const TileInfo& t, const Call& c, const Plan& p) {
+  // (FP8 on the 128-wide LDS-DMA tiles reads byte pairs: K even.)
   return t.final_fn[c.dt][p.a_path * 3 + p.b_path] != nullptr &&
+         !(c.dt >= DT_F8 && t.id != TILE_F8 && c.K % 2 != 0) &&
          !(t.n_mult && p.b_path == PATH_RVEC && (c.N % t.n_mult != 0 || c.N < t.n_mult)) &&
          !(t.max_k && c.K > t.max_k) && !(t.max_ld && max_stride(c) > t.max_ld);
 }
@@ -437,9 +439,12 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         ldb % 16 != 0 || ((uintptr_t)c.B & 15u) || c.lda_m > (INT64_C(1) << 24) ||
         ldb > (INT64_C(1) << 24) || (b_n && c.N % 16 != 0))
       return GEMM_ERR_LAYOUT;
+    // (The 128 x 128 and 64 x 128 LDS-DMA tiles also take FP8 with
+    // K-contiguous B and K even; a forced one with another layout hands
+    // over to the FP8 tile.)
     if ((variant == GEMM_VARIANT_SKINNY && (!(b_n || (b_k && c.M <= 16)) || want_tile)) ||
         variant == GEMM_VARIANT_TILE64X32 ||
-        (want_tile && want_tile != TILE_F8))
+        (want_tile && want_tile != TILE_F8 && want_tile != TILE_DMA128 && want_tile != TILE_DMA64X128))
       return GEMM_ERR_OPTS;
   }
 
@@ -470,8 +475,13 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       // against 23.7; 128 x 2048 x 2048 15.4 against 20.8; 96 x 8192 x 8192
       // 31.1 against 72.0; 1024 x 2048 x 2048 level).  For operands that
       // tile does not read, from K >= 2 max(M, N) and K >= 1024 (two K
-      // ranges of at least 512 on the 256x256 tile).
-      const bool split = dma128_reads(c) ? c.K >= 2048 : (c.K >= 2 * mn && c.K >= 1024);
+      // ranges of at least 512 on the 256x256 tile).  FP8 on that tile from
+      // K >= 4096 and K >= 4 max(M, N): its main plans run further ahead
+      // (1024^2 x 2048: 10.6 us on the 64 x 128 tile against 18.2 split;
+      // 1024^2 x 8192: 24.4 split against 37.8).
+      const bool dma = dma128_reads(c);
+      const bool split = f8 && dma ? (c.K >= 4096 && c.K >= 4 * mn)
+                                   : (dma ? c.K >= 2048 : (c.K >= 2 * mn && c.K >= 1024));
       p.variant = (2 * T <= cus && split) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
     }
   }
@@ -515,9 +525,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
   // Tile.
   switch (p.variant) {
     case GEMM_VARIANT_MAIN:
-      if (f8) {
-        p.tile_id = TILE_F8;
-      } else if (want_tile) {
+      if (want_tile) {
         p.tile_id = want_tile;
       } else {
         // The 128x128 LDS-DMA tile (fp16, K-contiguous A, B either way with
@@ -533,11 +541,17 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         // K >= 8192 (2048^2 x 8192: 86.5 against 89.9; x 16384: 140.8 against
         // 166.4; 1792^2 x 8192: 74.1 against 86.2); with a shorter K the
         // 128x128 DMA tile is ahead of it (2048^2 x 4096: 49.0 against 56.1;
-        // 2048^2 x 6144: 70.9 against 73.3; 1536^2 x 3072: 34.6 against 38.6).  Without that tile: 256x256 tiles from a
-        // quarter wave on when K is not short, else the 128x128 register tile.
+        // 2048^2 x 6144: 70.9 against 73.3; 1536^2 x 3072: 34.6 against 38.6).
+        // Without that tile: 256x256 tiles from a quarter wave on when K is
+        // not short, else the 128x128 register tile.  FP8 (B as [N, K] rows,
+        // K even) takes the same rule with the FP8 tile as the 256x256 one
+        // (per call: 1024^3 7.7 us against 13.6; 2048^3 14.9 against 21.1;
+        // 2048^2 x 4096 28.4 against 41.6; 2560^3 level; 3072^3 51.1 against
+        // 32.8 on the FP8 tile); other FP8 layouts run on the FP8 tile.
         if ((rc = need_cus())) return rc;
         const int64_t t256 = cdiv(c.M, 256) * cdiv(c.N, 256);
-        const bool t14 = dma_tile_takes(c, p);
+        const bool t14 = f8 || dma_tile_takes(c, p);
+        const int big_tile = f8 ? TILE_F8 : TILE_DMA256A128;
         const bool t7 = tile_takes(tile_info(TILE_DMA128), c, p);
         const bool big = 16 * t256 >= 5 * (int64_t)cus;
         const bool sk_small = small_grid_streamk(c, t256, cus) && (16 * t256 < 3 * (int64_t)cus ? c.K >= 4096 : c.K >= 8192);
@@ -549,9 +563,11 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
         // tiles) on it falls behind (22.3 against 20.0).
         const int64_t t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
         if (t14 && (packed_b || big || sk_small))
-          p.tile_id = TILE_DMA256A128;
+          p.tile_id = big_tile;
         else if (t7 && !big)
           p.tile_id = 4 * t128 <= (int64_t)cus ? TILE_DMA64X128 : TILE_DMA128;
+        else if (f8)
+          p.tile_id = TILE_F8;
         else
           p.tile_id = (2 * t256 >= cus || ((quarter || small_grid_streamk(c, t256, cus)) && t14))
                           ? TILE_DMA256A128 : TILE_T128;
@@ -570,24 +586,24 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       // the 256x256 full-line-A tile once the output holds a whole one (it
       // falls back to 128x128 for layouts it does not take).
       bool dma128 = false;
-      if (!f8 && !want_tile && !pack_any && tile_takes(tile_info(TILE_DMA128), c, p)) {
+      if (!want_tile && !pack_any && tile_takes(tile_info(TILE_DMA128), c, p)) {
         if ((rc = need_cus())) return rc;
         const int64_t t128 = cdiv(c.M, 128) * cdiv(c.N, 128);
         const int64_t s7 = std::min<int64_t>((int64_t)cus / t128, c.K / 512);
         dma128 = c.M < 256 || c.N < 256 || (s7 >= 1 && c.K <= 2048 * s7);
       }
-      if (f8)
-        p.tile_id = TILE_F8;
-      else if (want_tile)
+      if (want_tile)
         p.tile_id = want_tile;
       else if (dma128)
         p.tile_id = TILE_DMA128;
+      else if (f8)
+        p.tile_id = TILE_F8;
       else
         p.tile_id = (c.M >= 256 && c.N >= 256) ? TILE_DMA256A128 : TILE_T128;
       break;
     }
     case GEMM_VARIANT_STREAMK:
-      if (!f8 && want_tile && want_tile != TILE_DMA256A128) return GEMM_ERR_OPTS;
+      if (want_tile && want_tile != (f8 ? TILE_F8 : TILE_DMA256A128)) return GEMM_ERR_OPTS;
       p.tile_id = f8 ? TILE_F8 : TILE_DMA256A128;
       break;
     case GEMM_VARIANT_TILE64X32:
@@ -648,7 +664,7 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
     // to the 128x128 tile, which covers every layout in both formats.  A
     // chain that ends without a taker (a tile without this format) is an
     // option error, never a loop.
-    const int next = c.dt == DT_F16 ? t.fallback : TILE_T128;
+    const int next = c.dt == DT_F16 ? t.fallback : (c.dt == DT_BF16 ? TILE_T128 : TILE_F8);
     if (next <= 0 || next > TILE_MAX || next == p.tile_id) return GEMM_ERR_OPTS;
     p.tile_id = next;
   }

@@ -36,6 +36,7 @@
 namespace gemmf16 {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -93,7 +93,13 @@ TileInfo make_info(int id) {
 }
 
 // The LDS-DMA kernel takes K-contiguous A with K- or N-contiguous B only;
-// bfloat16 where asked.
+// bfloat16, and FP8 with K-contiguous B, where asked.
+template <int F8, class CF>
+void fill_dma_f8(TileInfo& t) {
+  t.final_fn[DT_F8 + F8][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, false, DT_F16, F8>;
+  t.partial_fn[DT_F8 + F8][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true, DT_F16, F8>;
+}
+
 template <class CF, bool WITH_BF16 = false>
 TileInfo make_dma_info(int id, int fallback) {
   TileInfo t;
@@ -112,6 +118,10 @@ TileInfo make_dma_info(int id, int fallback) {
     t.final_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, false, DT_BF16>;
     t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_KVEC] = gemm_dma_kernel<CF, true, true, DT_BF16>;
     t.partial_fn[DT_BF16][PATH_KVEC * 3 + PATH_RVEC] = gemm_dma_kernel<CF, false, true, DT_BF16>;
+    fill_dma_f8<0, CF>(t);
+    fill_dma_f8<1, CF>(t);
+    fill_dma_f8<2, CF>(t);
+    fill_dma_f8<3, CF>(t);
   }
   t.fallback = fallback;
   t.n_mult = 8;

@@ -243,15 +243,25 @@ def test_f8_plans():
     info = _lib.PlanInfo()
     for fa, fb in ((0, 0), (0, 1), (1, 0), (1, 1)):
         rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 1, 704, PC, 520, 600, 520, 700, fa, fb,
-                                ctypes.byref(_lib.Opts(1, 0, 4, 0)), ctypes.byref(info))
+                                ctypes.byref(_lib.Opts(1, 0, 4, 15)), ctypes.byref(info))
         assert rc == 0
         assert (info.tile_id, info.tile_m, info.tile_n, info.tile_k) == (15, 256, 256, 64)
         assert (info.split_k, info.grid, info.workspace_bytes) == (1, 9, 0)
-    rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 1, 704, PC, 520, 600, 520, 700, 0, 0,
-                            ctypes.byref(_lib.Opts(3, 3, -1, 0)), ctypes.byref(info))
-    assert rc == 0 and info.split_k == 3 and info.workspace_bytes == 3 * 600 * 520 * 4
-    assert g.lib.gemm_f8_workspace_bytes(600, 520, 700, ctypes.byref(_lib.Opts(3, 3, -1, 0))) \
-        == info.workspace_bytes
+    for tile in (15, 7, 8):                 # forced tiles plan without the device
+        rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 1, 704, PC, 520, 600, 520, 700, 0, 0,
+                                ctypes.byref(_lib.Opts(3, 3, -1, tile)), ctypes.byref(info))
+        assert rc == 0 and info.split_k == 3 and info.workspace_bytes == 3 * 600 * 520 * 4
+        assert info.tile_id == tile
+        assert g.lib.gemm_f8_workspace_bytes(600, 520, 700, ctypes.byref(_lib.Opts(3, 3, -1, tile))) \
+            == info.workspace_bytes
+    # the 128-wide tiles read FP8 byte pairs of K-contiguous B: B [K, N] rows
+    # or an odd K hand over to the FP8 tile
+    rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 528, 1, PC, 528, 600, 528, 700, 0, 0,
+                            ctypes.byref(_lib.Opts(1, 0, 4, 7)), ctypes.byref(info))
+    assert rc == 0 and info.tile_id == 15
+    rc = g.lib.gemm_f8_plan(PA, 704, 1, PB, 1, 704, PC, 520, 600, 520, 701, 0, 0,
+                            ctypes.byref(_lib.Opts(1, 0, 4, 8)), ctypes.byref(info))
+    assert rc == 0 and info.tile_id == 15
 
 
 def test_packed_b_rejected_before_any_device_work():

@@ -322,17 +322,84 @@ def test_f8_decode(fa, fb, mode, b_layout):
 
 
 def test_f8_decode_plan_bounds():
-    # The FP8 tile (split over K) from 17 rows of A with B as [N, K] rows and
-    # from 33 rows with B as [K, N] rows.
+    # The tiled plans (split over K) from 17 rows of A with B as [N, K] rows
+    # and from 33 rows with B as [K, N] rows.
     for M, nk in ((17, True), (33, False)):
         N, K = 512, 4096
         A, Bt = inputs(M, N, K, 14480 + M, "int", "e4m3", "e4m3")
         a = f8_rows(A, "e4m3")
         b = f8_rows(Bt, "e4m3").t() if nk else f8_rows(np.ascontiguousarray(Bt.T), "e4m3")
         p = g.plan(a, b)
-        assert p["variant"] != "skinny" and p["tile_id"] == 15, p
+        assert p["variant"] != "skinny" and p["tile_id"] in (7, 15), p
         assert_bits_equal(run(a, b, Out(M, N)), reference(A, Bt, "e4m3", "e4m3"), f"f8 M = {M}, nk {nk}")
     A, Bt = inputs(32, 512, 4096, 14532, "int", "e4m3", "e4m3")
     assert g.plan(f8_rows(A, "e4m3"), f8_rows(np.ascontiguousarray(Bt.T), "e4m3"))["variant"] == "skinny"
     A, Bt = inputs(16, 512, 4096, 14548, "int", "e4m3", "e4m3")
     assert g.plan(f8_rows(A, "e4m3"), f8_rows(Bt, "e4m3").t())["variant"] == "skinny"
+
+
+@pytest.mark.parametrize("tile", [7, 8])
+@pytest.mark.parametrize("mode", ["int", "uniform"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_f8_128_wide_dma_tiles(tile, fa, fb, mode):
+    # FP8 with B as [N, K] rows on the 128 x 128 and 64 x 128 LDS-DMA tiles:
+    # byte pairs through the 16-bit stages (64 k per stage) and one f8f6f4
+    # MFMA per block and stage; ragged M, N and K tails, rows padded with NaN
+    # bytes; main and split-K.
+    M, N, K = 600, 520, 700
+    A, Bt = inputs(M, N, K, 14600 + tile, mode, fa, fb)
+    ref = reference(A, Bt, fa, fb)
+    a, b = f8_rows(A, fa), f8_rows(Bt, fb).t()
+    for kw in (dict(variant="main", tile=tile), dict(variant="splitk", tile=tile, split_k=3)):
+        p = g.plan(a, b, **kw)
+        assert p["tile_id"] == tile, p
+        got = run(a, b, Out(M, N), **kw)
+        what = f"f8 tile {tile} {fa}x{fb} {mode} {kw}"
+        if mode == "int":
+            assert_bits_equal(got, ref, what)
+        else:
+            assert_close(got, ref, what)
+
+
+@pytest.mark.parametrize("K", [2, 64, 100, 128, 130, 254, 1000])
+def test_f8_128_wide_dma_tiles_k_tails(K):
+    M, N = 300, 264
+    A, Bt = inputs(M, N, K, 14700 + K, "int", "e5m2", "e4m3")
+    ref = reference(A, Bt, "e5m2", "e4m3")
+    a, b = f8_rows(A, "e5m2"), f8_rows(Bt, "e4m3").t()
+    for tile in (7, 8):
+        assert_bits_equal(run(a, b, Out(M, N), variant="main", tile=tile), ref, f"f8 tile {tile} K={K}")
+
+
+def test_f8_odd_k_hands_the_128_wide_tiles_over():
+    # Byte pairs need K even: an odd K, or B as [K, N] rows, runs on the FP8 tile.
+    M, N, K = 300, 272, 129
+    A, Bt = inputs(M, N, K, 14790, "int", "e4m3", "e4m3")
+    a = f8_rows(A, "e4m3")
+    for b in (f8_rows(Bt, "e4m3").t(), f8_rows(np.ascontiguousarray(Bt.T), "e4m3")):
+        p = g.plan(a, b, variant="main", tile=7)
+        assert p["tile_id"] == 15, p
+        assert_bits_equal(run(a, b, Out(M, N), variant="main", tile=7), reference(A, Bt, "e4m3", "e4m3"),
+                          f"f8 tile 7 handed over, b.stride={b.stride()}")
+
+
+@pytest.mark.parametrize("M,N,K,b_layout,variant,tile", [
+    (1024, 1024, 1024, "nk", "main", 8), (2048, 2048, 2048, "nk", "main", 7),
+    (3072, 3072, 3072, "nk", "main", 15), (1024, 1024, 2048, "nk", "main", 8),
+    (1024, 1024, 8192, "nk", "splitk", 7), (2048, 2048, 2048, "kn", "main", 15),
+    (2048, 2048, 2049, "nk", "main", 15)])
+def test_f8_tile_rule(M, N, K, b_layout, variant, tile):
+    # FP8 with B as [N, K] rows and K even takes the fp16 rule's 128-wide
+    # LDS-DMA tiles below 80 tiles of 256 x 256 (256 compute units), split K
+    # from K >= 4096 and 4 max(M, N); other layouts and larger grids take the
+    # FP8 tile.  Integer inputs: every plan gives the oracle's bits on
+    # sampled rows.
+    A, Bt = inputs(M, N, K, 14800 + M + K, "int", "e4m3", "e4m3")
+    a = f8_rows(A, "e4m3")
+    b = f8_rows(Bt, "e4m3").t() if b_layout == "nk" else f8_rows(np.ascontiguousarray(Bt.T), "e4m3")
+    p = g.plan(a, b)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (p["variant"], p["tile_id"]) == (variant, tile), p
+    got = run(a, b, Out(M, N))
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(7, M, 97)]))
+    assert_bits_equal(got[rows], reference(A, Bt, "e4m3", "e4m3", rows), f"f8 {M}x{N}x{K} {b_layout} plan {p}")

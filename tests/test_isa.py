@@ -102,9 +102,11 @@ def test_dma_tiles_keep_their_mfma(kernels):
         want = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_32x32x16_bf16"}[dt]
         assert ops[want] >= 16, (name, want, ops[want])
     for name, ops in _of(kernels, "gemm_dma_kernel").items():
-        dt = int(_targs(name)[3])           # <Cfg<..>, kmajor, partial, format>
-        want = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_32x32x16_bf16"}[dt]
-        assert ops[want] >= 16, (name, want, ops[want])
+        args = _targs(name)                 # <Cfg<..>, kmajor, partial, format, FP8 formats>
+        dt, f8 = int(args[3]), int(args[4])
+        want = ("v_mfma_f32_32x32x64_f8f6f4" if f8 >= 0 else
+                {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_32x32x16_bf16"}[dt])
+        assert ops[want] >= 4 if f8 >= 0 else ops[want] >= 16, (name, want, ops[want])
 
 
 def test_register_tiles_keep_their_mfma(kernels):
