@@ -114,7 +114,8 @@ typedef struct gemm_f16_opts {
  *      for the decode kernel)
  *   6  256x256 register path (fp16; where tile 13 cannot read the layout)
  *   7  128x128 LDS-DMA, 4-stage ring (fp16, bfloat16; K-contiguous A, B
- *      either way with N % 8 == 0 when B is N-contiguous)
+ *      either way with N % 8 == 0 when B is N-contiguous; FP8 with
+ *      K-contiguous B and K even)
  *   8  64x128 LDS-DMA, the same ring with two waves (as tile 7)
  *   13 256x256 LDS-DMA, 4-stage ring (fp16; the same layouts, any stride)
  *   14 256x256 LDS-DMA with 128-byte A rows (fp16, bfloat16; the same
@@ -122,7 +123,7 @@ typedef struct gemm_f16_opts {
  *   15 256x256 FP8 (the FP8 entry points only)
  * A tile that does not take the operand layout hands over to the next one
  * that does: fp16 along 7 -> 1, 8 -> 1 and 14 -> 13 -> 6, bfloat16 straight
- * to 1.
+ * to 1, FP8 to 15.
  * Forcing an id without kernels for the call's format returns
  * GEMM_ERR_OPTS. */
 
@@ -266,7 +267,11 @@ size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16
  * 2^24, and A and B are 16-byte aligned; any other
  * layout returns GEMM_ERR_LAYOUT before anything is enqueued.  M, N and K are
  * masked as in the 16-bit calls (zero fill on K).  Variants: AUTO, MAIN,
- * SPLITK and STREAMK on the 256 x 256 x 64 FP8 tile, and SKINNY (M <= 64
+ * SPLITK and STREAMK on the 256 x 256 x 64 FP8 tile (MAIN and SPLITK also
+ * on the 128 x 128 and 64 x 128 LDS-DMA tiles, tile ids 7 and 8, for
+ * K-contiguous B and K even: AUTO takes them below 80 tiles of 256 x 256 on
+ * 256 compute units, and splits K there from K >= 4096 and K >= 4 max(M, N)),
+ * and SKINNY (M <= 64
  * with N-contiguous B, M <= 16 with K-contiguous B): the decode kernel,
  * which widens the bytes to binary16 (exact for both formats) and runs the
  * 16-bit decode path; AUTO takes it up to 32 and 16 rows.  SKINNY outside
