@@ -226,10 +226,10 @@ size_t gemm_f16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_
  * The same product with bfloat16 inputs and output: A, B and C hold
  * bfloat16 (the upper 16 bits of an IEEE binary32) instead of binary16;
  * accumulation is fp32 and C is rounded to nearest-even bfloat16.  The same
- * arguments, validation, options (variant AUTO, MAIN, SKINNY or SPLITK; the
- * 64x32x32 variant and tiles other than the 128x128, skinny and full-line-A
- * ones are fp16-only and return GEMM_ERR_OPTS), workspace contract and
- * return codes as the fp16 functions above.  The pages fix fp16; bfloat16 is
+ * arguments, validation, options (every variant but TILE64X32; tiles 2, 6
+ * and 13 hold fp16 kernels only, and forcing them, or the 64x32x32
+ * variant, returns GEMM_ERR_OPTS), workspace contract and return codes as
+ * the fp16 functions above.  The pages fix fp16; bfloat16 is
  * the same computation in the other 16-bit format the matrix cores take
  * (TileLang tutorial, ch. 14, section 5: lower-precision variants keep the
  * GEMM skeleton and change the matrix instruction).

@@ -197,7 +197,14 @@ def test_bf16_options_and_plans():
         return g.lib.gemm_bf16_ex(PA, 64, 1, PB, 32, 1, PC, 32, 16, 32, 64, 0, 0, 0, o)
     assert bcall(_lib.Opts(4, 0, 0, 0)) == -7      # the 64x32x32 variant is fp16-only
     assert bcall(_lib.Opts(1, 0, 4, 11)) == -7     # a tile without bfloat16 kernels
+    for tile in (2, 6, 13, 15):                    # fp16-only (2, 6, 13) and FP8-only (15)
+        assert bcall(_lib.Opts(1, 0, 4, tile)) == -7, tile
     assert bcall(_lib.Opts(1, 0, 4, 99)) == -7
+    info = _lib.PlanInfo()
+    for tile in (7, 8, 14, 1):                     # bfloat16 kernels: forced tiles plan on the CPU
+        rc = g.lib.gemm_bf16_plan(PA, 1024, 1, PB, 512, 1, PC, 512, 300, 512, 1024,
+                                  ctypes.byref(_lib.Opts(1, 0, 4, tile)), ctypes.byref(info))
+        assert rc == 0 and info.tile_id == tile, (tile, rc, info.tile_id)
     info = _lib.PlanInfo()
     o = _lib.Opts(3, 4, -1, 1)                     # forced split-K on the 128x128 tile
     rc = g.lib.gemm_bf16_plan(PA, 1024, 1, PB, 32, 1, PC, 32, 16, 32, 1024, ctypes.byref(o),
