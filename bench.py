@@ -548,16 +548,24 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic("main_131072x2048x7168")
 
-    # ---- decode-shaped M = 1, B N-contiguous (the workload) and as [N, K] rows
-    def decode_line(b_layout):
+    # ---- decode-shaped M = 1, B N-contiguous (the workload) and as [N, K]
+    # rows; in fp16, and with E4M3 operands (fp16 out)
+    def decode_line(b_layout, fmt="f16"):
         m1 = 1
-        copies = 40                                   # 40 x 28 MiB of B > 1 GiB
-        a1 = to_dev(synth.matrix(m1, K, 3001, synth.TENSOR_A))
+        esz = 1 if fmt == "e4m3" else 2
+        copies = 40 * (2 // esz)                      # 40 x 28 MiB (80 x 14 MiB) of B > 1 GiB
+
+        def dev_bits(bits):
+            if fmt == "e4m3":
+                return torch.from_numpy(bits).to(dev).view(torch.float8_e4m3fn)
+            return to_dev(bits)
+        kw = {} if fmt == "f16" else {"fmt": fmt}
+        a1 = dev_bits(synth.matrix(m1, K, 3001, synth.TENSOR_A, **kw))
         if b_layout == "col":
-            b1 = to_dev(synth.matrix(K, N, 3001, synth.TENSOR_B, order="col")).t()
+            b1 = dev_bits(synth.matrix(K, N, 3001, synth.TENSOR_B, order="col", **kw)).t()
             bs = [b1.t().clone().t() for _ in range(copies)]
         else:
-            b1 = to_dev(synth.matrix(K, N, 3001, synth.TENSOR_B))
+            b1 = dev_bits(synth.matrix(K, N, 3001, synth.TENSOR_B, **kw))
             bs = [b1.clone() for _ in range(copies)]
         c1 = torch.empty((m1, N), dtype=torch.float16, device=dev)
         p1 = g.plan(a1, b1, c1)
@@ -592,9 +600,10 @@ def main():
                 per_call.append(e0.elapsed_time(e1) / copies)
         per_call.sort()
         med1 = per_call[len(per_call) // 2]
-        bytes1 = 2.0 * (m1 * K + K * N + m1 * N)
+        bytes1 = esz * (m1 * K + K * N) + 2.0 * m1 * N
         del graph, bs
         what = "B [K, N]" if b_layout == "row" else "B as [N, K] rows"
+        what += ", E4M3 operands, fp16 out" if fmt == "e4m3" else ""
         return {"workload": f"M={m1} N={N} K={K}, {what}, B rotated over {copies} copies",
                 "plan": {k: p1[k] for k in ("variant", "tile_m", "tile_n", "split_k", "grid",
                                              "grid2", "b_path")},
@@ -606,6 +615,8 @@ def main():
 
     skinny = decode_line("row")
     skinny_nk = decode_line("col")
+    skinny_f8 = decode_line("row", "e4m3")
+    skinny_f8_nk = decode_line("col", "e4m3")
 
     # ---- grouped product: the same tokens routed to 32 experts
     G = 32
@@ -762,6 +773,8 @@ def main():
                    "wall_s": wall},
         "skinny_m1": skinny,
         "skinny_m1_nk": skinny_nk,
+        "skinny_m1_f8": skinny_f8,
+        "skinny_m1_f8_nk": skinny_f8_nk,
         "grouped_moe": grouped,
         "bf16": bf16,
         "f8": f8,

@@ -279,12 +279,13 @@ def test_f8_bn_moe_shape_full_coverage():
 
 
 F8_DECODE_CASES = [(1, 2048, 7168, {}), (16, 1040, 1000, {}), (17, 272, 130, {}),
-                   (64, 528, 96, dict(variant="skinny")),
+                   (64, 528, 96, dict(variant="skinny")), (2, 16, 1, {}), (7, 48, 7, {}),
                    (3, 2048, 7168, dict(variant="skinny", split_k=1)),
                    (40, 1040, 2500, dict(variant="skinny", split_k=5))]
 
 
-F8_DECODE_NK_CASES = [(1, 2048, 7168, {}), (16, 1030, 1000, {}), (5, 272, 130, {}),
+F8_DECODE_NK_CASES = [(1, 2048, 7168, {}), (16, 1030, 1000, {}), (5, 272, 130, {}), (1, 3, 1, {}),
+                      (16, 1, 9, {}),
                       (3, 2048, 7168, dict(variant="skinny", split_k=1)),
                       (9, 1040, 2500, dict(variant="skinny", split_k=5))]
 
