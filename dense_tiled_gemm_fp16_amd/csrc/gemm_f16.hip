@@ -476,12 +476,11 @@ int make_plan(const Call& c, const gemm_f16_opts* o, Plan& p, bool allow_pack = 
       // 31.1 against 72.0; 1024 x 2048 x 2048 level).  For operands that
       // tile does not read, from K >= 2 max(M, N) and K >= 1024 (two K
       // ranges of at least 512 on the 256x256 tile).  FP8 on that tile from
-      // K >= 4096 and K >= 4 max(M, N): its main plans run further ahead
-      // (1024^2 x 2048: 10.6 us on the 64 x 128 tile against 18.2 split;
-      // 1024^2 x 8192: 24.4 split against 37.8).
+      // K >= 4096: its main plans run further ahead (1024^2 x 2048: 10.6 us
+      // on the 64 x 128 tile against 18.2 split; 1024^2 x 8192: 24.4 split
+      // against 37.8).
       const bool dma = dma128_reads(c);
-      const bool split = f8 && dma ? (c.K >= 4096 && c.K >= 4 * mn)
-                                   : (dma ? c.K >= 2048 : (c.K >= 2 * mn && c.K >= 1024));
+      const bool split = dma ? c.K >= (f8 ? 4096 : 2048) : (c.K >= 2 * mn && c.K >= 1024);
       p.variant = (2 * T <= cus && split) ? GEMM_VARIANT_SPLITK : GEMM_VARIANT_MAIN;
     }
   }

@@ -270,7 +270,7 @@ size_t gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16
  * SPLITK and STREAMK on the 256 x 256 x 64 FP8 tile (MAIN and SPLITK also
  * on the 128 x 128 and 64 x 128 LDS-DMA tiles, tile ids 7 and 8, for
  * K-contiguous B and K even: AUTO takes them below 80 tiles of 256 x 256 on
- * 256 compute units, and splits K there from K >= 4096 and K >= 4 max(M, N)),
+ * 256 compute units, and splits K there from K >= 4096),
  * and SKINNY (M <= 64
  * with N-contiguous B, M <= 16 with K-contiguous B): the decode kernel,
  * which widens the bytes to binary16 (exact for both formats) and runs the

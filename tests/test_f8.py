@@ -388,11 +388,12 @@ def test_f8_odd_k_hands_the_128_wide_tiles_over():
     (1024, 1024, 1024, "nk", "main", 8), (2048, 2048, 2048, "nk", "main", 7),
     (3072, 3072, 3072, "nk", "main", 15), (1024, 1024, 2048, "nk", "main", 8),
     (1024, 1024, 8192, "nk", "splitk", 7), (2048, 2048, 2048, "kn", "main", 15),
-    (2048, 2048, 2049, "nk", "main", 15)])
+    (2048, 2048, 2049, "nk", "main", 15), (32, 2048, 7168, "nk", "splitk", 7),
+    (48, 2048, 7168, "kn", "splitk", 15)])
 def test_f8_tile_rule(M, N, K, b_layout, variant, tile):
     # FP8 with B as [N, K] rows and K even takes the fp16 rule's 128-wide
     # LDS-DMA tiles below 80 tiles of 256 x 256 (256 compute units), split K
-    # from K >= 4096 and 4 max(M, N); other layouts and larger grids take the
+    # from K >= 4096; other layouts and larger grids take the
     # FP8 tile.  Integer inputs: every plan gives the oracle's bits on
     # sampled rows.
     A, Bt = inputs(M, N, K, 14800 + M + K, "int", "e4m3", "e4m3")
