@@ -303,6 +303,14 @@ int launch_pack_b(const uint16_t* B, int64_t ldb_k, int64_t ldb_n, int64_t K, in
       return GEMM_ERR_HIP;
     return GEMM_OK;
   }
+  if (kvec) {   // K-contiguous aligned rows: a line per 8 threads, over pairs of blocks
+    int64_t threads = cdiv(N, 256) * cdiv(S, 2) * 2048;
+    void* largs[] = {&B, &ldb_n, &K, &N, &S, &threads, &Bp};
+    if (hipLaunchKernel((const void*)pack_b_lines_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), largs,
+                        0, stream) != hipSuccess)
+      return GEMM_ERR_HIP;
+    return GEMM_OK;
+  }
   void* args[] = {&B, &ldb_k, &ldb_n, &K, &N, &S, &slots, &Bp, &kvec};
   if (hipLaunchKernel((const void*)pack_b_kernel, dim3((unsigned)cdiv(slots, 256)), dim3(256), args, 0,
                       stream) != hipSuccess)
