@@ -22,7 +22,7 @@ PATHS = {0: "gather", 1: "kvec", 2: "rvec", 3: "packed"}
 
 EXPORTS = ["gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_plan_cus", "gemm_f16_workspace_bytes",
            "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_plan", "gemm_bf16_workspace_bytes",
-           "gemm_f8", "gemm_f8_ex", "gemm_f8_plan", "gemm_f8_workspace_bytes",
+           "gemm_f8", "gemm_f8_ex", "gemm_f8_plan", "gemm_f8_plan_cus", "gemm_f8_workspace_bytes",
            "gemm_f16_packed_b_bytes", "gemm_f16_pack_b", "gemm_f16_packed",
            "gemm_f16_grouped", "gemm_bf16_grouped", "gemm_f8_grouped", "gemm_f16_grouped_workspace_bytes",
            "gemm_f16_noalloc", "gemm_f16_status_string", "gemm_f16_version"]
@@ -78,6 +78,9 @@ def _load():
     lib.gemm_f8_plan.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i32, i32,
                                  ctypes.POINTER(Opts), ctypes.POINTER(PlanInfo)]
     lib.gemm_f8_plan.restype = ctypes.c_int
+    lib.gemm_f8_plan_cus.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i32, i32, i32,
+                                     ctypes.POINTER(Opts), ctypes.POINTER(PlanInfo)]
+    lib.gemm_f8_plan_cus.restype = ctypes.c_int
     lib.gemm_f8_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(Opts)]
     lib.gemm_f8_workspace_bytes.restype = sz
     lib.gemm_f16_packed_b_bytes.argtypes = [i64, i64]

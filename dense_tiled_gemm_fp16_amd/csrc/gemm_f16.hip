@@ -1360,6 +1360,15 @@ int gemm_f8_plan(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int
   return plan_impl(dt, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info);
 }
 
+int gemm_f8_plan_cus(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
+                     int64_t ldb_n, const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                     int32_t fmt_a, int32_t fmt_b, int32_t cus, const gemm_f16_opts* opts,
+                     gemm_f16_plan_info* info) {
+  const int dt = f8_dt(fmt_a, fmt_b);
+  if (dt < 0 || cus < 1 || cus > 65536) return GEMM_ERR_OPTS;
+  return plan_impl(dt, A, lda_m, lda_k, B, ldb_k, ldb_n, C, ldc, M, N, K, opts, info, cus);
+}
+
 int gemm_f8_ex(const void* A, int64_t lda_m, int64_t lda_k, const void* B, int64_t ldb_k,
                int64_t ldb_n, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t fmt_a,
                int32_t fmt_b, void* stream, void* workspace, size_t workspace_bytes,

@@ -292,6 +292,13 @@ int gemm_f8_plan(const void* A, int64_t lda_m, int64_t lda_k,
                  const void* C, int64_t ldc,
                  int64_t M, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b,
                  const gemm_f16_opts* opts, gemm_f16_plan_info* info);
+/* gemm_f8_plan for a device with `cus` compute units, without any device
+ * query (as gemm_f16_plan_cus; cus outside [1, 65536] is GEMM_ERR_OPTS). */
+int gemm_f8_plan_cus(const void* A, int64_t lda_m, int64_t lda_k,
+                     const void* B, int64_t ldb_k, int64_t ldb_n,
+                     const void* C, int64_t ldc,
+                     int64_t M, int64_t N, int64_t K, int32_t fmt_a, int32_t fmt_b, int32_t cus,
+                     const gemm_f16_opts* opts, gemm_f16_plan_info* info);
 size_t gemm_f8_workspace_bytes(int64_t M, int64_t N, int64_t K, const gemm_f16_opts* opts);
 
 /*

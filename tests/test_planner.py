@@ -190,3 +190,40 @@ def test_forced_options_take_no_copies():
     o = _lib.Opts(1, 0, 0, 0)
     p = plan(2048, 2100, 2100, opts=o)
     assert (p.a_path, p.b_path, p.workspace_bytes) == (GATHER, GATHER, 0)
+
+
+# ------------------------------------------------------------------ FP8 (gemm_f8_plan_cus)
+
+def plan8(M, N, K, b="nk", cus=256, opts=None):
+    """FP8 A [M, K] K-contiguous (rows padded to 16 bytes); B as [N, K] rows
+    ("nk") or [K, N] rows ("kn", N % 16 == 0)."""
+    lda = K + (-K) % 16
+    ldb_k, ldb_n = (1, lda) if b == "nk" else (N, 1)
+    info = _lib.PlanInfo()
+    rc = g.lib.gemm_f8_plan_cus(PA, lda, 1, PB, ldb_k, ldb_n, PC, N, M, N, K, 0, 0, cus,
+                                ctypes.byref(opts) if opts else None, ctypes.byref(info))
+    assert rc == 0, rc
+    return info
+
+
+@pytest.mark.parametrize("M,N,K,b,variant,tile,split", [
+    (1, 2048, 7168, "kn", SKINNY, 3, 16), (32, 2048, 7168, "kn", SKINNY, 3, 16),   # decode kernel
+    (1, 2048, 7168, "nk", SKINNY, 3, 16), (16, 2048, 7168, "nk", SKINNY, 3, 16),
+    (33, 2048, 7168, "kn", SPLITK, 15, 14),      # beyond the decode bound, [K, N] rows: the FP8 tile
+    (17, 2048, 7168, "nk", SPLITK, 7, 8),        # [N, K] rows: split on the 128 x 128 LDS-DMA tile
+    (1024, 1024, 1024, "nk", MAIN, 8, 1), (1024, 1024, 2048, "nk", MAIN, 8, 1),
+    (2048, 2048, 2048, "nk", MAIN, 7, 1), (3072, 3072, 3072, "nk", MAIN, 15, 1),
+    (1024, 1024, 8192, "nk", SPLITK, 7, 4), (2048, 2048, 2048, "kn", MAIN, 15, 1),
+    (2048, 2048, 2049, "nk", MAIN, 15, 1)])     # odd K: no byte pairs
+def test_f8_rules(M, N, K, b, variant, tile, split):
+    p = plan8(M, N, K, b)
+    assert (p.variant, p.tile_id, p.split_k) == (variant, tile, split), (p.variant, p.tile_id, p.split_k)
+
+
+def test_f8_compute_unit_count_is_checked():
+    info = _lib.PlanInfo()
+    for cus in (0, 65537):
+        assert g.lib.gemm_f8_plan_cus(PA, 64, 1, PB, 1, 64, PC, 64, 64, 64, 64, 0, 0, cus, None,
+                                      ctypes.byref(info)) == -7
+    assert g.lib.gemm_f8_plan_cus(PA, 64, 1, PB, 1, 64, PC, 64, 64, 64, 64, 2, 0, 256, None,
+                                  ctypes.byref(info)) == -7        # format 2 does not exist
