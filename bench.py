@@ -394,9 +394,13 @@ def sweep_one(g, synth, dev, to_dev, i, name, m, n, k, bl, forced):
     with torch.cuda.stream(cap):
         g.gemm(a0, b0, out=c, workspace=ws, stream=cap, **opts)
     torch.cuda.synchronize()
-    # At least 4 calls per replay, so a large product is timed back to back
-    # (a replay of a single call measures a launch after an idle gap).
+    # Enough calls per replay that a replay holds about 1.5e13 FLOP (some
+    # 11 ms at the main kernel's rate; at most 1024 calls, at least 4): a
+    # replay of a few milliseconds runs partly after the idle gap that the
+    # wait between replays leaves, and read 10-15% under the steady rate
+    # (4096^3: 135 us per call against 119 back to back).
     reps = max(copies, 4) if byts * copies >= (1 << 28) else max(copies, 64)
+    reps = int(min(1024, max(reps, -(-1.5e13 // (2.0 * m * n * k)))))
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
         for r in range(reps):
