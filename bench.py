@@ -576,19 +576,23 @@ def main():
         ws1 = None
         if p1["workspace_bytes"]:
             ws1 = torch.empty(p1["workspace_bytes"] // 4 + 64, dtype=torch.float32, device=dev)
-        # One CUDA/HIP graph holds one call per copy of B, so the timing is GPU
-        # time per call (both launches and the gap between them), free of the
-        # Python wrapper's per-call host cost.
+        # One CUDA/HIP graph holds 25 passes of one call per copy of B (about
+        # 10 ms of calls), so the timing is GPU time per call (both launches
+        # and the gap between them) at the steady rate, free of the Python
+        # wrapper's per-call host cost and of the idle gap between replays.
         cap = torch.cuda.Stream(dev)
         with torch.cuda.stream(cap):
             g.gemm(a1, bs[0], out=c1, workspace=ws1, stream=cap)
         torch.cuda.synchronize()
         eager = c1.clone()
         graph = torch.cuda.CUDAGraph()
+        rounds = 25
         with torch.cuda.graph(graph, stream=cap):
-            for i in range(copies):
-                g.gemm(a1, bs[i], out=c1, workspace=ws1, stream=cap)
-        reps = max(1, args.skinny_reps // copies)
+            for rnd in range(rounds):
+                for i in range(copies):
+                    g.gemm(a1, bs[i], out=c1, workspace=ws1, stream=cap)
+        calls = rounds * copies
+        reps = max(3, args.skinny_reps // calls)
         per_call = []
         graph_ok = True
         for r in range(reps + 2):
@@ -601,7 +605,7 @@ def main():
             e1.synchronize()
             graph_ok = graph_ok and torch.equal(c1.view(torch.int16), eager.view(torch.int16))
             if r >= 2:
-                per_call.append(e0.elapsed_time(e1) / copies)
+                per_call.append(e0.elapsed_time(e1) / calls)
         per_call.sort()
         med1 = per_call[len(per_call) // 2]
         bytes1 = esz * (m1 * K + K * N) + 2.0 * m1 * N
@@ -614,7 +618,7 @@ def main():
                 "median_us": med1 * 1e3, "GBps": bytes1 / (med1 * 1e-3) / 1e9,
                 "frac_hbm": bytes1 / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "replays_match_eager": graph_ok,
-                "timing": f"HIP events around replays of a graph of {copies} calls "
+                "timing": f"HIP events around replays of a graph of {calls} calls ({rounds} passes over the copies) "
                           f"({reps} replays, median per call)"}
 
     skinny = decode_line("row")
